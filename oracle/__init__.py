@@ -1,0 +1,241 @@
+"""CPU oracle for the quantized decode matvec — TEST INFRASTRUCTURE ONLY.
+
+Thin ctypes wrapper over ``oracle.c`` (see ``oracle.h`` for the sources each
+function follows).  Only the tests, the smoke check and the benchmark's CPU
+baseline may import this package; the product library never does.
+
+All arguments are host numpy arrays.  Batched activations are looped here, one
+vector at a time, exactly as independent single-vector calls.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_SRC = os.path.join(_HERE, "oracle.c")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (-O2, no fast-math, no contraction)."""
+    if force or not os.path.exists(LIB_PATH):
+        tmp = LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+               "-Wall", "-Wextra", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True, cwd=_HERE)
+        os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+class _Cq(ctypes.Structure):
+    _fields_ = [("output", ctypes.c_int64), ("input", ctypes.c_int64),
+                ("input_padded", ctypes.c_int64), ("group", ctypes.c_int64),
+                ("bits", ctypes.c_int64), ("row_bytes", ctypes.c_int64),
+                ("packed", ctypes.c_void_p), ("norms", ctypes.c_void_p),
+                ("codebook", ctypes.c_void_p)]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+def use_library(path: str = None):
+    """Point the wrapper at another build of oracle.c (None: the default one).
+
+    The test suite uses this to run the pins against deliberately broken
+    copies of the oracle and confirm that each planted mistake is caught."""
+    global _lib
+    _lib = None if path is None else _load(path)
+
+
+def _load(path: str):
+    L = ctypes.CDLL(path)
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    CQ = ctypes.POINTER(_Cq)
+    L.oracle_f16.restype = ctypes.c_float
+    L.oracle_f16.argtypes = [ctypes.c_uint16]
+    L.oracle_fwht.restype = None
+    L.oracle_fwht.argtypes = [P, I64]
+    L.oracle_cq_index.restype = ctypes.c_uint32
+    L.oracle_cq_index.argtypes = [CQ, I64, I64]
+    L.oracle_cq_unpack_row.argtypes = [CQ, I64, P]
+    L.oracle_cq_prepare.argtypes = [CQ, P, P]
+    L.oracle_cq_matvec.argtypes = [CQ, P, I64, I64, P, P]
+    L.oracle_cq_dequantize_row.argtypes = [CQ, I64, P]
+    L.oracle_cq_gather.argtypes = [CQ, P, I64, P, P]
+    L.oracle_cq_dense_matvec.argtypes = [CQ, P, I64, I64, P]
+    L.oracle_e4m3.restype = ctypes.c_float
+    L.oracle_e4m3.argtypes = [ctypes.c_uint8]
+    L.oracle_e8m0.restype = ctypes.c_float
+    L.oracle_e8m0.argtypes = [ctypes.c_uint8]
+    L.oracle_f8_matvec.argtypes = [P, I64, I64, P, I64, I64, P, I64, I64, P, P]
+    for name in ("oracle_cq_unpack_row", "oracle_cq_prepare", "oracle_cq_matvec",
+                 "oracle_cq_dequantize_row", "oracle_cq_gather",
+                 "oracle_cq_dense_matvec", "oracle_f8_matvec"):
+        getattr(L, name).restype = ctypes.c_int
+    return L
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+class CqMatrix:
+    """Host-side CQ matrix: shape fields plus the packed, norm and codebook arrays."""
+
+    def __init__(self, output, input, input_padded, group, bits, row_bytes,
+                 packed, norms, codebook):
+        self.packed = np.ascontiguousarray(packed, dtype=np.uint8)
+        self.norms = np.ascontiguousarray(norms).view(np.uint16)
+        self.codebook = np.ascontiguousarray(codebook, dtype=np.float32)
+        self.output, self.input, self.input_padded = int(output), int(input), int(input_padded)
+        self.group, self.bits, self.row_bytes = int(group), int(bits), int(row_bytes)
+        self._s = _Cq(self.output, self.input, self.input_padded, self.group, self.bits,
+                      self.row_bytes, self.packed.ctypes.data, self.norms.ctypes.data,
+                      self.codebook.ctypes.data)
+
+    @classmethod
+    def from_case(cls, case):
+        s = case.shape
+        return cls(s.output, s.input, s.input_padded, s.group, s.bits, s.stride,
+                   case.packed, case.norms, case.codebook)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self._s)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its arguments (rc={rc})")
+
+
+def f16(h: int) -> float:
+    return lib().oracle_f16(int(h) & 0xFFFF)
+
+
+def f16_array(codes: np.ndarray) -> np.ndarray:
+    L = lib()
+    return np.array([L.oracle_f16(int(c)) for c in np.asarray(codes).ravel()],
+                    dtype=np.float32).reshape(np.shape(codes))
+
+
+def fwht(x: np.ndarray) -> np.ndarray:
+    y = np.array(x, dtype=np.float32, copy=True)
+    lib().oracle_fwht(_ptr(y), y.size)
+    return y
+
+
+def cq_index(m: CqMatrix, row: int, col: int) -> int:
+    return lib().oracle_cq_index(m.ref, row, col)
+
+
+def cq_unpack_row(m: CqMatrix, row: int) -> np.ndarray:
+    out = np.zeros(m.input_padded, dtype=np.uint8)
+    _check(lib().oracle_cq_unpack_row(m.ref, row, _ptr(out)), "cq_unpack_row")
+    return out
+
+
+def cq_prepare(m: CqMatrix, x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    xb = x.reshape(-1, m.input) if m.input else x.reshape(-1, 0)
+    out = np.zeros((xb.shape[0], m.input_padded), dtype=np.float32)
+    for b in range(xb.shape[0]):
+        xv = np.ascontiguousarray(xb[b])
+        ov = out[b]
+        _check(lib().oracle_cq_prepare(m.ref, _ptr(xv), ov.ctypes.data_as(ctypes.c_void_p)),
+               "cq_prepare")
+    return out.reshape(x.shape[:-1] + (m.input_padded,)) if x.ndim > 1 else out[0]
+
+
+def cq_matvec(m: CqMatrix, p: np.ndarray, row_begin: int = 0, row_count=None):
+    """Returns (y, mag), each float64 [batch][row_count] (or 1-D for a 1-D p)."""
+    if row_count is None:
+        row_count = m.output - row_begin
+    p = np.ascontiguousarray(p, dtype=np.float32)
+    pb = p.reshape(-1, m.input_padded)
+    y = np.zeros((pb.shape[0], row_count), dtype=np.float64)
+    mag = np.zeros_like(y)
+    for b in range(pb.shape[0]):
+        pv = np.ascontiguousarray(pb[b])
+        _check(lib().oracle_cq_matvec(m.ref, _ptr(pv), row_begin, row_count,
+                                      y[b].ctypes.data_as(ctypes.c_void_p),
+                                      mag[b].ctypes.data_as(ctypes.c_void_p)), "cq_matvec")
+    if p.ndim == 1:
+        return y[0], mag[0]
+    return y, mag
+
+
+def cq_dequantize_row(m: CqMatrix, row: int) -> np.ndarray:
+    out = np.zeros(m.input, dtype=np.float32)
+    _check(lib().oracle_cq_dequantize_row(m.ref, row, _ptr(out)), "cq_dequantize_row")
+    return out
+
+
+def cq_gather(m: CqMatrix, ids: np.ndarray):
+    """Returns (out float32 [n][input], gmag float64 [n][input])."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    out = np.zeros((ids.size, m.input), dtype=np.float32)
+    gmag = np.zeros((ids.size, m.input), dtype=np.float64)
+    _check(lib().oracle_cq_gather(m.ref, _ptr(ids), ids.size, _ptr(out), _ptr(gmag)), "cq_gather")
+    return out, gmag
+
+
+def cq_dense_matvec(m: CqMatrix, x: np.ndarray, row_begin: int = 0, row_count=None):
+    if row_count is None:
+        row_count = m.output - row_begin
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    xb = x.reshape(-1, m.input)
+    y = np.zeros((xb.shape[0], row_count), dtype=np.float64)
+    for b in range(xb.shape[0]):
+        xv = np.ascontiguousarray(xb[b])
+        _check(lib().oracle_cq_dense_matvec(m.ref, _ptr(xv), row_begin, row_count,
+                                            y[b].ctypes.data_as(ctypes.c_void_p)),
+               "cq_dense_matvec")
+    return y[0] if x.ndim == 1 else y
+
+
+def e4m3(code: int) -> float:
+    return lib().oracle_e4m3(int(code) & 0xFF)
+
+
+def e4m3_all() -> np.ndarray:
+    """Decoded value of every E4M3 code 0..255, as float32."""
+    L = lib()
+    return np.array([L.oracle_e4m3(c) for c in range(256)], dtype=np.float32)
+
+
+def e8m0_all() -> np.ndarray:
+    L = lib()
+    return np.array([L.oracle_e8m0(c) for c in range(256)], dtype=np.float32)
+
+
+def f8_matvec(w, R, C, s, SR, SC, x, row_begin: int = 0, row_count=None):
+    """Returns (y, mag), float64 [batch][row_count] (or 1-D for a 1-D x)."""
+    if row_count is None:
+        row_count = R - row_begin
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.uint8)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    xb = x.reshape(-1, C)
+    y = np.zeros((xb.shape[0], row_count), dtype=np.float64)
+    mag = np.zeros_like(y)
+    for b in range(xb.shape[0]):
+        xv = np.ascontiguousarray(xb[b])
+        _check(lib().oracle_f8_matvec(_ptr(w), R, C, _ptr(s), SR, SC, _ptr(xv), row_begin,
+                                      row_count, y[b].ctypes.data_as(ctypes.c_void_p),
+                                      mag[b].ctypes.data_as(ctypes.c_void_p)), "f8_matvec")
+    if x.ndim == 1:
+        return y[0], mag[0]
+    return y, mag

@@ -1,0 +1,269 @@
+/*
+ * CPU oracle for the quantized decode matvec — TEST INFRASTRUCTURE ONLY.
+ * See oracle.h for the sources, the precision rules and the contract.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- O1 -- */
+/* [P3] §3 "Decode FP16 control tensors": rebuild the fp32 bit pattern from
+ * sign, 5-bit exponent and 10-bit mantissa.  Zero exponent: signed zero, or a
+ * subnormal renormalized by shifting the mantissa up until its leading one
+ * reaches the hidden-bit position; all-ones exponent: infinity or NaN with the
+ * mantissa carried over; otherwise rebias the exponent from 15 to 127. */
+float oracle_f16(uint16_t h)
+{
+    uint32_t sign = ((uint32_t)h & 0x8000u) << 16;
+    int32_t exponent = (h >> 10) & 0x1f;
+    uint32_t mantissa = h & 0x3ffu;
+    uint32_t bits32;
+    if (exponent == 0) {
+        if (mantissa == 0) {
+            bits32 = sign;
+        } else {
+            int32_t e = 127 - 15 + 1;
+            while ((mantissa & 0x400u) == 0) {
+                mantissa <<= 1;
+                e--;
+            }
+            bits32 = sign | ((uint32_t)e << 23) | ((mantissa & 0x3ffu) << 13);
+        }
+    } else if (exponent == 0x1f) {
+        bits32 = sign | 0x7f800000u | (mantissa << 13);
+    } else {
+        bits32 = sign | ((uint32_t)(exponent - 15 + 127) << 23) | (mantissa << 13);
+    }
+    float f;
+    memcpy(&f, &bits32, sizeof f);
+    return f;
+}
+
+/* ------------------------------------------------------------ O3 core -- */
+/* [P1] §1: for stride = 1, 2, 4, ... < n, pair element j of each 2*stride
+ * block with element j + stride and replace them by their sum and their
+ * difference.  Each store rounds to fp32 (a Float32Array on the page). */
+void oracle_fwht(float *x, int64_t n)
+{
+    for (int64_t stride = 1; stride < n; stride <<= 1) {
+        for (int64_t base = 0; base < n; base += stride << 1) {
+            for (int64_t j = 0; j < stride; j++) {
+                float a = x[base + j];
+                float b = x[base + j + stride];
+                x[base + j] = a + b;
+                x[base + j + stride] = a - b;
+            }
+        }
+    }
+}
+
+static int is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+static int cq_ok(const oracle_cq *m)
+{
+    if (!m || !m->packed || !m->norms || !m->codebook) return 0;
+    if (m->bits < 2 || m->bits > 5) return 0;
+    if (!is_pow2(m->group)) return 0;
+    if (m->input < 0 || m->input > m->input_padded) return 0;
+    if (m->input_padded <= 0 || m->input_padded % m->group != 0) return 0;
+    if (m->output < 0) return 0;
+    if (m->row_bytes * 8 < m->input_padded * m->bits) return 0;
+    return 1;
+}
+
+/* ---------------------------------------------------------------- O2 -- */
+/* Index bit j of column col is bit (bits*col + j) of the row's byte stream,
+ * where bit t lives in byte t/8 at position t%8 (least significant first).
+ * For 2-bit this is the crumb rule of [P1] §3 (crumb k of a byte is
+ * (byte >> 2k) & 3); for 4-bit the low nibble holds the even column. */
+uint32_t oracle_cq_index(const oracle_cq *m, int64_t row, int64_t col)
+{
+    const uint8_t *r = m->packed + row * m->row_bytes;
+    uint32_t idx = 0;
+    for (int64_t j = 0; j < m->bits; j++) {
+        int64_t t = m->bits * col + j;
+        uint32_t bit = (r[t >> 3] >> (t & 7)) & 1u;
+        idx |= bit << j;
+    }
+    return idx;
+}
+
+int oracle_cq_unpack_row(const oracle_cq *m, int64_t row, uint8_t *idx)
+{
+    if (!cq_ok(m) || row < 0 || row >= m->output) return -1;
+    for (int64_t c = 0; c < m->input_padded; c++)
+        idx[c] = (uint8_t)oracle_cq_index(m, row, c);
+    return 0;
+}
+
+/* Multiply by 1/sqrt(group) the way the page does: the scale is a double,
+ * the product is formed in double and stored back to fp32. */
+static float scale_store(float v, int64_t group)
+{
+    double scale = 1.0 / sqrt((double)group);
+    return (float)((double)v * scale);
+}
+
+/* ---------------------------------------------------------------- O3 -- */
+/* [P1] §2: zero-pad to input_padded, transform every group, normalize. */
+int oracle_cq_prepare(const oracle_cq *m, const float *x, float *p)
+{
+    if (!cq_ok(m)) return -1;
+    for (int64_t k = 0; k < m->input_padded; k++) p[k] = k < m->input ? x[k] : 0.0f;
+    for (int64_t start = 0; start < m->input_padded; start += m->group) {
+        oracle_fwht(p + start, m->group);
+        for (int64_t k = 0; k < m->group; k++) p[start + k] = scale_store(p[start + k], m->group);
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------- O4 -- */
+/* [P1] §3: for each row and group, the group's sum of codebook[index] times
+ * prepared[column], times the fp16 norm of (row, group), added to the row
+ * sum.  JavaScript sums are doubles: accumulate in fp64. */
+int oracle_cq_matvec(const oracle_cq *m, const float *p, int64_t row_begin,
+                     int64_t row_count, double *y, double *mag)
+{
+    if (!cq_ok(m) || row_begin < 0 || row_count < 0 || row_begin + row_count > m->output)
+        return -1;
+    int64_t n_groups = m->input_padded / m->group;
+    for (int64_t i = 0; i < row_count; i++) {
+        int64_t row = row_begin + i;
+        double acc = 0.0, amag = 0.0;
+        for (int64_t g = 0; g < n_groups; g++) {
+            double part = 0.0, apart = 0.0;
+            for (int64_t k = g * m->group; k < (g + 1) * m->group; k++) {
+                double term = (double)m->codebook[oracle_cq_index(m, row, k)] * (double)p[k];
+                part += term;
+                apart += fabs(term);
+            }
+            double norm = (double)oracle_f16(m->norms[row * n_groups + g]);
+            acc += norm * part;
+            amag += fabs(norm) * apart;
+        }
+        if (y) y[i] = acc;
+        if (mag) mag[i] = amag;
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------- O5 -- */
+/* [P1] "Row gather": decode one group's levels multiplied by the norm
+ * (an fp32 product), run the normalized FWHT (the unnormalized butterfly,
+ * then the same 1/sqrt(group) store as prepare), keep the unpadded columns. */
+int oracle_cq_dequantize_row(const oracle_cq *m, int64_t row, float *out)
+{
+    if (!cq_ok(m) || row < 0 || row >= m->output) return -1;
+    int64_t n_groups = m->input_padded / m->group;
+    float *t = (float *)malloc(sizeof(float) * (size_t)m->input_padded);
+    if (!t) return -1;
+    for (int64_t g = 0; g < n_groups; g++) {
+        float norm = oracle_f16(m->norms[row * n_groups + g]);
+        float *tg = t + g * m->group;
+        for (int64_t k = 0; k < m->group; k++)
+            tg[k] = m->codebook[oracle_cq_index(m, row, g * m->group + k)] * norm;
+        oracle_fwht(tg, m->group);
+        for (int64_t k = 0; k < m->group; k++) tg[k] = scale_store(tg[k], m->group);
+    }
+    memcpy(out, t, sizeof(float) * (size_t)m->input);
+    free(t);
+    return 0;
+}
+
+/* ---------------------------------------------------------------- O6 -- */
+int oracle_cq_gather(const oracle_cq *m, const int32_t *ids, int64_t n,
+                     float *out, double *gmag)
+{
+    if (!cq_ok(m) || n < 0) return -1;
+    int64_t n_groups = m->input_padded / m->group;
+    double inv = 1.0 / sqrt((double)m->group);
+    for (int64_t i = 0; i < n; i++) {
+        if (ids[i] < 0 || ids[i] >= m->output) return -1;
+        if (oracle_cq_dequantize_row(m, ids[i], out + i * m->input) != 0) return -1;
+        if (!gmag) continue;
+        for (int64_t g = 0; g < n_groups; g++) {
+            double norm = fabs((double)oracle_f16(m->norms[(int64_t)ids[i] * n_groups + g]));
+            double s = 0.0;
+            for (int64_t k = g * m->group; k < (g + 1) * m->group; k++)
+                s += fabs((double)m->codebook[oracle_cq_index(m, ids[i], k)]) * norm;
+            for (int64_t k = g * m->group; k < (g + 1) * m->group && k < m->input; k++)
+                gmag[i * m->input + k] = s * inv;
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------- O7 -- */
+int oracle_cq_dense_matvec(const oracle_cq *m, const float *x, int64_t row_begin,
+                           int64_t row_count, double *y)
+{
+    if (!cq_ok(m) || row_begin < 0 || row_count < 0 || row_begin + row_count > m->output)
+        return -1;
+    float *row = (float *)malloc(sizeof(float) * (size_t)(m->input > 0 ? m->input : 1));
+    if (!row) return -1;
+    for (int64_t i = 0; i < row_count; i++) {
+        if (oracle_cq_dequantize_row(m, row_begin + i, row) != 0) { free(row); return -1; }
+        double acc = 0.0;
+        for (int64_t c = 0; c < m->input; c++) acc += (double)row[c] * (double)x[c];
+        y[i] = acc;
+    }
+    free(row);
+    return 0;
+}
+
+/* ---------------------------------------------------------------- O8 -- */
+/* [P4] Step 1 / Step 4: sign bit, 4-bit exponent e, 3-bit mantissa m.
+ * e = 0 is subnormal: (m/8) * 2^(1-7); otherwise (1 + m/8) * 2^(e-7).
+ * The e = 15 clamp bounds the magnitude at 448, so only mantissa 7 (which
+ * would give 480) changes. */
+float oracle_e4m3(uint8_t code)
+{
+    int s = code >> 7;
+    int e = (code >> 3) & 15;
+    int mant = code & 7;
+    double v;
+    if (e == 0)
+        v = ldexp((double)mant / 8.0, 1 - 7);
+    else
+        v = ldexp(1.0 + (double)mant / 8.0, e - 7);
+    if (v > 448.0) v = 448.0;
+    return (float)(s ? -v : v);
+}
+
+/* ---------------------------------------------------------------- O9 -- */
+/* [P4] Step 1: an E8M0 block scale is the power of two 2^(e-127); the byte
+ * 255 has no power-of-two meaning and decodes to NaN. */
+float oracle_e8m0(uint8_t e)
+{
+    if (e == 255) return NAN;
+    return (float)ldexp(1.0, (int)e - 127);
+}
+
+/* --------------------------------------------------------------- O10 -- */
+/* [P4] Step 1: element (r, c) of the weight takes the scale
+ * S[floor(r*SR/R)][floor(c*SC/C)]; the dot runs over all C columns. */
+int oracle_f8_matvec(const uint8_t *w, int64_t R, int64_t C, const uint8_t *s,
+                     int64_t SR, int64_t SC, const float *x, int64_t row_begin,
+                     int64_t row_count, double *y, double *mag)
+{
+    if (!w || !s || !x || R < 0 || C < 0 || SR < 1 || SC < 1 || SR > (R > 0 ? R : 1) ||
+        SC > (C > 0 ? C : 1) || row_begin < 0 || row_count < 0 || row_begin + row_count > R)
+        return -1;
+    for (int64_t i = 0; i < row_count; i++) {
+        int64_t r = row_begin + i;
+        int64_t sr = (r * SR) / R;
+        double acc = 0.0, amag = 0.0;
+        for (int64_t c = 0; c < C; c++) {
+            int64_t sc = (c * SC) / C;
+            double term = (double)oracle_e4m3(w[r * C + c]) *
+                          (double)oracle_e8m0(s[sr * SC + sc]) * (double)x[c];
+            acc += term;
+            amag += fabs(term);
+        }
+        if (y) y[i] = acc;
+        if (mag) mag[i] = amag;
+    }
+    return 0;
+}

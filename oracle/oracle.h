@@ -1,0 +1,106 @@
+/*
+ * CPU oracle for the quantized decode matvec — TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct C implementation of what the HIP path
+ * computes.  Only the test suite, the smoke check and the benchmark's CPU
+ * baseline leg may load it; the product library never links, loads or calls
+ * it, and it shares no header, helper, table or constant with the HIP path.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [P1] "Inference engine, part 2: kernels and token step" — §1 Fast
+ *        Walsh–Hadamard transform, §2 Prepare an activation for CQ, §3 Dot
+ *        packed rows directly, "Row gather".
+ *   [P3] "Inference engine, part 1: loader and tokenizer" — §3 Decode FP16
+ *        control tensors, §4 Retain packed matrices.
+ *   [P4] "attention + tokenizer + sampling: the path to real text
+ *        (milestone 6)" — "Step 1 done: F8 kernel", "Step 4 done: I8 +
+ *        F8_E4M3 SIMD matvecs".
+ *
+ * Precision: the pages' arrays are Float32Array (each store rounds to fp32)
+ * and their scalars are JavaScript numbers (fp64).  The oracle keeps exactly
+ * that: fp32 transform stages, fp64 scale multiply then one rounding, fp64
+ * accumulation of dots.  Built with -O2 -ffp-contract=off, no fast-math.
+ *
+ * Every function has a pin in the CPU test suite (no function is "parity
+ * unpinned").
+ *
+ * Return values: 0 on success, -1 on an invalid shape.
+ */
+#ifndef BQD_ORACLE_H
+#define BQD_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A CQ (codebook-quantized) matrix, as the record in [P3] §4. */
+typedef struct oracle_cq {
+    int64_t output;          /* rows                                        */
+    int64_t input;           /* unpadded columns                            */
+    int64_t input_padded;    /* stored (transform-domain) columns           */
+    int64_t group;           /* transform group size, a power of two        */
+    int64_t bits;            /* 2, 3, 4 or 5                                */
+    int64_t row_bytes;       /* stride between packed rows                  */
+    const uint8_t *packed;   /* [output][row_bytes]                         */
+    const uint16_t *norms;   /* fp16 bits [output][input_padded / group]    */
+    const float *codebook;   /* [1 << bits]                                 */
+} oracle_cq;
+
+/* O1: fp16 bit pattern -> fp32 value ([P3] §3). */
+float oracle_f16(uint16_t h);
+
+/* O3 core: unnormalized in-place Walsh–Hadamard butterfly over n floats,
+ * stride ascending, butterflies (a + b, a - b) in fp32 ([P1] §1). */
+void oracle_fwht(float *x, int64_t n);
+
+/* O2: the codebook index of (row, col): bits [bits*col, bits*col + bits) of
+ * the row's little-endian bit stream, read one bit at a time. */
+uint32_t oracle_cq_index(const oracle_cq *m, int64_t row, int64_t col);
+
+/* O2 for a whole row: idx[col] for col < input_padded. */
+int oracle_cq_unpack_row(const oracle_cq *m, int64_t row, uint8_t *idx);
+
+/* O3: prepare one activation vector ([P1] §2): zero-pad x[input] to
+ * p[input_padded], FWHT each group, multiply by 1/sqrt(group). */
+int oracle_cq_prepare(const oracle_cq *m, const float *x, float *p);
+
+/* O4: the method's packed-row dot ([P1] §3) on a prepared vector, rows
+ * [row_begin, row_begin + row_count).  y[i] is the row sum; mag[i] is
+ * sum_g |norm| * sum_k |codebook[idx] * p[k]| (the magnitude the tolerance
+ * scales with).  Either output may be NULL. */
+int oracle_cq_matvec(const oracle_cq *m, const float *p, int64_t row_begin,
+                     int64_t row_count, double *y, double *mag);
+
+/* O5: dequantizeRow ([P1] "Row gather"): per group, codebook value times
+ * norm (fp32), FWHT, times 1/sqrt(group); the first `input` columns. */
+int oracle_cq_dequantize_row(const oracle_cq *m, int64_t row, float *out);
+
+/* O6: gather rows ids[0..n) into out[n][input]; gmag[n][input] (may be NULL)
+ * is (1/sqrt(group)) * sum over the column's group of |codebook * norm|. */
+int oracle_cq_gather(const oracle_cq *m, const int32_t *ids, int64_t n,
+                     float *out, double *gmag);
+
+/* O7: the plain definition ([P1] "Row gather" identity): y[i] = sum over
+ * c < input of dequantizeRow(row)[c] * x[c], in fp64. */
+int oracle_cq_dense_matvec(const oracle_cq *m, const float *x, int64_t row_begin,
+                           int64_t row_count, double *y);
+
+/* O8: FP8 E4M3 code -> value ([P4] Step 1): e = 0 subnormal, values above
+ * 448 clamped to 448, sign kept (0x80 is -0.0). */
+float oracle_e4m3(uint8_t code);
+
+/* O9: E8M0 exponent byte -> 2^(e - 127); 255 -> NaN. */
+float oracle_e8m0(uint8_t e);
+
+/* O10: y[i] = sum_c e4m3(W[r][c]) * e8m0(S[r*SR/R][c*SC/C]) * x[c] for
+ * r = row_begin + i, indices by 64-bit floor division; mag likewise with
+ * absolute values.  Either output may be NULL. */
+int oracle_f8_matvec(const uint8_t *w, int64_t R, int64_t C, const uint8_t *s,
+                     int64_t SR, int64_t SC, const float *x, int64_t row_begin,
+                     int64_t row_count, double *y, double *mag);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,146 @@
+"""Seeded synthetic inputs for the quantized decode matvec workloads.
+
+This module only draws random arrays in the layouts the method reads.  It holds
+none of the method's arithmetic (no unpacking, no transform, no decode, no dot
+products), so the HIP path and the CPU oracle can both consume its output
+without sharing any computation.
+
+Layouts (all host numpy arrays, C-contiguous):
+
+* CQ matrix ("Inference engine, part 1: loader and tokenizer", section 4
+  "Retain packed matrices"): ``packed`` uint8 ``[output][row_bytes]`` (a
+  little-endian bit stream of ``bits``-wide codebook indices per row, one index
+  per padded input column), ``norms`` uint16 fp16 bit patterns
+  ``[output][input_padded // group]``, ``codebook`` float32 ``[2**bits]``.
+* Activations: float32 ``[batch][input]``.
+* FP8 head ("attention + tokenizer + sampling: the path to real text",
+  "Step 1 done: F8 kernel"): ``w`` uint8 E4M3 codes ``[R][C]``, ``scale``
+  uint8 E8M0 exponents ``[SR][SC]``, activation float32 ``[batch][C]``.
+
+Recipe (per case, a fresh ``numpy.random.default_rng(seed)``; draw order is
+fixed): 1. packed bytes or F8 weight bytes, uniform over all 256 byte values;
+2. norms (uniform in [0.5, 2] rounded to fp16) or scale exponents (uniform
+integers in [120, 130]); 3. activations, standard normal float32; 4. gather row
+ids, uniform in [0, output) with replacement.  Uniform random bytes are uniform
+random indices because every row's index bits tile its bytes exactly in the
+benchmark shapes; bits past the last index in a row (padding) stay random and
+must be ignored by a decoder.  The codebook is deterministic: the standard
+normal quantiles Phi^-1((i + 0.5) / 2**bits), evaluated in double and rounded
+once to float32.
+"""
+from __future__ import annotations
+
+import dataclasses
+import statistics
+
+import numpy as np
+
+
+def codebook(bits: int) -> np.ndarray:
+    """Standard-normal quantile codebook with 2**bits float32 entries."""
+    n = 1 << bits
+    nd = statistics.NormalDist()
+    return np.array([nd.inv_cdf((i + 0.5) / n) for i in range(n)],
+                    dtype=np.float64).astype(np.float32)
+
+
+def min_row_bytes(input_padded: int, bits: int) -> int:
+    """Smallest row stride that holds ``input_padded`` indices of ``bits`` bits."""
+    return (input_padded * bits + 7) // 8
+
+
+@dataclasses.dataclass(frozen=True)
+class CqShape:
+    output: int
+    input: int
+    input_padded: int
+    group: int
+    bits: int
+    row_bytes: int = 0          # 0 -> the minimum
+
+    @property
+    def stride(self) -> int:
+        return self.row_bytes or min_row_bytes(self.input_padded, self.bits)
+
+    @property
+    def n_groups(self) -> int:
+        return self.input_padded // self.group
+
+
+@dataclasses.dataclass
+class CqCase:
+    shape: CqShape
+    packed: np.ndarray      # uint8 [output][row_bytes]
+    norms: np.ndarray       # uint16 (fp16 bits) [output][n_groups]
+    codebook: np.ndarray    # float32 [2**bits]
+    x: np.ndarray           # float32 [batch][input]
+    ids: np.ndarray         # int32 [n_ids]
+
+
+@dataclasses.dataclass
+class F8Case:
+    R: int
+    C: int
+    SR: int
+    SC: int
+    w: np.ndarray           # uint8 [R][C]
+    scale: np.ndarray       # uint8 [SR][SC]
+    x: np.ndarray           # float32 [batch][C]
+
+
+def _random_bytes(rng: np.random.Generator, shape) -> np.ndarray:
+    return rng.integers(0, 256, size=shape, dtype=np.uint8)
+
+
+def make_cq(shape: CqShape, seed: int, batch: int = 1, n_ids: int = 0,
+            norm_range=(0.5, 2.0)) -> CqCase:
+    rng = np.random.default_rng(seed)
+    packed = _random_bytes(rng, (shape.output, shape.stride))
+    norms = rng.uniform(norm_range[0], norm_range[1],
+                        (shape.output, shape.n_groups)).astype(np.float16).view(np.uint16)
+    x = rng.standard_normal((batch, shape.input), dtype=np.float32)
+    ids = rng.integers(0, shape.output, size=n_ids, dtype=np.int64).astype(np.int32) \
+        if n_ids else np.zeros(0, dtype=np.int32)
+    return CqCase(shape, packed, np.ascontiguousarray(norms), codebook(shape.bits), x, ids)
+
+
+def make_f8(R: int, C: int, SR: int, SC: int, seed: int, batch: int = 1,
+            exp_range=(120, 130)) -> F8Case:
+    rng = np.random.default_rng(seed)
+    w = _random_bytes(rng, (R, C))
+    scale = rng.integers(exp_range[0], exp_range[1] + 1, size=(SR, SC), dtype=np.int64).astype(np.uint8)
+    x = rng.standard_normal((batch, C), dtype=np.float32)
+    return F8Case(R, C, SR, SC, w, scale, x)
+
+
+# The five workloads.  Each is a list of (name, builder) pairs; a builder takes
+# no arguments and returns a case.  Seeds restart per case.
+C1 = CqShape(output=256, input=200, input_padded=256, group=64, bits=2)
+C2_3 = CqShape(output=2048, input=512, input_padded=512, group=128, bits=3)
+C2_5 = CqShape(output=2048, input=512, input_padded=512, group=128, bits=5)
+C3 = CqShape(output=65536, input=512, input_padded=512, group=128, bits=4)
+C4 = CqShape(output=16384, input=4096, input_padded=4096, group=256, bits=4)
+HEAD = dict(R=246272, C=4096, SR=1924, SC=32)
+WKV = dict(R=512, C=4096, SR=4, SC=32)
+C3_GATHER_IDS = 4096
+
+
+def config_cases(i: int, batch8: bool = True):
+    """Cases of workload ``i`` (1-based), as (name, zero-argument builder)."""
+    if i == 1:
+        return [("cq2_256x200", lambda: make_cq(C1, seed=0))]
+    if i == 2:
+        return [("cq3_2048x512", lambda: make_cq(C2_3, seed=1)),
+                ("cq5_2048x512", lambda: make_cq(C2_5, seed=1))]
+    if i == 3:
+        return [("cq4_65536x512_vocab_gather",
+                 lambda: make_cq(C3, seed=2, n_ids=C3_GATHER_IDS))]
+    if i == 4:
+        out = [("cq4_16384x4096_b1", lambda: make_cq(C4, seed=3))]
+        if batch8:
+            out.append(("cq4_16384x4096_b8", lambda: make_cq(C4, seed=3, batch=8)))
+        return out
+    if i == 5:
+        return [("f8_head_246272x4096", lambda: make_f8(**HEAD, seed=4)),
+                ("f8_wkv_512x4096", lambda: make_f8(**WKV, seed=4))]
+    raise ValueError(f"no workload {i}")

@@ -1,0 +1,372 @@
+"""Pins of the CPU oracle to facts the pages and mathematics fix.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with a
+value printed on the pages (golden files, each cited in its header), a closed
+form, a textbook or library routine, or exact rational arithmetic on tiny
+inputs.  None of them re-types the oracle's own code: the checks go through
+numpy/scipy/torch routines or through closed forms.  ``tests/test_oracle_pins``
+runs them against the oracle; ``tests/test_oracle_mutants`` runs them against
+copies of the oracle with planted mistakes and expects each copy to fail one.
+"""
+from __future__ import annotations
+
+import math
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+import scipy.linalg
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ------------------------------------------------------------ test helpers --
+def pack_indices(idx: np.ndarray, bits: int, row_bytes: int) -> np.ndarray:
+    """Independent packer: numpy's little-endian bit packing of the index bits."""
+    idx = np.asarray(idx, dtype=np.uint32)
+    R, n = idx.shape
+    planes = ((idx[:, :, None] >> np.arange(bits, dtype=np.uint32)) & 1).astype(np.uint8)
+    stream = planes.reshape(R, n * bits)
+    packed = np.packbits(stream, axis=1, bitorder="little")
+    out = np.zeros((R, row_bytes), dtype=np.uint8)
+    out[:, :packed.shape[1]] = packed
+    return out
+
+
+def unpack_indices(packed: np.ndarray, bits: int, n: int) -> np.ndarray:
+    """Independent unpacker: numpy's little-endian bit unpacking."""
+    stream = np.unpackbits(packed, axis=1, bitorder="little")[:, :n * bits]
+    planes = stream.reshape(packed.shape[0], n, bits).astype(np.uint32)
+    return (planes << np.arange(bits, dtype=np.uint32)).sum(axis=2)
+
+
+def f16_np(norms: np.ndarray) -> np.ndarray:
+    return np.asarray(norms, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def dense_transform_weights(case) -> np.ndarray:
+    """norm[r, group(c)] * codebook[idx(r, c)] in float64 (transform domain)."""
+    s = case.shape
+    idx = unpack_indices(case.packed, s.bits, s.input_padded)
+    norm = np.repeat(f16_np(case.norms), s.group, axis=1)
+    return norm * case.codebook.astype(np.float64)[idx]
+
+
+def block_hadamard(n: int, g: int) -> np.ndarray:
+    """Block-diagonal Sylvester Hadamard matrix (scipy), normalized by 1/sqrt(g)."""
+    H = scipy.linalg.hadamard(g).astype(np.float64) / math.sqrt(g)
+    return scipy.linalg.block_diag(*([H] * (n // g)))
+
+
+def _read_table(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def small_cases():
+    """Small CQ shapes spanning every bit width, ragged inputs and padded rows."""
+    shapes = [
+        synth.CqShape(5, 3, 4, 4, 2),
+        synth.CqShape(7, 13, 16, 4, 3),
+        synth.CqShape(6, 30, 32, 8, 5),
+        synth.CqShape(9, 64, 64, 16, 4, row_bytes=40),
+        synth.CqShape(4, 100, 128, 32, 3, row_bytes=53),
+        synth.CqShape(3, 200, 256, 64, 2),
+        synth.CqShape(4, 250, 256, 128, 5),
+        synth.CqShape(3, 256, 256, 256, 4),
+    ]
+    return [synth.make_cq(s, seed=100 + i, batch=2) for i, s in enumerate(shapes)]
+
+
+# ------------------------------------------------------------------- pins --
+def pin_f16_golden():
+    for code, bits, _ in (r[:2] + [r[2:]] for r in _read_table("f16_anchors.txt")):
+        v = oracle.f16(int(code, 16))
+        if bits == "nan":
+            assert math.isnan(v), code
+        else:
+            got = struct.unpack("<I", struct.pack("<f", v))[0]
+            assert got == int(bits, 16), (code, hex(got), bits)
+
+
+def pin_f16_all_codes():
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.f16_array(codes)
+    ref = codes.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def pin_fwht_hadamard4_golden():
+    H = np.array([[int(v) for v in r] for r in _read_table("hadamard4.txt")], dtype=np.float32)
+    for i in range(4):
+        e = np.zeros(4, dtype=np.float32)
+        e[i] = 1
+        assert np.array_equal(oracle.fwht(e), H[i])
+
+
+def pin_fwht_sylvester():
+    rng = np.random.default_rng(7)
+    for n in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+        H = scipy.linalg.hadamard(n)
+        for j in range(n):
+            e = np.zeros(n, dtype=np.float32)
+            e[j] = 1
+            assert np.array_equal(oracle.fwht(e), H[:, j].astype(np.float32)), (n, j)
+        x = rng.integers(-50, 51, n).astype(np.float32)
+        assert np.array_equal(oracle.fwht(x), (H @ x.astype(np.int64)).astype(np.float32))
+
+
+def pin_fwht_involution():
+    rng = np.random.default_rng(8)
+    for n in (2, 8, 64, 256, 1024):
+        x = rng.integers(-100, 101, n).astype(np.float32)
+        assert np.array_equal(oracle.fwht(oracle.fwht(x)), (n * x).astype(np.float32))
+
+
+def pin_crumb_order_golden():
+    for row in _read_table("crumb_order.txt"):
+        byte = int(row[0], 16)
+        m = oracle.CqMatrix(1, 4, 4, 4, 2, 1, np.array([[byte]], np.uint8),
+                            np.zeros((1, 1), np.uint16), synth.codebook(2))
+        assert [oracle.cq_index(m, 0, c) for c in range(4)] == [int(v) for v in row[1:]], row
+
+
+def pin_crumb_rule_all_bytes():
+    cb = synth.codebook(2)
+    packed = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    m = oracle.CqMatrix(1, 1024, 1024, 4, 2, 256, packed, np.zeros((1, 256), np.uint16), cb)
+    idx = oracle.cq_unpack_row(m, 0)
+    for byte in range(256):
+        for crumb in range(4):
+            assert idx[4 * byte + crumb] == (byte >> (crumb * 2)) & 3
+
+
+def pin_nibble_order():
+    packed = np.array([[0xBA, 0x01]], np.uint8)
+    m = oracle.CqMatrix(1, 4, 4, 4, 4, 2, packed, np.zeros((1, 1), np.uint16), synth.codebook(4))
+    assert list(oracle.cq_unpack_row(m, 0)) == [0xA, 0xB, 0x1, 0x0]
+
+
+def pin_index_roundtrip():
+    rng = np.random.default_rng(9)
+    for bits in (2, 3, 4, 5):
+        for n in (1, 3, 8, 13, 24, 40, 64, 100):
+            rb = (n * bits + 7) // 8 + int(rng.integers(0, 3))
+            idx = rng.integers(0, 1 << bits, (3, n))
+            packed = pack_indices(idx, bits, rb)
+            # padding bits past the last index hold noise the decoder must ignore
+            tail_bits = rb * 8 - n * bits
+            if tail_bits:
+                noise = pack_indices(rng.integers(0, 2, (3, rb * 8)), 1, rb)
+                keep = pack_indices(np.concatenate([np.ones((3, n * bits)), np.zeros((3, tail_bits))], 1), 1, rb)
+                packed = (packed & keep) | (noise & ~keep)
+            m = oracle.CqMatrix(3, n, n, 1, bits, rb, packed, np.zeros((3, n), np.uint16),
+                                synth.codebook(bits))
+            for r in range(3):
+                assert np.array_equal(oracle.cq_unpack_row(m, r), idx[r]), (bits, n, r)
+
+
+def pin_prepare_one_hot():
+    for g, n_pad, inp in ((4, 8, 6), (64, 256, 200), (128, 512, 512), (256, 512, 300)):
+        m = oracle.CqMatrix(1, inp, n_pad, g, 4, n_pad, np.zeros((1, n_pad), np.uint8),
+                            np.zeros((1, n_pad // g), np.uint16), synth.codebook(4))
+        scale = 1.0 / math.sqrt(g)
+        for j in sorted({0, 1, g - 1, inp // 2, inp - 1}):
+            x = np.zeros(inp, np.float32)
+            x[j] = 1.0
+            p = oracle.cq_prepare(m, x)
+            g0 = (j // g) * g
+            ref = np.zeros(n_pad, np.float32)
+            for k in range(g):
+                sign = -1.0 if bin((j - g0) & k).count("1") % 2 else 1.0
+                ref[g0 + k] = np.float32(sign * scale)
+            assert np.array_equal(p, ref), (g, j)
+
+
+def pin_prepare_vs_scipy():
+    for case in small_cases():
+        s = case.shape
+        m = oracle.CqMatrix.from_case(case)
+        xp = np.zeros((2, s.input_padded))
+        xp[:, :s.input] = case.x
+        ref = xp @ block_hadamard(s.input_padded, s.group).T
+        got = oracle.cq_prepare(m, case.x)
+        bound = np.abs(xp).reshape(2, -1, s.group).sum(-1).repeat(s.group, 1) / math.sqrt(s.group)
+        assert np.all(np.abs(got - ref) <= 1e-6 * bound + 1e-30), s
+
+
+def pin_cq_matvec_vs_dense():
+    for case in small_cases():
+        m = oracle.CqMatrix.from_case(case)
+        p = oracle.cq_prepare(m, case.x)
+        y, mag = oracle.cq_matvec(m, p)
+        D = dense_transform_weights(case)
+        ref = p.astype(np.float64) @ D.T
+        refmag = np.abs(p.astype(np.float64)) @ np.abs(D).T
+        assert np.all(np.abs(y - ref) <= 1e-12 * refmag + 1e-300), case.shape
+        assert np.allclose(mag, refmag, rtol=1e-12, atol=0), case.shape
+
+
+def pin_cq_matvec_row_range():
+    case = small_cases()[3]
+    m = oracle.CqMatrix.from_case(case)
+    p = oracle.cq_prepare(m, case.x[0])
+    y_all, _ = oracle.cq_matvec(m, p)
+    y_mid, _ = oracle.cq_matvec(m, p, 2, 5)
+    assert np.array_equal(y_mid, y_all[2:7])
+
+
+def pin_matvec_gather_identity():
+    """The pages' test: cqMatvec(x)[row] ~ dot(dequantizeRow(row), x), every width."""
+    seen_bits = set()
+    for case in small_cases():
+        m = oracle.CqMatrix.from_case(case)
+        p = oracle.cq_prepare(m, case.x)
+        y, mag = oracle.cq_matvec(m, p)
+        y7 = oracle.cq_dense_matvec(m, case.x)
+        assert np.all(np.abs(y - y7) <= 1e-4 * mag + 1e-6), case.shape
+        seen_bits.add(case.shape.bits)
+    assert seen_bits == {2, 3, 4, 5}
+
+
+def pin_tiny_exact_rationals():
+    """R=3, input 5 -> 8, group 4 (scale 1/2 is exact): exact rational sums."""
+    case = synth.make_cq(synth.CqShape(3, 5, 8, 4, 3), seed=11)
+    s = case.shape
+    m = oracle.CqMatrix.from_case(case)
+    x = case.x[0]
+    idx = unpack_indices(case.packed, 3, 8)
+    H = scipy.linalg.hadamard(4)
+    xf = [Fraction(float(v)) for v in x] + [Fraction(0)] * 3
+    p_exact = []
+    for g0 in (0, 4):
+        for k in range(4):
+            p_exact.append(sum(int(H[k, j]) * xf[g0 + j] for j in range(4)) / 2)
+    p = oracle.cq_prepare(m, x)
+    y, mag = oracle.cq_matvec(m, p)
+    for r in range(3):
+        exact = Fraction(0)
+        for g in range(2):
+            norm = Fraction(float(np.uint16(case.norms[r, g]).view(np.float16)))
+            exact += norm * sum(Fraction(float(case.codebook[idx[r, k]])) * p_exact[k]
+                                for k in range(4 * g, 4 * g + 4))
+        assert abs(Fraction(y[r]) - exact) <= Fraction(1e-6) * Fraction(mag[r]), r
+    _ = s
+
+
+def pin_dequantize_row_vs_scipy():
+    for case in small_cases():
+        s = case.shape
+        m = oracle.CqMatrix.from_case(case)
+        D = dense_transform_weights(case)
+        ref = (D @ block_hadamard(s.input_padded, s.group))[:, :s.input]
+        for r in range(s.output):
+            got = oracle.cq_dequantize_row(m, r)
+            bound = (np.abs(D[r]).reshape(-1, s.group).sum(-1).repeat(s.group)
+                     / math.sqrt(s.group))[:s.input]
+            assert np.all(np.abs(got - ref[r]) <= 2e-6 * bound), (s, r)
+
+
+def pin_dequantize_inverse_identity():
+    """FWHT of the dequantized row (no column drop) gives back sqrt(g)*norm*codebook."""
+    case = synth.make_cq(synth.CqShape(4, 64, 64, 16, 4), seed=12)
+    s = case.shape
+    m = oracle.CqMatrix.from_case(case)
+    D = dense_transform_weights(case)
+    for r in range(s.output):
+        row = oracle.cq_dequantize_row(m, r)
+        back = np.concatenate([oracle.fwht(row[g:g + 16]) for g in range(0, 64, 16)])
+        assert np.allclose(back, D[r] * math.sqrt(16), rtol=0, atol=1e-5 * np.abs(D[r]).max())
+
+
+def pin_gather():
+    case = synth.make_cq(synth.CqShape(11, 100, 128, 32, 5), seed=13, n_ids=9)
+    ids = np.concatenate([case.ids, case.ids[:2]])  # duplicates give equal rows
+    m = oracle.CqMatrix.from_case(case)
+    out, gmag = oracle.cq_gather(m, ids)
+    D = dense_transform_weights(case)
+    for i, r in enumerate(ids):
+        assert np.array_equal(out[i], oracle.cq_dequantize_row(m, int(r)))
+        ref = np.abs(D[r]).reshape(-1, 32).sum(-1).repeat(32)[:100] / math.sqrt(32)
+        assert np.allclose(gmag[i], ref, rtol=1e-12, atol=0)
+    assert np.array_equal(out[-2:], out[:2])
+
+
+def pin_e4m3_golden():
+    for row in _read_table("e4m3_anchors.txt"):
+        code, val = int(row[0], 16), float(row[1])
+        got = oracle.e4m3(code)
+        assert got == val and math.copysign(1, got) == math.copysign(1, val), (row, got)
+
+
+def pin_e4m3_all_codes():
+    got = oracle.e4m3_all()
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    for c in range(256):
+        if c & 0x7F == 0x7F:           # NaN in the OCP format, the clamp on the pages
+            assert got[c] == (-448.0 if c & 0x80 else 448.0)
+        else:
+            assert got[c].view(np.uint32) == ref[c].view(np.uint32), hex(c)
+    # brute force over sign/exponent/mantissa in exact rationals
+    for c in range(256):
+        s, e, mt = c >> 7, (c >> 3) & 15, c & 7
+        v = Fraction(mt, 8) * Fraction(2) ** -6 if e == 0 else (1 + Fraction(mt, 8)) * Fraction(2) ** (e - 7)
+        v = min(v, Fraction(448))
+        assert Fraction(float(got[c])) == (-v if s else v), hex(c)
+
+
+def pin_e8m0_all_codes():
+    got = oracle.e8m0_all()
+    for e in range(256):
+        if e == 255:
+            assert math.isnan(got[e])
+        else:
+            assert got[e] == np.float32(math.ldexp(1.0, e - 127)) and got[e] > 0, e
+
+
+def _f8_dense(case):
+    W = torch.from_numpy(case.w.copy()).view(torch.float8_e4m3fn).double().numpy()
+    sat = (case.w & 0x7F) == 0x7F
+    W[sat] = np.where(case.w[sat] & 0x80, -448.0, 448.0)
+    rs = (np.arange(case.R, dtype=np.int64) * case.SR) // case.R
+    cs = (np.arange(case.C, dtype=np.int64) * case.SC) // case.C
+    S = np.ldexp(1.0, case.scale.astype(np.int64) - 127)[rs][:, cs]
+    return W * S
+
+
+def pin_f8_matvec_vs_dense():
+    for (R, C, SR, SC) in ((10, 7, 3, 2), (256, 64, 2, 4), (130, 260, 3, 5), (64, 128, 1, 1)):
+        case = synth.make_f8(R, C, SR, SC, seed=R + C, batch=2)
+        y, mag = oracle.f8_matvec(case.w, R, C, case.scale, SR, SC, case.x)
+        D = _f8_dense(case)
+        ref = case.x.astype(np.float64) @ D.T
+        refmag = np.abs(case.x.astype(np.float64)) @ np.abs(D).T
+        assert np.all(np.abs(y - ref) <= 1e-12 * refmag + 1e-300), (R, C, SR, SC)
+        assert np.allclose(mag, refmag, rtol=1e-12, atol=0)
+
+
+def pin_f8_matvec_one_hot():
+    case = synth.make_f8(256, 48, 2, 3, seed=5)
+    case.w[:, 17] = np.arange(256, dtype=np.uint8)    # every code through the dot
+    x = np.zeros(48, np.float32)
+    x[17] = 1.0
+    y, _ = oracle.f8_matvec(case.w, 256, 48, case.scale, 2, 3, x)
+    for r in range(256):
+        s = case.scale[(r * 2) // 256, (17 * 3) // 48]
+        v = Fraction(float(oracle.e4m3(r))) * Fraction(2) ** (int(s) - 127)
+        assert Fraction(y[r]) == v, r
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,69 @@
+"""CPU-only: the pins catch plausible mistakes planted in a copy of the oracle.
+
+Each mutant is a textual edit of ``oracle/oracle.c`` (a dropped term, a wrong
+sign, index or bias), compiled with gcc into a temporary library.  The test
+passes when at least one pin fails on it; the shipped oracle is untouched.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.LIB_PATH), "oracle.c")
+
+MUTANTS = {
+    "butterfly_sign": ("x[base + j + stride] = a - b;", "x[base + j + stride] = b - a;"),
+    "fwht_dropped_stage": ("stride < n; stride <<= 1", "stride < n / 2; stride <<= 1"),
+    "scale_not_sqrt": ("1.0 / sqrt((double)group)", "1.0 / (double)group"),
+    "index_msb_first": ("idx |= bit << j;", "idx |= bit << (m->bits - 1 - j);"),
+    "index_wrong_stride": ("int64_t t = m->bits * col + j;", "int64_t t = 4 * col + j;"),
+    "matvec_dropped_norm": ("acc += norm * part;", "acc += part;"),
+    "matvec_wrong_norm_index": ("m->norms[row * n_groups + g]);\n            acc",
+                                "m->norms[row * n_groups]);\n            acc"),
+    "prepare_no_pad_zero": ("p[k] = k < m->input ? x[k] : 0.0f;", "p[k] = k < m->input ? x[k] : 1.0f;"),
+    "dequant_dropped_norm": ("tg[k] = m->codebook[oracle_cq_index(m, row, g * m->group + k)] * norm;",
+                             "tg[k] = m->codebook[oracle_cq_index(m, row, g * m->group + k)];"),
+    "dense_dropped_column": ("for (int64_t c = 0; c < m->input; c++) acc +=",
+                             "for (int64_t c = 1; c < m->input; c++) acc +="),
+    "f16_bias": ("(exponent - 15 + 127) << 23", "(exponent - 16 + 127) << 23"),
+    "f16_subnormal_bias": ("int32_t e = 127 - 15 + 1;", "int32_t e = 127 - 15;"),
+    "e4m3_subnormal_exp": ("v = ldexp((double)mant / 8.0, 1 - 7);", "v = ldexp((double)mant / 8.0, 0 - 7);"),
+    "e4m3_no_clamp": ("if (v > 448.0) v = 448.0;", ""),
+    "e4m3_sign_dropped": ("return (float)(s ? -v : v);", "return (float)v;"),
+    "e8m0_bias": ("ldexp(1.0, (int)e - 127)", "ldexp(1.0, (int)e - 128)"),
+    "f8_scale_col_uses_R": ("int64_t sc = (c * SC) / C;", "int64_t sc = (c * SC) / R;"),
+    "f8_scale_row_transposed": ("int64_t sr = (r * SR) / R;", "int64_t sr = (r * SC) / R;"),
+}
+
+
+def _build_mutant(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique or missing"
+    mutated = tmp_path / f"{name}.c"
+    mutated.write_text(src.replace(old, new))
+    lib = tmp_path / f"lib{name}.so"
+    inc = os.path.dirname(SRC)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
+                    "-I", inc, "-o", str(lib), str(mutated), "-lm"], check=True)
+    return str(lib)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    old, new = MUTANTS[name]
+    lib = _build_mutant(tmp_path, name, old, new)
+    oracle.use_library(lib)
+    try:
+        caught = []
+        for pin in oracle_pins.ALL_PINS:
+            try:
+                pin()
+            except (AssertionError, ValueError):
+                caught.append(pin.__name__)
+                break
+        assert caught, f"no pin fails on mutant {name}"
+    finally:
+        oracle.use_library(None)
