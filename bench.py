@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Throughput of one decode step over the quantized matvec hot path (1 GPU).
+
+One step runs every stage of the path at the workloads' full sizes:
+  1. CQ 4-bit 16384 x 4096 (group 256): prepare + matvec, batch 1
+  2. the same matrix, 8 activation vectors: prepare + matvec
+  3. CQ 4-bit 65536 x 512 vocabulary table: dense gather of 4096 rows
+  4. FP8 E4M3 head 246272 x 4096 with E8M0 128 x 128 block scales: matvec
+Inputs are seeded synthetic arrays (synth.py) resident in HBM before timing.
+Weights rotate over enough copies that every step reads bytes that are not in
+the 256 MB Infinity Cache ("cold").  The value is the step's algorithmic HBM
+bytes (weights, activations in, outputs out) over the step time.
+
+Prints ONE JSON line.  `--gpus N` with N > 1 exits: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import threading
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "weight-stream GB/s & % of HBM peak, CQ/F8 decode matvec; rows/s"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="0: the affinity mask, at most 16")
+    ap.add_argument("--hot", action="store_true", help="one weight copy (cache-resident timing)")
+    return ap.parse_args()
+
+
+class Case:
+    """One stage of the step: a callable per weight copy plus its byte count."""
+
+    def __init__(self, name, calls, nbytes, rows):
+        self.name, self.calls, self.nbytes, self.rows = name, calls, nbytes, rows
+        self.ms = []
+
+
+def build_cases(torch, bqd, synth, hot):
+    dev = "cuda"
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    cases = []
+
+    # -- CQ 4-bit 16384 x 4096, batch 1 and batch 8 (one matrix, rotated copies)
+    log("generating CQ4 16384x4096 (seed 3)")
+    c4 = synth.make_cq(synth.C4, seed=3, batch=8)
+    s4 = c4.shape
+    k4 = 1 if hot else 16
+    packed4, norms4 = T(c4.packed), T(c4.norms.view(np.int16))
+    cb4 = T(c4.codebook)
+    mats4 = []
+    for k in range(k4):
+        pk, nm = (packed4, norms4) if k == 0 else (packed4.clone(), norms4.clone())
+        mats4.append(bqd.CqMatrix(pk, nm, cb4, output=s4.output, input=s4.input,
+                                  input_padded=s4.input_padded, group=s4.group, bits=s4.bits))
+    x1, x8 = T(c4.x[:1]), T(c4.x)
+    p1 = torch.empty(1, s4.input_padded, device=dev)
+    p8 = torch.empty(8, s4.input_padded, device=dev)
+    y1 = torch.empty(1, s4.output, device=dev)
+    y8 = torch.empty(8, s4.output, device=dev)
+    w4 = s4.output * s4.stride + s4.output * s4.n_groups * 2
+    cases.append(Case("cq4_16384x4096_prepare_b1",
+                      [lambda m=m: bqd.cq_prepare(m, x1, out=p1) for m in mats4],
+                      4 * (s4.input + s4.input_padded), 0))
+    cases.append(Case("cq4_16384x4096_matvec_b1",
+                      [lambda m=m: bqd.cq_matvec(m, p1, out=y1) for m in mats4],
+                      w4 + 4 * s4.input_padded + 4 * s4.output, s4.output))
+    cases.append(Case("cq4_16384x4096_prepare_b8",
+                      [lambda m=m: bqd.cq_prepare(m, x8, out=p8) for m in mats4],
+                      8 * 4 * (s4.input + s4.input_padded), 0))
+    cases.append(Case("cq4_16384x4096_matvec_b8",
+                      [lambda m=m: bqd.cq_matvec(m, p8, out=y8) for m in mats4],
+                      w4 + 8 * 4 * s4.input_padded + 8 * 4 * s4.output, 8 * s4.output))
+
+    # -- CQ 4-bit 65536 x 512 table: gather 4096 rows
+    log("generating CQ4 65536x512 table (seed 2)")
+    c3 = synth.make_cq(synth.C3, seed=2, n_ids=synth.C3_GATHER_IDS)
+    s3 = c3.shape
+    k3 = 1 if hot else 16
+    packed3, norms3, cb3 = T(c3.packed), T(c3.norms.view(np.int16)), T(c3.codebook)
+    mats3 = [bqd.CqMatrix(packed3 if k == 0 else packed3.clone(), norms3 if k == 0 else norms3.clone(),
+                          cb3, output=s3.output, input=s3.input, input_padded=s3.input_padded,
+                          group=s3.group, bits=s3.bits) for k in range(k3)]
+    ids = T(c3.ids)
+    g = torch.empty(len(c3.ids), s3.input, device=dev)
+    n_ids = len(c3.ids)
+    gather_bytes = n_ids * (s3.stride + 2 * s3.n_groups) + 4 * n_ids + 4 * n_ids * s3.input
+    cases.append(Case("cq4_65536x512_gather_4096",
+                      [lambda m=m: bqd.cq_gather_rows(m, ids, out=g) for m in mats3],
+                      gather_bytes, n_ids))
+
+    # -- FP8 head 246272 x 4096
+    log("generating F8 head 246272x4096 (seed 4)")
+    hd = synth.make_f8(**synth.HEAD, seed=4)
+    kh = 1 if hot else 2
+    wh0 = T(hd.w)
+    whs = [wh0] + [wh0.clone() for _ in range(kh - 1)]
+    sh, xh = T(hd.scale), T(hd.x)
+    yh = torch.empty(1, hd.R, device=dev)
+    head_bytes = hd.R * hd.C + hd.SR * hd.SC + 4 * hd.C + 4 * hd.R
+    cases.append(Case("f8_head_246272x4096_matvec",
+                      [lambda w=w: bqd.f8_matvec(w, sh, xh, out=yh) for w in whs],
+                      head_bytes, hd.R))
+    data = dict(c4=c4, c3=c3, head=hd)
+    return cases, data
+
+
+def cpu_baseline(data, threads):
+    """The oracle, as it stands, on a bounded sample of the same workload,
+    rows split over `threads` Python threads (ctypes releases the GIL)."""
+    import oracle
+
+    c4, c3, hd = data["c4"], data["c3"], data["head"]
+    h4 = oracle.CqMatrix.from_case(c4)
+    h3 = oracle.CqMatrix.from_case(c3)
+    p4 = oracle.cq_prepare(h4, c4.x[0])
+    # about a second of oracle work per thread on the head, plus the whole
+    # 16384-row CQ matvec and the whole 4096-id gather
+    n_head, n_c4, n_ids = min(hd.R, 12288 * threads), c4.shape.output, len(c3.ids)
+    s4 = c4.shape
+
+    def split(n):
+        per = (n + threads - 1) // threads
+        return [(i * per, min(per, n - i * per)) for i in range(threads) if i * per < n]
+
+    def run(jobs):
+        ts = [threading.Thread(target=f) for f in jobs]
+        t0 = time.perf_counter()
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+        return time.perf_counter() - t0
+
+    t_head = run([lambda a=a, b=b: oracle.f8_matvec(hd.w, hd.R, hd.C, hd.scale, hd.SR, hd.SC,
+                                                     hd.x[0], a, b) for a, b in split(n_head)])
+    t_c4 = run([lambda a=a, b=b: oracle.cq_matvec(h4, p4, a, b) for a, b in split(n_c4)])
+    t_g = run([lambda a=a, b=b: oracle.cq_gather(h3, c3.ids[a:a + b]) for a, b in split(n_ids)])
+    nbytes = (n_head * (hd.C + 4) + n_c4 * (s4.stride + 2 * s4.n_groups + 4)
+              + n_ids * (c3.shape.stride + 2 * c3.shape.n_groups + 4 + 4 * c3.shape.input))
+    secs = t_head + t_c4 + t_g
+    return {
+        "value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
+        "kind": "oracle",
+        "sample": (f"oracle on host cores: F8 head rows [0,{n_head}) of 246272 "
+                   f"({t_head:.2f} s), CQ4 16384x4096 rows [0,{n_c4}) batch 1 ({t_c4:.2f} s), "
+                   f"CQ4 65536x512 gather of {n_ids} ids ({t_g:.2f} s); "
+                   f"{threads} threads over row chunks"),
+        "seconds": round(secs, 3),
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(the rows of each matvec shard across GPUs by design only)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import bit_quantized_decode_amd as bqd
+    import synth
+
+    torch.cuda.set_device(0)
+    bqd.lib()
+    cases, data = build_cases(torch, bqd, synth, args.hot)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    head_case = cases[-1]
+
+    def step(i, events=None):
+        """One step; `events` collects (start, end) around the listed stages."""
+        for c in cases:
+            fn = c.calls[i % len(c.calls)]
+            if events is not None and c in events:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                events[c].append((e0, e1))
+            else:
+                fn()
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # The timed region: K whole steps.  HIP events on the launch stream bracket
+    # the dominant kernel (the F8 head) inside it for the roofline figure.
+    log(f"timing {args.steps} steps")
+    head_events = {head_case: []}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, head_events)
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    head_ms = np.array([a.elapsed_time(b) for a, b in head_events[head_case]])
+    # Per-stage breakdown: a second pass with events around every stage.
+    stage_events = {c: [] for c in cases}
+    for i in range(args.steps):
+        step(i, stage_events)
+    torch.cuda.synchronize()
+    for c in cases:
+        c.ms = [a.elapsed_time(b) for a, b in stage_events[c]]
+    per_case = {}
+    for c in cases:
+        ms = np.array(c.ms)
+        per_case[c.name] = dict(
+            us_mean=round(float(ms.mean() * 1e3), 3), us_median=round(float(np.median(ms) * 1e3), 3),
+            us_p10=round(float(np.percentile(ms, 10) * 1e3), 3),
+            us_p90=round(float(np.percentile(ms, 90) * 1e3), 3),
+            bytes=c.nbytes, gbs=round(c.nbytes / (ms.mean() * 1e-3) / 1e9, 1),
+            frac_hbm=round(c.nbytes / (ms.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            rows_per_s=round(c.rows / (ms.mean() * 1e-3), 1) if c.rows else None)
+    total_bytes = sum(c.nbytes for c in cases)
+    total_rows = sum(c.rows for c in cases)
+    value = total_bytes / (step_ms * 1e-3) / 1e9
+    head_gbs = head_case.nbytes / (head_ms.mean() * 1e-3) / 1e9
+    roofline = dict(bound="hbm", kernel="f8_matvec_fast (F8 head 246272x4096)",
+                    achieved=round(head_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(head_gbs / HBM_PEAK_GBS, 4), traffic=None,
+                    us_per_launch=round(float(head_ms.mean() * 1e3), 3),
+                    bytes_per_launch=head_case.nbytes)
+    cpu = None
+    if not args.no_cpu_baseline:
+        n = args.cpu_threads or min(16, len(os.sched_getaffinity(0)))
+        log(f"cpu baseline: oracle with {n} threads")
+        cpu = cpu_baseline(data, n)
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded; synth.py)",
+        "config": {"workload": "decode step: CQ4 16384x4096 g256 prepare+matvec at batch 1 and 8; "
+                               "CQ4 65536x512 g128 gather of 4096 rows; F8 E4M3 head 246272x4096 "
+                               "with E8M0 [1924x32] scales",
+                   "mode": "hot (one weight copy)" if args.hot else
+                           "cold (weights rotated past the 256 MB Infinity Cache)",
+                   "parallelism": "single GPU"},
+        "rows_per_s": round(total_rows / (step_ms * 1e-3), 1),
+        "frac_hbm_step": round(value / HBM_PEAK_GBS, 4),
+        "cases": per_case, "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,231 @@
+"""Quantized decode matvec on MI355X (gfx950): Python binding of libbqd.so.
+
+Argument marshalling only: every function checks that the torch tensors it is
+given live on the GPU with the dtype and layout the C ABI (``include/bqd.h``)
+documents, allocates the output tensor when none is passed, and calls the
+entry point of the same name on the current torch stream.  All computation
+runs in the HIP kernels of ``libbqd.so``; if the library is missing the calls
+raise instead of falling back to anything else.
+
+Operations ("Inference engine, part 2: kernels and token step" §1–§3 and
+"Row gather"; "attention + tokenizer + sampling: the path to real text",
+Step 1):
+
+* ``cq_prepare(m, x)``        zero-pad, per-group FWHT, times 1/sqrt(group)
+* ``cq_matvec(m, prepared)``  packed-row codebook dot with fp16 group norms
+* ``cq_gather_rows(m, rows)`` dense rows: decode x norm, normalized FWHT
+* ``f8_matvec(w, scale, x)``  E4M3 weights with E8M0 block scales
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["BqdError", "CqMatrix", "cq_prepare", "cq_matvec", "cq_gather_rows", "f8_matvec",
+           "dbg_cq_unpack", "dbg_f16_decode", "dbg_f8_decode", "dbg_e8m0_decode", "lib",
+           "LIB_PATH", "EXPORTS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbqd.so")
+
+# Every symbol include/bqd.h declares.
+EXPORTS = ("cq_prepare", "cq_matvec", "cq_gather_rows", "f8_matvec", "bqd_dbg_cq_unpack",
+           "bqd_dbg_f16_decode", "bqd_dbg_f8_decode", "bqd_dbg_e8m0_decode",
+           "bqd_status_string")
+
+_lib = None
+
+
+class BqdError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = lib().bqd_status_string(status).decode()
+        super().__init__(f"{fn}: {msg} (status {status})")
+
+
+class _CqStruct(ctypes.Structure):
+    _fields_ = [("output", ctypes.c_int64), ("input", ctypes.c_int64),
+                ("input_padded", ctypes.c_int64), ("group", ctypes.c_int64),
+                ("bits", ctypes.c_int64), ("row_bytes", ctypes.c_int64),
+                ("packed", ctypes.c_void_p), ("norms", ctypes.c_void_p),
+                ("codebook", ctypes.c_void_p)]
+
+
+def lib():
+    """The loaded libbqd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run bit_quantized_decode_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        S = ctypes.POINTER(_CqStruct)
+        for name, args in (
+                ("cq_prepare", [S, P, P, I64, P]),
+                ("cq_matvec", [S, P, P, I64, I64, I64, P]),
+                ("cq_gather_rows", [S, P, I64, P, P]),
+                ("f8_matvec", [P, I64, I64, P, I64, I64, P, P, I64, P]),
+                ("bqd_dbg_cq_unpack", [S, I64, P, P]),
+                ("bqd_dbg_f16_decode", [P, I64, P, P]),
+                ("bqd_dbg_f8_decode", [P, I64, P, P]),
+                ("bqd_dbg_e8m0_decode", [P, I64, P, P])):
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = I
+        L.bqd_status_string.argtypes = [I]
+        L.bqd_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _call(name: str, *args):
+    rc = getattr(lib(), name)(*args)
+    if rc != 0:
+        raise BqdError(name, rc)
+
+
+def _stream(t: torch.Tensor, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class CqMatrix:
+    """A codebook-quantized matrix resident in GPU memory.
+
+    packed: uint8 [output][row_bytes]; norms: int16 or uint16 holding fp16 bit
+    patterns, [output][input_padded // group]; codebook: float32 [2**bits].
+    """
+
+    def __init__(self, packed, norms, codebook, *, output, input, input_padded, group, bits,
+                 row_bytes=None):
+        self.packed = _dev(packed, torch.uint8, "packed")
+        self.norms = _dev(norms, (torch.int16, torch.uint16), "norms")
+        self.codebook = _dev(codebook, torch.float32, "codebook")
+        self.output, self.input, self.input_padded = int(output), int(input), int(input_padded)
+        self.group, self.bits = int(group), int(bits)
+        self.row_bytes = int(row_bytes if row_bytes is not None else packed.shape[-1])
+        self._s = _CqStruct(self.output, self.input, self.input_padded, self.group, self.bits,
+                            self.row_bytes, self.packed.data_ptr(), self.norms.data_ptr(),
+                            self.codebook.data_ptr())
+
+    @classmethod
+    def from_arrays(cls, packed, norms, codebook, *, output, input, input_padded, group, bits,
+                    row_bytes=None, device="cuda"):
+        """Copy host (numpy) arrays to the GPU."""
+        import numpy as np
+        t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(device)
+        return cls(t(packed, np.uint8), t(norms, np.int16), t(codebook, np.float32),
+                   output=output, input=input, input_padded=input_padded, group=group,
+                   bits=bits, row_bytes=row_bytes)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self._s)
+
+
+def cq_prepare(m: CqMatrix, x: torch.Tensor, out: torch.Tensor = None, stream=None):
+    """x float32 [batch][input] (or [input]) -> prepared float32 [batch][input_padded]."""
+    x = _dev(x, torch.float32, "x")
+    if x.shape[-1] != m.input:
+        raise ValueError("x must have m.input columns")
+    batch = x.numel() // m.input if m.input else (x.shape[0] if x.dim() > 1 else 1)
+    shape = x.shape[:-1] + (m.input_padded,)
+    out = torch.empty(shape, dtype=torch.float32, device=x.device) if out is None else \
+        _dev(out, torch.float32, "out")
+    if out.numel() != batch * m.input_padded:
+        raise ValueError("out has the wrong size")
+    _call("cq_prepare", m.ref, _ptr(x), _ptr(out), batch, _stream(x, stream))
+    return out
+
+
+def cq_matvec(m: CqMatrix, prepared: torch.Tensor, out: torch.Tensor = None, row_begin: int = 0,
+              row_count: int = None, stream=None):
+    """prepared float32 [batch][input_padded] -> y float32 [batch][row_count]."""
+    prepared = _dev(prepared, torch.float32, "prepared")
+    if prepared.shape[-1] != m.input_padded:
+        raise ValueError("prepared must have m.input_padded columns")
+    batch = prepared.numel() // m.input_padded
+    row_count = m.output - row_begin if row_count is None else int(row_count)
+    shape = prepared.shape[:-1] + (row_count,)
+    out = torch.empty(shape, dtype=torch.float32, device=prepared.device) if out is None else \
+        _dev(out, torch.float32, "out")
+    if out.numel() != batch * row_count:
+        raise ValueError("out has the wrong size")
+    _call("cq_matvec", m.ref, _ptr(prepared), _ptr(out), batch, int(row_begin), row_count,
+          _stream(prepared, stream))
+    return out
+
+
+def cq_gather_rows(m: CqMatrix, rows: torch.Tensor, out: torch.Tensor = None, stream=None):
+    """rows int32 [n] -> dense rows float32 [n][input]."""
+    rows = _dev(rows, torch.int32, "rows")
+    n = rows.numel()
+    out = torch.empty((n, m.input), dtype=torch.float32, device=rows.device) if out is None else \
+        _dev(out, torch.float32, "out")
+    if out.numel() != n * m.input:
+        raise ValueError("out has the wrong size")
+    _call("cq_gather_rows", m.ref, _ptr(rows), n, _ptr(out), _stream(rows, stream))
+    return out
+
+
+def f8_matvec(w: torch.Tensor, scale: torch.Tensor, x: torch.Tensor, out: torch.Tensor = None,
+              stream=None):
+    """w uint8 E4M3 [R][C], scale uint8 E8M0 [SR][SC], x float32 [batch][C] -> [batch][R]."""
+    w = _dev(w, torch.uint8, "w")
+    scale = _dev(scale, torch.uint8, "scale")
+    x = _dev(x, torch.float32, "x")
+    R, C = w.shape
+    SR, SC = scale.shape
+    if x.shape[-1] != C:
+        raise ValueError("x must have C columns")
+    batch = x.numel() // C
+    shape = x.shape[:-1] + (R,)
+    out = torch.empty(shape, dtype=torch.float32, device=x.device) if out is None else \
+        _dev(out, torch.float32, "out")
+    if out.numel() != batch * R:
+        raise ValueError("out has the wrong size")
+    _call("f8_matvec", _ptr(w), R, C, _ptr(scale), SR, SC, _ptr(x), _ptr(out), batch,
+          _stream(x, stream))
+    return out
+
+
+def dbg_cq_unpack(m: CqMatrix, row: int, stream=None):
+    """Codebook indices of one row (uint8 [input_padded]) via the kernels' decoder."""
+    out = torch.empty(m.input_padded, dtype=torch.uint8, device=m.packed.device)
+    _call("bqd_dbg_cq_unpack", m.ref, int(row), _ptr(out), _stream(out, stream))
+    return out
+
+
+def _decode(name, codes, dtype, stream):
+    codes = _dev(codes, dtype, "codes")
+    out = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
+    _call(name, _ptr(codes), codes.numel(), _ptr(out), _stream(codes, stream))
+    return out
+
+
+def dbg_f16_decode(codes, stream=None):
+    return _decode("bqd_dbg_f16_decode", codes, (torch.int16, torch.uint16), stream)
+
+
+def dbg_f8_decode(codes, stream=None):
+    return _decode("bqd_dbg_f8_decode", codes, torch.uint8, stream)
+
+
+def dbg_e8m0_decode(codes, stream=None):
+    return _decode("bqd_dbg_e8m0_decode", codes, torch.uint8, stream)

@@ -1,0 +1,78 @@
+// The C ABI entry points: validate on the host (validate.cpp, HIP-free), then
+// enqueue the kernels on the caller's stream.
+#include "launch.h"
+#include "validate.h"
+
+using namespace bqd;
+
+namespace {
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+}  // namespace
+
+extern "C" {
+
+int cq_prepare(const bqd_cq_matrix* m, const float* x, float* prepared, int64_t batch,
+               void* stream) {
+  int rc = check_prepare(m, x, prepared, batch);
+  if (rc || batch == 0) return rc;
+  return launch_cq_prepare(m, x, prepared, batch, as_stream(stream));
+}
+
+int cq_matvec(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t batch,
+              int64_t row_begin, int64_t row_count, void* stream) {
+  int rc = check_matvec(m, prepared, y, batch, row_begin, row_count);
+  if (rc || batch == 0 || row_count == 0) return rc;
+  return launch_cq_matvec(m, prepared, y, batch, row_begin, row_count, as_stream(stream));
+}
+
+int cq_gather_rows(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, float* out,
+                   void* stream) {
+  int rc = check_gather(m, rows, n, out);
+  if (rc || n == 0) return rc;
+  return launch_cq_gather(m, rows, n, out, as_stream(stream));
+}
+
+int f8_matvec(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
+              int64_t SC, const float* x, float* y, int64_t batch, void* stream) {
+  int rc = check_f8(w, R, C, scale, SR, SC, x, y, batch);
+  if (rc || batch == 0 || R == 0) return rc;
+  return launch_f8_matvec(w, R, C, scale, SR, SC, x, y, batch, as_stream(stream));
+}
+
+int bqd_dbg_cq_unpack(const bqd_cq_matrix* m, int64_t row, uint8_t* idx, void* stream) {
+  int rc = check_unpack(m, row, idx);
+  if (rc) return rc;
+  return launch_cq_unpack(m, row, idx, as_stream(stream));
+}
+
+int bqd_dbg_f16_decode(const uint16_t* codes, int64_t n, float* out, void* stream) {
+  int rc = check_decode(codes, n, out, 2);
+  if (rc || n == 0) return rc;
+  return launch_f16_decode(codes, n, out, as_stream(stream));
+}
+
+int bqd_dbg_f8_decode(const uint8_t* codes, int64_t n, float* out, void* stream) {
+  int rc = check_decode(codes, n, out, 1);
+  if (rc || n == 0) return rc;
+  return launch_f8_decode(codes, n, out, as_stream(stream));
+}
+
+int bqd_dbg_e8m0_decode(const uint8_t* codes, int64_t n, float* out, void* stream) {
+  int rc = check_decode(codes, n, out, 1);
+  if (rc || n == 0) return rc;
+  return launch_e8m0_decode(codes, n, out, as_stream(stream));
+}
+
+const char* bqd_status_string(int status) {
+  switch (status) {
+    case BQD_OK: return "ok";
+    case BQD_EINVAL: return "invalid shape or parameter";
+    case BQD_EOVERFLOW: return "size product overflows int64";
+    case BQD_EALIGN: return "pointer not aligned to its element size";
+    case BQD_ENULL: return "required pointer is NULL";
+    case BQD_EHIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

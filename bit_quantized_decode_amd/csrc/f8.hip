@@ -1,0 +1,215 @@
+// FP8 E4M3 matvec with E8M0 block scales for gfx950, plus the decode probes.
+//
+// Method: "attention + tokenizer + sampling: the path to real text (milestone
+// 6)" — Step 1 (E4M3 decode with e = 0 subnormal and the 448 clamp; E8M0
+// block scales where element (r, c) of an R x C weight takes the scale
+// [r*SR/R][c*SC/C] of an SR x SC grid) and Step 4 (the vector path applies
+// when each vector of columns stays inside one scale block).
+#include <algorithm>
+
+#include "device.h"
+#include "launch.h"
+
+namespace bqd {
+
+constexpr int kF8Threads = 256;
+
+// ----------------------------------------------------------- generic matvec
+// Any shape and alignment: one wavefront per row, lanes stride over columns,
+// the scale index of every element by integer floor division.
+__global__ __launch_bounds__(kF8Threads) void f8_matvec_generic(
+    const uint8_t* __restrict__ w, const uint8_t* __restrict__ scale, const float* __restrict__ x,
+    float* __restrict__ y, int64_t R, int64_t C, int64_t SR, int64_t SC, int64_t batch) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  for (int64_t r = (int64_t)blockIdx.x * (kF8Threads / kWave) + wave; r < R;
+       r += (int64_t)gridDim.x * (kF8Threads / kWave)) {
+    const uint8_t* wr = w + r * C;
+    const uint8_t* sr = scale + ((r * SR) / R) * SC;
+    for (int64_t b = 0; b < batch; ++b) {
+      const float* xb = x + b * C;
+      float acc = 0.0f;
+      for (int64_t c = lane; c < C; c += kWave) {
+        const float s = e8m0_to_f32(sr[(c * SC) / C]);
+        acc += (e4m3_to_f32(wr[c]) * s) * xb[c];
+      }
+      acc = group_sum<kWave>(acc);
+      if (lane == kWave - 1) y[b * R + r] = acc;
+    }
+  }
+}
+
+// -------------------------------------------------------------- fast matvec
+// Rows of C = 16 * n_chunk bytes with 16-byte aligned rows and scale blocks
+// that are a whole number of 16-column chunks wide.  LPR lanes share a row;
+// lane q owns chunks q + LPR*j, so each load instruction of a wavefront reads
+// 1 KiB of contiguous bytes.  The activation of a lane's columns stays in
+// registers; each chunk's partial dot is multiplied by its power-of-two block
+// scale (exact), then the row reduces across lanes with DPP.
+template <int NJ, int LPR, int U>
+__global__ __launch_bounds__(kF8Threads) void f8_matvec_fast(
+    const uint8_t* __restrict__ w, const uint8_t* __restrict__ scale, const float* __restrict__ x,
+    float* __restrict__ y, int64_t R, int64_t C, int64_t SR, int64_t SC, int64_t cols_per_block) {
+  constexpr int SLOTS = kF8Threads / LPR;
+  const int tid = threadIdx.x;
+  const int slot = tid / LPR;
+  const int q = tid % LPR;
+  float act[NJ][16];
+  int scol[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int64_t c = 16 * (int64_t)(q + LPR * j);
+    scol[j] = (int)(c / cols_per_block);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) act[j][k] = x[c + k];
+  }
+  const int64_t n_steps = (R + SLOTS - 1) / SLOTS;
+  for (int64_t s0 = (int64_t)blockIdx.x * U; s0 < n_steps; s0 += (int64_t)gridDim.x * U) {
+    uint4 d[U][NJ];
+    uint32_t sb[U][NJ];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int64_t r = (s0 + u) * SLOTS + slot;
+      r = r < R ? r : R - 1;  // in-bounds load; the result is dropped
+      const uint4* wr = reinterpret_cast<const uint4*>(w + r * C);
+      const uint8_t* srow = scale + ((r * SR) / R) * SC;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        d[u][j] = wr[q + LPR * j];
+        sb[u][j] = srow[scol[j]];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        float v[16];
+        e4m3x4_to_f32(d[u][j].x, v + 0);
+        e4m3x4_to_f32(d[u][j].y, v + 4);
+        e4m3x4_to_f32(d[u][j].z, v + 8);
+        e4m3x4_to_f32(d[u][j].w, v + 12);
+        float part = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) part += v[k] * act[j][k];
+        acc += part * e8m0_to_f32(sb[u][j]);
+      }
+      acc = group_sum<LPR>(acc);
+      const int64_t r = (s0 + u) * SLOTS + slot;
+      if (q == LPR - 1 && r < R) y[r] = acc;
+    }
+  }
+}
+
+namespace {
+
+constexpr int kMaxGrid = 4096;
+
+template <int NJ, int LPR>
+int launch_f8_fast(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
+                   int64_t SC, const float* x, float* y, hipStream_t s) {
+  constexpr int U = 2;
+  constexpr int SLOTS = kF8Threads / LPR;
+  const int64_t n_steps = (R + SLOTS - 1) / SLOTS;
+  const int64_t grid = std::min<int64_t>((n_steps + U - 1) / U, kMaxGrid);
+  hipLaunchKernelGGL((f8_matvec_fast<NJ, LPR, U>), dim3((unsigned)grid), dim3(kF8Threads), 0, s,
+                     w, scale, x, y, R, C, SR, SC, C / SC);
+  return launch_status();
+}
+
+int launch_f8_generic(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
+                      int64_t SC, const float* x, float* y, int64_t batch, hipStream_t s) {
+  const int64_t waves = kF8Threads / kWave;
+  const int64_t grid = std::min<int64_t>((R + waves - 1) / waves, kMaxGrid);
+  hipLaunchKernelGGL(f8_matvec_generic, dim3((unsigned)grid), dim3(kF8Threads), 0, s, w, scale, x,
+                     y, R, C, SR, SC, batch);
+  return launch_status();
+}
+
+// Lane layout for rows of n_chunk 16-byte chunks, or {0, 0}.
+struct F8Shape {
+  int lpr, nj;
+};
+
+F8Shape f8_shape(int64_t n_chunk) {
+  if (n_chunk >= 8 && n_chunk <= 64 && (n_chunk & (n_chunk - 1)) == 0) return {(int)n_chunk, 1};
+  if (n_chunk == 128) return {64, 2};
+  if (n_chunk == 256) return {64, 4};
+  if (n_chunk == 512) return {64, 8};
+  return {0, 0};
+}
+
+}  // namespace
+
+int launch_f8_matvec(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
+                     int64_t SC, const float* x, float* y, int64_t batch, hipStream_t s) {
+  const bool fast = C % 16 == 0 && is_aligned(w, 16) && is_aligned(x, 4) && C % SC == 0 &&
+                    (C / SC) % 16 == 0;
+  const F8Shape f = fast ? f8_shape(C / 16) : F8Shape{0, 0};
+  if (f.lpr == 0) return launch_f8_generic(w, R, C, scale, SR, SC, x, y, batch, s);
+  // One weight pass per activation vector (the workloads here are batch 1).
+  for (int64_t b = 0; b < batch; ++b) {
+    const float* xb = x + b * C;
+    float* yb = y + b * R;
+    int rc = BQD_EINVAL;
+    switch (f.lpr * 16 + f.nj) {
+      case 8 * 16 + 1: rc = launch_f8_fast<1, 8>(w, R, C, scale, SR, SC, xb, yb, s); break;
+      case 16 * 16 + 1: rc = launch_f8_fast<1, 16>(w, R, C, scale, SR, SC, xb, yb, s); break;
+      case 32 * 16 + 1: rc = launch_f8_fast<1, 32>(w, R, C, scale, SR, SC, xb, yb, s); break;
+      case 64 * 16 + 1: rc = launch_f8_fast<1, 64>(w, R, C, scale, SR, SC, xb, yb, s); break;
+      case 64 * 16 + 2: rc = launch_f8_fast<2, 64>(w, R, C, scale, SR, SC, xb, yb, s); break;
+      case 64 * 16 + 4: rc = launch_f8_fast<4, 64>(w, R, C, scale, SR, SC, xb, yb, s); break;
+      case 64 * 16 + 8: rc = launch_f8_fast<8, 64>(w, R, C, scale, SR, SC, xb, yb, s); break;
+    }
+    if (rc) return rc;
+  }
+  return BQD_OK;
+}
+
+// ------------------------------------------------------------ decode probes
+// Each thread decodes four consecutive codes with the matvec's own routine.
+__global__ void f8_decode_probe(const uint8_t* __restrict__ codes, int64_t n,
+                                float* __restrict__ out) {
+  const int64_t i0 = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+  if (i0 >= n) return;
+  uint32_t word = 0;
+  for (int k = 0; k < 4; ++k)
+    if (i0 + k < n) word |= (uint32_t)codes[i0 + k] << (8 * k);
+  float v[4];
+  e4m3x4_to_f32(word, v);
+  for (int k = 0; k < 4; ++k)
+    if (i0 + k < n) out[i0 + k] = v[k];
+}
+
+__global__ void e8m0_decode_probe(const uint8_t* __restrict__ codes, int64_t n,
+                                  float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = e8m0_to_f32(codes[i]);
+}
+
+__global__ void f16_decode_probe(const uint16_t* __restrict__ codes, int64_t n,
+                                 float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = f16_to_f32(codes[i]);
+}
+
+int launch_f8_decode(const uint8_t* codes, int64_t n, float* out, hipStream_t s) {
+  const int64_t threads = (n + 3) / 4;
+  hipLaunchKernelGGL(f8_decode_probe, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                     codes, n, out);
+  return launch_status();
+}
+
+int launch_e8m0_decode(const uint8_t* codes, int64_t n, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(e8m0_decode_probe, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, codes,
+                     n, out);
+  return launch_status();
+}
+
+int launch_f16_decode(const uint16_t* codes, int64_t n, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(f16_decode_probe, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, codes,
+                     n, out);
+  return launch_status();
+}
+
+}  // namespace bqd

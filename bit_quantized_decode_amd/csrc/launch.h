@@ -1,0 +1,36 @@
+// Kernel launchers behind the C ABI.  Arguments arrive validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bqd.h"
+
+namespace bqd {
+
+int launch_cq_prepare(const bqd_cq_matrix* m, const float* x, float* prepared, int64_t batch,
+                      hipStream_t s);
+int launch_cq_matvec(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t batch,
+                     int64_t row_begin, int64_t row_count, hipStream_t s);
+int launch_cq_gather(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, float* out,
+                     hipStream_t s);
+int launch_cq_unpack(const bqd_cq_matrix* m, int64_t row, uint8_t* idx, hipStream_t s);
+
+int launch_f8_matvec(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
+                     int64_t SC, const float* x, float* y, int64_t batch, hipStream_t s);
+int launch_f16_decode(const uint16_t* codes, int64_t n, float* out, hipStream_t s);
+int launch_f8_decode(const uint8_t* codes, int64_t n, float* out, hipStream_t s);
+int launch_e8m0_decode(const uint8_t* codes, int64_t n, float* out, hipStream_t s);
+
+inline int launch_status() {
+  return hipGetLastError() == hipSuccess ? BQD_OK : BQD_EHIP;
+}
+
+inline bool is_aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+inline int ilog2(int64_t v) {
+  int r = 0;
+  while ((int64_t(1) << (r + 1)) <= v) ++r;
+  return r;
+}
+
+}  // namespace bqd

@@ -1,0 +1,120 @@
+// Host-side argument validation of the C ABI ("Inference engine, part 1:
+// loader and tokenizer", §2: every range is checked before anything is read,
+// and size products are checked before they are used).  No HIP here.
+#include "validate.h"
+
+namespace bqd {
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// a * b * c must fit in int64 (all operands non-negative).
+bool mul_ok(int64_t a, int64_t b, int64_t c = 1) {
+  int64_t t;
+  if (__builtin_mul_overflow(a, b, &t)) return false;
+  if (__builtin_mul_overflow(t, c, &t)) return false;
+  return true;
+}
+
+}  // namespace
+
+int check_cq_shape(const bqd_cq_matrix* m) {
+  if (!m) return BQD_ENULL;
+  if (m->bits < 2 || m->bits > 5) return BQD_EINVAL;
+  if (!is_pow2(m->group) || m->group > kMaxGroup) return BQD_EINVAL;
+  if (m->input_padded <= 0 || m->input_padded >= kMaxColumns) return BQD_EINVAL;
+  if (m->input_padded % m->group != 0) return BQD_EINVAL;
+  if (m->input < 0 || m->input > m->input_padded) return BQD_EINVAL;
+  if (m->output < 0 || m->output >= kMaxRows) return BQD_EINVAL;
+  if (m->row_bytes <= 0) return BQD_EINVAL;
+  const int64_t need = (m->input_padded * m->bits + 7) / 8;
+  if (m->row_bytes < need) return BQD_EINVAL;
+  if (!mul_ok(m->output, m->row_bytes)) return BQD_EOVERFLOW;
+  if (!mul_ok(m->output, m->input_padded / m->group, 2)) return BQD_EOVERFLOW;
+  return BQD_OK;
+}
+
+int check_cq(const bqd_cq_matrix* m) {
+  int rc = check_cq_shape(m);
+  if (rc) return rc;
+  if (m->output > 0 && (!m->packed || !m->norms)) return BQD_ENULL;
+  if (!m->codebook) return BQD_ENULL;
+  if (!aligned(m->norms, 2) || !aligned(m->codebook, 4)) return BQD_EALIGN;
+  return BQD_OK;
+}
+
+int check_prepare(const bqd_cq_matrix* m, const float* x, const float* prepared, int64_t batch) {
+  int rc = check_cq_shape(m);
+  if (rc) return rc;
+  if (batch < 0) return BQD_EINVAL;
+  if (!mul_ok(batch, m->input_padded, 4)) return BQD_EOVERFLOW;
+  if (batch == 0) return BQD_OK;
+  if (!prepared || (m->input > 0 && !x)) return BQD_ENULL;
+  if (!aligned(x, 4) || !aligned(prepared, 4)) return BQD_EALIGN;
+  // x and prepared must not overlap
+  if (x) {
+    const char* xa = (const char*)x;
+    const char* xb = xa + batch * m->input * 4;
+    const char* pa = (const char*)prepared;
+    const char* pb = pa + batch * m->input_padded * 4;
+    if (xa < pb && pa < xb) return BQD_EINVAL;
+  }
+  return BQD_OK;
+}
+
+int check_matvec(const bqd_cq_matrix* m, const float* prepared, const float* y, int64_t batch,
+                 int64_t row_begin, int64_t row_count) {
+  int rc = check_cq(m);
+  if (rc) return rc;
+  if (batch < 0 || row_begin < 0 || row_count < 0) return BQD_EINVAL;
+  if (row_begin > m->output || row_count > m->output - row_begin) return BQD_EINVAL;
+  if (!mul_ok(batch, m->input_padded, 4) || !mul_ok(batch, row_count, 4)) return BQD_EOVERFLOW;
+  if (batch == 0 || row_count == 0) return BQD_OK;
+  if (!prepared || !y) return BQD_ENULL;
+  if (!aligned(prepared, 4) || !aligned(y, 4)) return BQD_EALIGN;
+  return BQD_OK;
+}
+
+int check_gather(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, const float* out) {
+  int rc = check_cq(m);
+  if (rc) return rc;
+  if (n < 0 || n >= kMaxRows) return BQD_EINVAL;
+  if (!mul_ok(n, m->input, 4)) return BQD_EOVERFLOW;
+  if (n == 0) return BQD_OK;
+  if (!rows || (m->input > 0 && !out)) return BQD_ENULL;
+  if (!aligned(rows, 4) || !aligned(out, 4)) return BQD_EALIGN;
+  return BQD_OK;
+}
+
+int check_f8(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
+             int64_t SC, const float* x, const float* y, int64_t batch) {
+  if (R < 0 || R >= kMaxRows || C < 1 || C >= kMaxColumns) return BQD_EINVAL;
+  if (SR < 1 || SR > (R > 0 ? R : 1) || SC < 1 || SC > C) return BQD_EINVAL;
+  if (batch < 0) return BQD_EINVAL;
+  if (!mul_ok(R, C) || !mul_ok(SR, SC) || !mul_ok(batch, C, 4) || !mul_ok(batch, R, 4) ||
+      !mul_ok(R, SR) || !mul_ok(C, SC))
+    return BQD_EOVERFLOW;
+  if (batch == 0 || R == 0) return BQD_OK;
+  if (!w || !scale || !x || !y) return BQD_ENULL;
+  if (!aligned(x, 4) || !aligned(y, 4)) return BQD_EALIGN;
+  return BQD_OK;
+}
+
+int check_unpack(const bqd_cq_matrix* m, int64_t row, const uint8_t* idx) {
+  int rc = check_cq(m);
+  if (rc) return rc;
+  if (row < 0 || row >= m->output) return BQD_EINVAL;
+  if (!idx) return BQD_ENULL;
+  return BQD_OK;
+}
+
+int check_decode(const void* codes, int64_t n, const float* out, int code_size) {
+  if (n < 0 || n >= kMaxRows) return BQD_EINVAL;
+  if (n == 0) return BQD_OK;
+  if (!codes || !out) return BQD_ENULL;
+  if (!aligned(codes, (uintptr_t)code_size) || !aligned(out, 4)) return BQD_EALIGN;
+  return BQD_OK;
+}
+
+}  // namespace bqd

@@ -1,0 +1,29 @@
+// Host-side argument validation of the C ABI.  Compiled without any HIP
+// header, so every status code can be produced and tested on a CPU-only host.
+#pragma once
+#include <stdint.h>
+
+#include "../../include/bqd.h"
+
+namespace bqd {
+
+// Shape fields of a CQ matrix (data pointers are not looked at).
+int check_cq_shape(const bqd_cq_matrix* m);
+// Shape fields plus the packed / norms / codebook pointers.
+int check_cq(const bqd_cq_matrix* m);
+
+int check_prepare(const bqd_cq_matrix* m, const float* x, const float* prepared, int64_t batch);
+int check_matvec(const bqd_cq_matrix* m, const float* prepared, const float* y, int64_t batch,
+                 int64_t row_begin, int64_t row_count);
+int check_gather(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, const float* out);
+int check_f8(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
+             int64_t SC, const float* x, const float* y, int64_t batch);
+int check_unpack(const bqd_cq_matrix* m, int64_t row, const uint8_t* idx);
+int check_decode(const void* codes, int64_t n, const float* out, int code_size);
+
+// Largest sizes the kernels index with their 32-bit row / column counters.
+constexpr int64_t kMaxRows = (int64_t)1 << 31;      // exclusive
+constexpr int64_t kMaxColumns = (int64_t)1 << 28;   // exclusive
+constexpr int64_t kMaxGroup = 1024;
+
+}  // namespace bqd

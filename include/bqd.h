@@ -1,0 +1,140 @@
+/*
+ * bqd.h — C ABI of the MI355X (gfx950) quantized decode matvec library.
+ *
+ * The operations are those of two public write-ups:
+ *   [P1] "Inference engine, part 2: kernels and token step" (needle.js
+ *        tutorial): §1 "Fast Walsh–Hadamard transform", §2 "Prepare an
+ *        activation for CQ", §3 "Dot packed rows directly", "Row gather",
+ *        §6 (row-range matvec, one prepared activation reused for several
+ *        matrices);
+ *   [P3] "Inference engine, part 1: loader and tokenizer": §2 "Make bounds
+ *        checks boring", §3 "Decode FP16 control tensors", §4 "Retain packed
+ *        matrices" (the CQ record);
+ *   [P4] "attention + tokenizer + sampling: the path to real text (milestone
+ *        6)": "Step 1 done: F8 kernel" (E4M3 decode, E8M0 block scales) and
+ *        "Step 4 done" (the vector decode).
+ *
+ * Conventions shared by every entry point:
+ *  - All data pointers are DEVICE pointers owned by the caller; the library
+ *    allocates nothing, keeps no per-call state and never frees.  Host
+ *    pointers (the bqd_cq_matrix descriptor itself) are read during the call
+ *    only.
+ *  - `stream` is a hipStream_t (NULL: the null stream).  Calls only enqueue
+ *    work and return; results are valid once the stream has reached them.
+ *  - Arrays are dense, C order, with the element types stated.  Pointers must
+ *    be aligned to their element size (float/int32: 4 bytes, fp16: 2 bytes).
+ *  - Every argument is validated on the host before anything is enqueued; a
+ *    call that returns an error has enqueued nothing.  Return value: BQD_OK
+ *    or one of the negative codes below.  A zero-sized problem (no rows, no
+ *    vectors, no ids) is valid and enqueues nothing.
+ *  - Results are deterministic: a fixed reduction order, no atomics.
+ *  - Concurrent calls on different streams are safe; the library holds no
+ *    mutable global state.
+ */
+#ifndef BQD_H
+#define BQD_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    BQD_OK = 0,
+    BQD_EINVAL = -1,    /* a shape or parameter outside the documented range */
+    BQD_EOVERFLOW = -2, /* a size product does not fit in int64              */
+    BQD_EALIGN = -3,    /* a pointer not aligned to its element size          */
+    BQD_ENULL = -4,     /* a required pointer is NULL                         */
+    BQD_EHIP = -5       /* the HIP runtime reported a launch error            */
+};
+
+/* A codebook-quantized matrix, the record of [P3] §4.  Row r, padded column
+ * c (0 <= c < input_padded) holds a `bits`-wide codebook index stored at bit
+ * offset bits*c of the row's little-endian bit stream (bit t of a row is bit
+ * t%8 of byte t/8): for 2-bit, crumb k of a byte is (byte >> 2k) & 3 as in
+ * [P1] §3; for 4-bit the low nibble is the even column.  Bits past the last
+ * index of a row are ignored.  The matrix acts on the Walsh–Hadamard domain:
+ * its dense row is recovered by the "Row gather" of [P1]. */
+typedef struct bqd_cq_matrix {
+    int64_t output;        /* rows, >= 0                                        */
+    int64_t input;         /* unpadded columns, 0 <= input <= input_padded      */
+    int64_t input_padded;  /* stored columns, > 0, a multiple of group          */
+    int64_t group;         /* transform block, a power of two in [1, 1024]      */
+    int64_t bits;          /* 2, 3, 4 or 5                                      */
+    int64_t row_bytes;     /* stride of packed rows, >= ceil(input_padded*bits/8) */
+    const uint8_t *packed;   /* [output][row_bytes]                               */
+    const uint16_t *norms;   /* fp16 bit patterns [output][input_padded / group]  */
+    const float *codebook;   /* [1 << bits] fp32                                  */
+} bqd_cq_matrix;
+
+/* [P1] §1–§2.  For each of `batch` vectors: p = x zero-padded to
+ * input_padded; for each group, the unnormalized fast Walsh–Hadamard
+ * transform (stride 1, 2, ..., group/2; pairs become (a + b, a - b) in fp32),
+ * then every element is multiplied by 1/sqrt(group) (formed in fp64, rounded
+ * once to fp32).  Bit-exact with that sequence of fp32 operations.
+ *   x:        fp32 [batch][m->input]          (may be NULL when input == 0)
+ *   prepared: fp32 [batch][m->input_padded]   (must not overlap x)
+ * Only the shape fields of `m` are read.  One prepared vector may feed any
+ * number of cq_matvec calls on matrices of the same input_padded and group.
+ * Errors: BQD_EINVAL (shape fields, batch < 0), BQD_ENULL, BQD_EALIGN,
+ * BQD_EOVERFLOW, BQD_EHIP. */
+int cq_prepare(const bqd_cq_matrix *m, const float *x, float *prepared,
+               int64_t batch, void *stream);
+
+/* [P1] §3 with the row range of §6: for b < batch and i < row_count, with
+ * r = row_begin + i,
+ *   y[b][i] = sum over groups g of  f16(norms[r][g]) *
+ *             sum over c in g of codebook[index(r, c)] * prepared[b][c].
+ * Accumulation is fp32 (tolerance against the fp64 sum:
+ * 1e-4 * sum|w*x| + 1e-6 per output).
+ *   prepared: fp32 [batch][m->input_padded]   (the output of cq_prepare)
+ *   y:        fp32 [batch][row_count]
+ * Errors: BQD_EINVAL (shape fields, batch < 0, row range outside
+ * [0, output]), BQD_ENULL, BQD_EALIGN, BQD_EOVERFLOW, BQD_EHIP. */
+int cq_matvec(const bqd_cq_matrix *m, const float *prepared, float *y,
+              int64_t batch, int64_t row_begin, int64_t row_count, void *stream);
+
+/* [P1] "Row gather": for i < n, out[i][c] for c < input is the dense row
+ * rows[i]: per group, codebook value times norm (fp32 product), the
+ * unnormalized transform as in cq_prepare, times 1/sqrt(group), keeping the
+ * first `input` columns.  Bit-exact with that sequence of fp32 operations.
+ * Ids may repeat.  An id outside [0, output) cannot be checked on the host
+ * without a synchronization: its output row is filled with quiet NaNs.
+ *   rows: int32 [n]              out: fp32 [n][m->input]
+ * Errors: BQD_EINVAL (shape fields, n < 0), BQD_ENULL, BQD_EALIGN,
+ * BQD_EOVERFLOW, BQD_EHIP. */
+int cq_gather_rows(const bqd_cq_matrix *m, const int32_t *rows, int64_t n,
+                   float *out, void *stream);
+
+/* [P4] Step 1: y[b][r] = sum over c < C of e4m3(w[r][c]) *
+ * e8m0(scale[r*SR/R][c*SC/C]) * x[b][c], with the scale indices by integer
+ * floor division.  E4M3: sign, 4-bit exponent e, 3-bit mantissa m; e = 0 is
+ * subnormal (m/8 * 2^-6), otherwise (1 + m/8) * 2^(e-7), magnitudes above 448
+ * clamped to 448 (codes 0x7F and 0xFF are +-448).  E8M0: 2^(e-127), the byte
+ * 255 is NaN.  Accumulation is fp32 (same tolerance as cq_matvec).
+ *   w:     E4M3 codes [R][C]     scale: E8M0 bytes [SR][SC]
+ *   x:     fp32 [batch][C]       y:     fp32 [batch][R]
+ * Requires R >= 0, C >= 1, 1 <= SR <= max(R, 1), 1 <= SC <= C, batch >= 0.
+ * Errors: BQD_EINVAL, BQD_ENULL, BQD_EALIGN, BQD_EOVERFLOW, BQD_EHIP. */
+int f8_matvec(const uint8_t *w, int64_t R, int64_t C, const uint8_t *scale,
+              int64_t SR, int64_t SC, const float *x, float *y, int64_t batch,
+              void *stream);
+
+/* Test probes: run the very device decode routines the kernels use.
+ * bqd_dbg_cq_unpack: idx[c] = index(row, c) for c < input_padded (uint8).
+ * bqd_dbg_f16_decode: out[i] = fp16 codes[i] as fp32 (the norm decode).
+ * bqd_dbg_f8_decode: out[i] = e4m3(codes[i]) (the weight decode).
+ * bqd_dbg_e8m0_decode: out[i] = e8m0(codes[i]) (the scale decode).
+ * Same conventions and error codes as above; n >= 0; row in [0, output). */
+int bqd_dbg_cq_unpack(const bqd_cq_matrix *m, int64_t row, uint8_t *idx, void *stream);
+int bqd_dbg_f16_decode(const uint16_t *codes, int64_t n, float *out, void *stream);
+int bqd_dbg_f8_decode(const uint8_t *codes, int64_t n, float *out, void *stream);
+int bqd_dbg_e8m0_decode(const uint8_t *codes, int64_t n, float *out, void *stream);
+
+/* A static, human-readable name for a status code. */
+const char *bqd_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BQD_H */

@@ -1,0 +1,143 @@
+"""CPU-only checks of the C ABI library: it loads, exports every symbol the
+header declares, and rejects bad arguments with the documented status codes
+before anything is enqueued (no call here reaches a kernel launch: each one
+either fails validation or describes an empty problem)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import bit_quantized_decode_amd as bqd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bqd.h")
+
+OK, EINVAL, EOVERFLOW, EALIGN, ENULL, EHIP = 0, -1, -2, -3, -4, -5
+FAKE = 0x10000  # an aligned, never dereferenced device address
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_four_operations():
+    names = declared_functions()
+    for n in ("cq_prepare", "cq_matvec", "cq_gather_rows", "f8_matvec"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(bqd.LIB_PATH)
+    names = declared_functions()
+    assert set(names) == set(bqd.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    L = bqd.lib()
+    for code in (OK, EINVAL, EOVERFLOW, EALIGN, ENULL, EHIP):
+        assert L.bqd_status_string(code) not in (None, b"", b"unknown status")
+    assert L.bqd_status_string(42) == b"unknown status"
+
+
+def cq(**kw):
+    f = dict(output=256, input=200, input_padded=256, group=64, bits=2, row_bytes=64,
+             packed=FAKE, norms=FAKE, codebook=FAKE)
+    f.update(kw)
+    return bqd._CqStruct(**f)
+
+
+def matvec(m, prepared=FAKE, y=FAKE, batch=1, row_begin=0, row_count=None):
+    rc_ = m.output - row_begin if row_count is None else row_count
+    return bqd.lib().cq_matvec(ctypes.byref(m), prepared, y, batch, row_begin, rc_, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bits=1), EINVAL), (dict(bits=6), EINVAL), (dict(bits=8), EINVAL),
+    (dict(group=3), EINVAL), (dict(group=0), EINVAL), (dict(group=2048, input_padded=2048), EINVAL),
+    (dict(input_padded=250), EINVAL), (dict(input_padded=0), EINVAL),
+    (dict(input=257), EINVAL), (dict(input=-1), EINVAL),
+    (dict(row_bytes=63), EINVAL), (dict(row_bytes=0), EINVAL), (dict(output=-1), EINVAL),
+    (dict(output=1 << 31), EINVAL),
+    (dict(row_bytes=1 << 62, output=8), EOVERFLOW),
+    (dict(packed=0), ENULL), (dict(norms=0), ENULL), (dict(codebook=0), ENULL),
+    (dict(norms=FAKE + 1), EALIGN), (dict(codebook=FAKE + 2), EALIGN),
+])
+def test_cq_matvec_rejects(kw, code):
+    assert matvec(cq(**kw)) == code
+
+
+def test_cq_matvec_argument_errors():
+    m = cq()
+    assert matvec(m, row_begin=-1, row_count=1) == EINVAL
+    assert matvec(m, row_begin=10, row_count=247) == EINVAL
+    assert matvec(m, row_begin=257, row_count=0) == EINVAL
+    assert matvec(m, batch=-1) == EINVAL
+    assert matvec(m, prepared=0) == ENULL
+    assert matvec(m, y=0) == ENULL
+    assert matvec(m, prepared=FAKE + 2) == EALIGN
+    assert matvec(m, y=FAKE + 1) == EALIGN
+    # empty problems are valid and enqueue nothing
+    assert matvec(m, batch=0) == OK
+    assert matvec(m, row_begin=256, row_count=0) == OK
+    assert matvec(cq(output=0), prepared=0, y=0) == OK
+
+
+def test_cq_prepare_argument_errors():
+    L = bqd.lib()
+    m = cq()
+    assert L.cq_prepare(ctypes.byref(m), FAKE, FAKE + 1 << 20, -1, None) == EINVAL
+    assert L.cq_prepare(ctypes.byref(m), 0, FAKE, 1, None) == ENULL
+    assert L.cq_prepare(ctypes.byref(m), FAKE + 1, FAKE << 4, 1, None) == EALIGN
+    assert L.cq_prepare(ctypes.byref(m), FAKE, FAKE + 16, 1, None) == EINVAL  # overlap
+    assert L.cq_prepare(ctypes.byref(cq(bits=9)), FAKE, FAKE << 4, 1, None) == EINVAL
+    assert L.cq_prepare(ctypes.byref(m), FAKE, FAKE << 4, 0, None) == OK
+    assert L.cq_prepare(None, FAKE, FAKE << 4, 1, None) == ENULL
+
+
+def test_cq_gather_argument_errors():
+    L = bqd.lib()
+    m = cq()
+    assert L.cq_gather_rows(ctypes.byref(m), FAKE, -1, FAKE << 4, None) == EINVAL
+    assert L.cq_gather_rows(ctypes.byref(m), 0, 4, FAKE << 4, None) == ENULL
+    assert L.cq_gather_rows(ctypes.byref(m), FAKE + 2, 4, FAKE << 4, None) == EALIGN
+    assert L.cq_gather_rows(ctypes.byref(cq(group=6)), FAKE, 4, FAKE << 4, None) == EINVAL
+    assert L.cq_gather_rows(ctypes.byref(m), FAKE, 0, FAKE << 4, None) == OK
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(R=-1), EINVAL), (dict(C=0), EINVAL), (dict(SR=0), EINVAL), (dict(SC=0), EINVAL),
+    (dict(SR=513), EINVAL), (dict(SC=4097), EINVAL), (dict(batch=-1), EINVAL),
+    (dict(R=1 << 31), EINVAL), (dict(C=1 << 28), EINVAL),
+    (dict(w=0), ENULL), (dict(scale=0), ENULL), (dict(x=0), ENULL), (dict(y=0), ENULL),
+    (dict(x=FAKE + 1), EALIGN), (dict(y=FAKE + 2), EALIGN),
+    (dict(batch=0), OK), (dict(R=0, SR=1), OK),
+])
+def test_f8_matvec_rejects(args, code):
+    a = dict(w=FAKE, R=512, C=4096, scale=FAKE, SR=4, SC=32, x=FAKE, y=FAKE, batch=1)
+    a.update(args)
+    rc = bqd.lib().f8_matvec(a["w"], a["R"], a["C"], a["scale"], a["SR"], a["SC"], a["x"],
+                             a["y"], a["batch"], None)
+    assert rc == code
+
+
+def test_probe_argument_errors():
+    L = bqd.lib()
+    assert L.bqd_dbg_f16_decode(FAKE + 1, 4, FAKE, None) == EALIGN
+    assert L.bqd_dbg_f8_decode(0, 4, FAKE, None) == ENULL
+    assert L.bqd_dbg_e8m0_decode(FAKE, -1, FAKE, None) == EINVAL
+    assert L.bqd_dbg_f8_decode(FAKE, 0, FAKE, None) == OK
+    m = cq()
+    assert L.bqd_dbg_cq_unpack(ctypes.byref(m), 256, FAKE, None) == EINVAL
+    assert L.bqd_dbg_cq_unpack(ctypes.byref(m), 0, 0, None) == ENULL
+
+
+def test_binding_refuses_host_tensors():
+    with pytest.raises(TypeError):
+        bqd.f8_matvec(torch.zeros(4, 16, dtype=torch.uint8), torch.zeros(1, 1, dtype=torch.uint8),
+                      torch.zeros(16))

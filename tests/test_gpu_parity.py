@@ -1,0 +1,382 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bit-exact: index decode, fp16 / E4M3 / E8M0 value decode, prepare, gather,
+and the one-hot cases whose sums are exact.  fp32 dots: per output
+|gpu - oracle| <= 1e-4 * sum|w*x| + 1e-6 (sum|w*x| from the oracle).
+Sizes: the five workloads at full size (the head's outputs sampled by row
+blocks the oracle computes one by one), plus small shapes that cover every
+bit width, every fast-kernel lane layout, ragged row counts, padded rows and
+the generic (unaligned / odd-width) path.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+import bit_quantized_decode_amd as bqd
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def tol_ok(got, ref, mag):
+    got = np.asarray(got, dtype=np.float64)
+    return np.abs(got - ref) <= 1e-4 * mag + 1e-6
+
+
+def assert_tol(got, ref, mag, what):
+    ok = tol_ok(got, ref, mag)
+    if not ok.all():
+        i = np.argwhere(~ok)[0]
+        raise AssertionError(f"{what}: {int((~ok).sum())} outputs out of tolerance, first at "
+                             f"{tuple(i)}: gpu={np.asarray(got)[tuple(i)]} oracle={ref[tuple(i)]} "
+                             f"mag={mag[tuple(i)]}")
+
+
+def dev_matrix(case):
+    s = case.shape
+    return bqd.CqMatrix.from_arrays(case.packed, case.norms, case.codebook, output=s.output,
+                                    input=s.input, input_padded=s.input_padded, group=s.group,
+                                    bits=s.bits, row_bytes=s.stride)
+
+
+def host_matrix(case):
+    return oracle.CqMatrix.from_case(case)
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def bits_eq(a, b):
+    a = np.asarray(a, np.float32)
+    b = np.asarray(b, np.float32)
+    return a.shape == b.shape and np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ---------------------------------------------------------------- workloads
+WORKLOADS = {name: build for i in range(1, 6) for name, build in synth.config_cases(i)}
+
+
+@pytest.fixture(scope="module")
+def cache():
+    return {}
+
+
+def workload(cache, name):
+    if name not in cache:
+        print(f"[case] building {name}", flush=True)
+        cache[name] = WORKLOADS[name]()
+    return cache[name]
+
+
+CQ_WORKLOADS = [n for n in WORKLOADS if n.startswith("cq")]
+
+# Small CQ shapes: every bit width and every fast lane layout (rows of 8..256
+# chunks of 32 columns), ragged row counts, padded rows; then generic-path
+# shapes (odd widths, groups under 32, rows not a dword multiple).
+SMALL = [
+    synth.CqShape(100, 256, 256, 32, 2), synth.CqShape(77, 500, 512, 64, 3),
+    synth.CqShape(45, 1000, 1024, 128, 4), synth.CqShape(33, 2048, 2048, 256, 5),
+    synth.CqShape(19, 4096, 4096, 512, 3), synth.CqShape(9, 8192, 8192, 1024, 4),
+    synth.CqShape(21, 300, 512, 32, 4, row_bytes=260), synth.CqShape(13, 256, 256, 64, 5, row_bytes=176),
+    synth.CqShape(5, 3, 4, 4, 2), synth.CqShape(7, 13, 16, 4, 3), synth.CqShape(6, 30, 32, 8, 5),
+    synth.CqShape(9, 64, 64, 16, 4, row_bytes=40), synth.CqShape(4, 100, 128, 32, 3, row_bytes=53),
+    synth.CqShape(11, 96, 96, 32, 2), synth.CqShape(3, 250, 256, 128, 5, row_bytes=161),
+]
+
+
+def small_case(i, batch=1):
+    return synth.make_cq(SMALL[i], seed=1000 + i, batch=batch, n_ids=23)
+
+
+# ------------------------------------------------------------ decode probes
+def test_probe_f8_all_codes():
+    for n in (256, 255, 5):
+        codes = np.arange(n, dtype=np.uint8)[::-1].copy()
+        got = bqd.dbg_f8_decode(to_dev(codes)).cpu().numpy()
+        ref = oracle.e4m3_all()[codes]
+        assert bits_eq(got, ref), np.flatnonzero(got.view(np.uint32) != ref.view(np.uint32))
+
+
+def test_probe_e8m0_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    got = bqd.dbg_e8m0_decode(to_dev(codes)).cpu().numpy()
+    ref = oracle.e8m0_all()
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert bits_eq(got[:255], ref[:255])
+
+
+def test_probe_f16_all_codes():
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = bqd.dbg_f16_decode(to_dev(codes.view(np.int16))).cpu().numpy()
+    ref = oracle.f16_array(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert bits_eq(got[~nan], ref[~nan])
+
+
+def check_unpack(case, rows):
+    m, h = dev_matrix(case), host_matrix(case)
+    for r in rows:
+        got = bqd.dbg_cq_unpack(m, int(r)).cpu().numpy()
+        assert np.array_equal(got, oracle.cq_unpack_row(h, int(r))), (case.shape, r)
+
+
+@pytest.mark.parametrize("name", ["cq2_256x200", "cq3_2048x512", "cq5_2048x512",
+                                  "cq4_65536x512_vocab_gather", "cq4_16384x4096_b1"])
+def test_unpack_workloads(cache, name):
+    case = workload(cache, name)
+    R = case.shape.output
+    rows = range(R) if R <= 256 else np.unique(np.r_[0, 1, R - 1, np.random.default_rng(0).integers(0, R, 40)])
+    check_unpack(case, rows)
+
+
+@pytest.mark.parametrize("i", range(len(SMALL)))
+def test_unpack_small(i):
+    case = small_case(i)
+    check_unpack(case, range(case.shape.output))
+
+
+# ------------------------------------------------------------------ prepare
+def check_prepare(case):
+    m, h = dev_matrix(case), host_matrix(case)
+    got = bqd.cq_prepare(m, to_dev(case.x)).cpu().numpy()
+    ref = oracle.cq_prepare(h, case.x)
+    assert bits_eq(got, ref), (case.shape, np.argwhere(got.view(np.uint32) != ref.view(np.uint32))[:5])
+
+
+@pytest.mark.parametrize("name", CQ_WORKLOADS)
+def test_prepare_workloads(cache, name):
+    check_prepare(workload(cache, name))
+
+
+@pytest.mark.parametrize("i", range(len(SMALL)))
+def test_prepare_small(i):
+    check_prepare(small_case(i, batch=3))
+
+
+# ------------------------------------------------------------------- matvec
+def check_matvec(case, row_begin=0, row_count=None):
+    s = case.shape
+    row_count = s.output - row_begin if row_count is None else row_count
+    m, h = dev_matrix(case), host_matrix(case)
+    p_dev = bqd.cq_prepare(m, to_dev(case.x))
+    p = p_dev.cpu().numpy()
+    got = bqd.cq_matvec(m, p_dev, row_begin=row_begin, row_count=row_count).cpu().numpy()
+    ref, mag = oracle.cq_matvec(h, p, row_begin, row_count)
+    assert_tol(got, ref, mag, f"cq_matvec {s} rows [{row_begin}, +{row_count})")
+    return got
+
+
+@pytest.mark.parametrize("name", CQ_WORKLOADS)
+def test_matvec_workloads(cache, name):
+    print(f"[case] matvec {name}", flush=True)
+    check_matvec(workload(cache, name))
+
+
+@pytest.mark.parametrize("i", range(len(SMALL)))
+@pytest.mark.parametrize("batch", [1, 3, 6])
+def test_matvec_small(i, batch):
+    check_matvec(small_case(i, batch=batch))
+
+
+def test_matvec_row_ranges(cache):
+    case = workload(cache, "cq4_16384x4096_b1")
+    for rb, rc in ((0, 1), (1000, 3001), (16383, 1), (5, 16379)):
+        check_matvec(case, rb, rc)
+    small = small_case(0, batch=2)
+    for rb, rc in ((0, 1), (3, 50), (99, 1)):
+        check_matvec(small, rb, rc)
+
+
+def one_hot_inputs(s, cols):
+    """x whose prepared vector is exactly e_k for each k in cols: column k of
+    the normalized Hadamard block of k's group (every entry +-1/sqrt(g), an
+    exact power of two for g = 4^n)."""
+    g = s.group
+    H = scipy.linalg.hadamard(g)
+    x = np.zeros((len(cols), s.input), np.float32)
+    for b, k in enumerate(cols):
+        g0 = (k // g) * g
+        x[b, g0:g0 + g] = H[:, k - g0] / math.sqrt(g)
+    return x
+
+
+@pytest.mark.parametrize("shape,cols", [
+    (synth.C4, [0, 31, 32, 255, 256 * 7 + 100, 4095]),
+    (synth.C1, [0, 63, 64, 130, 191]),
+    (synth.CqShape(64, 1024, 1024, 256, 3), [0, 33, 1023]),
+    (synth.CqShape(48, 2048, 2048, 64, 5), [5, 700, 2047]),
+    (synth.CqShape(40, 256, 256, 16, 2), [0, 17, 255]),
+])
+def test_matvec_one_hot_decodes_indices_exactly(shape, cols):
+    """codebook[i] = i, norms = 1: y[r] = idx(r, k) exactly, through the fast
+    kernels at batch 1 and the shared-weight batch path."""
+    case = synth.make_cq(shape, seed=77)
+    case.codebook = np.arange(1 << shape.bits, dtype=np.float32)
+    case.norms[:] = 0x3C00
+    case.x = one_hot_inputs(shape, cols)
+    m, h = dev_matrix(case), host_matrix(case)
+    p = bqd.cq_prepare(m, to_dev(case.x))
+    pe = np.zeros((len(cols), shape.input_padded), np.float32)
+    pe[np.arange(len(cols)), cols] = 1.0
+    assert bits_eq(p.cpu().numpy(), pe)
+    ref = np.stack([[oracle.cq_index(h, r, k) for r in range(shape.output)] for k in cols])
+    y1 = np.stack([bqd.cq_matvec(m, p[b:b + 1]).cpu().numpy()[0] for b in range(len(cols))])
+    yb = bqd.cq_matvec(m, p).cpu().numpy()
+    assert np.array_equal(y1, ref.astype(np.float32))
+    assert np.array_equal(yb, ref.astype(np.float32))
+
+
+def test_matvec_unaligned_packed_uses_generic_path():
+    case = synth.make_cq(synth.CqShape(50, 512, 512, 128, 4), seed=5)
+    s = case.shape
+    m = dev_matrix(case)
+    buf = torch.zeros(m.packed.numel() + 1, dtype=torch.uint8, device=DEV)
+    buf[1:] = m.packed.reshape(-1)
+    mo = bqd.CqMatrix(buf[1:], m.norms, m.codebook, output=s.output, input=s.input,
+                      input_padded=s.input_padded, group=s.group, bits=s.bits, row_bytes=s.stride)
+    p = bqd.cq_prepare(m, to_dev(case.x))
+    ref, mag = oracle.cq_matvec(host_matrix(case), p.cpu().numpy())
+    assert_tol(bqd.cq_matvec(mo, p).cpu().numpy(), ref, mag, "unaligned packed")
+    got = bqd.dbg_cq_unpack(mo, 7).cpu().numpy()
+    assert np.array_equal(got, oracle.cq_unpack_row(host_matrix(case), 7))
+
+
+def test_matvec_deterministic(cache):
+    case = workload(cache, "cq4_16384x4096_b8")
+    m = dev_matrix(case)
+    p = bqd.cq_prepare(m, to_dev(case.x))
+    a = bqd.cq_matvec(m, p).cpu().numpy()
+    b = bqd.cq_matvec(m, p).cpu().numpy()
+    assert bits_eq(a, b)
+
+
+# ------------------------------------------------------------------- gather
+def check_gather(case, ids):
+    m, h = dev_matrix(case), host_matrix(case)
+    got = bqd.cq_gather_rows(m, to_dev(ids.astype(np.int32))).cpu().numpy()
+    ref, _ = oracle.cq_gather(h, ids)
+    assert bits_eq(got, ref), (case.shape, np.argwhere(got.view(np.uint32) != ref.view(np.uint32))[:5])
+
+
+def test_gather_workload(cache):
+    case = workload(cache, "cq4_65536x512_vocab_gather")
+    check_gather(case, case.ids)
+
+
+@pytest.mark.parametrize("i", range(len(SMALL)))
+def test_gather_small(i):
+    case = small_case(i)
+    check_gather(case, np.concatenate([case.ids, case.ids[:3]]))
+
+
+def test_gather_identity_with_matvec(cache):
+    """The pages' test, end to end on the GPU: matvec[row] ~ dot(gathered row, x)."""
+    case = workload(cache, "cq4_65536x512_vocab_gather")
+    m = dev_matrix(case)
+    rows = case.ids[:512]
+    dense = bqd.cq_gather_rows(m, to_dev(rows)).cpu().numpy().astype(np.float64)
+    y = bqd.cq_matvec(m, bqd.cq_prepare(m, to_dev(case.x))).cpu().numpy()[0]
+    _, mag = oracle.cq_matvec(host_matrix(case), oracle.cq_prepare(host_matrix(case), case.x[0]))
+    assert np.all(np.abs(y[rows] - dense @ case.x[0].astype(np.float64)) <= 1e-4 * mag[rows] + 1e-6)
+
+
+def test_gather_out_of_range_ids_give_nan_rows():
+    case = small_case(1)
+    m = dev_matrix(case)
+    ids = np.array([0, -1, case.shape.output, 2], np.int32)
+    got = bqd.cq_gather_rows(m, to_dev(ids)).cpu().numpy()
+    ref, _ = oracle.cq_gather(host_matrix(case), ids[[0, 3]])
+    assert bits_eq(got[[0, 3]], ref)
+    assert np.isnan(got[1]).all() and np.isnan(got[2]).all()
+
+
+# ----------------------------------------------------------------------- F8
+def dev_f8(case):
+    return to_dev(case.w), to_dev(case.scale), to_dev(case.x)
+
+
+def check_f8(case, row_blocks=None):
+    w, s, x = dev_f8(case)
+    got = bqd.f8_matvec(w, s, x).cpu().numpy()
+    blocks = row_blocks or [(0, case.R)]
+    for rb, rc in blocks:
+        ref, mag = oracle.f8_matvec(case.w, case.R, case.C, case.scale, case.SR, case.SC, case.x,
+                                    rb, rc)
+        assert_tol(got[:, rb:rb + rc], ref, mag, f"f8 {case.R}x{case.C} rows [{rb}, +{rc})")
+    return got
+
+
+def test_f8_wkv(cache):
+    check_f8(workload(cache, "f8_wkv_512x4096"))
+
+
+def test_f8_head_sampled_rows(cache):
+    case = workload(cache, "f8_head_246272x4096")
+    rng = np.random.default_rng(1)
+    starts = rng.integers(0, case.R // 128, 14) * 128
+    blocks = [(0, 256), (case.R - 200, 200)] + [(int(s0), 128) for s0 in starts]
+    print("[case] f8 head full launch, sampled oracle rows", flush=True)
+    got = check_f8(case, blocks)
+    w, s, x = dev_f8(case)
+    again = bqd.f8_matvec(w, s, x).cpu().numpy()
+    assert bits_eq(got, again)
+
+
+@pytest.mark.parametrize("R,C,SR,SC,batch", [
+    (10, 7, 3, 2, 1), (130, 260, 3, 5, 2), (64, 128, 1, 1, 1), (257, 4096, 3, 32, 1),
+    (300, 1024, 3, 8, 3), (129, 2048, 2, 16, 1), (77, 8192, 1, 64, 1), (40, 768, 4, 3, 1),
+    (33, 128, 33, 8, 1),
+])
+def test_f8_shapes(R, C, SR, SC, batch):
+    check_f8(synth.make_f8(R, C, SR, SC, seed=R * 7 + C, batch=batch))
+
+
+def test_f8_one_hot_all_codes():
+    """Each of the 256 codes through the fast and the generic kernel: with
+    x = e_c the row sum is a single exact product."""
+    for C, SC, col in ((4096, 32, 1000), (100, 3, 42)):
+        case = synth.make_f8(256, C, 2, SC, seed=3)
+        case.w[:, col] = np.arange(256, dtype=np.uint8)
+        case.x = np.zeros((1, C), np.float32)
+        case.x[0, col] = 1.0
+        w, s, x = dev_f8(case)
+        got = bqd.f8_matvec(w, s, x).cpu().numpy()[0]
+        ref = np.array([oracle.e4m3(r) * math.ldexp(1.0, int(case.scale[(r * 2) // 256,
+                        (col * SC) // C]) - 127) for r in range(256)], np.float32)
+        assert np.array_equal(got, ref), C
+
+
+def test_f8_unaligned_weight_pointer():
+    case = synth.make_f8(64, 1024, 1, 8, seed=9)
+    buf = torch.zeros(64 * 1024 + 16, dtype=torch.uint8, device=DEV)
+    buf[3:3 + 64 * 1024] = to_dev(case.w).reshape(-1)
+    w = buf[3:3 + 64 * 1024].view(64, 1024)
+    got = bqd.f8_matvec(w, to_dev(case.scale), to_dev(case.x)).cpu().numpy()
+    ref, mag = oracle.f8_matvec(case.w, 64, 1024, case.scale, 1, 8, case.x)
+    assert_tol(got, ref, mag, "unaligned f8")
+
+
+# -------------------------------------------------------------- empty calls
+def test_empty_problems_are_no_ops():
+    case = small_case(0)
+    m = dev_matrix(case)
+    s = case.shape
+    y = torch.full((1, 0), 7.0, device=DEV)
+    bqd.cq_matvec(m, torch.zeros(1, s.input_padded, device=DEV), row_begin=s.output, row_count=0, out=y)
+    out = bqd.cq_gather_rows(m, torch.zeros(0, dtype=torch.int32, device=DEV))
+    assert out.shape == (0, s.input)
+    p = bqd.cq_prepare(m, torch.zeros(0, s.input, device=DEV))
+    assert p.shape == (0, s.input_padded)
+    yf = bqd.f8_matvec(torch.zeros(0, 16, dtype=torch.uint8, device=DEV),
+                       torch.full((1, 1), 127, dtype=torch.uint8, device=DEV),
+                       torch.zeros(1, 16, device=DEV))
+    assert yf.shape == (1, 0)
+    torch.cuda.synchronize()
