@@ -168,6 +168,21 @@ def cpu_baseline(data, threads):
     }
 
 
+def capture(torch, fn):
+    """A CUDA/HIP graph of fn(): warm up on a side stream, then capture."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -184,63 +199,59 @@ def main():
     cases, data = build_cases(torch, bqd, synth, args.hot)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    period = max(len(c.calls) for c in cases)  # weight copies rotate with this period
 
-    head_case = cases[-1]
-
-    def step(i, events=None):
-        """One step; `events` collects (start, end) around the listed stages."""
-        for c in cases:
-            fn = c.calls[i % len(c.calls)]
-            if events is not None and c in events:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                fn()
-                e1.record(stream)
-                events[c].append((e0, e1))
-            else:
-                fn()
+    # One graph per rotation index: the whole step (every stage, in order).
+    log(f"capturing {period} step graphs")
+    step_graphs = [capture(torch, lambda k=k: [c.calls[k % len(c.calls)]() for c in cases])
+                   for k in range(period)]
+    # Per stage: one graph of `period` back-to-back launches over the copies.
+    stage_graphs = {c.name: capture(torch, lambda c=c: [c.calls[k % len(c.calls)]()
+                                                       for k in range(period)])
+                    for c in cases}
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
-        step(i)
+        step_graphs[i % period].replay()
     torch.cuda.synchronize()
-    # The timed region: K whole steps.  HIP events on the launch stream bracket
-    # the dominant kernel (the F8 head) inside it for the roofline figure.
+    # The timed region: exactly K steps, synchronized on both sides.
     log(f"timing {args.steps} steps")
-    head_events = {head_case: []}
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, head_events)
+        step_graphs[i % period].replay()
     torch.cuda.synchronize()
     step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    head_ms = np.array([a.elapsed_time(b) for a, b in head_events[head_case]])
-    # Per-stage breakdown: a second pass with events around every stage.
-    stage_events = {c: [] for c in cases}
-    for i in range(args.steps):
-        step(i, stage_events)
-    torch.cuda.synchronize()
-    for c in cases:
-        c.ms = [a.elapsed_time(b) for a, b in stage_events[c]]
+
+    # Kernel durations: HIP events on the launch stream bracket replays of
+    # each stage's graph of `period` back-to-back launches.
+    reps = max(4, args.steps // period)
     per_case = {}
     for c in cases:
-        ms = np.array(c.ms)
+        g = stage_graphs[c.name]
+        g.replay()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) / period
+        c.ms = ms
+        gbs = c.nbytes / (ms.mean() * 1e-3) / 1e9
         per_case[c.name] = dict(
-            us_mean=round(float(ms.mean() * 1e3), 3), us_median=round(float(np.median(ms) * 1e3), 3),
-            us_p10=round(float(np.percentile(ms, 10) * 1e3), 3),
-            us_p90=round(float(np.percentile(ms, 90) * 1e3), 3),
-            bytes=c.nbytes, gbs=round(c.nbytes / (ms.mean() * 1e-3) / 1e9, 1),
-            frac_hbm=round(c.nbytes / (ms.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            us_mean=round(float(ms.mean() * 1e3), 3), us_p10=round(float(np.percentile(ms, 10) * 1e3), 3),
+            us_p90=round(float(np.percentile(ms, 90) * 1e3), 3), bytes=c.nbytes,
+            gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4),
             rows_per_s=round(c.rows / (ms.mean() * 1e-3), 1) if c.rows else None)
     total_bytes = sum(c.nbytes for c in cases)
     total_rows = sum(c.rows for c in cases)
     value = total_bytes / (step_ms * 1e-3) / 1e9
-    head_gbs = head_case.nbytes / (head_ms.mean() * 1e-3) / 1e9
+    head = per_case["f8_head_246272x4096_matvec"]
     roofline = dict(bound="hbm", kernel="f8_matvec_fast (F8 head 246272x4096)",
-                    achieved=round(head_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(head_gbs / HBM_PEAK_GBS, 4), traffic=None,
-                    us_per_launch=round(float(head_ms.mean() * 1e3), 3),
-                    bytes_per_launch=head_case.nbytes)
+                    achieved=head["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(head["gbs"] / HBM_PEAK_GBS, 4), traffic=None,
+                    us_per_launch=head["us_mean"], bytes_per_launch=head["bytes"])
     cpu = None
     if not args.no_cpu_baseline:
         n = args.cpu_threads or min(16, len(os.sched_getaffinity(0)))
@@ -256,6 +267,7 @@ def main():
                                "with E8M0 [1924x32] scales",
                    "mode": "hot (one weight copy)" if args.hot else
                            "cold (weights rotated past the 256 MB Infinity Cache)",
+                   "launch": "one HIP graph replay per step",
                    "parallelism": "single GPU"},
         "rows_per_s": round(total_rows / (step_ms * 1e-3), 1),
         "frac_hbm_step": round(value / HBM_PEAK_GBS, 4),

@@ -9,6 +9,7 @@
 // keep the unpadded columns) and §6 (a row range of a matrix).  The record
 // layout is that of "Inference engine, part 1: loader and tokenizer", §4.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 
 #include "device.h"
@@ -16,26 +17,20 @@
 
 namespace bqd {
 
-constexpr int kThreads = 256;       // 4 wavefronts per workgroup
-constexpr int kTransformChunk = 1024;  // floats per workgroup in prepare/gather
+constexpr int kThreads = 256;  // 4 wavefronts per workgroup
+constexpr int kWavesPerBlock = kThreads / kWave;
 
-// ---------------------------------------------------------------------------
-// Shared transform step: the butterflies of one chunk held in LDS, stride
-// ascending over 1 .. group/2, each pair (a, b) -> (a + b, a - b) in fp32 —
-// the same operations, operands and order as the scalar loop on the page, so
-// results are bit-identical to it.  `n` is a multiple of `group`.
-__device__ __forceinline__ void lds_fwht(float* buf, int n, int log2_group) {
-  for (int ls = 0; ls < log2_group; ++ls) {
-    const int s = 1 << ls;
-    for (int t = threadIdx.x; t < (n >> 1); t += kThreads) {
-      const int i = ((t >> ls) << (ls + 1)) | (t & (s - 1));
-      const float a = buf[i];
-      const float b = buf[i + s];
-      buf[i] = a + b;
-      buf[i + s] = a - b;
-    }
-    __syncthreads();
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
+  return n;
 }
 
 // 1/sqrt(group) is applied as the page does: the scale is an fp64 value, the
@@ -44,86 +39,121 @@ __device__ __forceinline__ float scale_store(float v, double scale) {
   return (float)((double)v * scale);
 }
 
+// Elements per lane of the wavefront transform: a wavefront spans one group
+// (64 * E = group) for groups of 64 and more, else 64 / group whole groups.
+inline int lane_elems(int64_t group) { return group >= 64 ? (int)(group / 64) : 1; }
+
 // ------------------------------------------------------------------ prepare
-// Workgroup (vector b, chunk ch) transforms `chunk` padded columns.
+// One wavefront per (vector, span of 64*E padded columns).
+template <int E>
 __global__ __launch_bounds__(kThreads) void cq_prepare_kernel(
     const float* __restrict__ x, float* __restrict__ p, int64_t input, int64_t input_padded,
-    int log2_group, int chunk, int64_t n_chunks, double scale) {
-  __shared__ float buf[kTransformChunk];
-  const int64_t b = blockIdx.x / n_chunks;
-  const int64_t c0 = (blockIdx.x % n_chunks) * (int64_t)chunk;
-  const int n = (int)min((int64_t)chunk, input_padded - c0);
+    int log2_group, int64_t spans, int64_t n_waves, double scale) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wv = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  if (wv >= n_waves) return;  // whole wavefront
+  const int64_t b = wv / spans;
+  const int64_t c0 = (wv % spans) * (64 * E) + lane * E;
   const float* xb = x + b * input;
-  for (int i = threadIdx.x; i < n; i += kThreads) {
-    const int64_t c = c0 + i;
-    buf[i] = c < input ? xb[c] : 0.0f;
-  }
-  __syncthreads();
-  lds_fwht(buf, n, log2_group);
-  float* pb = p + b * input_padded + c0;
-  for (int i = threadIdx.x; i < n; i += kThreads) pb[i] = scale_store(buf[i], scale);
+  float v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) v[e] = c0 + e < input ? xb[c0 + e] : 0.0f;
+  wave_fwht<E>(v, lane, log2_group);
+  float* pb = p + b * input_padded;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (c0 + e < input_padded) pb[c0 + e] = scale_store(v[e], scale);
+}
+
+template <int E>
+int launch_prepare_e(const bqd_cq_matrix* m, const float* x, float* prepared, int64_t batch,
+                     hipStream_t s) {
+  const int64_t spans = (m->input_padded + 64 * E - 1) / (64 * E);
+  const int64_t n_waves = spans * batch;
+  const int64_t grid = (n_waves + kWavesPerBlock - 1) / kWavesPerBlock;
+  hipLaunchKernelGGL((cq_prepare_kernel<E>), dim3((unsigned)grid), dim3(kThreads), 0, s, x,
+                     prepared, m->input, m->input_padded, ilog2(m->group), spans, n_waves,
+                     1.0 / std::sqrt((double)m->group));
+  return launch_status();
 }
 
 int launch_cq_prepare(const bqd_cq_matrix* m, const float* x, float* prepared, int64_t batch,
                       hipStream_t s) {
-  const int chunk = (int)std::max<int64_t>(m->group, std::min<int64_t>(kTransformChunk, m->input_padded));
-  const int64_t n_chunks = (m->input_padded + chunk - 1) / chunk;
-  const double scale = 1.0 / std::sqrt((double)m->group);
-  hipLaunchKernelGGL(cq_prepare_kernel, dim3((unsigned)(n_chunks * batch)), dim3(kThreads), 0, s,
-                     x, prepared, m->input, m->input_padded, ilog2(m->group), chunk, n_chunks,
-                     scale);
-  return launch_status();
+  switch (lane_elems(m->group)) {
+    case 1: return launch_prepare_e<1>(m, x, prepared, batch, s);
+    case 2: return launch_prepare_e<2>(m, x, prepared, batch, s);
+    case 4: return launch_prepare_e<4>(m, x, prepared, batch, s);
+    case 8: return launch_prepare_e<8>(m, x, prepared, batch, s);
+    case 16: return launch_prepare_e<16>(m, x, prepared, batch, s);
+  }
+  return BQD_EINVAL;  // unreachable: group <= 1024 is validated
 }
 
 // ------------------------------------------------------------------- gather
-// Workgroup (id i, chunk ch): decode codebook value times norm (an fp32
-// product), transform, scale, store the columns below `input`.
+// One wavefront per (id, span of 64*E columns): codebook value times norm
+// (an fp32 product), transform, scale, store the columns below `input`.
+template <int E>
 __global__ __launch_bounds__(kThreads) void cq_gather_kernel(
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
     const float* __restrict__ codebook, const int32_t* __restrict__ rows, float* __restrict__ out,
     int64_t output, int64_t input, int64_t input_padded, int64_t row_bytes, int bits,
-    int log2_group, int chunk, int64_t n_chunks, double scale) {
-  __shared__ float buf[kTransformChunk];
+    int log2_group, int64_t spans, int64_t n_waves, double scale) {
   __shared__ float cb[32];
-  const int64_t i = blockIdx.x / n_chunks;
-  const int64_t c0 = (blockIdx.x % n_chunks) * (int64_t)chunk;
-  if (c0 >= input) return;  // no visible column in this chunk (uniform)
-  const int n = (int)min((int64_t)chunk, input_padded - c0);
-  const int64_t r = rows[i];
-  float* o = out + i * input;
-  if (r < 0 || r >= output) {  // uniform: an id outside the table gives a NaN row
-    for (int k = threadIdx.x; k < n; k += kThreads)
-      if (c0 + k < input) o[c0 + k] = __uint_as_float(0x7fc00000u);
-    return;
-  }
   if (threadIdx.x < (1 << bits)) cb[threadIdx.x] = codebook[threadIdx.x];
   __syncthreads();
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wv = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  if (wv >= n_waves) return;  // whole wavefront
+  const int64_t i = wv / spans;
+  const int64_t c0 = (wv % spans) * (64 * E) + lane * E;
+  const int64_t r = rows[i];
+  float* o = out + i * input;
+  if (r < 0 || r >= output) {  // an id outside the table: a NaN row
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (c0 + e < input) o[c0 + e] = __uint_as_float(0x7fc00000u);
+    return;
+  }
   const uint8_t* prow = packed + r * row_bytes;
   const uint16_t* nrow = norms + r * (input_padded >> log2_group);
-  for (int k = threadIdx.x; k < n; k += kThreads) {
-    const int64_t c = c0 + k;
-    const float nm = f16_to_f32(nrow[c >> log2_group]);
-    buf[k] = cb[byte_index(prow, bits, c)] * nm;
+  float v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int64_t c = c0 + e;
+    v[e] = c < input_padded ? cb[byte_index(prow, bits, c)] * f16_to_f32(nrow[c >> log2_group])
+                            : 0.0f;
   }
-  __syncthreads();
-  lds_fwht(buf, n, log2_group);
-  for (int k = threadIdx.x; k < n; k += kThreads) {
-    const int64_t c = c0 + k;
-    if (c < input) o[c] = scale_store(buf[k], scale);
-  }
+  wave_fwht<E>(v, lane, log2_group);
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (c0 + e < input) o[c0 + e] = scale_store(v[e], scale);
+}
+
+template <int E>
+int launch_gather_e(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, float* out,
+                    hipStream_t s) {
+  // spans past the last visible column store nothing and are not launched
+  const int64_t spans = (m->input + 64 * E - 1) / (64 * E);
+  const int64_t n_waves = spans * n;
+  const int64_t grid = (n_waves + kWavesPerBlock - 1) / kWavesPerBlock;
+  hipLaunchKernelGGL((cq_gather_kernel<E>), dim3((unsigned)grid), dim3(kThreads), 0, s,
+                     m->packed, m->norms, m->codebook, rows, out, m->output, m->input,
+                     m->input_padded, m->row_bytes, (int)m->bits, ilog2(m->group), spans,
+                     n_waves, 1.0 / std::sqrt((double)m->group));
+  return launch_status();
 }
 
 int launch_cq_gather(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, float* out,
                      hipStream_t s) {
   if (m->input == 0) return BQD_OK;
-  const int chunk = (int)std::max<int64_t>(m->group, std::min<int64_t>(kTransformChunk, m->input_padded));
-  const int64_t n_chunks = (m->input_padded + chunk - 1) / chunk;
-  const double scale = 1.0 / std::sqrt((double)m->group);
-  hipLaunchKernelGGL(cq_gather_kernel, dim3((unsigned)(n_chunks * n)), dim3(kThreads), 0, s,
-                     m->packed, m->norms, m->codebook, rows, out, m->output, m->input,
-                     m->input_padded, m->row_bytes, (int)m->bits, ilog2(m->group), chunk,
-                     n_chunks, scale);
-  return launch_status();
+  switch (lane_elems(m->group)) {
+    case 1: return launch_gather_e<1>(m, rows, n, out, s);
+    case 2: return launch_gather_e<2>(m, rows, n, out, s);
+    case 4: return launch_gather_e<4>(m, rows, n, out, s);
+    case 8: return launch_gather_e<8>(m, rows, n, out, s);
+    case 16: return launch_gather_e<16>(m, rows, n, out, s);
+  }
+  return BQD_EINVAL;
 }
 
 // ----------------------------------------------------------- generic matvec
@@ -142,8 +172,8 @@ __global__ __launch_bounds__(kThreads) void cq_matvec_generic(
   const int wave = threadIdx.x / kWave;
   const int64_t group = int64_t(1) << log2_group;
   const int64_t n_groups = input_padded >> log2_group;
-  for (int64_t i = (int64_t)blockIdx.x * (kThreads / kWave) + wave; i < row_count;
-       i += (int64_t)gridDim.x * (kThreads / kWave)) {
+  for (int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + wave; i < row_count;
+       i += (int64_t)gridDim.x * kWavesPerBlock) {
     const int64_t r = row_begin + i;
     const uint8_t* prow = packed + r * row_bytes;
     for (int64_t b = 0; b < batch; ++b) {
@@ -161,26 +191,149 @@ __global__ __launch_bounds__(kThreads) void cq_matvec_generic(
   }
 }
 
-// -------------------------------------------------------------- fast matvec
+// ------------------------------------------------------ fast matvec, batch 1
 // Rows whose padded width is a multiple of 32 columns, groups of >= 32 and
-// dword-aligned rows.  A 32-column chunk is BITS dwords; `LPR` lanes share a
-// row (chunk q + LPR*j for j < NJ belongs to lane q), so one load instruction
-// of a wavefront reads 64 consecutive chunks: contiguous, coalesced bytes.
-// Each lane keeps the prepared activations of its chunks in registers for the
-// whole kernel (the same columns for every row), looks the codebook up in LDS
-// (2^BITS distinct words in distinct banks: conflict free), multiplies the
-// chunk partial by its group norm, and the LPR lanes of a row reduce with DPP.
-// NB activation vectors share each decoded weight.  U row steps are loaded
-// before any of them is consumed, to keep loads in flight.
+// dword-aligned rows.  A 32-column chunk is BITS dwords; LPR lanes share a
+// row and each owns NJ chunks: chunks q*NJ .. q*NJ+NJ-1 when CONTIG (one
+// contiguous span, so one group norm per row once groups span it), else
+// chunks q + LPR*j (each load instruction of a wavefront then reads 64
+// consecutive chunks).  Every lane keeps the prepared activations of its
+// chunks in registers for the whole kernel (the same columns for every row).
+// They are staged once per workgroup through LDS: coalesced global loads,
+// then 16-byte LDS reads from a layout padded by 4 floats per lane span so
+// that the 16 lanes of a read phase hit distinct banks.  The codebook is
+// looked up in LDS (2^BITS distinct words in distinct banks: conflict free),
+// each chunk partial is multiplied by its group norm, and the LPR lanes of a
+// row reduce with DPP.  The codebook lookups are the LDS's limit and their
+// latency is hidden by occupancy: the kernel is held to 128 VGPRs (4
+// wavefronts per SIMD; 2 for rows of 8192 columns, whose activations alone
+// take 128) and the grid is persistent, each workgroup walking steps of
+// SLOTS*U rows.
+template <int NJ, int LPR, bool CONTIG>
+struct ActLayout {
+  static constexpr int kUnit = CONTIG ? 32 * NJ : 32;  // floats read contiguously by a lane
+  static constexpr int kStride = kUnit + 4;            // padded LDS stride of a unit
+  // LDS float offset of float f of the padded row
+  __device__ static int offset(int f) {
+    const int c = f >> 5;  // chunk
+    const int unit = CONTIG ? c / NJ : c;
+    const int within = CONTIG ? (c % NJ) * 32 + (f & 31) : (f & 31);
+    return unit * kStride + within;
+  }
+  static int64_t floats(int64_t input_padded) {
+    const int64_t n_chunk = input_padded / 32;
+    return (CONTIG ? n_chunk / NJ : n_chunk) * kStride;
+  }
+};
+
+template <int BITS, int NJ, int LPR, int U, bool CONTIG>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NJ > 2 ? 2 : 4, NJ > 2 ? 2 : 4)))
+void cq_matvec_b1(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
+                  const float* __restrict__ codebook, const float* __restrict__ prepared,
+                  float* __restrict__ y, int64_t input_padded, int64_t row_bytes, int log2_group,
+                  int64_t row_begin, int64_t row_count) {
+  typedef ActLayout<NJ, LPR, CONTIG> L;
+  constexpr int SLOTS = kThreads / LPR;  // rows per step
+  extern __shared__ float act_lds[];
+  __shared__ float cb[32];
+  const int tid = threadIdx.x;
+  const int slot = tid / LPR;
+  const int q = tid % LPR;
+  const int n_groups = (int)(input_padded >> log2_group);
+  const int rows = (int)row_count;  // < 2^30, validated
+  const int n_steps = (rows + SLOTS - 1) / SLOTS;
+  const int stride = (int)gridDim.x * U;
+  auto chunk_of = [&](int j) { return CONTIG ? q * NJ + j : q + LPR * j; };
+  // one norm per row when the lane's chunks lie in one group
+  const bool one_norm = CONTIG && (32 * NJ) <= (1 << log2_group);
+  const uint8_t* lane_base = packed + row_begin * row_bytes + 4 * BITS * chunk_of(0);
+  const uint16_t* norm_base = norms + row_begin * n_groups;
+  int gidx[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) gidx[j] = (32 * chunk_of(j)) >> log2_group;
+
+  // stage the activations (coalesced float4 reads) and the codebook
+  const int n4 = (int)(input_padded >> 2);
+  for (int i = tid; i < n4; i += kThreads) {
+    const float4 v = reinterpret_cast<const float4*>(prepared)[i];
+    *reinterpret_cast<float4*>(act_lds + L::offset(4 * i)) = v;
+  }
+  if (tid < (1 << BITS)) cb[tid] = codebook[tid];
+  __syncthreads();
+  float act[NJ][32];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const float* src = act_lds + L::offset(32 * chunk_of(j));
+#pragma unroll
+    for (int k = 0; k < 32; k += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(src + k);
+      act[j][k] = v.x;
+      act[j][k + 1] = v.y;
+      act[j][k + 2] = v.z;
+      act[j][k + 3] = v.w;
+    }
+  }
+
+  for (int s0 = (int)blockIdx.x * U; s0 < n_steps; s0 += stride) {
+    uint32_t d[U][NJ][BITS];
+    uint16_t nb[U][NJ];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = min((s0 + u) * SLOTS + slot, rows - 1);  // in bounds; dropped if clamped
+      const uint32_t* pc = reinterpret_cast<const uint32_t*>(lane_base + (int64_t)i * row_bytes);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int off = CONTIG ? BITS * j : BITS * LPR * j;
+#pragma unroll
+        for (int t = 0; t < BITS; ++t) d[u][j][t] = pc[off + t];
+      }
+      const uint16_t* nr = norm_base + (int64_t)i * n_groups;
+      if (one_norm) {
+        const uint16_t n0 = nr[gidx[0]];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) nb[u][j] = n0;
+      } else {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) nb[u][j] = nr[gidx[j]];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        uint32_t a[32];
+        chunk_addresses<BITS>(d[u][j], a);
+        float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 32; k += 2) {
+          p0 += lds_at(cb, a[k]) * act[j][k];
+          p1 += lds_at(cb, a[k + 1]) * act[j][k + 1];
+        }
+        acc += f16_to_f32(nb[u][j]) * (p0 + p1);
+      }
+      acc = group_sum<LPR>(acc);
+      const int i = (s0 + u) * SLOTS + slot;
+      if (q == LPR - 1 && i < rows) y[i] = acc;
+    }
+  }
+}
+
+// -------------------------------------------------- fast matvec, NB vectors
+// Same lane layout; NB activation vectors share each decoded weight.  Rows
+// wider than one wavefront (LPR > 64) are split over LPR/64 wavefronts whose
+// partial sums meet in LDS.
 template <int BITS, int NJ, int LPR, int NB, int U>
-__global__ __launch_bounds__(kThreads) void cq_matvec_fast(
+__global__ __launch_bounds__(kThreads) void cq_matvec_nb(
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
     const float* __restrict__ codebook, const float* __restrict__ prepared, float* __restrict__ y,
     int64_t input_padded, int64_t row_bytes, int log2_group, int64_t row_begin, int64_t row_count,
-    int nb) {
+    int64_t y_stride, int nb) {
   constexpr int SLOTS = LPR <= kThreads ? kThreads / LPR : 1;  // rows per step
   constexpr int WPS = LPR > kWave ? LPR / kWave : 1;            // wavefronts per row
-  constexpr int RED = LPR > kWave ? kThreads / kWave * U * NB : 1;
+  constexpr int RED = LPR > kWave ? kWavesPerBlock * U * NB : 1;
+  typedef ActLayout<NJ, LPR, false> L;
+  extern __shared__ float act_lds[];  // one padded activation row at a time
   __shared__ float cb[32];
   __shared__ float red[RED];
   const int tid = threadIdx.x;
@@ -192,18 +345,31 @@ __global__ __launch_bounds__(kThreads) void cq_matvec_fast(
   float act[NB][NJ][32];
   int gidx[NJ];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int64_t c = 32 * (int64_t)(q + LPR * j);
-    gidx[j] = (int)(c >> log2_group);
+  for (int j = 0; j < NJ; ++j) gidx[j] = (int)((32 * (int64_t)(q + LPR * j)) >> log2_group);
+  // Activations reach registers through LDS: coalesced float4 loads of one
+  // vector, then 16-byte reads of each lane's chunks from the padded layout.
+  // Vectors past nb reuse the last one; their sums are never stored.
+  const int n4 = (int)(input_padded >> 2);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      // vectors past nb reuse the last one; their sums are never stored
-      const float* pb = prepared + (int64_t)(b < nb ? b : nb - 1) * input_padded + c;
+  for (int b = 0; b < NB; ++b) {
+    const float4* src = reinterpret_cast<const float4*>(prepared + (int64_t)(b < nb ? b : nb - 1) * input_padded);
+    for (int i = tid; i < n4; i += kThreads)
+      *reinterpret_cast<float4*>(act_lds + L::offset(4 * i)) = src[i];
+    __syncthreads();
 #pragma unroll
-      for (int k = 0; k < 32; ++k) act[b][j][k] = pb[k];
+    for (int j = 0; j < NJ; ++j) {
+      const float* a = act_lds + L::offset(32 * (q + LPR * j));
+#pragma unroll
+      for (int k = 0; k < 32; k += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(a + k);
+        act[b][j][k] = v.x;
+        act[b][j][k + 1] = v.y;
+        act[b][j][k + 2] = v.z;
+        act[b][j][k + 3] = v.w;
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
 
   const int64_t n_steps = (row_count + SLOTS - 1) / SLOTS;
   for (int64_t s0 = (int64_t)blockIdx.x * U; s0 < n_steps; s0 += (int64_t)gridDim.x * U) {
@@ -219,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void cq_matvec_fast(
       for (int j = 0; j < NJ; ++j) {
         const uint32_t* pc = prow + BITS * (q + LPR * j);
 #pragma unroll
-        for (int t = 0; t < BITS; ++t) d[u][j][t] = __builtin_nontemporal_load(pc + t);
+        for (int t = 0; t < BITS; ++t) d[u][j][t] = pc[t];
         nrm[u][j] = f16_to_f32(norms[r * n_groups + gidx[j]]);
       }
     }
@@ -230,12 +396,14 @@ __global__ __launch_bounds__(kThreads) void cq_matvec_fast(
       for (int b = 0; b < NB; ++b) acc[b] = 0.0f;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
+        uint32_t a[32];
+        chunk_addresses<BITS>(d[u][j], a);
         float part[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) part[b] = 0.0f;
 #pragma unroll
         for (int k = 0; k < 32; ++k) {
-          const float w = cb[chunk_index<BITS>(d[u][j], k)];
+          const float w = lds_at(cb, a[k]);
 #pragma unroll
           for (int b = 0; b < NB; ++b) part[b] += w * act[b][j][k];
         }
@@ -249,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void cq_matvec_fast(
         if (q == LPR - 1 && i < row_count) {
 #pragma unroll
           for (int b = 0; b < NB; ++b)
-            if (b < nb) y[b * row_count + i] = acc[b];
+            if (b < nb) y[b * y_stride + i] = acc[b];
         }
       } else {
         const int w_in_slot = q / kWave;
@@ -268,7 +436,7 @@ __global__ __launch_bounds__(kThreads) void cq_matvec_fast(
         float v = 0.0f;
         for (int w = 0; w < WPS; ++w) v += red[((sl * WPS + w) * U + u) * NB + b];
         const int64_t i = (s0 + u) * SLOTS + sl;
-        if (b < nb && i < row_count) y[b * row_count + i] = v;
+        if (b < nb && i < row_count) y[b * y_stride + i] = v;
       }
       __syncthreads();
     }
@@ -278,12 +446,14 @@ __global__ __launch_bounds__(kThreads) void cq_matvec_fast(
 namespace {
 
 constexpr int kMaxGrid = 4096;
+constexpr int kB1BlocksPerCu = 4;
+constexpr int kNbBlocksPerCu = 2;
 
 struct FastShape {
   int lpr, nj;
 };
 
-// The fast kernel's lane layout for a row of n_chunk 32-column chunks, or
+// The fast kernels' lane layout for a row of n_chunk 32-column chunks, or
 // {0, 0} when no instantiation covers it.
 FastShape fast_shape(int64_t n_chunk, int nb_max) {
   if (nb_max == 1) {
@@ -301,59 +471,91 @@ bool fast_ok(const bqd_cq_matrix* m) {
          is_aligned(m->packed, 4);
 }
 
-template <int BITS, int NJ, int LPR, int NB>
-int launch_fast(const bqd_cq_matrix* m, const float* prepared, float* y, int nb,
-                int64_t row_begin, int64_t row_count, hipStream_t s) {
-  constexpr int U = NB == 1 ? 4 : 2;
+template <int BITS, int NJ, int LPR>
+int launch_b1(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t row_begin,
+              int64_t row_count, hipStream_t s) {
+  constexpr int U = 2;
+  constexpr int SLOTS = kThreads / LPR;
+  const int64_t n_steps = (row_count + SLOTS - 1) / SLOTS;
+  const int per_cu = NJ > 2 ? 2 : kB1BlocksPerCu;  // the kernel's occupancy
+  const int64_t grid = std::min<int64_t>((n_steps + U - 1) / U, (int64_t)cu_count() * per_cu);
+  constexpr bool CONTIG = false;  // measured faster: each load instruction reads 64 consecutive chunks
+  const size_t lds = sizeof(float) * ActLayout<NJ, LPR, CONTIG>::floats(m->input_padded);
+  hipLaunchKernelGGL((cq_matvec_b1<BITS, NJ, LPR, U, CONTIG>), dim3((unsigned)grid), dim3(kThreads), lds, s,
+                     m->packed, m->norms, m->codebook, prepared, y, m->input_padded, m->row_bytes,
+                     ilog2(m->group), row_begin, row_count);
+  return launch_status();
+}
+
+template <int BITS, int LPR>
+int launch_nb(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t y_stride, int nb,
+              int64_t row_begin, int64_t row_count, hipStream_t s) {
+  constexpr int U = 2;
   constexpr int SLOTS = LPR <= kThreads ? kThreads / LPR : 1;
   const int64_t n_steps = (row_count + SLOTS - 1) / SLOTS;
-  const int64_t grid = std::min<int64_t>((n_steps + U - 1) / U, kMaxGrid);
-  hipLaunchKernelGGL((cq_matvec_fast<BITS, NJ, LPR, NB, U>), dim3((unsigned)grid), dim3(kThreads),
-                     0, s, m->packed, m->norms, m->codebook, prepared, y, m->input_padded,
-                     m->row_bytes, ilog2(m->group), row_begin, row_count, nb);
+  // persistent: every workgroup loads all its activations once, so the
+  // grid is kept to what the CUs hold at once (2 per CU at 128+ VGPRs)
+  const int64_t grid = std::min<int64_t>((n_steps + U - 1) / U, (int64_t)cu_count() * kNbBlocksPerCu);
+  const size_t lds = sizeof(float) * ActLayout<1, LPR, false>::floats(m->input_padded);
+  hipLaunchKernelGGL((cq_matvec_nb<BITS, 1, LPR, 4, U>), dim3((unsigned)grid), dim3(kThreads), lds,
+                     s, m->packed, m->norms, m->codebook, prepared, y, m->input_padded,
+                     m->row_bytes, ilog2(m->group), row_begin, row_count, y_stride, nb);
   return launch_status();
 }
 
 template <int BITS>
-int dispatch_fast(const bqd_cq_matrix* m, FastShape f, int nb_max, const float* prepared, float* y,
-                  int nb, int64_t row_begin, int64_t row_count, hipStream_t s) {
-  if (nb_max == 1) {
-    switch (f.lpr * 16 + f.nj) {
-      case 8 * 16 + 1: return launch_fast<BITS, 1, 8, 1>(m, prepared, y, nb, row_begin, row_count, s);
-      case 16 * 16 + 1: return launch_fast<BITS, 1, 16, 1>(m, prepared, y, nb, row_begin, row_count, s);
-      case 32 * 16 + 1: return launch_fast<BITS, 1, 32, 1>(m, prepared, y, nb, row_begin, row_count, s);
-      case 64 * 16 + 1: return launch_fast<BITS, 1, 64, 1>(m, prepared, y, nb, row_begin, row_count, s);
-      case 64 * 16 + 2: return launch_fast<BITS, 2, 64, 1>(m, prepared, y, nb, row_begin, row_count, s);
-      case 64 * 16 + 4: return launch_fast<BITS, 4, 64, 1>(m, prepared, y, nb, row_begin, row_count, s);
-    }
-  } else {
-    switch (f.lpr) {
-      case 8: return launch_fast<BITS, 1, 8, 4>(m, prepared, y, nb, row_begin, row_count, s);
-      case 16: return launch_fast<BITS, 1, 16, 4>(m, prepared, y, nb, row_begin, row_count, s);
-      case 32: return launch_fast<BITS, 1, 32, 4>(m, prepared, y, nb, row_begin, row_count, s);
-      case 64: return launch_fast<BITS, 1, 64, 4>(m, prepared, y, nb, row_begin, row_count, s);
-      case 128: return launch_fast<BITS, 1, 128, 4>(m, prepared, y, nb, row_begin, row_count, s);
-      case 256: return launch_fast<BITS, 1, 256, 4>(m, prepared, y, nb, row_begin, row_count, s);
-    }
+int dispatch_b1(const bqd_cq_matrix* m, FastShape f, const float* prepared, float* y,
+                int64_t row_begin, int64_t row_count, hipStream_t s) {
+  switch (f.lpr * 16 + f.nj) {
+    case 8 * 16 + 1: return launch_b1<BITS, 1, 8>(m, prepared, y, row_begin, row_count, s);
+    case 16 * 16 + 1: return launch_b1<BITS, 1, 16>(m, prepared, y, row_begin, row_count, s);
+    case 32 * 16 + 1: return launch_b1<BITS, 1, 32>(m, prepared, y, row_begin, row_count, s);
+    case 64 * 16 + 1: return launch_b1<BITS, 1, 64>(m, prepared, y, row_begin, row_count, s);
+    case 64 * 16 + 2: return launch_b1<BITS, 2, 64>(m, prepared, y, row_begin, row_count, s);
+    case 64 * 16 + 4: return launch_b1<BITS, 4, 64>(m, prepared, y, row_begin, row_count, s);
   }
   return BQD_EINVAL;  // unreachable: fast_shape() only returns instantiated layouts
 }
 
-int run_fast(const bqd_cq_matrix* m, FastShape f, int nb_max, const float* prepared, float* y,
-             int nb, int64_t row_begin, int64_t row_count, hipStream_t s) {
+template <int BITS>
+int dispatch_nb(const bqd_cq_matrix* m, FastShape f, const float* prepared, float* y,
+                int64_t y_stride, int nb, int64_t row_begin, int64_t row_count, hipStream_t s) {
+  switch (f.lpr) {
+    case 8: return launch_nb<BITS, 8>(m, prepared, y, y_stride, nb, row_begin, row_count, s);
+    case 16: return launch_nb<BITS, 16>(m, prepared, y, y_stride, nb, row_begin, row_count, s);
+    case 32: return launch_nb<BITS, 32>(m, prepared, y, y_stride, nb, row_begin, row_count, s);
+    case 64: return launch_nb<BITS, 64>(m, prepared, y, y_stride, nb, row_begin, row_count, s);
+    case 128: return launch_nb<BITS, 128>(m, prepared, y, y_stride, nb, row_begin, row_count, s);
+    case 256: return launch_nb<BITS, 256>(m, prepared, y, y_stride, nb, row_begin, row_count, s);
+  }
+  return BQD_EINVAL;
+}
+
+int run_b1(const bqd_cq_matrix* m, FastShape f, const float* prepared, float* y,
+           int64_t row_begin, int64_t row_count, hipStream_t s) {
   switch (m->bits) {
-    case 2: return dispatch_fast<2>(m, f, nb_max, prepared, y, nb, row_begin, row_count, s);
-    case 3: return dispatch_fast<3>(m, f, nb_max, prepared, y, nb, row_begin, row_count, s);
-    case 4: return dispatch_fast<4>(m, f, nb_max, prepared, y, nb, row_begin, row_count, s);
-    case 5: return dispatch_fast<5>(m, f, nb_max, prepared, y, nb, row_begin, row_count, s);
+    case 2: return dispatch_b1<2>(m, f, prepared, y, row_begin, row_count, s);
+    case 3: return dispatch_b1<3>(m, f, prepared, y, row_begin, row_count, s);
+    case 4: return dispatch_b1<4>(m, f, prepared, y, row_begin, row_count, s);
+    case 5: return dispatch_b1<5>(m, f, prepared, y, row_begin, row_count, s);
+  }
+  return BQD_EINVAL;
+}
+
+int run_nb(const bqd_cq_matrix* m, FastShape f, const float* prepared, float* y, int64_t y_stride,
+           int nb, int64_t row_begin, int64_t row_count, hipStream_t s) {
+  switch (m->bits) {
+    case 2: return dispatch_nb<2>(m, f, prepared, y, y_stride, nb, row_begin, row_count, s);
+    case 3: return dispatch_nb<3>(m, f, prepared, y, y_stride, nb, row_begin, row_count, s);
+    case 4: return dispatch_nb<4>(m, f, prepared, y, y_stride, nb, row_begin, row_count, s);
+    case 5: return dispatch_nb<5>(m, f, prepared, y, y_stride, nb, row_begin, row_count, s);
   }
   return BQD_EINVAL;
 }
 
 int launch_generic(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t batch,
                    int64_t row_begin, int64_t row_count, hipStream_t s) {
-  const int64_t waves = kThreads / kWave;
-  const int64_t grid = std::min<int64_t>((row_count + waves - 1) / waves, kMaxGrid);
+  const int64_t grid = std::min<int64_t>((row_count + kWavesPerBlock - 1) / kWavesPerBlock, kMaxGrid);
   hipLaunchKernelGGL(cq_matvec_generic, dim3((unsigned)grid), dim3(kThreads), 0, s, m->packed,
                      m->norms, m->codebook, prepared, y, m->input_padded, m->row_bytes,
                      (int)m->bits, ilog2(m->group), row_begin, row_count, batch);
@@ -366,30 +568,34 @@ int launch_cq_matvec(const bqd_cq_matrix* m, const float* prepared, float* y, in
                      int64_t row_begin, int64_t row_count, hipStream_t s) {
   if (!fast_ok(m)) return launch_generic(m, prepared, y, batch, row_begin, row_count, s);
   const int64_t n_chunk = m->input_padded / 32;
-  if (batch == 1) {
-    const FastShape f = fast_shape(n_chunk, 1);
-    if (f.lpr == 0) return launch_generic(m, prepared, y, batch, row_begin, row_count, s);
-    return run_fast(m, f, 1, prepared, y, 1, row_begin, row_count, s);
-  }
-  // Several vectors: up to four share each decoded weight per launch.
-  const FastShape f4 = fast_shape(n_chunk, 4);
   const FastShape f1 = fast_shape(n_chunk, 1);
-  if (f4.lpr == 0 && f1.lpr == 0) return launch_generic(m, prepared, y, batch, row_begin, row_count, s);
-  for (int64_t b = 0; b < batch;) {
-    const int64_t nb = f4.lpr ? std::min<int64_t>(4, batch - b) : 1;
-    const int rc = f4.lpr ? run_fast(m, f4, 4, prepared + b * m->input_padded, y + b * row_count,
-                                     (int)nb, row_begin, row_count, s)
-                          : run_fast(m, f1, 1, prepared + b * m->input_padded, y + b * row_count,
-                                     1, row_begin, row_count, s);
-    if (rc) return rc;
-    b += nb;
+  const FastShape f4 = fast_shape(n_chunk, 4);
+  if (batch == 1 && f1.lpr) return run_b1(m, f1, prepared, y, row_begin, row_count, s);
+  if (f4.lpr) {
+    // up to four vectors share each decoded weight per launch
+    for (int64_t b = 0; b < batch; b += 4) {
+      const int nb = (int)std::min<int64_t>(4, batch - b);
+      const int rc = run_nb(m, f4, prepared + b * m->input_padded, y + b * row_count, row_count,
+                            nb, row_begin, row_count, s);
+      if (rc) return rc;
+    }
+    return BQD_OK;
   }
-  return BQD_OK;
+  if (f1.lpr) {
+    for (int64_t b = 0; b < batch; ++b) {
+      const int rc = run_b1(m, f1, prepared + b * m->input_padded, y + b * row_count, row_begin,
+                            row_count, s);
+      if (rc) return rc;
+    }
+    return BQD_OK;
+  }
+  return launch_generic(m, prepared, y, batch, row_begin, row_count, s);
 }
 
 // ------------------------------------------------------------- unpack probe
 // idx[c] for one row through the same decode the matvec uses for this
-// matrix: chunk decode from dwords on the fast layout, byte decode otherwise.
+// matrix: the chunk address decode from dwords on the fast layout (address /
+// 4 is the index), the byte decode otherwise.
 template <int BITS>
 __global__ void cq_unpack_chunks(const uint8_t* __restrict__ prow, uint8_t* __restrict__ idx,
                                  int64_t n_chunk) {
@@ -399,8 +605,10 @@ __global__ void cq_unpack_chunks(const uint8_t* __restrict__ prow, uint8_t* __re
   uint32_t d[BITS];
 #pragma unroll
   for (int t = 0; t < BITS; ++t) d[t] = pc[t];
+  uint32_t a[32];
+  chunk_addresses<BITS>(d, a);
 #pragma unroll
-  for (int k = 0; k < 32; ++k) idx[32 * ch + k] = (uint8_t)chunk_index<BITS>(d, k);
+  for (int k = 0; k < 32; ++k) idx[32 * ch + k] = (uint8_t)(a[k] >> 2);
 }
 
 __global__ void cq_unpack_bytes(const uint8_t* __restrict__ prow, uint8_t* __restrict__ idx,

@@ -22,7 +22,7 @@ int check_unpack(const bqd_cq_matrix* m, int64_t row, const uint8_t* idx);
 int check_decode(const void* codes, int64_t n, const float* out, int code_size);
 
 // Largest sizes the kernels index with their 32-bit row / column counters.
-constexpr int64_t kMaxRows = (int64_t)1 << 31;      // exclusive
+constexpr int64_t kMaxRows = (int64_t)1 << 30;      // exclusive
 constexpr int64_t kMaxColumns = (int64_t)1 << 28;   // exclusive
 constexpr int64_t kMaxGroup = 1024;
 

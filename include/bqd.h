@@ -56,9 +56,9 @@ enum {
  * index of a row are ignored.  The matrix acts on the Walsh–Hadamard domain:
  * its dense row is recovered by the "Row gather" of [P1]. */
 typedef struct bqd_cq_matrix {
-    int64_t output;        /* rows, >= 0                                        */
+    int64_t output;        /* rows, 0 <= output < 2^30                          */
     int64_t input;         /* unpadded columns, 0 <= input <= input_padded      */
-    int64_t input_padded;  /* stored columns, > 0, a multiple of group          */
+    int64_t input_padded;  /* stored columns, > 0, < 2^28, a multiple of group  */
     int64_t group;         /* transform block, a power of two in [1, 1024]      */
     int64_t bits;          /* 2, 3, 4 or 5                                      */
     int64_t row_bytes;     /* stride of packed rows, >= ceil(input_padded*bits/8) */
@@ -101,7 +101,7 @@ int cq_matvec(const bqd_cq_matrix *m, const float *prepared, float *y,
  * Ids may repeat.  An id outside [0, output) cannot be checked on the host
  * without a synchronization: its output row is filled with quiet NaNs.
  *   rows: int32 [n]              out: fp32 [n][m->input]
- * Errors: BQD_EINVAL (shape fields, n < 0), BQD_ENULL, BQD_EALIGN,
+ * Errors: BQD_EINVAL (shape fields, n < 0 or n >= 2^30), BQD_ENULL, BQD_EALIGN,
  * BQD_EOVERFLOW, BQD_EHIP. */
 int cq_gather_rows(const bqd_cq_matrix *m, const int32_t *rows, int64_t n,
                    float *out, void *stream);
@@ -114,7 +114,8 @@ int cq_gather_rows(const bqd_cq_matrix *m, const int32_t *rows, int64_t n,
  * 255 is NaN.  Accumulation is fp32 (same tolerance as cq_matvec).
  *   w:     E4M3 codes [R][C]     scale: E8M0 bytes [SR][SC]
  *   x:     fp32 [batch][C]       y:     fp32 [batch][R]
- * Requires R >= 0, C >= 1, 1 <= SR <= max(R, 1), 1 <= SC <= C, batch >= 0.
+ * Requires 0 <= R < 2^30, 1 <= C < 2^28, 1 <= SR <= max(R, 1), 1 <= SC <= C,
+ * batch >= 0.
  * Errors: BQD_EINVAL, BQD_ENULL, BQD_EALIGN, BQD_EOVERFLOW, BQD_EHIP. */
 int f8_matvec(const uint8_t *w, int64_t R, int64_t C, const uint8_t *scale,
               int64_t SR, int64_t SC, const float *x, float *y, int64_t batch,

@@ -63,7 +63,7 @@ def matvec(m, prepared=FAKE, y=FAKE, batch=1, row_begin=0, row_count=None):
     (dict(input_padded=250), EINVAL), (dict(input_padded=0), EINVAL),
     (dict(input=257), EINVAL), (dict(input=-1), EINVAL),
     (dict(row_bytes=63), EINVAL), (dict(row_bytes=0), EINVAL), (dict(output=-1), EINVAL),
-    (dict(output=1 << 31), EINVAL),
+    (dict(output=1 << 30), EINVAL),
     (dict(row_bytes=1 << 62, output=8), EOVERFLOW),
     (dict(packed=0), ENULL), (dict(norms=0), ENULL), (dict(codebook=0), ENULL),
     (dict(norms=FAKE + 1), EALIGN), (dict(codebook=FAKE + 2), EALIGN),
@@ -113,7 +113,7 @@ def test_cq_gather_argument_errors():
 @pytest.mark.parametrize("args,code", [
     (dict(R=-1), EINVAL), (dict(C=0), EINVAL), (dict(SR=0), EINVAL), (dict(SC=0), EINVAL),
     (dict(SR=513), EINVAL), (dict(SC=4097), EINVAL), (dict(batch=-1), EINVAL),
-    (dict(R=1 << 31), EINVAL), (dict(C=1 << 28), EINVAL),
+    (dict(R=1 << 30), EINVAL), (dict(C=1 << 28), EINVAL),
     (dict(w=0), ENULL), (dict(scale=0), ENULL), (dict(x=0), ENULL), (dict(y=0), ENULL),
     (dict(x=FAKE + 1), EALIGN), (dict(y=FAKE + 2), EALIGN),
     (dict(batch=0), OK), (dict(R=0, SR=1), OK),

@@ -380,3 +380,49 @@ def test_empty_problems_are_no_ops():
                        torch.zeros(1, 16, device=DEV))
     assert yf.shape == (1, 0)
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------- graph replay
+def test_graph_replay_matches_eager(cache):
+    """The path captured in a HIP graph: every replay, with eager work and
+    synchronizations between replays, equals the eager result bitwise."""
+    c4 = workload(cache, "cq4_16384x4096_b8")
+    c3 = workload(cache, "cq4_65536x512_vocab_gather")
+    f = workload(cache, "f8_wkv_512x4096")
+    m4, m3 = dev_matrix(c4), dev_matrix(c3)
+    x8, ids = to_dev(c4.x), to_dev(c3.ids)
+    w, s, x = dev_f8(f)
+    p = torch.empty(8, c4.shape.input_padded, device=DEV)
+    y = torch.empty(8, c4.shape.output, device=DEV)
+    y1 = torch.empty(1, c4.shape.output, device=DEV)
+    g_out = torch.empty(len(c3.ids), c3.shape.input, device=DEV)
+    yf = torch.empty(1, f.R, device=DEV)
+
+    def work():
+        bqd.cq_prepare(m4, x8, out=p)
+        bqd.cq_matvec(m4, p, out=y)
+        bqd.cq_matvec(m4, p[:1], out=y1)
+        bqd.cq_gather_rows(m3, ids, out=g_out)
+        bqd.f8_matvec(w, s, x, out=yf)
+
+    work()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (p, y, y1, g_out, yf)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    for _ in range(4):
+        for t in (p, y, y1, g_out, yf):
+            t.fill_(-1.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, r in zip((p, y, y1, g_out, yf), ref):
+            assert torch.equal(t, r)
+        work()  # eager work between replays
+        torch.cuda.synchronize()
