@@ -29,6 +29,21 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "weight-stream GB/s & % of HBM peak, CQ/F8 decode matvec; rows/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "f8_head_246272x4096_hbm_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_quantized_decode_amd", "csrc", f) for f in ("f8.hip", "device.h")]
+
+
+def measured_traffic():
+    """HBM bytes per head launch from the committed counter runs (FETCH_SIZE and
+    WRITE_SIZE scaled by a plain 1 GiB copy), or None if the kernel sources
+    changed since the counters were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256(b"".join(open(f, "rb").read() for f in KERNEL_SOURCES)).hexdigest()[:16]
+    return rec["traffic_bytes"] if rec.get("source_sha256_16") == h else None
 
 
 def log(msg):
@@ -43,6 +58,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="0: the affinity mask, at most 16")
     ap.add_argument("--hot", action="store_true", help="one weight copy (cache-resident timing)")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="for counter runs: 8 F8 head launches, then 8 plain 1 GiB device copies")
     return ap.parse_args()
 
 
@@ -183,6 +200,26 @@ def capture(torch, fn):
     return g
 
 
+def traffic_probe(torch, bqd, synth):
+    """A fixed launch sequence for rocprofv3 --pmc runs: the dominant kernel,
+    then a plain device copy of known size to calibrate the byte counters."""
+    hd = synth.make_f8(**synth.HEAD, seed=4)
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    w, s, x = T(hd.w), T(hd.scale), T(hd.x)
+    y = torch.empty(1, hd.R, device="cuda")
+    for _ in range(8):
+        bqd.f8_matvec(w, s, x, out=y)
+    torch.cuda.synchronize()
+    del w
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(7)
+    b = torch.empty_like(a)
+    for _ in range(8):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"f8_head_bytes": hd.R * hd.C + hd.SR * hd.SC, "copy_bytes": n}), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -196,6 +233,9 @@ def main():
 
     torch.cuda.set_device(0)
     bqd.lib()
+    if args.traffic_probe:
+        traffic_probe(torch, bqd, synth)
+        return
     cases, data = build_cases(torch, bqd, synth, args.hot)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
@@ -250,8 +290,19 @@ def main():
     head = per_case["f8_head_246272x4096_matvec"]
     roofline = dict(bound="hbm", kernel="f8_matvec_fast (F8 head 246272x4096)",
                     achieved=head["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(head["gbs"] / HBM_PEAK_GBS, 4), traffic=None,
+                    frac=round(head["gbs"] / HBM_PEAK_GBS, 4), traffic=measured_traffic(),
                     us_per_launch=head["us_mean"], bytes_per_launch=head["bytes"])
+    # context: a plain 1 GiB read by a library reduction kernel on the same GPU
+    buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    buf.sum()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(8):
+        buf.sum()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    read_ref = (1 << 30) / (e0.elapsed_time(e1) / 8 * 1e-3) / 1e9
+    del buf
     cpu = None
     if not args.no_cpu_baseline:
         n = args.cpu_threads or min(16, len(os.sched_getaffinity(0)))
@@ -271,6 +322,7 @@ def main():
                    "parallelism": "single GPU"},
         "rows_per_s": round(total_rows / (step_ms * 1e-3), 1),
         "frac_hbm_step": round(value / HBM_PEAK_GBS, 4),
+        "read_reference_gbs": {"kernel": "torch float32 sum over 1 GiB", "gbs": round(read_ref, 1)},
         "cases": per_case, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

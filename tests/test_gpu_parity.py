@@ -30,6 +30,8 @@ def tol_ok(got, ref, mag):
 
 
 def assert_tol(got, ref, mag, what):
+    ratio = np.abs(np.asarray(got, dtype=np.float64) - ref) / (1e-4 * mag + 1e-6)
+    print(f"[tol] {what}: max |gpu-oracle| / (1e-4*sum|w*x| + 1e-6) = {ratio.max():.3g}", flush=True)
     ok = tol_ok(got, ref, mag)
     if not ok.all():
         i = np.argwhere(~ok)[0]
