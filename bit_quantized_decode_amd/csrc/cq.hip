@@ -5,8 +5,8 @@
 // unnormalized Walsh–Hadamard butterfly), §2 (prepare: zero-pad, transform
 // each group, multiply by 1/sqrt(group)), §3 (dot packed rows directly: per
 // row and group, the fp16 norm times the sum of codebook[index] * prepared),
-// "Row gather" (decode a group's levels times its norm, normalized transform,
-// keep the unpadded columns) and §6 (a row range of a matrix).  The record
+// "Row gather" (each group's codebook values scaled by the group norm, the
+// normalized transform, the columns below the unpadded width) and §6 (a row range of a matrix).  The record
 // layout is that of "Inference engine, part 1: loader and tokenizer", §4.
 #include <algorithm>
 #include <atomic>
@@ -443,6 +443,171 @@ __global__ __launch_bounds__(kThreads) void cq_matvec_nb(
   }
 }
 
+// ------------------------------------------------ matrix-core matvec, B >= 2
+// Several activation vectors share each decoded weight; the contraction runs
+// on the matrix cores (v_mfma_f32_16x16x32_bf16: a 16-row x 32-column tile of
+// weights times 32 columns x 16 vectors).  fp32 operands are carried exactly
+// enough as bf16 pairs: x = hi + lo with hi = bf16(x), lo = bf16(x - hi), so
+// |x - hi - lo| <= 2^-18 |x|; three products (hi*hi, hi*lo, lo*hi) per tile
+// accumulate in fp32 (the dropped lo*lo term is below 2^-18 of each product).
+// The codebook table in LDS holds each entry's (hi | lo << 16), so one LDS read
+// per weight feeds both weight operands.
+//
+// A workgroup has one wavefront per 256-column span of the padded row (groups
+// are >= 256, so a span has one norm per row).  Lane l owns tile row l % 16
+// (and vector slot l % 16 of the B operand) and the 64-column quarter l / 16 of
+// its span; K-block kb of the span takes, from quarter g, columns
+// 64g + 8kb .. 64g + 8kb + 7.  Each wavefront keeps its span's activations as
+// B operands in registers for the whole kernel and walks 16-row tiles; per
+// tile the span partials (times their norms) meet in LDS and are summed in
+// span order.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {  // finite x
+  uint32_t u = __float_as_uint(x);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+// (hi, lo) bf16 split of x, packed as hi | lo << 16
+__device__ __forceinline__ uint32_t bf16_split(float x) {
+  const uint32_t hi = bf16_rne_bits(x);
+  const float rest = x - __uint_as_float(hi << 16);
+  return hi | (bf16_rne_bits(rest) << 16);
+}
+
+template <int BITS>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void cq_matvec_mfma(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
+                    const float* __restrict__ codebook, const float* __restrict__ prepared,
+                    float* __restrict__ y, int64_t input_padded, int64_t row_bytes,
+                    int log2_group, int64_t row_begin, int64_t row_count, int64_t y_stride,
+                    int nb) {
+  constexpr int kSpanBytes = 32 * BITS;  // 256 columns of BITS-bit indices
+  __shared__ uint32_t cbs[32];
+  __shared__ float red[16][16][17];      // [span][tile row][vector], padded
+  const int tid = threadIdx.x;
+  const int span = tid >> 6;             // wavefront = span
+  const int n_spans = blockDim.x >> 6;
+  const int l = tid & 63;
+  const int r16 = l & 15;                // tile row (A, D) and vector slot (B)
+  const int qg = l >> 4;                 // 64-column quarter of the span
+  const int rows = (int)row_count;
+  const int n_tiles = (rows + 15) >> 4;
+  const int n_groups = (int)(input_padded >> log2_group);
+  const int group = (256 * span) >> log2_group;  // the span's group (groups >= 256)
+
+  // The first tile's weights and norms load before the operand set-up, so
+  // their latency overlaps it; afterwards each tile's loads are issued before
+  // the previous tile is decoded (ping-pong buffers, unconditional loads of
+  // clamped rows).
+  const uint8_t* lane_base = packed + row_begin * row_bytes + kSpanBytes * span + 8 * BITS * qg;
+  typedef uint32_t Words[2 * BITS];  // this lane's 64 indices
+  auto load_tile = [&](Words& d, float (&nrm)[4], int t) {
+    const int r = min(16 * t + r16, rows - 1);  // in bounds; dropped if clamped
+    const uint32_t* pc = reinterpret_cast<const uint32_t*>(lane_base + (int64_t)r * row_bytes);
+#pragma unroll
+    for (int i = 0; i < 2 * BITS; ++i) d[i] = pc[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = min(16 * t + 4 * qg + i, rows - 1);
+      nrm[i] = f16_to_f32(norms[(row_begin + rr) * n_groups + group]);
+    }
+  };
+  auto tile = [&](const Words& d, const float (&nrm)[4], const u32x4_t (&bhi)[8],
+                  const u32x4_t (&blo)[8], int t) {
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      uint32_t v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = 8 * kb + e;  // index position in the lane's 64
+        const int bit = BITS * k, w = bit >> 5, sh = bit & 31;
+        uint32_t idx;
+        if (sh + BITS <= 32) idx = (d[w] >> sh) & ((1u << BITS) - 1u);
+        else idx = __builtin_amdgcn_alignbit(d[w + 1], d[w], sh) & ((1u << BITS) - 1u);
+        v[e] = cbs[idx];
+      }
+      u32x4_t ahi, alo;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ahi[j] = __builtin_amdgcn_perm(v[2 * j + 1], v[2 * j], 0x05040100u);
+        alo[j] = __builtin_amdgcn_perm(v[2 * j + 1], v[2 * j], 0x07060302u);
+      }
+      const bf16x8_t a_hi = __builtin_bit_cast(bf16x8_t, ahi);
+      const bf16x8_t a_lo = __builtin_bit_cast(bf16x8_t, alo);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, __builtin_bit_cast(bf16x8_t, bhi[kb]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, __builtin_bit_cast(bf16x8_t, blo[kb]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo, __builtin_bit_cast(bf16x8_t, bhi[kb]), acc, 0, 0, 0);
+    }
+    // acc[i] = tile row 4*qg + i, vector r16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[span][4 * qg + i][r16] = acc[i] * nrm[i];
+    __syncthreads();
+    // 256 outputs per tile; blocks of fewer than 4 spans have fewer threads
+    for (int o = tid; o < 256; o += blockDim.x) {
+      const int row = o >> 4, vec = o & 15;
+      float sum = 0.0f;
+      for (int sp = 0; sp < n_spans; ++sp) sum += red[sp][row][vec];
+      const int i = 16 * t + row;
+      if (vec < nb && i < rows) y[vec * y_stride + i] = sum;
+    }
+    __syncthreads();
+  };
+
+  int t = blockIdx.x;  // < n_tiles: the grid has at most n_tiles blocks
+  Words da, db;
+  float na[4], nbn[4];
+  load_tile(da, na, t);
+  if (tid < (1 << BITS)) cbs[tid] = bf16_split(codebook[tid]);
+  // B operands: vector r16's columns 256*span + 64*qg + 8*kb + e.  The loads
+  // sit in one block under the lane's own condition, so slots past nb fetch
+  // nothing and the 64 loads of a live lane are all in flight at once.
+  u32x4_t bhi[8], blo[8];
+  {
+    float xv[64];
+    if (r16 < nb) {
+      const float* src = prepared + (int64_t)r16 * input_padded + 256 * span + 64 * qg;
+#pragma unroll
+      for (int k = 0; k < 64; ++k) xv[k] = src[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < 64; ++k) xv[k] = 0.0f;
+    }
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      uint32_t h[8], o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t sp = bf16_split(xv[8 * kb + e]);
+        h[e] = sp & 0xffffu;
+        o[e] = sp >> 16;
+      }
+#pragma unroll
+      for (int dd = 0; dd < 4; ++dd) {
+        bhi[kb][dd] = h[2 * dd] | (h[2 * dd + 1] << 16);
+        blo[kb][dd] = o[2 * dd] | (o[2 * dd + 1] << 16);
+      }
+    }
+  }
+  __syncthreads();
+  const int stride = (int)gridDim.x;
+  while (true) {
+    load_tile(db, nbn, t + stride);
+    __builtin_amdgcn_sched_barrier(0);
+    tile(da, na, bhi, blo, t);
+    t += stride;
+    if (t >= n_tiles) break;
+    load_tile(da, na, t + stride);
+    __builtin_amdgcn_sched_barrier(0);
+    tile(db, nbn, bhi, blo, t);
+    t += stride;
+    if (t >= n_tiles) break;
+  }
+}
+
 namespace {
 
 constexpr int kMaxGrid = 4096;
@@ -553,6 +718,38 @@ int run_nb(const bqd_cq_matrix* m, FastShape f, const float* prepared, float* y,
   return BQD_EINVAL;
 }
 
+// The matrix-core kernel's conditions: groups of >= 256, whole 256-column
+// spans, at most 16 spans (one 1024-thread workgroup per row tile), dword
+// rows.
+bool mfma_ok(const bqd_cq_matrix* m) {
+  return m->group >= 256 && m->input_padded % 256 == 0 && m->input_padded <= 4096 &&
+         m->row_bytes % 4 == 0 && is_aligned(m->packed, 4);
+}
+
+template <int BITS>
+int launch_mfma_b(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t y_stride,
+                  int nb, int64_t row_begin, int64_t row_count, hipStream_t s) {
+  const int n_spans = (int)(m->input_padded / 256);
+  const int64_t n_tiles = (row_count + 15) / 16;
+  const int per_cu = 16 / n_spans;  // 16 wavefronts per CU at 4 per SIMD
+  const int64_t grid = std::min<int64_t>(n_tiles, (int64_t)cu_count() * per_cu);
+  hipLaunchKernelGGL((cq_matvec_mfma<BITS>), dim3((unsigned)grid), dim3(64 * n_spans), 0, s,
+                     m->packed, m->norms, m->codebook, prepared, y, m->input_padded,
+                     m->row_bytes, ilog2(m->group), row_begin, row_count, y_stride, nb);
+  return launch_status();
+}
+
+int run_mfma(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t y_stride, int nb,
+             int64_t row_begin, int64_t row_count, hipStream_t s) {
+  switch (m->bits) {
+    case 2: return launch_mfma_b<2>(m, prepared, y, y_stride, nb, row_begin, row_count, s);
+    case 3: return launch_mfma_b<3>(m, prepared, y, y_stride, nb, row_begin, row_count, s);
+    case 4: return launch_mfma_b<4>(m, prepared, y, y_stride, nb, row_begin, row_count, s);
+    case 5: return launch_mfma_b<5>(m, prepared, y, y_stride, nb, row_begin, row_count, s);
+  }
+  return BQD_EINVAL;
+}
+
 int launch_generic(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t batch,
                    int64_t row_begin, int64_t row_count, hipStream_t s) {
   const int64_t grid = std::min<int64_t>((row_count + kWavesPerBlock - 1) / kWavesPerBlock, kMaxGrid);
@@ -571,6 +768,16 @@ int launch_cq_matvec(const bqd_cq_matrix* m, const float* prepared, float* y, in
   const FastShape f1 = fast_shape(n_chunk, 1);
   const FastShape f4 = fast_shape(n_chunk, 4);
   if (batch == 1 && f1.lpr) return run_b1(m, f1, prepared, y, row_begin, row_count, s);
+  if (batch >= 2 && mfma_ok(m)) {
+    // up to sixteen vectors per launch on the matrix cores
+    for (int64_t b = 0; b < batch; b += 16) {
+      const int nb = (int)std::min<int64_t>(16, batch - b);
+      const int rc = run_mfma(m, prepared + b * m->input_padded, y + b * row_count, row_count, nb,
+                              row_begin, row_count, s);
+      if (rc) return rc;
+    }
+    return BQD_OK;
+  }
   if (f4.lpr) {
     // up to four vectors share each decoded weight per launch
     for (int64_t b = 0; b < batch; b += 4) {

@@ -150,9 +150,10 @@ int oracle_cq_matvec(const oracle_cq *m, const float *p, int64_t row_begin,
 }
 
 /* ---------------------------------------------------------------- O5 -- */
-/* [P1] "Row gather": decode one group's levels multiplied by the norm
- * (an fp32 product), run the normalized FWHT (the unnormalized butterfly,
- * then the same 1/sqrt(group) store as prepare), keep the unpadded columns. */
+/* [P1] "Row gather": per group, each codebook value times the group norm
+ * (an fp32 product), then the normalized transform (the unnormalized
+ * butterfly, then the same 1/sqrt(group) store as prepare); the columns below
+ * the unpadded width are the dense row. */
 int oracle_cq_dequantize_row(const oracle_cq *m, int64_t row, float *out)
 {
     if (!cq_ok(m) || row < 0 || row >= m->output) return -1;

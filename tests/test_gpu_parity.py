@@ -81,7 +81,8 @@ CQ_WORKLOADS = [n for n in WORKLOADS if n.startswith("cq")]
 
 # Small CQ shapes: every bit width and every fast lane layout (rows of 8..256
 # chunks of 32 columns), ragged row counts, padded rows; then generic-path
-# shapes (odd widths, groups under 32, rows not a dword multiple).
+# shapes (odd widths, groups under 32, rows not a dword multiple); then shapes
+# for the matrix-core batch kernel.
 SMALL = [
     synth.CqShape(100, 256, 256, 32, 2), synth.CqShape(77, 500, 512, 64, 3),
     synth.CqShape(45, 1000, 1024, 128, 4), synth.CqShape(33, 2048, 2048, 256, 5),
@@ -90,6 +91,8 @@ SMALL = [
     synth.CqShape(5, 3, 4, 4, 2), synth.CqShape(7, 13, 16, 4, 3), synth.CqShape(6, 30, 32, 8, 5),
     synth.CqShape(9, 64, 64, 16, 4, row_bytes=40), synth.CqShape(4, 100, 128, 32, 3, row_bytes=53),
     synth.CqShape(11, 96, 96, 32, 2), synth.CqShape(3, 250, 256, 128, 5, row_bytes=161),
+    # matrix-core batch path: groups >= 256, whole 256-column spans, ragged row tiles
+    synth.CqShape(37, 700, 768, 256, 2), synth.CqShape(20, 4096, 4096, 1024, 4, row_bytes=2052),
 ]
 
 
