@@ -446,165 +446,292 @@ __global__ __launch_bounds__(kThreads) void cq_matvec_nb(
 // ------------------------------------------------ matrix-core matvec, B >= 2
 // Several activation vectors share each decoded weight; the contraction runs
 // on the matrix cores (v_mfma_f32_16x16x32_bf16: a 16-row x 32-column tile of
-// weights times 32 columns x 16 vectors).  fp32 operands are carried exactly
-// enough as bf16 pairs: x = hi + lo with hi = bf16(x), lo = bf16(x - hi), so
-// |x - hi - lo| <= 2^-18 |x|; three products (hi*hi, hi*lo, lo*hi) per tile
-// accumulate in fp32 (the dropped lo*lo term is below 2^-18 of each product).
-// The codebook table in LDS holds each entry's (hi | lo << 16), so one LDS read
-// per weight feeds both weight operands.
+// weights times a 32 x 16 operand).  fp32 values are carried as bf16 pairs,
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi) (both rounded to
+// nearest even), so |x - hi - lo| <= 2^-18 |x|.  The 16 operand columns hold
+// the high halves of up to eight vectors and then their low halves, so two
+// products per block (weight high halves, weight low halves) give hi*hi,
+// hi*lo, lo*hi and lo*lo at once; column v and column v + 8 are added at the
+// end.
 //
-// A workgroup has one wavefront per 256-column span of the padded row (groups
-// are >= 256, so a span has one norm per row).  Lane l owns tile row l % 16
-// (and vector slot l % 16 of the B operand) and the 64-column quarter l / 16 of
-// its span; K-block kb of the span takes, from quarter g, columns
-// 64g + 8kb .. 64g + 8kb + 7.  Each wavefront keeps its span's activations as
-// B operands in registers for the whole kernel and walks 16-row tiles; per
-// tile the span partials (times their norms) meet in LDS and are summed in
-// span order.
+// Columns come in 256-wide spans (groups are >= 256, so a span has one norm
+// per row) and each wavefront owns one span for the whole kernel.  Lane l
+// owns tile row l % 16 and, with q = l / 16, the 64 columns 32 q + 0..31 and
+// 128 + 32 q + 0..31 of the span: its operand positions in K-block j (0..7)
+// are the eight columns 8 j .. 8 j + 7 of that list, so a K-block's weight
+// operand is one dword of packed 4-bit indices per lane, and each weight load
+// instruction reads 64 consecutive bytes of 16 rows.  The span's activation
+// operands stay in registers: lane l holds vector l % 8, high halves for
+// l % 16 < 8 and low halves otherwise; lanes l and l ^ 8 split half of the
+// values each and swap the halves they do not keep.  The activations reach
+// the lanes through LDS: the workgroup loads them with whole-line reads and
+// each lane then reads its own 32 values.
+//
+// 4-bit weights decode two indices at a time: tables indexed by a packed
+// byte give the (high, low) bf16 halves of both codebook values as one dword
+// each, already in operand order.  Each table row holds 32 copies of an
+// entry, lane l reading copy l % 32, so no two lanes of a half-wavefront meet
+// in one LDS bank; the byte-to-address step is a single byte permute.  Other
+// widths read a per-index table of (hi | lo << 16) and pair the halves with
+// byte permutes.
+//
+// A wavefront takes T tiles of 16 rows per row block, issuing all their
+// weight loads at once; the workgroup's wavefronts are its spans times rg row
+// groups.  The span partials (times their norms) of each row meet in LDS once
+// per row block and are summed in span order.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {  // finite x
-  uint32_t u = __float_as_uint(x);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+constexpr int kMfmaMaxSpans = 16;  // 4096 columns: a workgroup has <= 16 wavefronts
+constexpr int kMfmaTiles = 4;      // 16-row tiles per wavefront and row block
+constexpr int kRedStride = 9;      // floats per row of span partials (8 vectors + pad)
+constexpr int kRowRor8 = 0x128;    // DPP row_ror:8, lane i <- lane (i + 8) % 16 of its row
+constexpr int kPairCopies = 32;    // lane copies per 4-bit pair-table row
+// Table row b (256 bytes): copies of the high-half pair of byte b in its first
+// 128 bytes; the low-half pair of byte b sits kPairLoOffset bytes further (the
+// second half of row b + 4), a distance no paired LDS read can encode, so the
+// two reads of one byte keep separate destination registers.
+constexpr int kPairLoOffset = 4 * 256 + 128;
+constexpr int kPairTableBytes = (256 + 4) * 256;
+// LDS of the kernel, in phases: the staged activations (8 vectors x 4096
+// floats) first; then the tables, the span partials and the row block's norms.
+constexpr int kMaxBlockRows = 16 * kMfmaTiles * kMfmaMaxSpans;
+constexpr int kRedBytes = kMaxBlockRows * kRedStride * 4;
+constexpr int kMfmaLdsBytes = 8 * 4096 * 4;
+static_assert(kPairTableBytes + kRedBytes + 2 * kMaxBlockRows <= kMfmaLdsBytes, "LDS phases");
+
+// bf16 of a and b (round to nearest even), a in the low half
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
-// (hi, lo) bf16 split of x, packed as hi | lo << 16
-__device__ __forceinline__ uint32_t bf16_split(float x) {
-  const uint32_t hi = bf16_rne_bits(x);
-  const float rest = x - __uint_as_float(hi << 16);
-  return hi | (bf16_rne_bits(rest) << 16);
+// (hi, lo) splits of a and b: *hp = hi(a) | hi(b) << 16, *lp likewise for lo
+__device__ __forceinline__ void bf16_split_pair(float a, float b, uint32_t* hp, uint32_t* lp) {
+  const uint32_t h = bf16_pair(a, b);
+  *hp = h;
+  *lp = bf16_pair(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xffff0000u));
 }
 
-template <int BITS>
+// Position of 16-byte chunk cc of staged vector v: rotated by v + 8 (bit 5
+// of cc) within its group of 16 chunks, so that the 16 lanes of a row of a
+// wavefront (vectors 0..7, both halves) read 16 different bank groups.
+__device__ __forceinline__ int stage_pos(int v, int cc, int chunks_per_vector) {
+  return v * chunks_per_vector + (cc & ~15) + ((cc + v + 8 * ((cc >> 5) & 1)) & 15);
+}
+
+template <int BITS, int T>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void cq_matvec_mfma(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
                     const float* __restrict__ codebook, const float* __restrict__ prepared,
-                    float* __restrict__ y, int64_t input_padded, int64_t row_bytes,
-                    int log2_group, int64_t row_begin, int64_t row_count, int64_t y_stride,
-                    int nb) {
-  constexpr int kSpanBytes = 32 * BITS;  // 256 columns of BITS-bit indices
-  __shared__ uint32_t cbs[32];
-  __shared__ float red[16][16][17];      // [span][tile row][vector], padded
+                    float* __restrict__ y, int input_padded, int64_t row_bytes, int log2_group,
+                    int rows, int64_t y_stride, int nb, int rg_n) {
+  static_assert(T == kMfmaTiles, "LDS sized for kMfmaTiles");
+  constexpr bool kPairs = BITS == 4;
+  constexpr int kHalfBytes = 4 * BITS;  // one lane's 32 indices of a half span
+  __shared__ __align__(16) uint8_t smem[kMfmaLdsBytes];
+  u32x4_t* stage = reinterpret_cast<u32x4_t*>(smem);
+  uint32_t* lut = reinterpret_cast<uint32_t*>(smem);  // pair tables, or 32 entries
+  float* red = reinterpret_cast<float*>(smem + kPairTableBytes);  // [span][row][vector]
+  uint16_t* nrm_lds = reinterpret_cast<uint16_t*>(smem + kPairTableBytes + kRedBytes);
+
   const int tid = threadIdx.x;
-  const int span = tid >> 6;             // wavefront = span
-  const int n_spans = blockDim.x >> 6;
-  const int l = tid & 63;
-  const int r16 = l & 15;                // tile row (A, D) and vector slot (B)
-  const int qg = l >> 4;                 // 64-column quarter of the span
-  const int rows = (int)row_count;
-  const int n_tiles = (rows + 15) >> 4;
-  const int n_groups = (int)(input_padded >> log2_group);
-  const int group = (256 * span) >> log2_group;  // the span's group (groups >= 256)
+  const int wave = tid >> 6, l = tid & 63, r16 = l & 15, q = l >> 4;
+  const int n_spans = input_padded >> 8;
+  const int span = wave % n_spans, rg = wave / n_spans;
+  const int block_rows = 16 * T * rg_n;
+  const int n_blocks = (rows + block_rows - 1) / block_rows;
+  const int n_groups = input_padded >> log2_group;
+  const int g = (256 * span) >> log2_group;
+  // the row block's norms, [row][group]: groups >= 256 give
+  // block_rows * n_groups <= 64 T rg_n * n_spans <= blockDim entries
+  const int block_norms = block_rows * n_groups;
+  const uint8_t* lane_bytes = packed + 32 * BITS * span + kHalfBytes * q;
 
-  // The first tile's weights and norms load before the operand set-up, so
-  // their latency overlaps it; afterwards each tile's loads are issued before
-  // the previous tile is decoded (ping-pong buffers, unconditional loads of
-  // clamped rows).
-  const uint8_t* lane_base = packed + row_begin * row_bytes + kSpanBytes * span + 8 * BITS * qg;
-  typedef uint32_t Words[2 * BITS];  // this lane's 64 indices
-  auto load_tile = [&](Words& d, float (&nrm)[4], int t) {
-    const int r = min(16 * t + r16, rows - 1);  // in bounds; dropped if clamped
-    const uint32_t* pc = reinterpret_cast<const uint32_t*>(lane_base + (int64_t)r * row_bytes);
+  // Loads, in the order they are consumed: codebook, the activations, the row
+  // block's norms, then the weights of its first two tiles; each wait then
+  // covers only what it needs.  Later tiles load two tiles ahead of the one
+  // being decoded: a wavefront blocked on issuing loads into a full memory
+  // pipeline stalls only itself, not the set-up that the workgroup shares.
+  const float cbv = codebook[kPairs ? (l & 15) : min(tid, (1 << BITS) - 1)];
+  // Activation chunk k of this thread: 16-byte chunk cc of vector v, with
+  // 2 input_padded / 4 chunks over blockDim >= input_padded / 4 threads.
+  const int cpv = input_padded >> 2;  // chunks per vector
+  float4 xs[8];
 #pragma unroll
-    for (int i = 0; i < 2 * BITS; ++i) d[i] = pc[i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = min(16 * t + 4 * qg + i, rows - 1);
-      nrm[i] = f16_to_f32(norms[(row_begin + rr) * n_groups + group]);
-    }
+  for (int k = 0; k < 8; ++k) {
+    const int c = tid + k * (int)blockDim.x;
+    const int v = c / cpv;
+    if (c < 8 * cpv && v < nb)
+      xs[k] = reinterpret_cast<const float4*>(prepared)[(int64_t)v * cpv + (c - v * cpv)];
+  }
+  int rb = blockIdx.x;  // < n_blocks: the grid has at most n_blocks workgroups
+  auto load_norm = [&](int rb) {  // entry tid of the row block's norms (tid < block_norms)
+    const int64_t e = min((int64_t)rb * block_norms + min(tid, block_norms - 1),
+                          (int64_t)rows * n_groups - 1);
+    return norms[e];
   };
-  auto tile = [&](const Words& d, const float (&nrm)[4], const u32x4_t (&bhi)[8],
-                  const u32x4_t (&blo)[8], int t) {
-    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  uint16_t nv = load_norm(rb);
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t d[T][2 * BITS];
+  // Tile i of row block rb into d[i]: an unconditional load of a clamped row,
+  // whose result is dropped if clamped.
+  auto load_tile = [&](int rb, int i) {
+    const int r = min(rb * block_rows + 16 * T * rg + 16 * i + r16, rows - 1);
+    const uint8_t* p = lane_bytes + (int64_t)r * row_bytes;
+    const uint32_t* p0 = reinterpret_cast<const uint32_t*>(p);
+    const uint32_t* p1 = reinterpret_cast<const uint32_t*>(p + 16 * BITS);
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-      uint32_t v[8];
+    for (int w = 0; w < BITS; ++w) d[i][w] = p0[w];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int k = 8 * kb + e;  // index position in the lane's 64
-        const int bit = BITS * k, w = bit >> 5, sh = bit & 31;
-        uint32_t idx;
-        if (sh + BITS <= 32) idx = (d[w] >> sh) & ((1u << BITS) - 1u);
-        else idx = __builtin_amdgcn_alignbit(d[w + 1], d[w], sh) & ((1u << BITS) - 1u);
-        v[e] = cbs[idx];
-      }
-      u32x4_t ahi, alo;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ahi[j] = __builtin_amdgcn_perm(v[2 * j + 1], v[2 * j], 0x05040100u);
-        alo[j] = __builtin_amdgcn_perm(v[2 * j + 1], v[2 * j], 0x07060302u);
-      }
-      const bf16x8_t a_hi = __builtin_bit_cast(bf16x8_t, ahi);
-      const bf16x8_t a_lo = __builtin_bit_cast(bf16x8_t, alo);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, __builtin_bit_cast(bf16x8_t, bhi[kb]), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, __builtin_bit_cast(bf16x8_t, blo[kb]), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo, __builtin_bit_cast(bf16x8_t, bhi[kb]), acc, 0, 0, 0);
-    }
-    // acc[i] = tile row 4*qg + i, vector r16
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[span][4 * qg + i][r16] = acc[i] * nrm[i];
-    __syncthreads();
-    // 256 outputs per tile; blocks of fewer than 4 spans have fewer threads
-    for (int o = tid; o < 256; o += blockDim.x) {
-      const int row = o >> 4, vec = o & 15;
-      float sum = 0.0f;
-      for (int sp = 0; sp < n_spans; ++sp) sum += red[sp][row][vec];
-      const int i = 16 * t + row;
-      if (vec < nb && i < rows) y[vec * y_stride + i] = sum;
-    }
-    __syncthreads();
+    for (int w = 0; w < BITS; ++w) d[i][BITS + w] = p1[w];
   };
+  load_tile(rb, 0);
+  load_tile(rb, 1);
+  __builtin_amdgcn_sched_barrier(0);
 
-  int t = blockIdx.x;  // < n_tiles: the grid has at most n_tiles blocks
-  Words da, db;
-  float na[4], nbn[4];
-  load_tile(da, na, t);
-  if (tid < (1 << BITS)) cbs[tid] = bf16_split(codebook[tid]);
-  // B operands: vector r16's columns 256*span + 64*qg + 8*kb + e.  The loads
-  // sit in one block under the lane's own condition, so slots past nb fetch
-  // nothing and the 64 loads of a live lane are all in flight at once.
-  u32x4_t bhi[8], blo[8];
-  {
-    float xv[64];
-    if (r16 < nb) {
-      const float* src = prepared + (int64_t)r16 * input_padded + 256 * span + 64 * qg;
+  // Stage the activations, then read this lane's 32 values: vector r16 % 8,
+  // columns 128 part + 32 q + 0..31 of the span, part = r16 / 8.
 #pragma unroll
-      for (int k = 0; k < 64; ++k) xv[k] = src[k];
-    } else {
-#pragma unroll
-      for (int k = 0; k < 64; ++k) xv[k] = 0.0f;
-    }
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-      uint32_t h[8], o[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t sp = bf16_split(xv[8 * kb + e]);
-        h[e] = sp & 0xffffu;
-        o[e] = sp >> 16;
-      }
-#pragma unroll
-      for (int dd = 0; dd < 4; ++dd) {
-        bhi[kb][dd] = h[2 * dd] | (h[2 * dd + 1] << 16);
-        blo[kb][dd] = o[2 * dd] | (o[2 * dd + 1] << 16);
-      }
-    }
+  for (int k = 0; k < 8; ++k) {
+    const int c = tid + k * (int)blockDim.x;
+    const int v = c / cpv;
+    if (c < 8 * cpv && v < nb)
+      stage[stage_pos(v, c - v * cpv, cpv)] = __builtin_bit_cast(u32x4_t, xs[k]);
   }
   __syncthreads();
-  const int stride = (int)gridDim.x;
+  const int part = r16 >> 3;
+  float xv[32];
+  {
+    const int v = r16 & 7;
+    const int cc0 = 64 * span + 32 * part + 8 * q;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u32x4_t t = stage[stage_pos(v, cc0 + i, cpv)];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xv[4 * i + e] = __uint_as_float(t[e]);
+    }
+  }
+  // Activation operands of the span, K-block j: lanes of part 0 (DPP banks 0
+  // and 1 of each row) keep the high halves of values 0..31 and receive those
+  // of 32..63 from the lane 8 above; lanes of part 1 keep the low halves of
+  // 32..63 and receive those of 0..31.  A DPP move that writes only the
+  // receiving part places each value without selects.  Vectors from nb on
+  // hold stale LDS data; their columns are never stored.
+  u32x4_t bx[8];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t hp, lp;
+    bf16_split_pair(xv[2 * i], xv[2 * i + 1], &hp, &lp);
+    bx[i >> 2][i & 3] = __builtin_amdgcn_update_dpp(hp, lp, kRowRor8, 0xf, 0xc, false);
+    bx[4 + (i >> 2)][i & 3] = __builtin_amdgcn_update_dpp(lp, hp, kRowRor8, 0xf, 0x3, false);
+  }
+  __syncthreads();  // the staged activations are read; the tables overwrite them
+
+  // Codebook tables.
+  if constexpr (kPairs) {
+    uint32_t hs, ls;  // lane l % 16: halves of codebook[l % 16]
+    bf16_split_pair(cbv, cbv, &hs, &ls);
+    hs &= 0xffffu;
+    ls &= 0xffffu;
+    // slot t writes copies 4 (t % 8) .. + 3 of rows 16 h + 4 (t / 256) + 0..3,
+    // h = (t / 16) % 16, in the high-half table for even t / 8 and the low-half
+    // one for odd: the 16 lanes of one store pass cover a high row and a low
+    // row, which sit in opposite halves of the banks.
+    for (int t = tid; t < 1024; t += (int)blockDim.x) {
+      const int c4 = 4 * (t & 7), lo_tab = (t >> 3) & 1, h = (t >> 4) & 15, e0 = 4 * (t >> 8);
+      // odd column: index h
+      const uint32_t hh = (uint32_t)__shfl((int)hs, h), lh = (uint32_t)__shfl((int)ls, h);
+      const uint32_t hi16 = (lo_tab ? lh : hh) << 16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {  // even column: index e0 + e (wave-uniform)
+        const int b = 16 * h + e0 + e;
+        const uint32_t he = (uint32_t)__builtin_amdgcn_readlane((int)hs, e0 + e);
+        const uint32_t le = (uint32_t)__builtin_amdgcn_readlane((int)ls, e0 + e);
+        const uint32_t val = (lo_tab ? le : he) | hi16;
+        const u32x4_t v4 = {val, val, val, val};
+        *reinterpret_cast<u32x4_t*>(&lut[lo_tab ? (b + 4) * 64 + 32 + c4 : b * 64 + c4]) = v4;
+      }
+    }
+  } else {
+    if (tid < (1 << BITS)) {
+      uint32_t h, lo;
+      bf16_split_pair(cbv, cbv, &h, &lo);
+      lut[tid] = (h & 0xffffu) | (lo << 16);
+    }
+  }
+
+  const uint32_t lane_off = 4u * (uint32_t)(l & (kPairCopies - 1));  // this lane's copy
   while (true) {
-    load_tile(db, nbn, t + stride);
-    __builtin_amdgcn_sched_barrier(0);
-    tile(da, na, bhi, blo, t);
-    t += stride;
-    if (t >= n_tiles) break;
-    load_tile(da, na, t + stride);
-    __builtin_amdgcn_sched_barrier(0);
-    tile(db, nbn, bhi, blo, t);
-    t += stride;
-    if (t >= n_tiles) break;
+    if (tid < block_norms) nrm_lds[tid] = nv;
+    __syncthreads();  // tables and norms written; the previous partials read
+    const int next = rb + (int)gridDim.x;
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      // two tiles ahead: this row block's, then the next one's first two
+      if (i + 2 < T) {
+        load_tile(rb, i + 2);
+      } else if (next < n_blocks) {
+        if (i + 2 == T) nv = load_norm(next);
+        load_tile(next, i + 2 - T);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        u32x4_t ahi, alo;
+        if constexpr (kPairs) {
+          const uint32_t w = d[i][j];  // indices of the lane's columns 8 j .. 8 j + 7
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            // row (byte p of w) of the tables, copy lane % 32
+            const uint32_t a = __builtin_amdgcn_perm(w, lane_off, 0x0c0c0400u | ((4u + p) << 8));
+            ahi[p] = *reinterpret_cast<const uint32_t*>(smem + a);
+            alo[p] = *reinterpret_cast<const uint32_t*>(smem + a + kPairLoOffset);
+          }
+        } else {
+          uint32_t v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int k = 8 * j + e;  // index position in the lane's 64
+            const int bit = BITS * k, w = bit >> 5, sh = bit & 31;
+            uint32_t idx;
+            if (sh + BITS <= 32) idx = (d[i][w] >> sh) & ((1u << BITS) - 1u);
+            else idx = __builtin_amdgcn_alignbit(d[i][w + 1], d[i][w], sh) & ((1u << BITS) - 1u);
+            v[e] = lut[idx];
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ahi[e] = __builtin_amdgcn_perm(v[2 * e + 1], v[2 * e], 0x05040100u);
+            alo[e] = __builtin_amdgcn_perm(v[2 * e + 1], v[2 * e], 0x07060302u);
+          }
+        }
+        const bf16x8_t bo = __builtin_bit_cast(bf16x8_t, bx[j]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ahi), bo, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, alo), bo, acc, 0, 0, 0);
+      }
+      // acc[k]: row 16 T rg + 16 i + 4 q + k of the block, operand column r16;
+      // times its norm, then column v (high halves) + column v + 8 (low halves)
+      const int row = 16 * T * rg + 16 * i + 4 * q;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float s = acc[k] * f16_to_f32(nrm_lds[(row + k) * n_groups + g]);
+        const float v = s + dpp<kRowRor8, 0xf, false>(0.0f, s);
+        if (r16 < 8) red[(span * block_rows + row + k) * kRedStride + r16] = v;
+      }
+    }
+    __syncthreads();
+    for (int o = tid; o < block_rows * nb; o += (int)blockDim.x) {
+      const int v = o / block_rows, row = o - v * block_rows;
+      float sum = 0.0f;
+      for (int s = 0; s < n_spans; ++s) sum += red[(s * block_rows + row) * kRedStride + v];
+      const int r = rb * block_rows + row;
+      if (r < rows) y[v * y_stride + r] = sum;
+    }
+    rb = next;
+    if (rb >= n_blocks) break;
   }
 }
 
@@ -719,23 +846,31 @@ int run_nb(const bqd_cq_matrix* m, FastShape f, const float* prepared, float* y,
 }
 
 // The matrix-core kernel's conditions: groups of >= 256, whole 256-column
-// spans, at most 16 spans (one 1024-thread workgroup per row tile), dword
-// rows.
-bool mfma_ok(const bqd_cq_matrix* m) {
-  return m->group >= 256 && m->input_padded % 256 == 0 && m->input_padded <= 4096 &&
-         m->row_bytes % 4 == 0 && is_aligned(m->packed, 4);
+// spans, at most 16 spans (one wavefront each), dword rows, and activations
+// that load as float4.
+bool mfma_ok(const bqd_cq_matrix* m, const float* prepared) {
+  return m->group >= 256 && m->input_padded % 256 == 0 &&
+         m->input_padded <= 256 * kMfmaMaxSpans && m->row_bytes % 4 == 0 &&
+         is_aligned(m->packed, 4) && is_aligned(prepared, 16);
 }
 
 template <int BITS>
 int launch_mfma_b(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t y_stride,
                   int nb, int64_t row_begin, int64_t row_count, hipStream_t s) {
+  constexpr int T = kMfmaTiles;
   const int n_spans = (int)(m->input_padded / 256);
-  const int64_t n_tiles = (row_count + 15) / 16;
-  const int per_cu = 16 / n_spans;  // 16 wavefronts per CU at 4 per SIMD
-  const int64_t grid = std::min<int64_t>(n_tiles, (int64_t)cu_count() * per_cu);
-  hipLaunchKernelGGL((cq_matvec_mfma<BITS>), dim3((unsigned)grid), dim3(64 * n_spans), 0, s,
-                     m->packed, m->norms, m->codebook, prepared, y, m->input_padded,
-                     m->row_bytes, ilog2(m->group), row_begin, row_count, y_stride, nb);
+  // row groups per workgroup: enough to spread the rows over every CU, at
+  // most 16 wavefronts
+  const int64_t tiles = (row_count + 16 * T - 1) / (16 * T);
+  const int64_t rg_need = (tiles + cu_count() - 1) / cu_count();
+  const int rg = (int)std::max<int64_t>(1, std::min<int64_t>(rg_need, kMfmaMaxSpans / n_spans));
+  const int64_t block_rows = 16 * T * rg;
+  const int64_t grid = std::min<int64_t>((row_count + block_rows - 1) / block_rows, cu_count());
+  hipLaunchKernelGGL((cq_matvec_mfma<BITS, T>), dim3((unsigned)grid), dim3((unsigned)(64 * n_spans * rg)),
+                     0, s, m->packed + row_begin * m->row_bytes,
+                     m->norms + row_begin * (m->input_padded / m->group), m->codebook, prepared, y,
+                     (int)m->input_padded, m->row_bytes, ilog2(m->group), (int)row_count, y_stride,
+                     nb, rg);
   return launch_status();
 }
 
@@ -768,10 +903,10 @@ int launch_cq_matvec(const bqd_cq_matrix* m, const float* prepared, float* y, in
   const FastShape f1 = fast_shape(n_chunk, 1);
   const FastShape f4 = fast_shape(n_chunk, 4);
   if (batch == 1 && f1.lpr) return run_b1(m, f1, prepared, y, row_begin, row_count, s);
-  if (batch >= 2 && mfma_ok(m)) {
-    // up to sixteen vectors per launch on the matrix cores
-    for (int64_t b = 0; b < batch; b += 16) {
-      const int nb = (int)std::min<int64_t>(16, batch - b);
+  if (batch >= 2 && mfma_ok(m, prepared)) {
+    // up to eight vectors per launch on the matrix cores
+    for (int64_t b = 0; b < batch; b += 8) {
+      const int nb = (int)std::min<int64_t>(8, batch - b);
       const int rc = run_mfma(m, prepared + b * m->input_padded, y + b * row_count, row_count, nb,
                               row_begin, row_count, s);
       if (rc) return rc;

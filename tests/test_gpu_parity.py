@@ -200,6 +200,27 @@ def test_matvec_row_ranges(cache):
         check_matvec(small, rb, rc)
 
 
+# Matrix-core batch path: eight-vector launches and a remainder launch, row
+# ranges, a row count that gives part of the persistent grid a second row
+# block (over 256 x 64 rows at 4096 columns), groups of two and four spans,
+# and a 15-span row (one span per wavefront, 15 wavefronts).
+MFMA_CASES = [
+    (synth.CqShape(17084, 4096, 4096, 512, 3), 2, 0, None),
+    (synth.CqShape(300, 2048, 2048, 256, 4), 9, 0, None),
+    (synth.CqShape(300, 2000, 2048, 256, 5), 16, 7, 250),
+    (synth.CqShape(130, 1024, 1024, 1024, 2), 8, 1, 129),
+    (synth.CqShape(64, 256, 256, 256, 4), 5, 0, None),
+    (synth.CqShape(1000, 3840, 3840, 256, 4), 8, 0, None),
+]
+
+
+@pytest.mark.parametrize("k", range(len(MFMA_CASES)))
+def test_matvec_batch_matrix_core(k):
+    shape, batch, rb, rc = MFMA_CASES[k]
+    print(f"[case] matrix-core {shape} batch {batch} rows [{rb}, +{rc})", flush=True)
+    check_matvec(synth.make_cq(shape, seed=500 + k, batch=batch), rb, rc)
+
+
 def one_hot_inputs(s, cols):
     """x whose prepared vector is exactly e_k for each k in cols: column k of
     the normalized Hadamard block of k's group (every entry +-1/sqrt(g), an
