@@ -58,6 +58,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="0: the affinity mask, at most 16")
     ap.add_argument("--hot", action="store_true", help="one weight copy (cache-resident timing)")
+    ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn the two --traffic-probe counter runs into the traffic record "
+                         "under profiles/ (no GPU needed)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for counter runs: 8 F8 head launches, then 8 plain 1 GiB device copies")
     return ap.parse_args()
@@ -220,8 +223,59 @@ def traffic_probe(torch, bqd, synth):
     print(json.dumps({"f8_head_bytes": hd.R * hd.C + hd.SR * hd.SC, "copy_bytes": n}), flush=True)
 
 
+def _dispatch_kib(out_dir, counter):
+    """Median per-dispatch value of `counter` for the head kernel and for the
+    1 GiB copy, from a rocprofv3 --pmc csv directory."""
+    import csv
+    import glob
+    import statistics
+    vals = {"head": [], "copy": []}
+    for f in glob.glob(os.path.join(out_dir, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"]
+            key = "head" if "f8_matvec_fast" in name else "copy" if "copyBuffer" in name else None
+            if key:
+                vals[key].append(float(row["Counter_Value"]))
+    if len(vals["head"]) < 8 or len(vals["copy"]) < 8:
+        raise SystemExit(f"{out_dir}: expected 8 head and 8 copy dispatches for {counter}")
+    return statistics.median(vals["head"]), statistics.median(vals["copy"])
+
+
+def traffic_record(fetch_dir, write_dir):
+    """HBM bytes per head launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
+    each scaled by what the same counter reads for a 1 GiB device copy."""
+    import hashlib
+    import synth
+    hd = synth.HEAD
+    head_f, copy_f = _dispatch_kib(fetch_dir, "FETCH_SIZE")
+    head_w, copy_w = _dispatch_kib(write_dir, "WRITE_SIZE")
+    gib_kib = float(1 << 20)
+    fetch_scale = round(gib_kib / copy_f, 2)
+    write_scale = round(gib_kib / copy_w, 2)
+    read_b = round(head_f * 1024 * fetch_scale)
+    write_b = round(head_w * 1024 * write_scale)
+    alg = hd["R"] * hd["C"] + hd["SR"] * hd["SC"]  # weights and scales
+    rec = {
+        "kernel": "f8_matvec_fast (F8 E4M3 head %dx%d, E8M0 scales %dx%d)" % (hd["R"], hd["C"], hd["SR"], hd["SC"]),
+        "source_sha256_16": hashlib.sha256(b"".join(open(f, "rb").read() for f in KERNEL_SOURCES)).hexdigest()[:16],
+        "fetch_kib_per_dispatch_raw": head_f, "write_kib_per_dispatch_raw": head_w,
+        "copy_1gib_fetch_kib_raw": copy_f, "copy_1gib_write_kib_raw": copy_w,
+        "fetch_scale": fetch_scale, "write_scale": write_scale,
+        "read_bytes": read_b, "write_bytes": write_b, "traffic_bytes": read_b + write_b,
+        "algorithmic_read_bytes": alg, "read_over_algorithmic": round(read_b / alg, 4),
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def main():
     args = parse_args()
+    if args.traffic_record:
+        traffic_record(*args.traffic_record)
+        return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
               f"(the rows of each matvec shard across GPUs by design only)", file=sys.stderr)

@@ -12,7 +12,7 @@
 #include <atomic>
 #include <cmath>
 
-#include "device.h"
+#include "cq_device.h"
 #include "launch.h"
 
 namespace bqd {
@@ -92,8 +92,9 @@ int launch_cq_prepare(const bqd_cq_matrix* m, const float* x, float* prepared, i
 // ------------------------------------------------------------------- gather
 // One wavefront per (id, span of 64*E columns): codebook value times norm
 // (an fp32 product), transform, scale, store the columns below `input`.
+// Generic form: any bit width and group, one index decode per element.
 template <int E>
-__global__ __launch_bounds__(kThreads) void cq_gather_kernel(
+__global__ __launch_bounds__(kThreads) void cq_gather_generic(
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
     const float* __restrict__ codebook, const int32_t* __restrict__ rows, float* __restrict__ out,
     int64_t output, int64_t input, int64_t input_padded, int64_t row_bytes, int bits,
@@ -129,31 +130,116 @@ __global__ __launch_bounds__(kThreads) void cq_gather_kernel(
     if (c0 + e < input) o[c0 + e] = scale_store(v[e], scale);
 }
 
+// Groups of 8 and more: lane l owns E = 8 or 16 consecutive columns, which lie
+// in one group (one norm) and in E * BITS / 8 whole bytes of the row; all the
+// lane's loads are issued together before any is used.  Rows whose visible
+// columns fill the lane are stored as float4s when the output rows are
+// 16-byte aligned.
+template <int BITS, int E>
+__global__ __launch_bounds__(kThreads) void cq_gather_kernel(
+    const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
+    const float* __restrict__ codebook, const int32_t* __restrict__ rows, float* __restrict__ out,
+    int64_t output, int64_t input, int64_t input_padded, int64_t row_bytes, int log2_group,
+    int64_t spans, int64_t n_waves, double scale, bool vec_store) {
+  constexpr int kBytes = E * BITS / 8;
+  __shared__ float cb[32];
+  if (threadIdx.x < (1 << BITS)) cb[threadIdx.x] = codebook[threadIdx.x];
+  __syncthreads();
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wv = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  if (wv >= n_waves) return;  // whole wavefront
+  const int64_t i = wv / spans;
+  const int64_t c0 = (wv % spans) * (64 * E) + lane * E;
+  const int64_t r = rows[i];
+  float* o = out + i * input + c0;
+  if (r < 0 || r >= output) {  // an id outside the table: a NaN row
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (c0 + e < input) o[e] = __uint_as_float(0x7fc00000u);
+    return;
+  }
+  // input_padded is a multiple of the group, so a lane's E columns are all
+  // inside the stored row or all past it
+  const bool live = c0 < input_padded;
+  const int64_t cl = live ? c0 : 0;  // past the row: load column 0, use nothing
+  const uint8_t* pb = packed + r * row_bytes + cl * BITS / 8;
+  uint32_t byte[kBytes];
+#pragma unroll
+  for (int k = 0; k < kBytes; ++k) byte[k] = pb[k];
+  const float nrm = f16_to_f32(norms[r * (input_padded >> log2_group) + (cl >> log2_group)]);
+  float v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int bit = BITS * e, k = bit >> 3, sh = bit & 7;
+    uint32_t w = byte[k];
+    if (sh + BITS > 8) w |= byte[k + 1] << 8;
+    const float c = cb[(w >> sh) & ((1u << BITS) - 1u)] * nrm;
+    v[e] = live ? c : 0.0f;
+  }
+  wave_fwht<E>(v, lane, log2_group);
+  if (vec_store && c0 + E <= input) {
+#pragma unroll
+    for (int e = 0; e < E; e += 4)
+      *reinterpret_cast<float4*>(o + e) =
+          make_float4(scale_store(v[e], scale), scale_store(v[e + 1], scale),
+                      scale_store(v[e + 2], scale), scale_store(v[e + 3], scale));
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (c0 + e < input) o[e] = scale_store(v[e], scale);
+  }
+}
+
 template <int E>
-int launch_gather_e(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, float* out,
-                    hipStream_t s) {
+int launch_gather_generic(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, float* out,
+                          hipStream_t s) {
   // spans past the last visible column store nothing and are not launched
   const int64_t spans = (m->input + 64 * E - 1) / (64 * E);
   const int64_t n_waves = spans * n;
   const int64_t grid = (n_waves + kWavesPerBlock - 1) / kWavesPerBlock;
-  hipLaunchKernelGGL((cq_gather_kernel<E>), dim3((unsigned)grid), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((cq_gather_generic<E>), dim3((unsigned)grid), dim3(kThreads), 0, s,
                      m->packed, m->norms, m->codebook, rows, out, m->output, m->input,
                      m->input_padded, m->row_bytes, (int)m->bits, ilog2(m->group), spans,
                      n_waves, 1.0 / std::sqrt((double)m->group));
   return launch_status();
 }
 
+template <int BITS, int E>
+int launch_gather_fast(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, float* out,
+                       hipStream_t s) {
+  const int64_t spans = (m->input + 64 * E - 1) / (64 * E);
+  const int64_t n_waves = spans * n;
+  const int64_t grid = (n_waves + kWavesPerBlock - 1) / kWavesPerBlock;
+  const bool vec_store = m->input % 4 == 0 && is_aligned(out, 16);
+  hipLaunchKernelGGL((cq_gather_kernel<BITS, E>), dim3((unsigned)grid), dim3(kThreads), 0, s,
+                     m->packed, m->norms, m->codebook, rows, out, m->output, m->input,
+                     m->input_padded, m->row_bytes, ilog2(m->group), spans, n_waves,
+                     1.0 / std::sqrt((double)m->group), vec_store);
+  return launch_status();
+}
+
+template <int E>
+int launch_gather_bits(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, float* out,
+                       hipStream_t s) {
+  switch (m->bits) {
+    case 2: return launch_gather_fast<2, E>(m, rows, n, out, s);
+    case 3: return launch_gather_fast<3, E>(m, rows, n, out, s);
+    case 4: return launch_gather_fast<4, E>(m, rows, n, out, s);
+    case 5: return launch_gather_fast<5, E>(m, rows, n, out, s);
+  }
+  return BQD_EINVAL;
+}
+
 int launch_cq_gather(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, float* out,
                      hipStream_t s) {
   if (m->input == 0) return BQD_OK;
+  // groups of 8..512 on 8 columns per lane, 1024 on 16
+  if (m->group >= 8 && m->group <= 512) return launch_gather_bits<8>(m, rows, n, out, s);
+  if (m->group == 1024) return launch_gather_bits<16>(m, rows, n, out, s);
   switch (lane_elems(m->group)) {
-    case 1: return launch_gather_e<1>(m, rows, n, out, s);
-    case 2: return launch_gather_e<2>(m, rows, n, out, s);
-    case 4: return launch_gather_e<4>(m, rows, n, out, s);
-    case 8: return launch_gather_e<8>(m, rows, n, out, s);
-    case 16: return launch_gather_e<16>(m, rows, n, out, s);
+    case 1: return launch_gather_generic<1>(m, rows, n, out, s);
   }
-  return BQD_EINVAL;
+  return BQD_EINVAL;  // unreachable: group <= 1024 is validated
 }
 
 // ----------------------------------------------------------- generic matvec
@@ -488,7 +574,6 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kMfmaMaxSpans = 16;  // 4096 columns: a workgroup has <= 16 wavefronts
 constexpr int kMfmaTiles = 4;      // 16-row tiles per wavefront and row block
 constexpr int kRedStride = 9;      // floats per row of span partials (8 vectors + pad)
-constexpr int kRowRor8 = 0x128;    // DPP row_ror:8, lane i <- lane (i + 8) % 16 of its row
 constexpr int kPairCopies = 32;    // lane copies per 4-bit pair-table row
 // Table row b (256 bytes): copies of the high-half pair of byte b in its first
 // 128 bytes; the low-half pair of byte b sits kPairLoOffset bytes further (the
