@@ -405,6 +405,136 @@ void cq_matvec_b1(const uint8_t* __restrict__ packed, const uint16_t* __restrict
   }
 }
 
+// ------------------------------------------- batch-1 matvec, 4-bit pair tables
+// 4-bit rows of 16..128 chunks: a packed byte holds two indices, and an LDS
+// table indexed by the byte returns both codebook values as one 8-byte read.
+// Each table row holds 32 copies of its entry and lane l reads copy l % 32, so
+// no two lanes of a half-wavefront meet in one LDS bank; the byte-to-address
+// step is one byte permute.  Per pair of weights: one permute, one LDS read,
+// two FMAs.  Lanes own chunks q, q + LPR, ... of the row (each load
+// instruction reads LPR consecutive chunks) and keep those chunks'
+// activations in registers; the activations reach them through LDS (one
+// coalesced read of the vector per workgroup), in the space the table then
+// takes.
+constexpr int kPairRowBytes = 32 * 8;                  // 32 copies of (float, float)
+constexpr int kPairTableFloats = 256 * kPairRowBytes / 4;
+constexpr int kB1PairThreads = 512;                    // two workgroups per CU share the LDS
+static_assert(kB1PairThreads * 8 * 4 == kPairTableFloats, "eight table slots per thread");
+
+template <int NJ, int LPR, int U>
+__global__ __launch_bounds__(kB1PairThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void cq_matvec_b1_pairs(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
+                        const float* __restrict__ codebook, const float* __restrict__ prepared,
+                        float* __restrict__ y, int64_t input_padded, int64_t row_bytes,
+                        int log2_group, int rows) {
+  constexpr int SLOTS = kB1PairThreads / LPR;  // rows per step
+  __shared__ __align__(16) float tab[kPairTableFloats];
+  const int tid = threadIdx.x;
+  const int slot = tid / LPR;
+  const int q = tid % LPR;
+  const int n_groups = (int)(input_padded >> log2_group);
+  const int n_steps = (rows + SLOTS - 1) / SLOTS;
+  const int stride = (int)gridDim.x * U;
+  const uint8_t* lane_base = packed + 16 * q;
+  int gidx[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) gidx[j] = (32 * (q + LPR * j)) >> log2_group;
+
+  const float cbv = codebook[tid & 15];  // lanes 0..15 of every wavefront: the codebook
+  // The first step's weights and norms are requested before the set-up, so
+  // the weight stream runs while the activations and the table are prepared.
+  uint32_t d[U][NJ][4];
+  uint16_t nb[U][NJ];
+  auto load_step = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = min((s0 + u) * SLOTS + slot, rows - 1);  // in bounds; dropped if clamped
+      const uint32_t* pc = reinterpret_cast<const uint32_t*>(lane_base + (int64_t)i * row_bytes);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) d[u][j][t] = pc[4 * LPR * j + t];
+      const uint16_t* nr = norms + (int64_t)i * n_groups;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) nb[u][j] = nr[gidx[j]];
+    }
+  };
+  int s0 = (int)blockIdx.x * U;  // < n_steps: the grid has at most ceil(n_steps / U) workgroups
+  const int n4 = (int)(input_padded >> 2);
+  float4 xs[2];  // this thread's share of the activations (input_padded <= 32 * 128 floats)
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = min(tid + k * kB1PairThreads, n4 - 1);
+    xs[k] = reinterpret_cast<const float4*>(prepared)[i];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  load_step(s0);
+  __builtin_amdgcn_sched_barrier(0);
+  // Activations, staged with a stride of 36 floats per 32-float chunk (the 16
+  // lanes of a read pass then cover all banks), then chunk q + LPR j of this
+  // lane into registers.
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = tid + k * kB1PairThreads;
+    if (i < n4) *reinterpret_cast<float4*>(tab + 36 * (i >> 3) + 4 * (i & 7)) = xs[k];
+  }
+  __syncthreads();
+  float act[NJ][32];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const float* src = tab + 36 * (q + LPR * j);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float4 v = *reinterpret_cast<const float4*>(src + 4 * k);
+      act[j][4 * k] = v.x; act[j][4 * k + 1] = v.y; act[j][4 * k + 2] = v.z; act[j][4 * k + 3] = v.w;
+    }
+  }
+  __syncthreads();  // the staged activations are read; the table overwrites them
+  // Table: row b = copies of (codebook[b % 16], codebook[b / 16]); 16-byte
+  // slot s of the table is row s / 16, copies 2 (s % 16) and 2 (s % 16) + 1.
+  // Slot tid + 512 k has b % 16 = (tid / 16) % 16 and b / 16 = tid / 256 + 2 k,
+  // the latter uniform over a wavefront.
+  {
+    const float lo = __shfl(cbv, (tid >> 4) & 15);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cbv), (tid >> 8) + 2 * k));
+      *reinterpret_cast<float4*>(tab + 4 * (tid + kB1PairThreads * k)) = make_float4(lo, hi, lo, hi);
+    }
+  }
+  __syncthreads();
+  const uint32_t lane_off = 8u * (uint32_t)(tid & 31);
+  const char* tab_bytes = reinterpret_cast<const char*>(tab);
+
+  while (true) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            // columns 8 t + 2 p (low nibble) and 8 t + 2 p + 1 of the chunk
+            const uint32_t a = __builtin_amdgcn_perm(d[u][j][t], lane_off, 0x0c0c0400u | ((4u + p) << 8));
+            const float2 c = *reinterpret_cast<const float2*>(tab_bytes + a);
+            p0 += c.x * act[j][8 * t + 2 * p];
+            p1 += c.y * act[j][8 * t + 2 * p + 1];
+          }
+        acc += f16_to_f32(nb[u][j]) * (p0 + p1);
+      }
+      acc = group_sum<LPR>(acc);
+      const int i = (s0 + u) * SLOTS + slot;
+      if (q == LPR - 1 && i < rows) y[i] = acc;
+    }
+    s0 += stride;
+    if (s0 >= n_steps) break;
+    load_step(s0);
+  }
+}
+
 // -------------------------------------------------- fast matvec, NB vectors
 // Same lane layout; NB activation vectors share each decoded weight.  Rows
 // wider than one wavefront (LPR > 64) are split over LPR/64 wavefronts whose
@@ -908,6 +1038,38 @@ int dispatch_nb(const bqd_cq_matrix* m, FastShape f, const float* prepared, floa
   return BQD_EINVAL;
 }
 
+constexpr int kNoKernel = 1;  // no instantiation covers the shape
+
+template <int NJ, int LPR>
+int launch_b1_pairs(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t row_begin,
+                    int64_t row_count, hipStream_t s) {
+  constexpr int U = 2;  // rows per wavefront and step
+  constexpr int SLOTS = kB1PairThreads / LPR;
+  const int64_t n_steps = (row_count + SLOTS - 1) / SLOTS;
+  const int64_t grid = std::min<int64_t>((n_steps + U - 1) / U, (int64_t)cu_count() * 2);
+  hipLaunchKernelGGL((cq_matvec_b1_pairs<NJ, LPR, U>), dim3((unsigned)grid), dim3(kB1PairThreads),
+                     0, s, m->packed + row_begin * m->row_bytes,
+                     m->norms + row_begin * (m->input_padded / m->group), m->codebook, prepared, y,
+                     m->input_padded, m->row_bytes, ilog2(m->group), (int)row_count);
+  return launch_status();
+}
+
+// 4-bit rows of 16, 32, 64 or 128 whole chunks with 16-byte aligned rows and
+// activations; kNoKernel otherwise.
+int run_b1_pairs(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t row_begin,
+                 int64_t row_count, hipStream_t s) {
+  if (m->input_padded % 32 || m->group < 32 || m->row_bytes % 16 || !is_aligned(m->packed, 16) ||
+      !is_aligned(prepared, 16))
+    return kNoKernel;
+  switch (m->input_padded / 32) {
+    case 16: return launch_b1_pairs<1, 16>(m, prepared, y, row_begin, row_count, s);
+    case 32: return launch_b1_pairs<1, 32>(m, prepared, y, row_begin, row_count, s);
+    case 64: return launch_b1_pairs<1, 64>(m, prepared, y, row_begin, row_count, s);
+    case 128: return launch_b1_pairs<2, 64>(m, prepared, y, row_begin, row_count, s);
+  }
+  return kNoKernel;
+}
+
 int run_b1(const bqd_cq_matrix* m, FastShape f, const float* prepared, float* y,
            int64_t row_begin, int64_t row_count, hipStream_t s) {
   switch (m->bits) {
@@ -987,6 +1149,10 @@ int launch_cq_matvec(const bqd_cq_matrix* m, const float* prepared, float* y, in
   const int64_t n_chunk = m->input_padded / 32;
   const FastShape f1 = fast_shape(n_chunk, 1);
   const FastShape f4 = fast_shape(n_chunk, 4);
+  if (batch == 1 && m->bits == 4) {
+    const int rc = run_b1_pairs(m, prepared, y, row_begin, row_count, s);
+    if (rc != kNoKernel) return rc;
+  }
   if (batch == 1 && f1.lpr) return run_b1(m, f1, prepared, y, row_begin, row_count, s);
   if (batch >= 2 && mfma_ok(m, prepared)) {
     // up to eight vectors per launch on the matrix cores
