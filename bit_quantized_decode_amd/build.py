@@ -21,8 +21,11 @@ HIP_SOURCES = ["cq.hip", "f8.hip", "capi.hip"]
 HOST_SOURCES = ["validate.cpp"]
 ARCH = "gfx950"
 # Packed fp32 VALU instructions are turned off for every device pass.
+# -disable-promote-alloca-to-lds: private arrays stay in registers; moved to
+# LDS they would silently raise a kernel's LDS size and cut its occupancy.
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
-               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", f"-I{INCLUDE}"]
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-mllvm", "-disable-promote-alloca-to-lds", f"-I{INCLUDE}"]
 GXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}"]
 
 

@@ -461,22 +461,23 @@ void cq_matvec_b1_pairs(const uint8_t* __restrict__ packed, const uint16_t* __re
   };
   int s0 = (int)blockIdx.x * U;  // < n_steps: the grid has at most ceil(n_steps / U) workgroups
   const int n4 = (int)(input_padded >> 2);
-  float4 xs[2];  // this thread's share of the activations (input_padded <= 32 * 128 floats)
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int i = min(tid + k * kB1PairThreads, n4 - 1);
-    xs[k] = reinterpret_cast<const float4*>(prepared)[i];
-  }
-  __builtin_amdgcn_sched_barrier(0);
+  // this thread's share of the activations (input_padded <= 32 * 128 floats);
+  // two named registers, not an array the compiler could move to LDS
+  const float4 xs0 = reinterpret_cast<const float4*>(prepared)[min(tid, n4 - 1)];
+  const float4 xs1 = reinterpret_cast<const float4*>(prepared)[min(tid + kB1PairThreads, n4 - 1)];
+  // Every wavefront's activation requests go ahead of the workgroup's weight
+  // requests: the CU returns loads in order, and the set-up needs the
+  // activations first.
+  __syncthreads();
   load_step(s0);
   __builtin_amdgcn_sched_barrier(0);
   // Activations, staged with a stride of 36 floats per 32-float chunk (the 16
   // lanes of a read pass then cover all banks), then chunk q + LPR j of this
   // lane into registers.
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int i = tid + k * kB1PairThreads;
-    if (i < n4) *reinterpret_cast<float4*>(tab + 36 * (i >> 3) + 4 * (i & 7)) = xs[k];
+  if (tid < n4) *reinterpret_cast<float4*>(tab + 36 * (tid >> 3) + 4 * (tid & 7)) = xs0;
+  if (tid + kB1PairThreads < n4) {
+    const int i = tid + kB1PairThreads;
+    *reinterpret_cast<float4*>(tab + 36 * (i >> 3) + 4 * (i & 7)) = xs1;
   }
   __syncthreads();
   float act[NJ][32];
