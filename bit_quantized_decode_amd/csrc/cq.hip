@@ -371,7 +371,7 @@ void cq_matvec_b1(const uint8_t* __restrict__ packed, const uint16_t* __restrict
       for (int j = 0; j < NJ; ++j) {
         const int off = CONTIG ? BITS * j : BITS * LPR * j;
 #pragma unroll
-        for (int t = 0; t < BITS; ++t) d[u][j][t] = pc[off + t];
+        for (int t = 0; t < BITS; ++t) d[u][j][t] = stream_load(pc + off + t);
       }
       const uint16_t* nr = norm_base + (int64_t)i * n_groups;
       if (one_norm) {
@@ -453,7 +453,7 @@ void cq_matvec_b1_pairs(const uint8_t* __restrict__ packed, const uint16_t* __re
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) d[u][j][t] = pc[4 * LPR * j + t];
+        for (int t = 0; t < 4; ++t) d[u][j][t] = stream_load(pc + 4 * LPR * j + t);
       const uint16_t* nr = norms + (int64_t)i * n_groups;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) nb[u][j] = nr[gidx[j]];
@@ -602,7 +602,7 @@ __global__ __launch_bounds__(kThreads) void cq_matvec_nb(
       for (int j = 0; j < NJ; ++j) {
         const uint32_t* pc = prow + BITS * (q + LPR * j);
 #pragma unroll
-        for (int t = 0; t < BITS; ++t) d[u][j][t] = pc[t];
+        for (int t = 0; t < BITS; ++t) d[u][j][t] = stream_load(pc + t);
         nrm[u][j] = f16_to_f32(norms[r * n_groups + gidx[j]]);
       }
     }
@@ -758,12 +758,22 @@ void cq_matvec_mfma(const uint8_t* __restrict__ packed, const uint16_t* __restri
   const int n_spans = input_padded >> 8;
   const int span = wave % n_spans, rg = wave / n_spans;
   const int block_rows = 16 * T * rg_n;
-  const int n_blocks = (rows + block_rows - 1) / block_rows;
+  const int n_tiles = (rows + 15) >> 4;
   const int n_groups = input_padded >> log2_group;
   const int g = (256 * span) >> log2_group;
-  // the row block's norms, [row][group]: groups >= 256 give
+  // Round `it` gives local tile T r + i (row group r, tile i) of the
+  // workgroup global tile ((it T + i) rg_n + r) grid + blockIdx: in a round
+  // the whole grid reads one contiguous run of tiles, tile by tile, so the
+  // weight stream moves through memory as a front rather than as one
+  // scattered request per workgroup.
+  const int grid = (int)gridDim.x;
+  auto tile_of = [&](int it, int lt) {
+    return ((it * T + lt % T) * rg_n + lt / T) * grid + (int)blockIdx.x;
+  };
+  // the round's norms, [local row][group]: groups >= 256 give
   // block_rows * n_groups <= 64 T rg_n * n_spans <= blockDim entries
   const int block_norms = block_rows * n_groups;
+  const int tile_norms = 16 * n_groups;
   const uint8_t* lane_bytes = packed + 32 * BITS * span + kHalfBytes * q;
 
   // Loads, in the order they are consumed: codebook, the activations, the row
@@ -783,29 +793,30 @@ void cq_matvec_mfma(const uint8_t* __restrict__ packed, const uint16_t* __restri
     if (c < 8 * cpv && v < nb)
       xs[k] = reinterpret_cast<const float4*>(prepared)[(int64_t)v * cpv + (c - v * cpv)];
   }
-  int rb = blockIdx.x;  // < n_blocks: the grid has at most n_blocks workgroups
-  auto load_norm = [&](int rb) {  // entry tid of the row block's norms (tid < block_norms)
-    const int64_t e = min((int64_t)rb * block_norms + min(tid, block_norms - 1),
+  int it = 0;  // tile_of(0, 0) < n_tiles: the grid has at most n_tiles workgroups
+  auto load_norm = [&](int it) {  // entry tid of the round's norms (tid < block_norms)
+    const int t = min(tid, block_norms - 1);
+    const int64_t e = min((int64_t)tile_of(it, t / tile_norms) * tile_norms + t % tile_norms,
                           (int64_t)rows * n_groups - 1);
     return norms[e];
   };
-  uint16_t nv = load_norm(rb);
+  uint16_t nv = load_norm(it);
   __builtin_amdgcn_sched_barrier(0);
   uint32_t d[T][2 * BITS];
-  // Tile i of row block rb into d[i]: an unconditional load of a clamped row,
-  // whose result is dropped if clamped.
-  auto load_tile = [&](int rb, int i) {
-    const int r = min(rb * block_rows + 16 * T * rg + 16 * i + r16, rows - 1);
+  // Tile i of this wavefront's row group in round it into d[i]: an
+  // unconditional load of a clamped row, whose result is dropped if clamped.
+  auto load_tile = [&](int it, int i) {
+    const int r = min(16 * tile_of(it, T * rg + i) + r16, rows - 1);
     const uint8_t* p = lane_bytes + (int64_t)r * row_bytes;
     const uint32_t* p0 = reinterpret_cast<const uint32_t*>(p);
     const uint32_t* p1 = reinterpret_cast<const uint32_t*>(p + 16 * BITS);
 #pragma unroll
-    for (int w = 0; w < BITS; ++w) d[i][w] = p0[w];
+    for (int w = 0; w < BITS; ++w) d[i][w] = stream_load(p0 + w);
 #pragma unroll
-    for (int w = 0; w < BITS; ++w) d[i][BITS + w] = p1[w];
+    for (int w = 0; w < BITS; ++w) d[i][BITS + w] = stream_load(p1 + w);
   };
-  load_tile(rb, 0);
-  load_tile(rb, 1);
+  load_tile(it, 0);
+  load_tile(it, 1);
   __builtin_amdgcn_sched_barrier(0);
 
   // Stage the activations, then read this lane's 32 values: vector r16 % 8,
@@ -883,15 +894,15 @@ void cq_matvec_mfma(const uint8_t* __restrict__ packed, const uint16_t* __restri
   while (true) {
     if (tid < block_norms) nrm_lds[tid] = nv;
     __syncthreads();  // tables and norms written; the previous partials read
-    const int next = rb + (int)gridDim.x;
+    const bool more = tile_of(it + 1, 0) < n_tiles;
 #pragma unroll
     for (int i = 0; i < T; ++i) {
-      // two tiles ahead: this row block's, then the next one's first two
+      // two tiles ahead: this round's, then the next round's first two
       if (i + 2 < T) {
-        load_tile(rb, i + 2);
-      } else if (next < n_blocks) {
-        if (i + 2 == T) nv = load_norm(next);
-        load_tile(next, i + 2 - T);
+        load_tile(it, i + 2);
+      } else if (more) {
+        if (i + 2 == T) nv = load_norm(it + 1);
+        load_tile(it + 1, i + 2 - T);
       }
       __builtin_amdgcn_sched_barrier(0);
       f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -943,11 +954,11 @@ void cq_matvec_mfma(const uint8_t* __restrict__ packed, const uint16_t* __restri
       const int v = o / block_rows, row = o - v * block_rows;
       float sum = 0.0f;
       for (int s = 0; s < n_spans; ++s) sum += red[(s * block_rows + row) * kRedStride + v];
-      const int r = rb * block_rows + row;
+      const int r = 16 * tile_of(it, row >> 4) + (row & 15);
       if (r < rows) y[v * y_stride + r] = sum;
     }
-    rb = next;
-    if (rb >= n_blocks) break;
+    if (!more) break;
+    ++it;
   }
 }
 
@@ -1113,7 +1124,9 @@ int launch_mfma_b(const bqd_cq_matrix* m, const float* prepared, float* y, int64
   const int64_t rg_need = (tiles + cu_count() - 1) / cu_count();
   const int rg = (int)std::max<int64_t>(1, std::min<int64_t>(rg_need, kMfmaMaxSpans / n_spans));
   const int64_t block_rows = 16 * T * rg;
-  const int64_t grid = std::min<int64_t>((row_count + block_rows - 1) / block_rows, cu_count());
+  // every workgroup has a first tile: grid <= n_tiles
+  const int64_t grid = std::min<int64_t>(std::min<int64_t>((row_count + block_rows - 1) / block_rows,
+                                                           cu_count()), (row_count + 15) / 16);
   hipLaunchKernelGGL((cq_matvec_mfma<BITS, T>), dim3((unsigned)grid), dim3((unsigned)(64 * n_spans * rg)),
                      0, s, m->packed + row_begin * m->row_bytes,
                      m->norms + row_begin * (m->input_padded / m->group), m->codebook, prepared, y,

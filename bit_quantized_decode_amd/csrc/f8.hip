@@ -75,7 +75,8 @@ __global__ __launch_bounds__(kF8Threads) void f8_matvec_fast(
       const uint8_t* srow = scale + ((r * SR) / R) * SC;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        d[u][j] = wr[q + LPR * j];
+        const u32x4_nt t = stream_load(reinterpret_cast<const u32x4_nt*>(wr + q + LPR * j));
+        d[u][j] = make_uint4(t.x, t.y, t.z, t.w);
         sb[u][j] = srow[scol[j]];
       }
     }
