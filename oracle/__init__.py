@@ -80,6 +80,14 @@ def _load(path: str):
     L.oracle_e8m0.restype = ctypes.c_float
     L.oracle_e8m0.argtypes = [ctypes.c_uint8]
     L.oracle_f8_matvec.argtypes = [P, I64, I64, P, I64, I64, P, I64, I64, P, P]
+    L.oracle_xorshift32.restype = ctypes.c_uint32
+    L.oracle_xorshift32.argtypes = [ctypes.c_uint32]
+    L.oracle_topk.restype = ctypes.c_int
+    L.oracle_topk.argtypes = [P, I64, I64, P, P]
+    L.oracle_sample_u.restype = ctypes.c_int32
+    L.oracle_sample_u.argtypes = [P, P, I64, ctypes.c_double, ctypes.c_double]
+    L.oracle_sample.restype = ctypes.c_int32
+    L.oracle_sample.argtypes = [P, P, I64, ctypes.c_double, ctypes.POINTER(ctypes.c_uint32)]
     for name in ("oracle_cq_unpack_row", "oracle_cq_prepare", "oracle_cq_matvec",
                  "oracle_cq_dequantize_row", "oracle_cq_gather",
                  "oracle_cq_dense_matvec", "oracle_f8_matvec"):
@@ -239,3 +247,31 @@ def f8_matvec(w, R, C, s, SR, SC, x, row_begin: int = 0, row_count=None):
     if x.ndim == 1:
         return y[0], mag[0]
     return y, mag
+
+
+def xorshift32(s: int) -> int:
+    return lib().oracle_xorshift32(s)
+
+
+def topk(logits: np.ndarray, k: int):
+    """(ids int32 [k], vals float32 [k]) of the k best logits (O12)."""
+    x = np.ascontiguousarray(logits, dtype=np.float32)
+    ids = np.zeros(k, np.int32)
+    vals = np.zeros(k, np.float32)
+    _check(lib().oracle_topk(_ptr(x), x.size, k, _ptr(ids), _ptr(vals)), "topk")
+    return ids, vals
+
+
+def sample_u(vals: np.ndarray, ids: np.ndarray, temperature: float, u: float) -> int:
+    v = np.ascontiguousarray(vals, dtype=np.float32)
+    i = np.ascontiguousarray(ids, dtype=np.int32)
+    return lib().oracle_sample_u(_ptr(v), _ptr(i), v.size, temperature, u)
+
+
+def sample(vals: np.ndarray, ids: np.ndarray, temperature: float, state: int):
+    """(token, next state) (O13 with O11)."""
+    v = np.ascontiguousarray(vals, dtype=np.float32)
+    i = np.ascontiguousarray(ids, dtype=np.int32)
+    s = ctypes.c_uint32(state)
+    tok = lib().oracle_sample(_ptr(v), _ptr(i), v.size, temperature, ctypes.byref(s))
+    return tok, s.value

@@ -268,3 +268,68 @@ int oracle_f8_matvec(const uint8_t *w, int64_t R, int64_t C, const uint8_t *s,
     }
     return 0;
 }
+
+/* --------------------------------------------------------------- O11 -- */
+uint32_t oracle_xorshift32(uint32_t s)
+{
+    s ^= s << 13;
+    s ^= s >> 17;
+    s ^= s << 5;
+    return s;
+}
+
+/* --------------------------------------------------------------- O12 -- */
+/* [P4] work item 3: the k best candidates for sampling.  A plain sort of
+ * all indices by (value descending, index ascending), NaNs last. */
+static const float *topk_logits;
+
+static int topk_cmp(const void *pa, const void *pb)
+{
+    int64_t a = *(const int64_t *)pa, b = *(const int64_t *)pb;
+    float va = topk_logits[a], vb = topk_logits[b];
+    int na = isnan(va), nb = isnan(vb);
+    if (na != nb) return na ? 1 : -1;          /* NaN after every number */
+    if (!na && va != vb) return va > vb ? -1 : 1;
+    return a < b ? -1 : (a > b ? 1 : 0);       /* equal values: lower index */
+}
+
+int oracle_topk(const float *logits, int64_t n, int64_t k, int32_t *ids, float *vals)
+{
+    if (!logits || n < 1 || k < 1 || k > n) return -1;
+    int64_t *order = (int64_t *)malloc(sizeof(int64_t) * (size_t)n);
+    if (!order) return -1;
+    for (int64_t i = 0; i < n; i++) order[i] = i;
+    topk_logits = logits;
+    qsort(order, (size_t)n, sizeof(int64_t), topk_cmp);
+    for (int64_t i = 0; i < k; i++) {
+        ids[i] = (int32_t)order[i];
+        vals[i] = logits[order[i]];
+    }
+    free(order);
+    return 0;
+}
+
+/* --------------------------------------------------------------- O13 -- */
+/* [P4] "Step 3 done": a softmax over the candidates at the temperature,
+ * then the inverse of its cumulative sum at the uniform draw. */
+int32_t oracle_sample_u(const float *vals, const int32_t *ids, int64_t k,
+                        double temperature, double u)
+{
+    if (temperature <= 0.0 || k == 1 || !isfinite(vals[0])) return ids[0];
+    double S = 0.0;
+    for (int64_t i = 0; i < k; i++)
+        S += isnan(vals[i]) ? 0.0 : exp(((double)vals[i] - (double)vals[0]) / temperature);
+    double target = u * S, run = 0.0;
+    for (int64_t i = 0; i < k; i++) {
+        run += isnan(vals[i]) ? 0.0 : exp(((double)vals[i] - (double)vals[0]) / temperature);
+        if (target < run) return ids[i];
+    }
+    return ids[k - 1];
+}
+
+int32_t oracle_sample(const float *vals, const int32_t *ids, int64_t k,
+                      double temperature, uint32_t *state)
+{
+    *state = oracle_xorshift32(*state);
+    return oracle_sample_u(vals, ids, k, temperature, (double)*state / 4294967296.0);
+}

@@ -14,7 +14,9 @@
  *        control tensors, §4 Retain packed matrices.
  *   [P4] "attention + tokenizer + sampling: the path to real text
  *        (milestone 6)" — "Step 1 done: F8 kernel", "Step 4 done: I8 +
- *        F8_E4M3 SIMD matvecs".
+ *        F8_E4M3 SIMD matvecs", and the sampling of work item 3 and "Step 3
+ *        done" (head logits, top-k / temperature sampling, a deterministic
+ *        softmax + xorshift sampler).
  *
  * Precision: the pages' arrays are Float32Array (each store rounds to fp32)
  * and their scalars are JavaScript numbers (fp64).  The oracle keeps exactly
@@ -99,6 +101,30 @@ float oracle_e8m0(uint8_t e);
 int oracle_f8_matvec(const uint8_t *w, int64_t R, int64_t C, const uint8_t *s,
                      int64_t SR, int64_t SC, const float *x, int64_t row_begin,
                      int64_t row_count, double *y, double *mag);
+
+/* O11: one step of the 32-bit xorshift generator (Marsaglia's (13, 17, 5)
+ * triple; [P4] names only "xorshift"): s ^= s << 13; s ^= s >> 17;
+ * s ^= s << 5.  Maps nonzero states to nonzero states. */
+uint32_t oracle_xorshift32(uint32_t s);
+
+/* O12: the k largest logits ([P4] work item 3, top-k): ids[0..k) and
+ * vals[0..k) in order: larger value first; equal values (+0 = -0) by lower
+ * index first; NaNs after every number.  1 <= k <= n. */
+int oracle_topk(const float *logits, int64_t n, int64_t k, int32_t *ids, float *vals);
+
+/* O13: temperature sampling over a top-k list given the uniform draw u in
+ * [0, 1) ([P4] "Step 3 done": softmax + xorshift).  temperature <= 0, k = 1,
+ * or a top value that is not finite: ids[0].  Otherwise, in fp64,
+ * p_i = exp((vals[i] - vals[0]) / temperature) (NaN values weigh 0),
+ * S = sum of p_i in list order, and the token is the first ids[i] whose
+ * running sum exceeds u * S (ids[k-1] if rounding leaves none). */
+int32_t oracle_sample_u(const float *vals, const int32_t *ids, int64_t k,
+                        double temperature, double u);
+
+/* O13 with the generator: *state advances once (O11), u = state * 2^-32,
+ * then O13.  *state must be nonzero. */
+int32_t oracle_sample(const float *vals, const int32_t *ids, int64_t k,
+                      double temperature, uint32_t *state);
 
 #ifdef __cplusplus
 }

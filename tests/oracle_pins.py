@@ -369,4 +369,106 @@ def pin_f8_matvec_one_hot():
         assert Fraction(y[r]) == v, r
 
 
+
+# ----------------------------------------------------------------- sampling
+def _gf2_matrix_of(f):
+    """The 32x32 matrix over GF(2) of a linear map on uint32 (column j = f(e_j))."""
+    M = np.zeros((32, 32), np.uint8)
+    for j in range(32):
+        v = f(1 << j)
+        for i in range(32):
+            M[i, j] = (v >> i) & 1
+    return M
+
+
+def _gf2_pow(M, e):
+    R = np.eye(32, dtype=np.int64)
+    B = M.astype(np.int64)
+    while e:
+        if e & 1:
+            R = (R @ B) % 2
+        B = (B @ B) % 2
+        e >>= 1
+    return R
+
+
+def pin_xorshift_full_period():
+    """O11 is linear over GF(2) and has the maximal period 2^32 - 1 (the
+    property that defines a usable xorshift generator): with T its matrix,
+    T^(2^32-1) = I and T^((2^32-1)/p) != I for every prime p dividing
+    2^32 - 1 = 3 * 5 * 17 * 257 * 65537."""
+    rng = np.random.default_rng(11)
+    for _ in range(20):  # linearity: f(a ^ b) = f(a) ^ f(b)
+        a, b = (int(v) for v in rng.integers(1, 2**32, 2, dtype=np.uint64))
+        assert oracle.xorshift32(a ^ b) == oracle.xorshift32(a) ^ oracle.xorshift32(b)
+    T = _gf2_matrix_of(oracle.xorshift32)
+    order = 2**32 - 1
+    assert np.array_equal(_gf2_pow(T, order), np.eye(32, dtype=np.int64))
+    for prime in (3, 5, 17, 257, 65537):
+        assert not np.array_equal(_gf2_pow(T, order // prime), np.eye(32, dtype=np.int64)), prime
+    # a full-period state sequence never reaches 0 from a nonzero state
+    s = 1
+    for _ in range(1000):
+        s = oracle.xorshift32(s)
+        assert s != 0
+
+
+def _topk_numpy(x, k):
+    """Sort key (NaN flag, -value, index); +0 and -0 compare equal."""
+    idx = np.arange(x.size)
+    nan = np.isnan(x)
+    neg = np.where(nan, 0.0, -x.astype(np.float64)) + 0.0  # -0.0 -> +0.0
+    order = np.lexsort((idx, neg, nan))
+    return order[:k].astype(np.int32)
+
+
+def pin_topk_vs_numpy_lexsort():
+    """O12 against numpy's lexsort on random, tie-heavy and special values."""
+    rng = np.random.default_rng(12)
+    cases = [rng.standard_normal(5000).astype(np.float32),
+             rng.integers(-3, 4, 3000).astype(np.float32),  # many ties
+             np.array([1, 3, 3, 2, np.nan, -0.0, 0.0, np.inf, -np.inf, np.inf], np.float32)]
+    x = rng.standard_normal(700).astype(np.float32)
+    x[rng.integers(0, 700, 60)] = np.nan
+    cases.append(x)
+    for x in cases:
+        for k in (1, 2, 7, 64, min(x.size, 100)):
+            k = min(k, x.size)
+            ids, vals = oracle.topk(x, k)
+            ref = _topk_numpy(x, k)
+            assert np.array_equal(ids, ref), (k, ids[:8], ref[:8])
+            assert np.array_equal(vals.view(np.uint32), x[ref].view(np.uint32))
+
+
+def pin_sample_inverse_cdf_grid():
+    """O13 inverts the softmax CDF: over the grid u_j = (j + 1/2)/M the
+    number of draws that land on candidate i is M * p_i within 1, with p
+    from scipy's softmax of vals / temperature."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(13)
+    for k, T in ((5, 1.0), (16, 0.7), (64, 2.5), (3, 0.05)):
+        vals = np.sort(rng.standard_normal(k).astype(np.float32))[::-1].copy()
+        ids = rng.permutation(10 * k)[:k].astype(np.int32)
+        p = softmax(vals.astype(np.float64) / T)
+        M = 20000
+        counts = {int(i): 0 for i in ids}
+        for j in range(M):
+            counts[oracle.sample_u(vals, ids, T, (j + 0.5) / M)] += 1
+        for i, pi in zip(ids, p):
+            assert abs(counts[int(i)] - M * pi) <= 1.0 + 1e-9, (k, T, i, counts[int(i)], M * pi)
+
+
+def pin_sample_degenerate_cases():
+    """Temperature 0 and k = 1 give the top candidate; the generator form
+    advances the state exactly once and draws u = state / 2^32."""
+    vals = np.array([2.0, 1.0, 0.5], np.float32)
+    ids = np.array([40, 10, 30], np.int32)
+    for u in (0.0, 0.5, 0.999999):
+        assert oracle.sample_u(vals, ids, 0.0, u) == 40
+        assert oracle.sample_u(vals[:1], ids[:1], 1.0, u) == 40
+    for s in (1, 12345, 0xdeadbeef):
+        tok, s2 = oracle.sample(vals, ids, 1.0, s)
+        assert s2 == oracle.xorshift32(s)
+        assert tok == oracle.sample_u(vals, ids, 1.0, s2 / 2**32)
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

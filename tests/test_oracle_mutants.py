@@ -36,6 +36,12 @@ MUTANTS = {
     "e8m0_bias": ("ldexp(1.0, (int)e - 127)", "ldexp(1.0, (int)e - 128)"),
     "f8_scale_col_uses_R": ("int64_t sc = (c * SC) / C;", "int64_t sc = (c * SC) / R;"),
     "f8_scale_row_transposed": ("int64_t sr = (r * SR) / R;", "int64_t sr = (r * SC) / R;"),
+    "xorshift_wrong_shift": ("s ^= s >> 17;", "s ^= s >> 15;"),
+    "topk_ties_by_higher_index": ("return a < b ? -1 : (a > b ? 1 : 0);", "return a < b ? 1 : (a > b ? -1 : 0);"),
+    "topk_nan_first": ("if (na != nb) return na ? 1 : -1;", "if (na != nb) return na ? -1 : 1;"),
+    "sample_no_temperature": ("exp(((double)vals[i] - (double)vals[0]) / temperature);\n        if",
+                              "exp(((double)vals[i] - (double)vals[0]));\n        if"),
+    "sample_cdf_off_by_one": ("if (target < run) return ids[i];", "if (target <= run) return ids[i > 0 ? i - 1 : 0];"),
 }
 
 
