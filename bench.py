@@ -139,7 +139,7 @@ def build_cases(torch, bqd, synth, hot):
     cases.append(Case("f8_head_246272x4096_matvec",
                       [lambda w=w: bqd.f8_matvec(w, sh, xh, out=yh) for w in whs],
                       head_bytes, hd.R))
-    data = dict(c4=c4, c3=c3, head=hd)
+    data = dict(c4=c4, c3=c3, head=hd, head_logits=yh)
     return cases, data
 
 
@@ -338,6 +338,26 @@ def main():
             us_p90=round(float(np.percentile(ms, 90) * 1e3), 3), bytes=c.nbytes,
             gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4),
             rows_per_s=round(c.rows / (ms.mean() * 1e-3), 1) if c.rows else None)
+    # Beyond the step: top-k (k = 64) and a temperature draw over the head's
+    # logits, timed the same way (the sampler's state advances on the GPU).
+    logits = data["head_logits"].reshape(-1)
+    state = torch.tensor([12345], dtype=torch.int32, device="cuda")
+    ws = torch.empty(bqd.logits_sample_workspace_bytes(logits.numel(), 64), dtype=torch.uint8,
+                     device="cuda")
+    g = capture(torch, lambda: [bqd.logits_sample(logits, 64, 0.8, state, ws)
+                                for _ in range(period)])
+    g.replay()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) / period
+    extras = {"head_logits_sample_k64": dict(
+        us_mean=round(float(ms.mean() * 1e3), 3), logits=logits.numel(), k=64, temperature=0.8,
+        note="not part of the step: the sampler over the head's logits")}
     total_bytes = sum(c.nbytes for c in cases)
     total_rows = sum(c.rows for c in cases)
     value = total_bytes / (step_ms * 1e-3) / 1e9
@@ -377,7 +397,7 @@ def main():
         "rows_per_s": round(total_rows / (step_ms * 1e-3), 1),
         "frac_hbm_step": round(value / HBM_PEAK_GBS, 4),
         "read_reference_gbs": {"kernel": "torch float32 sum over 1 GiB", "gbs": round(read_ref, 1)},
-        "cases": per_case, "roofline": roofline, "cpu_baseline": cpu,
+        "cases": per_case, "extras": extras, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 

@@ -24,6 +24,7 @@ import os
 import torch
 
 __all__ = ["BqdError", "CqMatrix", "cq_prepare", "cq_matvec", "cq_gather_rows", "f8_matvec",
+           "logits_sample", "logits_sample_workspace_bytes",
            "dbg_cq_unpack", "dbg_f16_decode", "dbg_f8_decode", "dbg_e8m0_decode", "lib",
            "LIB_PATH", "EXPORTS"]
 
@@ -31,9 +32,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbqd.so")
 
 # Every symbol include/bqd.h declares.
-EXPORTS = ("cq_prepare", "cq_matvec", "cq_gather_rows", "f8_matvec", "bqd_dbg_cq_unpack",
-           "bqd_dbg_f16_decode", "bqd_dbg_f8_decode", "bqd_dbg_e8m0_decode",
-           "bqd_status_string")
+EXPORTS = ("cq_prepare", "cq_matvec", "cq_gather_rows", "f8_matvec", "logits_sample",
+           "logits_sample_workspace_bytes", "bqd_dbg_cq_unpack", "bqd_dbg_f16_decode",
+           "bqd_dbg_f8_decode", "bqd_dbg_e8m0_decode", "bqd_status_string")
 
 _lib = None
 
@@ -70,10 +71,13 @@ def lib():
                 ("bqd_dbg_cq_unpack", [S, I64, P, P]),
                 ("bqd_dbg_f16_decode", [P, I64, P, P]),
                 ("bqd_dbg_f8_decode", [P, I64, P, P]),
-                ("bqd_dbg_e8m0_decode", [P, I64, P, P])):
+                ("bqd_dbg_e8m0_decode", [P, I64, P, P]),
+                ("logits_sample", [P, I64, I64, ctypes.c_float, P, P, I64, P, P, P, P])):
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = I
+        L.logits_sample_workspace_bytes.argtypes = [I64, I64]
+        L.logits_sample_workspace_bytes.restype = I64
         L.bqd_status_string.argtypes = [I]
         L.bqd_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -203,6 +207,34 @@ def f8_matvec(w: torch.Tensor, scale: torch.Tensor, x: torch.Tensor, out: torch.
     _call("f8_matvec", _ptr(w), R, C, _ptr(scale), SR, SC, _ptr(x), _ptr(out), batch,
           _stream(x, stream))
     return out
+
+
+def logits_sample_workspace_bytes(n: int, k: int) -> int:
+    need = lib().logits_sample_workspace_bytes(int(n), int(k))
+    if need < 0:
+        raise BqdError("logits_sample_workspace_bytes", int(need))
+    return int(need)
+
+
+def logits_sample(logits: torch.Tensor, k: int, temperature: float, state: torch.Tensor,
+                  workspace: torch.Tensor = None, stream=None):
+    """Top-k of float32 logits [n] and one sampled token; `state` (int32 or
+    uint32 [1] on the GPU, the xorshift32 state) advances in place.
+    Returns (token int32 [1], topk_ids int32 [k], topk_logits float32 [k])."""
+    logits = _dev(logits, torch.float32, "logits")
+    state = _dev(state, (torch.int32, torch.uint32), "state")
+    n = logits.numel()
+    need = logits_sample_workspace_bytes(n, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=logits.device)
+    workspace = _dev(workspace, torch.uint8, "workspace")
+    token = torch.empty(1, dtype=torch.int32, device=logits.device)
+    ids = torch.empty(k, dtype=torch.int32, device=logits.device)
+    vals = torch.empty(k, dtype=torch.float32, device=logits.device)
+    _call("logits_sample", _ptr(logits), n, int(k), float(temperature), _ptr(state),
+          _ptr(workspace), workspace.numel(), _ptr(token), _ptr(ids), _ptr(vals),
+          _stream(logits, stream))
+    return token, ids, vals
 
 
 def dbg_cq_unpack(m: CqMatrix, row: int, stream=None):

@@ -63,6 +63,20 @@ int bqd_dbg_e8m0_decode(const uint8_t* codes, int64_t n, float* out, void* strea
   return launch_e8m0_decode(codes, n, out, as_stream(stream));
 }
 
+int64_t logits_sample_workspace_bytes(int64_t n, int64_t k) {
+  return sample_workspace_need(n, k);
+}
+
+int logits_sample(const float* logits, int64_t n, int64_t k, float temperature, uint32_t* state,
+                  void* workspace, int64_t workspace_bytes, int32_t* token, int32_t* topk_ids,
+                  float* topk_logits, void* stream) {
+  int rc = check_sample(logits, n, k, temperature, state, workspace, workspace_bytes, token,
+                        topk_ids, topk_logits);
+  if (rc) return rc;
+  return launch_logits_sample(logits, n, k, temperature, state, workspace, token, topk_ids,
+                              topk_logits, as_stream(stream));
+}
+
 const char* bqd_status_string(int status) {
   switch (status) {
     case BQD_OK: return "ok";

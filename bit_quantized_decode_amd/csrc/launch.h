@@ -20,6 +20,9 @@ int launch_f8_matvec(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scal
 int launch_f16_decode(const uint16_t* codes, int64_t n, float* out, hipStream_t s);
 int launch_f8_decode(const uint8_t* codes, int64_t n, float* out, hipStream_t s);
 int launch_e8m0_decode(const uint8_t* codes, int64_t n, float* out, hipStream_t s);
+int launch_logits_sample(const float* logits, int64_t n, int64_t k, float temperature,
+                         uint32_t* state, void* workspace, int32_t* token, int32_t* topk_ids,
+                         float* topk_logits, hipStream_t s);
 
 inline int launch_status() {
   return hipGetLastError() == hipSuccess ? BQD_OK : BQD_EHIP;

@@ -1,0 +1,220 @@
+// Top-k and temperature sampling over a logits vector for gfx950.
+//
+// Method: "attention + tokenizer + sampling: the path to real text (milestone
+// 6)" — work item 3 (logits = head x state; top-k / temperature sampling) and
+// "Step 3 done" (a deterministic sampler: softmax + xorshift, same seed, same
+// token).
+//
+// Order of candidates: a larger value first; equal values (+0 = -0) by the
+// lower index; NaNs after every number.  Every logit becomes one 64-bit key
+// whose unsigned order is exactly that order, with no two keys equal:
+//   high 32 bits: the float's bits mapped to an unsigned order (NaN lowest),
+//   low 32 bits:  0xffffffff - index.
+// Sorting keys then orders candidates with no tie handling.  Padding slots
+// get small distinct keys (below every real key, whose low half is at least
+// 2^32 - 2^20); they are never selected, since k <= n real logits compete.
+//
+// Two launches.  Blocks of 4096 logits: each wavefront sorts four runs of 64
+// keys across its lanes (a bitonic network on lane exchanges, no barriers),
+// merges them into its top 64, and the wavefronts' lists merge in LDS down to
+// the block's top 64, of which the first k go to the caller's workspace.  One
+// block then merges the blocks' lists the same way, takes the first k, and
+// draws the token in fp64.  Keys carry the index, so the logits are re-read
+// for the k values (copied bit for bit).
+#include <math.h>
+
+#include "cq_device.h"
+#include "launch.h"
+
+namespace bqd {
+
+constexpr int kSampleThreads = 1024;
+constexpr int kChunk = 4096;          // logits per first-stage block (4 per thread)
+constexpr int kMaxCandidates = 16384; // second-stage capacity (16 per thread)
+constexpr int kMaxK = 64;
+
+// Unsigned key of a logit: the order of values, NaN below everything, -0 = +0.
+__device__ __forceinline__ uint32_t value_key(float v) {
+  if (v != v) return 0u;
+  uint32_t b = __float_as_uint(v);
+  if ((b << 1) == 0u) b = 0u;  // -0 -> +0
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t cand_key(float v, uint32_t index) {
+  return ((uint64_t)value_key(v) << 32) | (uint64_t)(0xffffffffu - index);
+}
+
+// A 64-bit key of lane (lane ^ D): both halves through the transform's lane
+// exchange (DPP within 16-lane rows, ds_bpermute beyond), which moves bits
+// unchanged.
+template <int D>
+__device__ __forceinline__ uint64_t key_xor(uint64_t v) {
+  const uint32_t lo = __float_as_uint(lane_xor<D>(__uint_as_float((uint32_t)v)));
+  const uint32_t hi = __float_as_uint(lane_xor<D>(__uint_as_float((uint32_t)(v >> 32))));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t key_from_lane(uint64_t v, int src) {
+  const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, src, 64);
+  const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// One compare-exchange stage across lanes l and l ^ D: the lane keeps the
+// larger key if (lower lane) == descending, else the smaller.
+template <int D>
+__device__ __forceinline__ uint64_t cx(uint64_t v, bool desc) {
+  const uint64_t o = key_xor<D>(v);
+  const bool lower = (threadIdx.x & D) == 0;
+  return (lower == desc) ? (v > o ? v : o) : (v < o ? v : o);
+}
+
+// Sort the 64 keys of the wavefront (one per lane) descending: lane l ends
+// with the l-th largest.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
+  const int l = threadIdx.x & 63;
+#define BQD_SORT_STAGE(SIZE, D) v = cx<D>(v, (SIZE) == 64 || (l & (SIZE)) == 0)
+  BQD_SORT_STAGE(2, 1);
+  BQD_SORT_STAGE(4, 2); BQD_SORT_STAGE(4, 1);
+  BQD_SORT_STAGE(8, 4); BQD_SORT_STAGE(8, 2); BQD_SORT_STAGE(8, 1);
+  BQD_SORT_STAGE(16, 8); BQD_SORT_STAGE(16, 4); BQD_SORT_STAGE(16, 2); BQD_SORT_STAGE(16, 1);
+  BQD_SORT_STAGE(32, 16); BQD_SORT_STAGE(32, 8); BQD_SORT_STAGE(32, 4); BQD_SORT_STAGE(32, 2);
+  BQD_SORT_STAGE(32, 1);
+  BQD_SORT_STAGE(64, 32); BQD_SORT_STAGE(64, 16); BQD_SORT_STAGE(64, 8); BQD_SORT_STAGE(64, 4);
+  BQD_SORT_STAGE(64, 2); BQD_SORT_STAGE(64, 1);
+#undef BQD_SORT_STAGE
+  return v;
+}
+
+// The 64 largest of two descending lists, descending: a holds A[l], b_rev
+// holds B[63 - l].  max(A[l], B[63 - l]) is a bitonic sequence holding the 64
+// largest; a bitonic merge sorts it.
+__device__ __forceinline__ uint64_t wave_merge_desc(uint64_t a, uint64_t b_rev) {
+  uint64_t v = a > b_rev ? a : b_rev;
+  v = cx<32>(v, true);
+  v = cx<16>(v, true);
+  v = cx<8>(v, true);
+  v = cx<4>(v, true);
+  v = cx<2>(v, true);
+  v = cx<1>(v, true);
+  return v;
+}
+
+// In-place tree merge of `n_lists` descending lists of 64 keys in LDS (list i
+// at lists[64 i ..]) down to list 0.  Every thread of the workgroup calls it.
+__device__ void block_merge_lists(uint64_t* lists, int n_lists) {
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  constexpr int kWaves = kSampleThreads / 64;
+  while (n_lists > 1) {
+    const int pairs = n_lists >> 1;
+    uint64_t merged[(kMaxCandidates / 64 / 2 + kWaves - 1) / kWaves];
+    int m = 0;
+    __syncthreads();
+    for (int pi = wave; pi < pairs; pi += kWaves, ++m)
+      merged[m] = wave_merge_desc(lists[64 * (2 * pi) + l], lists[64 * (2 * pi + 1) + 63 - l]);
+    __syncthreads();
+    m = 0;
+    for (int pi = wave; pi < pairs; pi += kWaves, ++m) lists[64 * pi + l] = merged[m];
+    if ((n_lists & 1) && wave == 0) lists[64 * pairs + l] = lists[64 * (n_lists - 1) + l];
+    n_lists = pairs + (n_lists & 1);
+  }
+  __syncthreads();
+}
+
+// Stage 1: block b keeps the first k keys of logits [4096 b, 4096 b + 4096)
+// in workspace slots [k b, k b + k).
+__global__ __launch_bounds__(kSampleThreads) void topk_chunk_kernel(
+    const float* __restrict__ logits, int64_t n, int k, uint64_t* __restrict__ ws) {
+  __shared__ uint64_t lists[kChunk / 4];  // one list of 64 per wavefront
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  uint64_t run[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {  // run r: chunk elements 256 wave + 64 r + lane
+    const int t = 256 * wave + 64 * r + l;
+    const int64_t i = (int64_t)blockIdx.x * kChunk + t;
+    run[r] = i < n ? cand_key(logits[i], (uint32_t)i) : (uint64_t)(i - n);  // padding < kChunk
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) run[r] = wave_sort_desc(run[r]);
+  const uint64_t m01 = wave_merge_desc(run[0], key_from_lane(run[1], 63 - l));
+  const uint64_t m23 = wave_merge_desc(run[2], key_from_lane(run[3], 63 - l));
+  lists[64 * wave + l] = wave_merge_desc(m01, key_from_lane(m23, 63 - l));
+  block_merge_lists(lists, kSampleThreads / 64);
+  if ((int)threadIdx.x < k) ws[(int64_t)blockIdx.x * k + threadIdx.x] = lists[threadIdx.x];
+}
+
+// Stage 2: the blocks' lists (k keys each, padded to 64) merged, the first k
+// kept, then the draw.
+__global__ __launch_bounds__(kSampleThreads) void topk_final_kernel(
+    const float* __restrict__ logits, const uint64_t* __restrict__ ws, int n_lists, int k,
+    float temperature, uint32_t* __restrict__ state, int32_t* __restrict__ token,
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_vals) {
+  __shared__ uint64_t lists[kMaxCandidates];
+  __shared__ float sel_v[kMaxK];
+  __shared__ int32_t sel_i[kMaxK];
+  for (int c = threadIdx.x; c < 64 * n_lists; c += kSampleThreads) {
+    const int b = c >> 6, j = c & 63;
+    const uint64_t v = j < k ? ws[(int64_t)b * k + j] : 0;
+    // padding (a short chunk's, or past k): distinct keys below every real
+    // key, decreasing along the list so that each list stays sorted
+    lists[c] = v < (uint64_t)kMaxCandidates ? (uint64_t)(kMaxCandidates - 1 - c) : v;
+  }
+  block_merge_lists(lists, n_lists);
+  const int t = threadIdx.x;
+  if (t < k) {
+    const int32_t i = (int32_t)(0xffffffffu - (uint32_t)lists[t]);
+    sel_i[t] = i;
+    sel_v[t] = logits[i];
+    topk_ids[t] = i;
+    topk_vals[t] = sel_v[t];
+  }
+  __syncthreads();
+  if (t == 0) {
+    // one xorshift step (13, 17, 5), u = state / 2^32, then the inverse of the
+    // cumulative softmax, all in fp64 and in list order
+    uint32_t s = *state;
+    s ^= s << 13;
+    s ^= s >> 17;
+    s ^= s << 5;
+    *state = s;
+    int32_t tok = sel_i[0];
+    const float top = sel_v[0];
+    if (temperature > 0.0f && k > 1 && isfinite(top)) {
+      const double inv_t = 1.0 / (double)temperature;
+      double S = 0.0;
+      for (int j = 0; j < k; ++j) {
+        const float v = sel_v[j];
+        S += (v != v) ? 0.0 : exp(((double)v - (double)top) * inv_t);
+      }
+      const double target = ((double)s / 4294967296.0) * S;
+      double run = 0.0;
+      tok = sel_i[k - 1];
+      for (int j = 0; j < k; ++j) {
+        const float v = sel_v[j];
+        run += (v != v) ? 0.0 : exp(((double)v - (double)top) * inv_t);
+        if (target < run) {
+          tok = sel_i[j];
+          break;
+        }
+      }
+    }
+    *token = tok;
+  }
+}
+
+int launch_logits_sample(const float* logits, int64_t n, int64_t k, float temperature,
+                         uint32_t* state, void* workspace, int32_t* token, int32_t* topk_ids,
+                         float* topk_logits, hipStream_t s) {
+  const int64_t chunks = (n + kChunk - 1) / kChunk;
+  uint64_t* ws = reinterpret_cast<uint64_t*>(workspace);
+  hipLaunchKernelGGL(topk_chunk_kernel, dim3((unsigned)chunks), dim3(kSampleThreads), 0, s,
+                     logits, n, (int)k, ws);
+  int rc = launch_status();
+  if (rc) return rc;
+  hipLaunchKernelGGL(topk_final_kernel, dim3(1), dim3(kSampleThreads), 0, s, logits, ws,
+                     (int)chunks, (int)k, temperature, state, token, topk_ids, topk_logits);
+  return launch_status();
+}
+
+}  // namespace bqd

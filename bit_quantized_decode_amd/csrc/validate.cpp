@@ -117,4 +117,23 @@ int check_decode(const void* codes, int64_t n, const float* out, int code_size) 
   return BQD_OK;
 }
 
+int64_t sample_workspace_need(int64_t n, int64_t k) {
+  if (n < 1 || n > kMaxSampleLogits || k < 1 || k > kMaxSampleK || k > n) return BQD_EINVAL;
+  return (n + 4095) / 4096 * k * 8;
+}
+
+int check_sample(const float* logits, int64_t n, int64_t k, float temperature,
+                 const uint32_t* state, const void* workspace, int64_t workspace_bytes,
+                 const int32_t* token, const int32_t* topk_ids, const float* topk_logits) {
+  const int64_t need = sample_workspace_need(n, k);
+  if (need < 0) return BQD_EINVAL;
+  if (!(temperature >= 0.0f) || temperature > 3.4e38f) return BQD_EINVAL;  // NaN, < 0, inf
+  if (!logits || !state || !workspace || !token || !topk_ids || !topk_logits) return BQD_ENULL;
+  if (workspace_bytes < need) return BQD_EINVAL;
+  if (!aligned(logits, 4) || !aligned(state, 4) || !aligned(workspace, 4) || !aligned(token, 4) ||
+      !aligned(topk_ids, 4) || !aligned(topk_logits, 4))
+    return BQD_EALIGN;
+  return BQD_OK;
+}
+
 }  // namespace bqd

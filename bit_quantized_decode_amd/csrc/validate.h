@@ -20,10 +20,16 @@ int check_f8(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64
              int64_t SC, const float* x, const float* y, int64_t batch);
 int check_unpack(const bqd_cq_matrix* m, int64_t row, const uint8_t* idx);
 int check_decode(const void* codes, int64_t n, const float* out, int code_size);
+int64_t sample_workspace_need(int64_t n, int64_t k);  // or BQD_EINVAL
+int check_sample(const float* logits, int64_t n, int64_t k, float temperature,
+                 const uint32_t* state, const void* workspace, int64_t workspace_bytes,
+                 const int32_t* token, const int32_t* topk_ids, const float* topk_logits);
 
 // Largest sizes the kernels index with their 32-bit row / column counters.
 constexpr int64_t kMaxRows = (int64_t)1 << 30;      // exclusive
 constexpr int64_t kMaxColumns = (int64_t)1 << 28;   // exclusive
 constexpr int64_t kMaxGroup = 1024;
+constexpr int64_t kMaxSampleLogits = (int64_t)1 << 20;  // inclusive
+constexpr int64_t kMaxSampleK = 64;
 
 }  // namespace bqd

@@ -11,8 +11,10 @@
  *        checks boring", §3 "Decode FP16 control tensors", §4 "Retain packed
  *        matrices" (the CQ record);
  *   [P4] "attention + tokenizer + sampling: the path to real text (milestone
- *        6)": "Step 1 done: F8 kernel" (E4M3 decode, E8M0 block scales) and
- *        "Step 4 done" (the vector decode).
+ *        6)": "Step 1 done: F8 kernel" (E4M3 decode, E8M0 block scales),
+ *        "Step 4 done" (the vector decode), work item 3 and "Step 3 done"
+ *        (head logits, top-k / temperature sampling, a deterministic
+ *        softmax + xorshift sampler).
  *
  * Conventions shared by every entry point:
  *  - All data pointers are DEVICE pointers owned by the caller; the library
@@ -120,6 +122,34 @@ int cq_gather_rows(const bqd_cq_matrix *m, const int32_t *rows, int64_t n,
 int f8_matvec(const uint8_t *w, int64_t R, int64_t C, const uint8_t *scale,
               int64_t SR, int64_t SC, const float *x, float *y, int64_t batch,
               void *stream);
+
+/* Bytes of device workspace logits_sample needs: ceil(n / 4096) * k * 8.
+ * Returns BQD_EINVAL (negative) for n or k outside logits_sample's range. */
+int64_t logits_sample_workspace_bytes(int64_t n, int64_t k);
+
+/* [P4] work item 3 and "Step 3 done": the k best logits and one token drawn
+ * from them at a temperature with a seeded xorshift generator.
+ *   Order: a larger value first; equal values (+0 = -0) by the lower index;
+ *   NaNs after every number.  topk_ids[0..k) / topk_logits[0..k) receive the
+ *   k best in that order (logits copied bit for bit).
+ *   Draw: *state advances one xorshift32 step (s ^= s << 13; s ^= s >> 17;
+ *   s ^= s << 5) and u = state * 2^-32.  If temperature is 0, k is 1, or the
+ *   top logit is not finite, the token is topk_ids[0].  Otherwise, in fp64,
+ *   p_i = exp((topk_logits[i] - topk_logits[0]) / temperature) (NaNs weigh
+ *   0), S = sum of p_i in list order, and the token is the first topk_ids[i]
+ *   whose running sum exceeds u * S (topk_ids[k-1] if rounding leaves none).
+ *   The same state and logits give the same token; successive calls on one
+ *   state continue the generator's sequence.  A zero state stays zero.
+ *   logits:      fp32 [n]                 state: uint32 [1], read and written
+ *   workspace:   logits_sample_workspace_bytes(n, k) bytes, 4-byte aligned
+ *   token:       int32 [1]                topk_ids: int32 [k]   topk_logits: fp32 [k]
+ * All pointers are device pointers.  Requires 1 <= n <= 2^20,
+ * 1 <= k <= min(64, n), 0 <= temperature < inf.
+ * Errors: BQD_EINVAL (ranges, temperature, workspace_bytes too small),
+ * BQD_ENULL, BQD_EALIGN, BQD_EHIP. */
+int logits_sample(const float *logits, int64_t n, int64_t k, float temperature,
+                  uint32_t *state, void *workspace, int64_t workspace_bytes,
+                  int32_t *token, int32_t *topk_ids, float *topk_logits, void *stream);
 
 /* Test probes: run the very device decode routines the kernels use.
  * bqd_dbg_cq_unpack: idx[c] = index(row, c) for c < input_padded (uint8).

@@ -137,6 +137,38 @@ def test_probe_argument_errors():
     assert L.bqd_dbg_cq_unpack(ctypes.byref(m), 0, 0, None) == ENULL
 
 
+SAMPLE_NEED = (246272 + 4095) // 4096 * 64 * 8  # workspace bytes for n = 246272, k = 64
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(n=0), EINVAL), (dict(n=(1 << 20) + 1), EINVAL), (dict(k=0), EINVAL),
+    (dict(k=65), EINVAL), (dict(n=10, k=11), EINVAL), (dict(temperature=-1.0), EINVAL),
+    (dict(temperature=float("nan")), EINVAL), (dict(temperature=float("inf")), EINVAL),
+    (dict(ws_bytes=SAMPLE_NEED - 1), EINVAL),
+    (dict(logits=0), ENULL), (dict(state=0), ENULL), (dict(ws=0), ENULL), (dict(token=0), ENULL),
+    (dict(ids=0), ENULL), (dict(vals=0), ENULL),
+    (dict(logits=FAKE + 2), EALIGN), (dict(state=FAKE + 1), EALIGN), (dict(ws=FAKE + 2), EALIGN),
+    (dict(token=FAKE + 3), EALIGN), (dict(ids=FAKE + 2), EALIGN), (dict(vals=FAKE + 1), EALIGN),
+])
+def test_logits_sample_rejects(args, code):
+    a = dict(logits=FAKE, n=246272, k=64, temperature=0.7, state=FAKE, ws=FAKE,
+             ws_bytes=SAMPLE_NEED, token=FAKE, ids=FAKE, vals=FAKE)
+    a.update(args)
+    rc = bqd.lib().logits_sample(a["logits"], a["n"], a["k"], a["temperature"], a["state"],
+                                 a["ws"], a["ws_bytes"], a["token"], a["ids"], a["vals"], None)
+    assert rc == code
+
+
+def test_logits_sample_workspace_bytes():
+    L = bqd.lib()
+    assert L.logits_sample_workspace_bytes(246272, 64) == SAMPLE_NEED
+    assert L.logits_sample_workspace_bytes(1, 1) == 8
+    assert L.logits_sample_workspace_bytes(4097, 3) == 2 * 3 * 8
+    assert L.logits_sample_workspace_bytes(1 << 20, 64) == 256 * 64 * 8
+    for n, k in ((0, 1), (10, 11), (100, 0), (100, 65), ((1 << 20) + 1, 1)):
+        assert L.logits_sample_workspace_bytes(n, k) == EINVAL
+
+
 def test_binding_refuses_host_tensors():
     with pytest.raises(TypeError):
         bqd.f8_matvec(torch.zeros(4, 16, dtype=torch.uint8), torch.zeros(1, 1, dtype=torch.uint8),

@@ -452,3 +452,69 @@ def test_graph_replay_matches_eager(cache):
             assert torch.equal(t, r)
         work()  # eager work between replays
         torch.cuda.synchronize()
+
+
+
+# ------------------------------------------------------------------ sampling
+def _state_tensor(seed):
+    return torch.tensor([int(np.array([seed], np.uint32).view(np.int32)[0])], dtype=torch.int32,
+                        device=DEV)
+
+
+def _near_cdf_boundary(vals, T, u, tol=1e-12):
+    """True if u * S lies within tol * S of a running sum of the softmax
+    weights: there two fp64 exp() implementations may pick neighbours."""
+    v = vals.astype(np.float64)
+    w = np.where(np.isnan(v), 0.0, np.exp((v - v[0]) / T))
+    S = w.sum()
+    return bool(np.any(np.abs(np.cumsum(w) - u * S) <= tol * S))
+
+
+def check_sample(logits, k, T, seed, calls=1):
+    x = to_dev(np.ascontiguousarray(logits, dtype=np.float32))
+    state = _state_tensor(seed)
+    s = seed
+    ref_ids, ref_vals = oracle.topk(logits, k)
+    for _ in range(calls):
+        tok, ids, vals = bqd.logits_sample(x, k, T, state)
+        ids, vals = ids.cpu().numpy(), vals.cpu().numpy()
+        assert np.array_equal(ids, ref_ids), (k, ids[:8], ref_ids[:8])
+        assert bits_eq(vals, ref_vals)
+        ref_tok, s = oracle.sample(ref_vals, ref_ids, T, s)
+        assert int(state.cpu().numpy().view(np.uint32)[0]) == s
+        got = int(tok.item())
+        if got != ref_tok:  # only where the draw sits on a CDF boundary
+            print(f"[boundary] token {got} vs {ref_tok} at u = {s / 2**32!r}", flush=True)
+            assert T > 0 and _near_cdf_boundary(ref_vals, T, s / 2**32), (got, ref_tok)
+
+
+def _logits(kind, n, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "normal":
+        return (3.0 * rng.standard_normal(n)).astype(np.float32)
+    if kind == "ties":
+        return rng.integers(-3, 4, n).astype(np.float32)
+    x = rng.standard_normal(n).astype(np.float32)
+    sp = np.array([np.nan, np.inf, -np.inf, -0.0, 0.0], np.float32)
+    x[rng.integers(0, n, max(1, n // 50))] = sp[rng.integers(0, 5, max(1, n // 50))]
+    return x
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "special"])
+@pytest.mark.parametrize("k,T", [(1, 1.0), (8, 0.0), (8, 0.7), (64, 1.0), (64, 2.5)])
+def test_sample_head_sized(kind, k, T):
+    """Logits of the F8 head's size (246272): top-k bit-exact, the state and
+    the token equal to the oracle's over chained draws."""
+    check_sample(_logits(kind, 246272, 90 + k), k, T, seed=0x9E3779B9 + k, calls=4)
+
+
+@pytest.mark.parametrize("n,k", [(1, 1), (5, 5), (64, 64), (4095, 7), (4096, 64), (4097, 64),
+                                 (8191, 3), (65536 + 17, 33), (1 << 20, 64)])
+def test_sample_ragged_sizes(n, k):
+    check_sample(_logits("normal", n, n), k, 0.8, seed=12345 + n)
+    check_sample(_logits("ties", n, n + 1), k, 1.3, seed=777 + n)
+
+
+def test_sample_chain_of_twenty():
+    """Twenty draws on one device state continue the oracle's sequence."""
+    check_sample(_logits("normal", 50000, 5), 16, 1.0, seed=1, calls=20)
