@@ -61,20 +61,25 @@ __device__ __forceinline__ uint64_t key_from_lane(uint64_t v, int src) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// One compare-exchange stage across lanes l and l ^ D: the lane keeps the
-// larger key if (lower lane) == descending, else the smaller.
-template <int D>
-__device__ __forceinline__ uint64_t cx(uint64_t v, bool desc) {
-  const uint64_t o = key_xor<D>(v);
-  const bool lower = (threadIdx.x & D) == 0;
-  return (lower == desc) ? (v > o ? v : o) : (v < o ? v : o);
+// One compare-exchange stage across lanes l and l ^ D on R independent keys
+// per lane: the lane keeps the larger key if (lower lane) == descending, else
+// the smaller (keys are distinct).
+template <int D, int R>
+__device__ __forceinline__ void cx(uint64_t (&v)[R], bool desc) {
+  const bool take_max = ((threadIdx.x & D) == 0) == desc;
+  uint64_t o[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) o[r] = key_xor<D>(v[r]);
+#pragma unroll
+  for (int r = 0; r < R; ++r) v[r] = ((v[r] > o[r]) == take_max) ? v[r] : o[r];
 }
 
-// Sort the 64 keys of the wavefront (one per lane) descending: lane l ends
-// with the l-th largest.
-__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
+// Sort R sets of 64 keys of the wavefront (one key per lane and set)
+// descending: lane l ends with the l-th largest of each set.
+template <int R>
+__device__ __forceinline__ void wave_sort_desc(uint64_t (&v)[R]) {
   const int l = threadIdx.x & 63;
-#define BQD_SORT_STAGE(SIZE, D) v = cx<D>(v, (SIZE) == 64 || (l & (SIZE)) == 0)
+#define BQD_SORT_STAGE(SIZE, D) cx<D, R>(v, (SIZE) == 64 || (l & (SIZE)) == 0)
   BQD_SORT_STAGE(2, 1);
   BQD_SORT_STAGE(4, 2); BQD_SORT_STAGE(4, 1);
   BQD_SORT_STAGE(8, 4); BQD_SORT_STAGE(8, 2); BQD_SORT_STAGE(8, 1);
@@ -84,21 +89,20 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
   BQD_SORT_STAGE(64, 32); BQD_SORT_STAGE(64, 16); BQD_SORT_STAGE(64, 8); BQD_SORT_STAGE(64, 4);
   BQD_SORT_STAGE(64, 2); BQD_SORT_STAGE(64, 1);
 #undef BQD_SORT_STAGE
-  return v;
 }
 
 // The 64 largest of two descending lists, descending: a holds A[l], b_rev
 // holds B[63 - l].  max(A[l], B[63 - l]) is a bitonic sequence holding the 64
 // largest; a bitonic merge sorts it.
 __device__ __forceinline__ uint64_t wave_merge_desc(uint64_t a, uint64_t b_rev) {
-  uint64_t v = a > b_rev ? a : b_rev;
-  v = cx<32>(v, true);
-  v = cx<16>(v, true);
-  v = cx<8>(v, true);
-  v = cx<4>(v, true);
-  v = cx<2>(v, true);
-  v = cx<1>(v, true);
-  return v;
+  uint64_t v[1] = {a > b_rev ? a : b_rev};
+  cx<32, 1>(v, true);
+  cx<16, 1>(v, true);
+  cx<8, 1>(v, true);
+  cx<4, 1>(v, true);
+  cx<2, 1>(v, true);
+  cx<1, 1>(v, true);
+  return v[0];
 }
 
 // In-place tree merge of `n_lists` descending lists of 64 keys in LDS (list i
@@ -135,8 +139,7 @@ __global__ __launch_bounds__(kSampleThreads) void topk_chunk_kernel(
     const int64_t i = (int64_t)blockIdx.x * kChunk + t;
     run[r] = i < n ? cand_key(logits[i], (uint32_t)i) : (uint64_t)(i - n);  // padding < kChunk
   }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) run[r] = wave_sort_desc(run[r]);
+  wave_sort_desc<4>(run);
   const uint64_t m01 = wave_merge_desc(run[0], key_from_lane(run[1], 63 - l));
   const uint64_t m23 = wave_merge_desc(run[2], key_from_lane(run[3], 63 - l));
   lists[64 * wave + l] = wave_merge_desc(m01, key_from_lane(m23, 63 - l));
@@ -153,6 +156,7 @@ __global__ __launch_bounds__(kSampleThreads) void topk_final_kernel(
   __shared__ uint64_t lists[kMaxCandidates];
   __shared__ float sel_v[kMaxK];
   __shared__ int32_t sel_i[kMaxK];
+  __shared__ double weight[kMaxK];
   for (int c = threadIdx.x; c < 64 * n_lists; c += kSampleThreads) {
     const int b = c >> 6, j = c & 63;
     const uint64_t v = j < k ? ws[(int64_t)b * k + j] : 0;
@@ -170,29 +174,30 @@ __global__ __launch_bounds__(kSampleThreads) void topk_final_kernel(
     topk_vals[t] = sel_v[t];
   }
   __syncthreads();
+  const float top = sel_v[0];
+  const bool draw = temperature > 0.0f && k > 1 && isfinite(top);
+  if (draw && t < k) {  // the softmax weights in fp64, one per lane
+    const float v = sel_v[t];
+    weight[t] = (v != v) ? 0.0 : exp(((double)v - (double)top) / (double)temperature);
+  }
+  __syncthreads();
   if (t == 0) {
     // one xorshift step (13, 17, 5), u = state / 2^32, then the inverse of the
-    // cumulative softmax, all in fp64 and in list order
+    // cumulative softmax: sums in list order, in fp64
     uint32_t s = *state;
     s ^= s << 13;
     s ^= s >> 17;
     s ^= s << 5;
     *state = s;
     int32_t tok = sel_i[0];
-    const float top = sel_v[0];
-    if (temperature > 0.0f && k > 1 && isfinite(top)) {
-      const double inv_t = 1.0 / (double)temperature;
+    if (draw) {
       double S = 0.0;
-      for (int j = 0; j < k; ++j) {
-        const float v = sel_v[j];
-        S += (v != v) ? 0.0 : exp(((double)v - (double)top) * inv_t);
-      }
+      for (int j = 0; j < k; ++j) S += weight[j];
       const double target = ((double)s / 4294967296.0) * S;
       double run = 0.0;
       tok = sel_i[k - 1];
       for (int j = 0; j < k; ++j) {
-        const float v = sel_v[j];
-        run += (v != v) ? 0.0 : exp(((double)v - (double)top) * inv_t);
+        run += weight[j];
         if (target < run) {
           tok = sel_i[j];
           break;
