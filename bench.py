@@ -2,9 +2,12 @@
 """Throughput of one decode step over the quantized matvec hot path (1 GPU).
 
 One step runs every stage of the path at the workloads' full sizes:
-  1. CQ 4-bit 16384 x 4096 (group 256): prepare + matvec, batch 1
-  2. the same matrix, 8 activation vectors: prepare + matvec
-  3. CQ 4-bit 65536 x 512 vocabulary table: dense gather of 4096 rows
+  1. CQ 4-bit 16384 x 4096 (group 256): prepare + matvec of one vector, one
+     launch (cq_prepare_matvec)
+  2. the same matrix, 8 activation vectors: prepare, then matvec
+  3. CQ 4-bit 65536 x 512 vocabulary table (group 128): the vocabulary
+     projection of one vector (cq_prepare_matvec) and a dense gather of 4096
+     rows
   4. FP8 E4M3 head 246272 x 4096 with E8M0 128 x 128 block scales: matvec
 Inputs are seeded synthetic arrays (synth.py) resident in HBM before timing.
 Weights rotate over enough copies that every step reads bytes that are not in
@@ -97,12 +100,16 @@ def build_cases(torch, bqd, synth, hot):
     y1 = torch.empty(1, s4.output, device=dev)
     y8 = torch.empty(8, s4.output, device=dev)
     w4 = s4.output * s4.stride + s4.output * s4.n_groups * 2
-    cases.append(Case("cq4_16384x4096_prepare_b1",
-                      [lambda m=m: bqd.cq_prepare(m, x1, out=p1) for m in mats4],
-                      4 * (s4.input + s4.input_padded), 0))
-    cases.append(Case("cq4_16384x4096_matvec_b1",
-                      [lambda m=m: bqd.cq_matvec(m, p1, out=y1) for m in mats4],
-                      w4 + 4 * s4.input_padded + 4 * s4.output, s4.output))
+    # batch 1: x in, the prepared vector and y out, in one launch
+    cases.append(Case("cq4_16384x4096_prepare_matvec_b1",
+                      [lambda m=m: bqd.cq_prepare_matvec(m, x1, prepared=p1, out=y1) for m in mats4],
+                      w4 + 4 * s4.input + 4 * s4.input_padded + 4 * s4.output, s4.output))
+    extras = [Case("cq4_16384x4096_matvec_b1",
+                   [lambda m=m: bqd.cq_matvec(m, p1, out=y1) for m in mats4],
+                   w4 + 4 * s4.input_padded + 4 * s4.output, s4.output),
+              Case("cq4_16384x4096_prepare_b1",
+                   [lambda m=m: bqd.cq_prepare(m, x1, out=p1) for m in mats4],
+                   4 * (s4.input + s4.input_padded), 0)]
     cases.append(Case("cq4_16384x4096_prepare_b8",
                       [lambda m=m: bqd.cq_prepare(m, x8, out=p8) for m in mats4],
                       8 * 4 * (s4.input + s4.input_padded), 0))
@@ -119,6 +126,13 @@ def build_cases(torch, bqd, synth, hot):
     mats3 = [bqd.CqMatrix(packed3 if k == 0 else packed3.clone(), norms3 if k == 0 else norms3.clone(),
                           cb3, output=s3.output, input=s3.input, input_padded=s3.input_padded,
                           group=s3.group, bits=s3.bits) for k in range(k3)]
+    x3 = T(c3.x[:1])
+    p3 = torch.empty(1, s3.input_padded, device=dev)
+    y3 = torch.empty(1, s3.output, device=dev)
+    w3 = s3.output * s3.stride + s3.output * s3.n_groups * 2
+    cases.append(Case("cq4_65536x512_prepare_matvec_b1",
+                      [lambda m=m: bqd.cq_prepare_matvec(m, x3, prepared=p3, out=y3) for m in mats3],
+                      w3 + 4 * s3.input + 4 * s3.input_padded + 4 * s3.output, s3.output))
     ids = T(c3.ids)
     g = torch.empty(len(c3.ids), s3.input, device=dev)
     n_ids = len(c3.ids)
@@ -140,7 +154,7 @@ def build_cases(torch, bqd, synth, hot):
                       [lambda w=w: bqd.f8_matvec(w, sh, xh, out=yh) for w in whs],
                       head_bytes, hd.R))
     data = dict(c4=c4, c3=c3, head=hd, head_logits=yh)
-    return cases, data
+    return cases, extras, data
 
 
 def cpu_baseline(data, threads):
@@ -174,15 +188,20 @@ def cpu_baseline(data, threads):
                                                      hd.x[0], a, b) for a, b in split(n_head)])
     t_c4 = run([lambda a=a, b=b: oracle.cq_matvec(h4, p4, a, b) for a, b in split(n_c4)])
     t_g = run([lambda a=a, b=b: oracle.cq_gather(h3, c3.ids[a:a + b]) for a, b in split(n_ids)])
+    s3 = c3.shape
+    p3 = oracle.cq_prepare(h3, c3.x[0])
+    t_c3 = run([lambda a=a, b=b: oracle.cq_matvec(h3, p3, a, b) for a, b in split(s3.output)])
     nbytes = (n_head * (hd.C + 4) + n_c4 * (s4.stride + 2 * s4.n_groups + 4)
-              + n_ids * (c3.shape.stride + 2 * c3.shape.n_groups + 4 + 4 * c3.shape.input))
-    secs = t_head + t_c4 + t_g
+              + s3.output * (s3.stride + 2 * s3.n_groups + 4)
+              + n_ids * (s3.stride + 2 * s3.n_groups + 4 + 4 * s3.input))
+    secs = t_head + t_c4 + t_g + t_c3
     return {
         "value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
         "kind": "oracle",
         "sample": (f"oracle on host cores: F8 head rows [0,{n_head}) of 246272 "
                    f"({t_head:.2f} s), CQ4 16384x4096 rows [0,{n_c4}) batch 1 ({t_c4:.2f} s), "
-                   f"CQ4 65536x512 gather of {n_ids} ids ({t_g:.2f} s); "
+                   f"CQ4 65536x512 all rows batch 1 ({t_c3:.2f} s) and gather of {n_ids} ids "
+                   f"({t_g:.2f} s); "
                    f"{threads} threads over row chunks"),
         "seconds": round(secs, 3),
     }
@@ -290,7 +309,7 @@ def main():
     if args.traffic_probe:
         traffic_probe(torch, bqd, synth)
         return
-    cases, data = build_cases(torch, bqd, synth, args.hot)
+    cases, extra_cases, data = build_cases(torch, bqd, synth, args.hot)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     period = max(len(c.calls) for c in cases)  # weight copies rotate with this period
@@ -302,7 +321,7 @@ def main():
     # Per stage: one graph of `period` back-to-back launches over the copies.
     stage_graphs = {c.name: capture(torch, lambda c=c: [c.calls[k % len(c.calls)]()
                                                        for k in range(period)])
-                    for c in cases}
+                    for c in cases + extra_cases}
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
@@ -320,7 +339,8 @@ def main():
     # each stage's graph of `period` back-to-back launches.
     reps = max(4, args.steps // period)
     per_case = {}
-    for c in cases:
+    extras = {}
+    for c in cases + extra_cases:
         g = stage_graphs[c.name]
         g.replay()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -333,11 +353,15 @@ def main():
         ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) / period
         c.ms = ms
         gbs = c.nbytes / (ms.mean() * 1e-3) / 1e9
-        per_case[c.name] = dict(
+        rec = dict(
             us_mean=round(float(ms.mean() * 1e3), 3), us_p10=round(float(np.percentile(ms, 10) * 1e3), 3),
             us_p90=round(float(np.percentile(ms, 90) * 1e3), 3), bytes=c.nbytes,
             gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4),
             rows_per_s=round(c.rows / (ms.mean() * 1e-3), 1) if c.rows else None)
+        if c in cases:
+            per_case[c.name] = rec
+        else:
+            extras[c.name] = dict(rec, note="not part of the step: the same stage as two calls")
     # Beyond the step: top-k (k = 64) and a temperature draw over the head's
     # logits, timed the same way (the sampler's state advances on the GPU).
     logits = data["head_logits"].reshape(-1)
@@ -355,9 +379,9 @@ def main():
         e1.record(stream)
     torch.cuda.synchronize()
     ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) / period
-    extras = {"head_logits_sample_k64": dict(
+    extras["head_logits_sample_k64"] = dict(
         us_mean=round(float(ms.mean() * 1e3), 3), logits=logits.numel(), k=64, temperature=0.8,
-        note="not part of the step: the sampler over the head's logits")}
+        note="not part of the step: the sampler over the head's logits")
     total_bytes = sum(c.nbytes for c in cases)
     total_rows = sum(c.rows for c in cases)
     value = total_bytes / (step_ms * 1e-3) / 1e9
@@ -388,8 +412,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded; synth.py)",
         "config": {"workload": "decode step: CQ4 16384x4096 g256 prepare+matvec at batch 1 and 8; "
-                               "CQ4 65536x512 g128 gather of 4096 rows; F8 E4M3 head 246272x4096 "
-                               "with E8M0 [1924x32] scales",
+                               "CQ4 65536x512 g128 vocabulary projection (batch 1) and gather of "
+                               "4096 rows; F8 E4M3 head 246272x4096 with E8M0 [1924x32] scales",
                    "mode": "hot (one weight copy)" if args.hot else
                            "cold (weights rotated past the 256 MB Infinity Cache)",
                    "launch": "one HIP graph replay per step",

@@ -13,6 +13,7 @@ Step 1):
 
 * ``cq_prepare(m, x)``        zero-pad, per-group FWHT, times 1/sqrt(group)
 * ``cq_matvec(m, prepared)``  packed-row codebook dot with fp16 group norms
+* ``cq_prepare_matvec(m, x)`` both in one call (the page's cqMatvec(matrix, x))
 * ``cq_gather_rows(m, rows)`` dense rows: decode x norm, normalized FWHT
 * ``f8_matvec(w, scale, x)``  E4M3 weights with E8M0 block scales
 """
@@ -23,7 +24,8 @@ import os
 
 import torch
 
-__all__ = ["BqdError", "CqMatrix", "cq_prepare", "cq_matvec", "cq_gather_rows", "f8_matvec",
+__all__ = ["BqdError", "CqMatrix", "cq_prepare", "cq_matvec", "cq_prepare_matvec",
+           "cq_gather_rows", "f8_matvec",
            "logits_sample", "logits_sample_workspace_bytes",
            "dbg_cq_unpack", "dbg_f16_decode", "dbg_f8_decode", "dbg_e8m0_decode", "lib",
            "LIB_PATH", "EXPORTS"]
@@ -32,7 +34,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbqd.so")
 
 # Every symbol include/bqd.h declares.
-EXPORTS = ("cq_prepare", "cq_matvec", "cq_gather_rows", "f8_matvec", "logits_sample",
+EXPORTS = ("cq_prepare", "cq_matvec", "cq_prepare_matvec", "cq_gather_rows", "f8_matvec", "logits_sample",
            "logits_sample_workspace_bytes", "bqd_dbg_cq_unpack", "bqd_dbg_f16_decode",
            "bqd_dbg_f8_decode", "bqd_dbg_e8m0_decode", "bqd_status_string")
 
@@ -66,6 +68,7 @@ def lib():
         for name, args in (
                 ("cq_prepare", [S, P, P, I64, P]),
                 ("cq_matvec", [S, P, P, I64, I64, I64, P]),
+                ("cq_prepare_matvec", [S, P, P, P, I64, I64, I64, P]),
                 ("cq_gather_rows", [S, P, I64, P, P]),
                 ("f8_matvec", [P, I64, I64, P, I64, I64, P, P, I64, P]),
                 ("bqd_dbg_cq_unpack", [S, I64, P, P]),
@@ -174,6 +177,28 @@ def cq_matvec(m: CqMatrix, prepared: torch.Tensor, out: torch.Tensor = None, row
     _call("cq_matvec", m.ref, _ptr(prepared), _ptr(out), batch, int(row_begin), row_count,
           _stream(prepared, stream))
     return out
+
+
+def cq_prepare_matvec(m: CqMatrix, x: torch.Tensor, prepared: torch.Tensor = None,
+                      out: torch.Tensor = None, row_begin: int = 0, row_count: int = None,
+                      stream=None):
+    """x float32 [batch][input] -> (prepared [batch][input_padded], y [batch][row_count]),
+    the results of cq_prepare followed by cq_matvec."""
+    x = _dev(x, torch.float32, "x")
+    if x.shape[-1] != m.input:
+        raise ValueError("x must have m.input columns")
+    batch = x.numel() // m.input if m.input else (x.shape[0] if x.dim() > 1 else 1)
+    row_count = m.output - row_begin if row_count is None else int(row_count)
+    prepared = torch.empty(x.shape[:-1] + (m.input_padded,), dtype=torch.float32,
+                           device=x.device) if prepared is None else \
+        _dev(prepared, torch.float32, "prepared")
+    out = torch.empty(x.shape[:-1] + (row_count,), dtype=torch.float32, device=x.device) \
+        if out is None else _dev(out, torch.float32, "out")
+    if prepared.numel() != batch * m.input_padded or out.numel() != batch * row_count:
+        raise ValueError("prepared or out has the wrong size")
+    _call("cq_prepare_matvec", m.ref, _ptr(x), _ptr(prepared), _ptr(out), batch, int(row_begin),
+          row_count, _stream(x, stream))
+    return prepared, out
 
 
 def cq_gather_rows(m: CqMatrix, rows: torch.Tensor, out: torch.Tensor = None, stream=None):

@@ -25,6 +25,14 @@ int cq_matvec(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t b
   return launch_cq_matvec(m, prepared, y, batch, row_begin, row_count, as_stream(stream));
 }
 
+int cq_prepare_matvec(const bqd_cq_matrix* m, const float* x, float* prepared, float* y,
+                      int64_t batch, int64_t row_begin, int64_t row_count, void* stream) {
+  int rc = check_prepare_matvec(m, x, prepared, y, batch, row_begin, row_count);
+  if (rc || batch == 0) return rc;
+  return launch_cq_prepare_matvec(m, x, prepared, y, batch, row_begin, row_count,
+                                  as_stream(stream));
+}
+
 int cq_gather_rows(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, float* out,
                    void* stream) {
   int rc = check_gather(m, rows, n, out);

@@ -405,134 +405,193 @@ void cq_matvec_b1(const uint8_t* __restrict__ packed, const uint16_t* __restrict
   }
 }
 
-// ------------------------------------------- batch-1 matvec, 4-bit pair tables
-// 4-bit rows of 16..128 chunks: a packed byte holds two indices, and an LDS
-// table indexed by the byte returns both codebook values as one 8-byte read.
-// Each table row holds 32 copies of its entry and lane l reads copy l % 32, so
-// no two lanes of a half-wavefront meet in one LDS bank; the byte-to-address
-// step is one byte permute.  Per pair of weights: one permute, one LDS read,
-// two FMAs.  Lanes own chunks q, q + LPR, ... of the row (each load
-// instruction reads LPR consecutive chunks) and keep those chunks'
-// activations in registers; the activations reach them through LDS (one
-// coalesced read of the vector per workgroup), in the space the table then
-// takes.
+// ------------------------------------------------------ 4-bit pair tables
+// A packed 4-bit byte holds two indices; an LDS table indexed by the byte
+// returns both codebook values as one 8-byte read.  Each table row holds 32
+// copies of its entry and lane l reads copy l % 32, so no two lanes of a
+// half-wavefront meet in one LDS bank; the byte-to-address step is one byte
+// permute.  Per pair of weights: one permute, one LDS read, two FMAs.
 constexpr int kPairRowBytes = 32 * 8;                  // 32 copies of (float, float)
 constexpr int kPairTableFloats = 256 * kPairRowBytes / 4;
-constexpr int kB1PairThreads = 512;                    // two workgroups per CU share the LDS
-static_assert(kB1PairThreads * 8 * 4 == kPairTableFloats, "eight table slots per thread");
 
-template <int NJ, int LPR, int U>
-__global__ __launch_bounds__(kB1PairThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
-void cq_matvec_b1_pairs(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
-                        const float* __restrict__ codebook, const float* __restrict__ prepared,
-                        float* __restrict__ y, int64_t input_padded, int64_t row_bytes,
-                        int log2_group, int rows) {
-  constexpr int SLOTS = kB1PairThreads / LPR;  // rows per step
+// ------------------------------------------- batch-1 matvec, a ring of rows
+// 4-bit rows of input_padded = 128 * S * BPL columns (512 ... 8192).  A
+// 1024-thread workgroup owns RPB = (16 / S) * 8 rows.  Wavefront w covers
+// column slice w % S of rows (w / S) * 8 ... + 7: lane l owns the BPL
+// consecutive packed bytes (2 * BPL columns, inside one group) at l * BPL of
+// the slice, so every load instruction reads 64 * BPL contiguous bytes of one
+// row, and the lane keeps only its own 2 * BPL activations in registers.
+//  - Each wavefront keeps a ring of DR rows in flight and requests row k + DR
+//    before it decodes row k, so the weight stream and the decode overlap
+//    from the first row to the last (requesting every row up front stalls:
+//    a CU holds only so many outstanding loads, and the decode of rows that
+//    arrive late then piles up at the end).
+//  - Decode through the 4-bit pair table above: a byte permute forms the
+//    table address, one 8-byte LDS read returns the codebook values of both
+//    nibbles, two FMAs; the lane's partial times the fp16 norm of its group.
+//  - The eight row partials of a lane are reduced across the wavefront by a
+//    transposed reduction (two lane-swap steps and one DPP step leave lane l
+//    with row (l / 8) % 8 of the wavefront, three DPP adds finish it), and
+//    the S slice partials of each row meet in LDS, summed in slice order.
+// E > 0 fuses the prepare ([P1] §2) into the kernel: `act` is then the raw
+// input (input floats), every workgroup zero-pads it and transforms its
+// groups in registers exactly as cq_prepare does (E elements per lane,
+// groups of 2^log2_group, the same butterflies and fp64 scale), and
+// workgroup 0 also stores the prepared vector to `prepared_out` when it is
+// not null.  E == 0: `act` is the prepared vector.
+constexpr int kRingThreads = 1024;
+constexpr int kRingRows = 8;  // rows per wavefront
+
+template <int BPL> struct RingLoad;
+template <> struct RingLoad<4> { typedef uint32_t T; };
+template <> struct RingLoad<8> { typedef uint32_t T __attribute__((ext_vector_type(2))); };
+template <> struct RingLoad<16> { typedef uint32_t T __attribute__((ext_vector_type(4))); };
+
+template <int BPL>
+__device__ __forceinline__ uint32_t ring_word(const typename RingLoad<BPL>::T& v, int t) {
+  if constexpr (BPL == 4) return v; else return v[t];
+}
+
+template <int BPL, int S, int E>
+__global__ __launch_bounds__(kRingThreads) void cq_matvec_ring(
+    const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
+    const float* __restrict__ codebook, const float* __restrict__ act,
+    float* __restrict__ prepared_out, float* __restrict__ y, int64_t row_bytes, int log2_group,
+    int rows, int input, double scale) {
+  constexpr int C = 128 * S * BPL;   // input_padded
+  constexpr int CPL = 2 * BPL;       // columns per lane
+  constexpr int AST = CPL + 4;       // padded floats per lane chunk in LDS
+  constexpr int RS = 16 / S;         // row subsets
+  constexpr int RPB = RS * kRingRows;
+  constexpr int DR = BPL == 16 ? 2 : 3;
+  typedef typename RingLoad<BPL>::T V;
   __shared__ __align__(16) float tab[kPairTableFloats];
-  const int tid = threadIdx.x;
-  const int slot = tid / LPR;
-  const int q = tid % LPR;
-  const int n_groups = (int)(input_padded >> log2_group);
-  const int n_steps = (rows + SLOTS - 1) / SLOTS;
-  const int stride = (int)gridDim.x * U;
-  const uint8_t* lane_base = packed + 16 * q;
-  int gidx[NJ];
+  __shared__ __align__(16) float act_s[64 * S * AST];
+  __shared__ float part[S][RPB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sl = wave % S, rs = wave / S;
+  const int wg0 = (int)blockIdx.x * RPB;
+  const int row0 = wg0 + rs * kRingRows;
+  // loads in the order they are needed: codebook (table), activations,
+  // norms, then the first DR rows of weights
+  const float cb_lo = codebook[(tid >> 4) & 15];
+  float cb_hi[4];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) gidx[j] = (32 * (q + LPR * j)) >> log2_group;
-
-  const float cbv = codebook[tid & 15];  // lanes 0..15 of every wavefront: the codebook
-  // The first step's weights and norms are requested before the set-up, so
-  // the weight stream runs while the activations and the table are prepared.
-  uint32_t d[U][NJ][4];
-  uint16_t nb[U][NJ];
-  auto load_step = [&](int s0) {
+  for (int p = 0; p < 4; ++p) cb_hi[p] = codebook[(tid >> 8) + 4 * p];
+  constexpr int XP = (C / 4 + kRingThreads - 1) / kRingThreads;  // float4 per thread (E == 0)
+  constexpr int SPANS = E > 0 ? C / (64 * E) : 1;                // transform spans (E > 0)
+  constexpr int SPW = (SPANS + 15) / 16;                         // spans per wavefront
+  float4 xv[E == 0 ? XP : 1];
+  float xr[E > 0 ? SPW : 1][E > 0 ? E : 1];
+  if constexpr (E == 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = min((s0 + u) * SLOTS + slot, rows - 1);  // in bounds; dropped if clamped
-      const uint32_t* pc = reinterpret_cast<const uint32_t*>(lane_base + (int64_t)i * row_bytes);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) d[u][j][t] = stream_load(pc + 4 * LPR * j + t);
-      const uint16_t* nr = norms + (int64_t)i * n_groups;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) nb[u][j] = nr[gidx[j]];
+    for (int p = 0; p < XP; ++p) {
+      const int i = tid + kRingThreads * p;
+      if (i < C / 4) xv[p] = reinterpret_cast<const float4*>(act)[i];
     }
+  } else {
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const int c0 = (wave + 16 * j) * (64 * E) + lane * E;
+#pragma unroll
+      for (int e = 0; e < E; ++e) xr[j][e] = (c0 + e < input && wave + 16 * j < SPANS) ? act[c0 + e] : 0.0f;
+    }
+  }
+  const int g = ((sl * 64 + lane) * CPL) >> log2_group;
+  const int n_groups = C >> log2_group;
+  uint16_t nb[kRingRows];
+#pragma unroll
+  for (int k = 0; k < kRingRows; ++k) nb[k] = norms[(int64_t)min(row0 + k, rows - 1) * n_groups + g];
+  V d[kRingRows];
+  const uint8_t* base = packed + sl * 64 * BPL + lane * BPL;
+  auto issue = [&](int k) {
+    d[k] = stream_load(reinterpret_cast<const V*>(base + (int64_t)min(row0 + k, rows - 1) * row_bytes));
   };
-  int s0 = (int)blockIdx.x * U;  // < n_steps: the grid has at most ceil(n_steps / U) workgroups
-  const int n4 = (int)(input_padded >> 2);
-  // this thread's share of the activations (input_padded <= 32 * 128 floats);
-  // two named registers, not an array the compiler could move to LDS
-  const float4 xs0 = reinterpret_cast<const float4*>(prepared)[min(tid, n4 - 1)];
-  const float4 xs1 = reinterpret_cast<const float4*>(prepared)[min(tid + kB1PairThreads, n4 - 1)];
-  // Every wavefront's activation requests go ahead of the workgroup's weight
-  // requests: the CU returns loads in order, and the set-up needs the
-  // activations first.
-  __syncthreads();
-  load_step(s0);
+#pragma unroll
+  for (int k = 0; k < DR; ++k) issue(k);
   __builtin_amdgcn_sched_barrier(0);
-  // Activations, staged with a stride of 36 floats per 32-float chunk (the 16
-  // lanes of a read pass then cover all banks), then chunk q + LPR j of this
-  // lane into registers.
-  if (tid < n4) *reinterpret_cast<float4*>(tab + 36 * (tid >> 3) + 4 * (tid & 7)) = xs0;
-  if (tid + kB1PairThreads < n4) {
-    const int i = tid + kB1PairThreads;
-    *reinterpret_cast<float4*>(tab + 36 * (i >> 3) + 4 * (i & 7)) = xs1;
-  }
-  __syncthreads();
-  float act[NJ][32];
+  // Table: 16-byte slot t = tid + 1024 p holds row b = t / 16, copies
+  // 2 (t % 16) and 2 (t % 16) + 1, each (codebook[b % 16], codebook[b / 16]).
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const float* src = tab + 36 * (q + LPR * j);
+  for (int p = 0; p < 4; ++p)
+    *reinterpret_cast<float4*>(tab + 4 * (tid + kRingThreads * p)) =
+        make_float4(cb_lo, cb_hi[p], cb_lo, cb_hi[p]);
+  if constexpr (E == 0) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float4 v = *reinterpret_cast<const float4*>(src + 4 * k);
-      act[j][4 * k] = v.x; act[j][4 * k + 1] = v.y; act[j][4 * k + 2] = v.z; act[j][4 * k + 3] = v.w;
-    }
-  }
-  __syncthreads();  // the staged activations are read; the table overwrites them
-  // Table: row b = copies of (codebook[b % 16], codebook[b / 16]); 16-byte
-  // slot s of the table is row s / 16, copies 2 (s % 16) and 2 (s % 16) + 1.
-  // Slot tid + 512 k has b % 16 = (tid / 16) % 16 and b / 16 = tid / 256 + 2 k,
-  // the latter uniform over a wavefront.
-  {
-    const float lo = __shfl(cbv, (tid >> 4) & 15);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cbv), (tid >> 8) + 2 * k));
-      *reinterpret_cast<float4*>(tab + 4 * (tid + kB1PairThreads * k)) = make_float4(lo, hi, lo, hi);
-    }
-  }
-  __syncthreads();
-  const uint32_t lane_off = 8u * (uint32_t)(tid & 31);
-  const char* tab_bytes = reinterpret_cast<const char*>(tab);
-
-  while (true) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        float p0 = 0.0f, p1 = 0.0f;
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            // columns 8 t + 2 p (low nibble) and 8 t + 2 p + 1 of the chunk
-            const uint32_t a = __builtin_amdgcn_perm(d[u][j][t], lane_off, 0x0c0c0400u | ((4u + p) << 8));
-            const float2 c = *reinterpret_cast<const float2*>(tab_bytes + a);
-            p0 += c.x * act[j][8 * t + 2 * p];
-            p1 += c.y * act[j][8 * t + 2 * p + 1];
-          }
-        acc += f16_to_f32(nb[u][j]) * (p0 + p1);
+    for (int p = 0; p < XP; ++p) {
+      const int i = tid + kRingThreads * p;
+      if (i < C / 4) {
+        const int f = 4 * i;
+        *reinterpret_cast<float4*>(act_s + (f / CPL) * AST + (f % CPL)) = xv[p];
       }
-      acc = group_sum<LPR>(acc);
-      const int i = (s0 + u) * SLOTS + slot;
-      if (q == LPR - 1 && i < rows) y[i] = acc;
     }
-    s0 += stride;
-    if (s0 >= n_steps) break;
-    load_step(s0);
+  } else {
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      if (SPANS % 16 == 0 || wave + 16 * j < SPANS) {  // wavefront-uniform
+        wave_fwht<E>(xr[j], lane, log2_group);
+        const int c0 = (wave + 16 * j) * (64 * E) + lane * E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float v = scale_store(xr[j][e], scale);
+          const int c = c0 + e;
+          act_s[(c / CPL) * AST + (c % CPL)] = v;
+          if (prepared_out != nullptr && blockIdx.x == 0) prepared_out[c] = v;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  float a[CPL];
+#pragma unroll
+  for (int k = 0; k < CPL; k += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(act_s + (sl * 64 + lane) * AST + k);
+    a[k] = v.x; a[k + 1] = v.y; a[k + 2] = v.z; a[k + 3] = v.w;
+  }
+  const uint32_t lane_off = 8u * (uint32_t)(lane & 31);
+  const char* tb = reinterpret_cast<const char*>(tab);
+  float acc[kRingRows];
+#pragma unroll
+  for (int k = 0; k < kRingRows; ++k) {
+    if (k + DR < kRingRows) issue(k + DR);
+    __builtin_amdgcn_sched_barrier(0);
+    float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+    for (int t = 0; t < BPL / 4; ++t)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        // byte b of the dword: columns 8 t + 2 b (low nibble) and + 1
+        const uint32_t adr = __builtin_amdgcn_perm(ring_word<BPL>(d[k], t), lane_off, 0x0c0c0400u | ((4u + b) << 8));
+        const float2 c = *reinterpret_cast<const float2*>(tb + adr);
+        p0 += c.x * a[8 * t + 2 * b];
+        p1 += c.y * a[8 * t + 2 * b + 1];
+      }
+    acc[k] = (p0 + p1) * f16_to_f32(nb[k]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // transposed reduction of the eight rows
+#pragma unroll
+  for (int k = 0; k < 4; ++k) acc[k] = swap_add32(acc[k], acc[k + 4]);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) acc[k] = swap_add16(acc[k], acc[k + 2]);
+  float v;
+  {
+    const bool up = (lane & 8) != 0;
+    const float keep = up ? acc[1] : acc[0];
+    const float send = up ? acc[0] : acc[1];
+    v = keep + lane_xor<8>(send);
+  }
+  v += lane_xor<4>(v);
+  v += lane_xor<2>(v);
+  v += lane_xor<1>(v);
+  if ((lane & 7) == 0) part[sl][rs * kRingRows + (lane >> 3)] = v;
+  __syncthreads();
+  if (tid < RPB) {
+    float t = 0.0f;
+#pragma unroll
+    for (int j = 0; j < S; ++j) t += part[j][tid];
+    const int r = wg0 + tid;
+    if (r < rows) y[r] = t;
   }
 }
 
@@ -1050,36 +1109,51 @@ int dispatch_nb(const bqd_cq_matrix* m, FastShape f, const float* prepared, floa
   return BQD_EINVAL;
 }
 
-constexpr int kNoKernel = 1;  // no instantiation covers the shape
 
-template <int NJ, int LPR>
-int launch_b1_pairs(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t row_begin,
-                    int64_t row_count, hipStream_t s) {
-  constexpr int U = 2;  // rows per wavefront and step
-  constexpr int SLOTS = kB1PairThreads / LPR;
-  const int64_t n_steps = (row_count + SLOTS - 1) / SLOTS;
-  const int64_t grid = std::min<int64_t>((n_steps + U - 1) / U, (int64_t)cu_count() * 2);
-  hipLaunchKernelGGL((cq_matvec_b1_pairs<NJ, LPR, U>), dim3((unsigned)grid), dim3(kB1PairThreads),
-                     0, s, m->packed + row_begin * m->row_bytes,
-                     m->norms + row_begin * (m->input_padded / m->group), m->codebook, prepared, y,
-                     m->input_padded, m->row_bytes, ilog2(m->group), (int)row_count);
+// The ring kernel's shapes: 4-bit, input_padded in {512, ..., 8192}, groups
+// that hold a lane's columns, 16-byte aligned rows.  Returns (BPL, S) or
+// (0, 0) when the shape is not covered.
+struct RingShape { int bpl, s; };
+RingShape ring_shape(const bqd_cq_matrix* m) {
+  if (m->bits != 4 || m->row_bytes % 16 || !is_aligned(m->packed, 16)) return {0, 0};
+  RingShape r{0, 0};
+  switch (m->input_padded) {
+    case 512: r = {4, 1}; break;
+    case 1024: r = {8, 1}; break;
+    case 2048: r = {16, 1}; break;
+    case 4096: r = {16, 2}; break;
+    case 8192: r = {16, 4}; break;
+    default: return {0, 0};
+  }
+  if (m->group < 2 * r.bpl) return {0, 0};
+  return r;
+}
+
+template <int BPL, int S, int E>
+int launch_ring_t(const bqd_cq_matrix* m, const float* act, float* prepared_out, float* y,
+                  int64_t row_begin, int64_t row_count, hipStream_t s) {
+  constexpr int RPB = (16 / S) * kRingRows;
+  const int64_t grid = (row_count + RPB - 1) / RPB;
+  hipLaunchKernelGGL((cq_matvec_ring<BPL, S, E>), dim3((unsigned)grid), dim3(kRingThreads), 0, s,
+                     m->packed + row_begin * m->row_bytes,
+                     m->norms + row_begin * (m->input_padded / m->group), m->codebook, act,
+                     prepared_out, y, m->row_bytes, ilog2(m->group), (int)row_count,
+                     (int)m->input, 1.0 / std::sqrt((double)m->group));
   return launch_status();
 }
 
-// 4-bit rows of 16, 32, 64 or 128 whole chunks with 16-byte aligned rows and
-// activations; kNoKernel otherwise.
-int run_b1_pairs(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t row_begin,
-                 int64_t row_count, hipStream_t s) {
-  if (m->input_padded % 32 || m->group < 32 || m->row_bytes % 16 || !is_aligned(m->packed, 16) ||
-      !is_aligned(prepared, 16))
-    return kNoKernel;
-  switch (m->input_padded / 32) {
-    case 16: return launch_b1_pairs<1, 16>(m, prepared, y, row_begin, row_count, s);
-    case 32: return launch_b1_pairs<1, 32>(m, prepared, y, row_begin, row_count, s);
-    case 64: return launch_b1_pairs<1, 64>(m, prepared, y, row_begin, row_count, s);
-    case 128: return launch_b1_pairs<2, 64>(m, prepared, y, row_begin, row_count, s);
+// E: 0 for a prepared activation, else the transform's elements per lane.
+template <int E>
+int launch_ring(const bqd_cq_matrix* m, RingShape r, const float* act, float* prepared_out,
+                float* y, int64_t row_begin, int64_t row_count, hipStream_t s) {
+  if (r.bpl == 4) return launch_ring_t<4, 1, E>(m, act, prepared_out, y, row_begin, row_count, s);
+  if (r.bpl == 8) return launch_ring_t<8, 1, E>(m, act, prepared_out, y, row_begin, row_count, s);
+  switch (r.s) {
+    case 1: return launch_ring_t<16, 1, E>(m, act, prepared_out, y, row_begin, row_count, s);
+    case 2: return launch_ring_t<16, 2, E>(m, act, prepared_out, y, row_begin, row_count, s);
+    case 4: return launch_ring_t<16, 4, E>(m, act, prepared_out, y, row_begin, row_count, s);
   }
-  return kNoKernel;
+  return BQD_EINVAL;  // unreachable: ring_shape() only returns instantiated shapes
 }
 
 int run_b1(const bqd_cq_matrix* m, FastShape f, const float* prepared, float* y,
@@ -1159,14 +1233,15 @@ int launch_generic(const bqd_cq_matrix* m, const float* prepared, float* y, int6
 
 int launch_cq_matvec(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t batch,
                      int64_t row_begin, int64_t row_count, hipStream_t s) {
+  if (batch == 1) {
+    const RingShape r = ring_shape(m);
+    if (r.bpl && is_aligned(prepared, 16))
+      return launch_ring<0>(m, r, prepared, nullptr, y, row_begin, row_count, s);
+  }
   if (!fast_ok(m)) return launch_generic(m, prepared, y, batch, row_begin, row_count, s);
   const int64_t n_chunk = m->input_padded / 32;
   const FastShape f1 = fast_shape(n_chunk, 1);
   const FastShape f4 = fast_shape(n_chunk, 4);
-  if (batch == 1 && m->bits == 4) {
-    const int rc = run_b1_pairs(m, prepared, y, row_begin, row_count, s);
-    if (rc != kNoKernel) return rc;
-  }
   if (batch == 1 && f1.lpr) return run_b1(m, f1, prepared, y, row_begin, row_count, s);
   if (batch >= 2 && mfma_ok(m, prepared)) {
     // up to eight vectors per launch on the matrix cores
@@ -1197,6 +1272,28 @@ int launch_cq_matvec(const bqd_cq_matrix* m, const float* prepared, float* y, in
     return BQD_OK;
   }
   return launch_generic(m, prepared, y, batch, row_begin, row_count, s);
+}
+
+// [P1] §2 then §3 in one call: `prepared` receives the prepared vectors and y
+// the matvec, exactly as cq_prepare followed by cq_matvec.  A single 4-bit
+// vector on a ring shape with groups of at most 256 takes one launch (the
+// prepare runs inside every workgroup of the matvec, workgroup 0 stores it);
+// everything else takes the two launches.
+int launch_cq_prepare_matvec(const bqd_cq_matrix* m, const float* x, float* prepared, float* y,
+                             int64_t batch, int64_t row_begin, int64_t row_count, hipStream_t s) {
+  if (batch == 1 && row_count > 0 && is_aligned(prepared, 16)) {
+    const RingShape r = ring_shape(m);
+    if (r.bpl) {
+      switch (lane_elems(m->group)) {
+        case 1: return launch_ring<1>(m, r, x, prepared, y, row_begin, row_count, s);
+        case 2: return launch_ring<2>(m, r, x, prepared, y, row_begin, row_count, s);
+        case 4: return launch_ring<4>(m, r, x, prepared, y, row_begin, row_count, s);
+      }
+    }
+  }
+  const int rc = launch_cq_prepare(m, x, prepared, batch, s);
+  if (rc || row_count == 0) return rc;
+  return launch_cq_matvec(m, prepared, y, batch, row_begin, row_count, s);
 }
 
 // ------------------------------------------------------------- unpack probe

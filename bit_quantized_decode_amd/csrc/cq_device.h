@@ -87,11 +87,30 @@ __device__ __forceinline__ uint32_t byte_index(const uint8_t* row, int bits, int
 }
 
 // ---------------------------------------------------------------------------
+// The values of lanes l and l ^ D (D = 16 or 32), lower lane first: one
+// gfx950 lane-swap instruction on two copies of v hands every lane both
+// members of its pair (v_permlane16_swap trades 16-lane rows 1 and 3 of its
+// first operand for rows 0 and 2 of its second; v_permlane32_swap trades
+// the upper half of the first for the lower half of the second), with no
+// LDS round trip.  .x is the value of the lane whose bit D is clear.
+template <int D>
+__device__ __forceinline__ float2 lane_pair(float v) {
+  static_assert(D == 16 || D == 32, "lane swaps cross 16-lane rows or wavefront halves");
+  const uint32_t u = __float_as_uint(v);
+  if constexpr (D == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+}
+
 // Value of lane (lane ^ D) of the wavefront.  D < 16 stays inside a 16-lane
 // DPP row: xor 1 and 2 are quad permutes, xor 8 is a rotation by 8, and xor 4
 // reads lane i + 4 (a right rotation by 12) in lanes with bit 2 clear and lane
 // i - 4 (a right rotation by 4, written to DPP banks 1 and 3 only) in the
-// others.  Larger D crosses rows and goes through ds_bpermute.
+// others.  D = 16 and 32 take the lane swaps of lane_pair.
 template <int D>
 __device__ __forceinline__ float lane_xor(float v) {
   if constexpr (D == 1) {
@@ -105,7 +124,8 @@ __device__ __forceinline__ float lane_xor(float v) {
   } else if constexpr (D == 8) {
     return dpp<kRowRor8, 0xf, false>(0.0f, v);
   } else {
-    return __shfl_xor(v, D, kWave);
+    const float2 p = lane_pair<D>(v);
+    return (__lane_id() & D) ? p.x : p.y;
   }
 }
 
@@ -116,8 +136,13 @@ __device__ __forceinline__ void lane_stage(float (&v)[E], int lane) {
   const bool upper = (lane & D) != 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const float o = lane_xor<D>(v[e]);
-    v[e] = upper ? o - v[e] : v[e] + o;
+    if constexpr (D >= 16) {
+      const float2 p = lane_pair<D>(v[e]);  // (a, b): the lower and the upper element
+      v[e] = upper ? p.x - p.y : p.x + p.y;
+    } else {
+      const float o = lane_xor<D>(v[e]);
+      v[e] = upper ? o - v[e] : v[e] + o;
+    }
   }
 }
 

@@ -85,6 +85,25 @@ constexpr int kRowRor4 = 0x124;        // lane i <- lane (i - 4) % 16 = (i + 12)
 constexpr int kRowRor8 = 0x128;        // lane i <- lane (i + 8) % 16
 constexpr int kRowRor12 = 0x12c;       // lane i <- lane (i + 4) % 16
 
+// Transposed (multi-row) reductions.  Each lane holds partial sums of several
+// rows; one exchange step halves the rows a lane holds and doubles the lanes
+// each sum covers, so a wavefront reduces n rows in about n exchanges instead
+// of 6n.  The gfx950 lane-swap instructions do the two cross-row steps in one
+// instruction each:
+//  swap_add32(a, b): lanes 0-31 receive a(l) + a(l + 32), lanes 32-63 receive
+//    b(l - 32) + b(l) (v_permlane32_swap: the upper half of a trades places
+//    with the lower half of b);
+//  swap_add16(a, b): in 16-lane rows 0 and 2, a(l) + a(l + 16); in rows 1 and
+//    3, b(l - 16) + b(l) (v_permlane16_swap: odd rows of a with even rows of b).
+__device__ __forceinline__ float swap_add32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_add16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum over aligned groups of N lanes (N a power of two, <= 64).  After the
 // call the group's last lane (lane % N == N - 1) holds the group total; the
 // summation order is fixed, so results are reproducible.

@@ -11,6 +11,8 @@ int launch_cq_prepare(const bqd_cq_matrix* m, const float* x, float* prepared, i
                       hipStream_t s);
 int launch_cq_matvec(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t batch,
                      int64_t row_begin, int64_t row_count, hipStream_t s);
+int launch_cq_prepare_matvec(const bqd_cq_matrix* m, const float* x, float* prepared, float* y,
+                             int64_t batch, int64_t row_begin, int64_t row_count, hipStream_t s);
 int launch_cq_gather(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, float* out,
                      hipStream_t s);
 int launch_cq_unpack(const bqd_cq_matrix* m, int64_t row, uint8_t* idx, hipStream_t s);

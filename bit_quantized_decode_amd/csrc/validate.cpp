@@ -76,6 +76,26 @@ int check_matvec(const bqd_cq_matrix* m, const float* prepared, const float* y, 
   return BQD_OK;
 }
 
+int check_prepare_matvec(const bqd_cq_matrix* m, const float* x, const float* prepared,
+                         const float* y, int64_t batch, int64_t row_begin, int64_t row_count) {
+  int rc = check_prepare(m, x, prepared, batch);
+  if (rc) return rc;
+  rc = check_matvec(m, prepared, y, batch, row_begin, row_count);
+  if (rc || batch == 0 || row_count == 0) return rc;
+  // y must overlap neither input
+  const char* ya = (const char*)y;
+  const char* yb = ya + batch * row_count * 4;
+  const char* pa = (const char*)prepared;
+  const char* pb = pa + batch * m->input_padded * 4;
+  if (ya < pb && pa < yb) return BQD_EINVAL;
+  if (x) {
+    const char* xa = (const char*)x;
+    const char* xb = xa + batch * m->input * 4;
+    if (ya < xb && xa < yb) return BQD_EINVAL;
+  }
+  return BQD_OK;
+}
+
 int check_gather(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, const float* out) {
   int rc = check_cq(m);
   if (rc) return rc;

@@ -15,6 +15,8 @@ int check_cq(const bqd_cq_matrix* m);
 int check_prepare(const bqd_cq_matrix* m, const float* x, const float* prepared, int64_t batch);
 int check_matvec(const bqd_cq_matrix* m, const float* prepared, const float* y, int64_t batch,
                  int64_t row_begin, int64_t row_count);
+int check_prepare_matvec(const bqd_cq_matrix* m, const float* x, const float* prepared,
+                         const float* y, int64_t batch, int64_t row_begin, int64_t row_count);
 int check_gather(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, const float* out);
 int check_f8(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
              int64_t SC, const float* x, const float* y, int64_t batch);

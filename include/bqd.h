@@ -96,6 +96,22 @@ int cq_prepare(const bqd_cq_matrix *m, const float *x, float *prepared,
 int cq_matvec(const bqd_cq_matrix *m, const float *prepared, float *y,
               int64_t batch, int64_t row_begin, int64_t row_count, void *stream);
 
+/* [P1] §2 followed by §3 in one call: the page's cqMatvec(matrix, x), which
+ * prepares the raw activation and then dots the packed rows.  Results are
+ * those of cq_prepare(m, x, prepared, batch) followed by cq_matvec(m,
+ * prepared, y, batch, row_begin, row_count), bit for bit: `prepared` receives
+ * the prepared vectors (a caller buffer; reuse it for further matrices, [P1]
+ * §6), y the outputs.  For one 4-bit vector with input_padded in {512, 1024,
+ * 2048, 4096, 8192}, group <= 256 and 16-byte aligned rows the two steps run
+ * as one kernel launch; otherwise as two.
+ *   x:        fp32 [batch][m->input]
+ *   prepared: fp32 [batch][m->input_padded]   (written; must not overlap x or y)
+ *   y:        fp32 [batch][row_count]         (must not overlap x)
+ * Errors: those of cq_prepare and cq_matvec, and BQD_EINVAL when y overlaps
+ * x or prepared. */
+int cq_prepare_matvec(const bqd_cq_matrix *m, const float *x, float *prepared, float *y,
+                      int64_t batch, int64_t row_begin, int64_t row_count, void *stream);
+
 /* [P1] "Row gather": for i < n, out[i][c] for c < input is the dense row
  * rows[i]: per group, codebook value times norm (fp32 product), the
  * unnormalized transform as in cq_prepare, times 1/sqrt(group), keeping the

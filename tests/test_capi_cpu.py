@@ -100,6 +100,30 @@ def test_cq_prepare_argument_errors():
     assert L.cq_prepare(None, FAKE, FAKE << 4, 1, None) == ENULL
 
 
+def test_cq_prepare_matvec_argument_errors():
+    L = bqd.lib()
+    m = cq()
+    X, P, Y = FAKE, FAKE << 4, FAKE << 8
+
+    def call(x=X, p=P, y=Y, batch=1, row_begin=0, row_count=256, mm=m):
+        return L.cq_prepare_matvec(ctypes.byref(mm), x, p, y, batch, row_begin, row_count, None)
+
+    assert call(batch=-1) == EINVAL
+    assert call(x=0) == ENULL
+    assert call(p=0) == ENULL
+    assert call(y=0) == ENULL
+    assert call(x=X + 1) == EALIGN
+    assert call(y=Y + 2) == EALIGN
+    assert call(p=X + 16) == EINVAL            # prepared overlaps x
+    assert call(y=P + 64) == EINVAL            # y overlaps prepared
+    assert call(y=X + 4) == EINVAL             # y overlaps x
+    assert call(row_begin=10, row_count=247) == EINVAL
+    assert call(mm=cq(bits=7)) == EINVAL
+    assert call(mm=cq(codebook=0)) == ENULL
+    assert call(batch=0) == OK
+    assert L.cq_prepare_matvec(None, X, P, Y, 1, 0, 1, None) == ENULL
+
+
 def test_cq_gather_argument_errors():
     L = bqd.lib()
     m = cq()

@@ -260,6 +260,63 @@ def test_matvec_one_hot_decodes_indices_exactly(shape, cols):
     assert np.array_equal(yb, ref.astype(np.float32))
 
 
+# Batch-1 4-bit ring kernel and the fused prepare + matvec entry point: every
+# row width the ring kernel covers (512 ... 8192), groups from 8 to 1024 (the
+# fused transform runs in the kernel for groups <= 256, two launches above),
+# unpadded widths below input_padded, row counts that leave the last
+# workgroup partly empty, and row ranges.
+RING_CASES = [
+    (synth.CqShape(300, 300, 512, 8, 4), 0, None),
+    (synth.CqShape(129, 512, 512, 64, 4), 0, None),
+    (synth.CqShape(257, 1000, 1024, 16, 4), 3, 200),
+    (synth.CqShape(130, 2048, 2048, 128, 4), 0, None),
+    (synth.CqShape(200, 4000, 4096, 256, 4), 0, None),
+    (synth.CqShape(65, 4096, 4096, 32, 4), 1, 63),
+    (synth.CqShape(70, 8192, 8192, 256, 4), 0, None),
+    (synth.CqShape(40, 8192, 8192, 1024, 4), 5, 33),
+    (synth.CqShape(33, 4096, 4096, 512, 4, row_bytes=2064), 0, None),
+]
+
+
+@pytest.mark.parametrize("k", range(len(RING_CASES)))
+def test_prepare_matvec_fused(k):
+    shape, rb, rc = RING_CASES[k]
+    row_count = shape.output - rb if rc is None else rc
+    print(f"[case] prepare+matvec {shape} rows [{rb}, +{row_count})", flush=True)
+    case = synth.make_cq(shape, seed=900 + k)
+    m, h = dev_matrix(case), host_matrix(case)
+    x = to_dev(case.x)
+    p, y = bqd.cq_prepare_matvec(m, x, row_begin=rb, row_count=row_count)
+    p_ref = oracle.cq_prepare(h, case.x)
+    assert bits_eq(p.cpu().numpy(), p_ref)
+    ref, mag = oracle.cq_matvec(h, p_ref, rb, row_count)
+    assert_tol(y.cpu().numpy(), ref, mag, f"cq_prepare_matvec {shape}")
+    # the same bits as the two calls it stands for
+    y2 = bqd.cq_matvec(m, bqd.cq_prepare(m, x), row_begin=rb, row_count=row_count)
+    assert bits_eq(y.cpu().numpy(), y2.cpu().numpy())
+
+
+def test_prepare_matvec_workload_and_batches(cache):
+    case = workload(cache, "cq4_16384x4096_b1")
+    m, h = dev_matrix(case), host_matrix(case)
+    p, y = bqd.cq_prepare_matvec(m, to_dev(case.x))
+    p_ref = oracle.cq_prepare(h, case.x)
+    assert bits_eq(p.cpu().numpy(), p_ref)
+    ref, mag = oracle.cq_matvec(h, p_ref)
+    assert_tol(y.cpu().numpy(), ref, mag, "cq_prepare_matvec CQ4 16384x4096")
+    # batches and other widths take the two-launch path
+    small = small_case(0, batch=3)
+    ms, hs = dev_matrix(small), host_matrix(small)
+    p, y = bqd.cq_prepare_matvec(ms, to_dev(small.x))
+    p_ref = oracle.cq_prepare(hs, small.x)
+    assert bits_eq(p.cpu().numpy(), p_ref)
+    ref, mag = oracle.cq_matvec(hs, p_ref)
+    assert_tol(y.cpu().numpy(), ref, mag, "cq_prepare_matvec batch 3")
+    # an empty row range still prepares
+    p, y = bqd.cq_prepare_matvec(m, to_dev(case.x), row_begin=100, row_count=0)
+    assert bits_eq(p.cpu().numpy(), oracle.cq_prepare(h, case.x)) and y.numel() == 0
+
+
 def test_matvec_unaligned_packed_uses_generic_path():
     case = synth.make_cq(synth.CqShape(50, 512, 512, 128, 4), seed=5)
     s = case.shape
