@@ -34,14 +34,19 @@ int cu_count() {
 }
 
 // 1/sqrt(group) is applied as the page does: the scale is an fp64 value, the
-// product is formed in fp64 and rounded once to fp32.
+// product is formed in fp64 and rounded once to fp32.  For groups that are
+// powers of four the scale is a power of two: the fp64 product is then exact
+// and its rounding equals the fp32 product, which is what runs.
 __device__ __forceinline__ float scale_store(float v, double scale) {
+  const float sf = (float)scale;
+  if ((double)sf == scale && (__float_as_uint(sf) & 0x007fffffu) == 0) return v * sf;
   return (float)((double)v * scale);
 }
 
 // Elements per lane of the wavefront transform: a wavefront spans one group
 // (64 * E = group) for groups of 64 and more, else 64 / group whole groups.
 inline int lane_elems(int64_t group) { return group >= 64 ? (int)(group / 64) : 1; }
+constexpr int ilog2_c(int v) { return v <= 1 ? 0 : 1 + ilog2_c(v / 2); }
 
 // ------------------------------------------------------------------ prepare
 // One wavefront per (vector, span of 64*E padded columns).
@@ -457,7 +462,7 @@ __global__ __launch_bounds__(kRingThreads) void cq_matvec_ring(
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
     const float* __restrict__ codebook, const float* __restrict__ act,
     float* __restrict__ prepared_out, float* __restrict__ y, int64_t row_bytes, int log2_group,
-    int rows, int input, double scale) {
+    int rows, int input, double scale, int x_vec) {
   constexpr int C = 128 * S * BPL;   // input_padded
   constexpr int CPL = 2 * BPL;       // columns per lane
   constexpr int AST = CPL + 4;       // padded floats per lane chunk in LDS
@@ -493,8 +498,15 @@ __global__ __launch_bounds__(kRingThreads) void cq_matvec_ring(
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
       const int c0 = (wave + 16 * j) * (64 * E) + lane * E;
+      if (E == 4 && x_vec && (SPANS % 16 == 0 || wave + 16 * j < SPANS)) {
+        // an unpadded, 16-byte aligned input: one float4 per lane and span
+        const float4 v = reinterpret_cast<const float4*>(act)[c0 / 4];
+        xr[j][0] = v.x; xr[j][1] = v.y; xr[j][2] = v.z; xr[j][3] = v.w;
+      } else {
 #pragma unroll
-      for (int e = 0; e < E; ++e) xr[j][e] = (c0 + e < input && wave + 16 * j < SPANS) ? act[c0 + e] : 0.0f;
+        for (int e = 0; e < E; ++e)
+          xr[j][e] = (c0 + e < input && wave + 16 * j < SPANS) ? act[c0 + e] : 0.0f;
+      }
     }
   }
   const int g = ((sl * 64 + lane) * CPL) >> log2_group;
@@ -529,7 +541,8 @@ __global__ __launch_bounds__(kRingThreads) void cq_matvec_ring(
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
       if (SPANS % 16 == 0 || wave + 16 * j < SPANS) {  // wavefront-uniform
-        wave_fwht<E>(xr[j], lane, log2_group);
+        // E >= 2 means group = 64 E: the stages are known at compile time
+        wave_fwht<E>(xr[j], lane, E >= 2 ? 6 + ilog2_c(E) : log2_group);
         const int c0 = (wave + 16 * j) * (64 * E) + lane * E;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -1134,11 +1147,12 @@ int launch_ring_t(const bqd_cq_matrix* m, const float* act, float* prepared_out,
                   int64_t row_begin, int64_t row_count, hipStream_t s) {
   constexpr int RPB = (16 / S) * kRingRows;
   const int64_t grid = (row_count + RPB - 1) / RPB;
+  const int x_vec = E > 0 && m->input == m->input_padded && is_aligned(act, 16);
   hipLaunchKernelGGL((cq_matvec_ring<BPL, S, E>), dim3((unsigned)grid), dim3(kRingThreads), 0, s,
                      m->packed + row_begin * m->row_bytes,
                      m->norms + row_begin * (m->input_padded / m->group), m->codebook, act,
                      prepared_out, y, m->row_bytes, ilog2(m->group), (int)row_count,
-                     (int)m->input, 1.0 / std::sqrt((double)m->group));
+                     (int)m->input, 1.0 / std::sqrt((double)m->group), x_vec);
   return launch_status();
 }
 
