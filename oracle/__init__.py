@@ -88,9 +88,14 @@ def _load(path: str):
     L.oracle_sample_u.argtypes = [P, P, I64, ctypes.c_double, ctypes.c_double]
     L.oracle_sample.restype = ctypes.c_int32
     L.oracle_sample.argtypes = [P, P, I64, ctypes.c_double, ctypes.POINTER(ctypes.c_uint32)]
+    L.oracle_i8_matvec.argtypes = [P, I64, I64, P, I64, P, I64, I64, P, P]
+    L.oracle_store_int8.argtypes = [P, I64, P, P]
+    L.oracle_int8_dot.argtypes = [P, P, I64, I64, P, I64, I64, P, P]
+    L.oracle_hadamard_mlp.argtypes = [P, I64, I64, P, P, P, P, P, P, P]
     for name in ("oracle_cq_unpack_row", "oracle_cq_prepare", "oracle_cq_matvec",
                  "oracle_cq_dequantize_row", "oracle_cq_gather",
-                 "oracle_cq_dense_matvec", "oracle_f8_matvec"):
+                 "oracle_cq_dense_matvec", "oracle_f8_matvec", "oracle_i8_matvec",
+                 "oracle_store_int8", "oracle_int8_dot", "oracle_hadamard_mlp"):
         getattr(L, name).restype = ctypes.c_int
     return L
 
@@ -275,3 +280,71 @@ def sample(vals: np.ndarray, ids: np.ndarray, temperature: float, state: int):
     s = ctypes.c_uint32(state)
     tok = lib().oracle_sample(_ptr(v), _ptr(i), v.size, temperature, ctypes.byref(s))
     return tok, s.value
+
+
+def i8_matvec(w, R, C, s, G, x, row_begin: int = 0, row_count=None):
+    """O14.  w int8 [R][C], s uint8 [R][ceil(C/G)]; returns (y, mag) float64
+    [batch][row_count] (or 1-D for a 1-D x)."""
+    if row_count is None:
+        row_count = R - row_begin
+    w = np.ascontiguousarray(w, dtype=np.int8)
+    s = np.ascontiguousarray(s, dtype=np.uint8)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    xb = x.reshape(-1, C)
+    y = np.zeros((xb.shape[0], row_count), dtype=np.float64)
+    mag = np.zeros_like(y)
+    for b in range(xb.shape[0]):
+        xv = np.ascontiguousarray(xb[b])
+        _check(lib().oracle_i8_matvec(_ptr(w), R, C, _ptr(s), G, _ptr(xv), row_begin, row_count,
+                                      y[b].ctypes.data_as(ctypes.c_void_p),
+                                      mag[b].ctypes.data_as(ctypes.c_void_p)), "i8_matvec")
+    if x.ndim == 1:
+        return y[0], mag[0]
+    return y, mag
+
+
+def store_int8(v: np.ndarray):
+    """O15 on each row of v ([n] or [rows][n]): (q int8, scale float32)."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    vb = v.reshape(-1, v.shape[-1]) if v.ndim else v.reshape(1, 1)
+    q = np.zeros(vb.shape, dtype=np.int8)
+    sc = np.zeros(vb.shape[0], dtype=np.float32)
+    for i in range(vb.shape[0]):
+        row = np.ascontiguousarray(vb[i])
+        qi = q[i]
+        si = sc[i:i + 1]
+        _check(lib().oracle_store_int8(_ptr(row), row.size, qi.ctypes.data_as(ctypes.c_void_p),
+                                       si.ctypes.data_as(ctypes.c_void_p)), "store_int8")
+    if v.ndim == 1:
+        return q[0], sc[0]
+    return q.reshape(v.shape), sc.reshape(v.shape[:-1])
+
+
+def int8_dot(K, scales, x, row_begin: int = 0, row_count=None):
+    """O16.  K int8 [R][d], scales float32 [R], x float32 [d]: (y, mag) float64."""
+    K = np.ascontiguousarray(K, dtype=np.int8)
+    R, d = K.shape
+    if row_count is None:
+        row_count = R - row_begin
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.zeros(row_count, dtype=np.float64)
+    mag = np.zeros_like(y)
+    _check(lib().oracle_int8_dot(_ptr(K), _ptr(scales), R, d, _ptr(x), row_begin, row_count,
+                                 _ptr(y), _ptr(mag)), "int8_dot")
+    return y, mag
+
+
+def hadamard_mlp(n, H, d1, d2, d3, resid, u=None):
+    """O17.  n, resid, u float32 [hidden]; d1, d2, d3 float32 [H].
+    Returns (out float32 [hidden], mag float64 [hidden])."""
+    f = lambda a: np.ascontiguousarray(a, dtype=np.float32)
+    n, d1, d2, d3, resid = f(n), f(d1), f(d2), f(d3), f(resid)
+    hidden = n.size
+    out = np.zeros(hidden, dtype=np.float32)
+    mag = np.zeros(hidden, dtype=np.float64)
+    uu = None if u is None else f(u)
+    _check(lib().oracle_hadamard_mlp(_ptr(n), hidden, H, _ptr(d1), _ptr(d2), _ptr(d3), _ptr(resid),
+                                     None if uu is None else _ptr(uu), _ptr(out), _ptr(mag)),
+           "hadamard_mlp")
+    return out, mag

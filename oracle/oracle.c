@@ -333,3 +333,132 @@ int32_t oracle_sample(const float *vals, const int32_t *ids, int64_t k,
     *state = oracle_xorshift32(*state);
     return oracle_sample_u(vals, ids, k, temperature, (double)*state / 4294967296.0);
 }
+
+/* --------------------------------------------------------------- O14 -- */
+/* [P4] "Step 4 done": the I8 matvec widens int8 weights and applies one E8M0
+ * scale per group of G consecutive columns of a row (G = 16 on the page).
+ * Row r's scales are s[r][0 .. ceil(C/G)). */
+int oracle_i8_matvec(const int8_t *w, int64_t R, int64_t C, const uint8_t *s, int64_t G,
+                     const float *x, int64_t row_begin, int64_t row_count, double *y,
+                     double *mag)
+{
+    if (!w || !s || !x || R < 0 || C < 1 || G < 1 || row_begin < 0 || row_count < 0 ||
+        row_begin + row_count > R)
+        return -1;
+    int64_t ns = (C + G - 1) / G;
+    for (int64_t i = 0; i < row_count; i++) {
+        int64_t r = row_begin + i;
+        double acc = 0.0, amag = 0.0;
+        for (int64_t c = 0; c < C; c++) {
+            double term = (double)w[r * C + c] * (double)oracle_e8m0(s[r * ns + c / G]) *
+                          (double)x[c];
+            acc += term;
+            amag += fabs(term);
+        }
+        if (y) y[i] = acc;
+        if (mag) mag[i] = amag;
+    }
+    return 0;
+}
+
+/* --------------------------------------------------------------- O15 -- */
+/* [P1] §7 "Per-vector int8 quantization" (storeInt8): the largest magnitude,
+ * floored at 1e-12, over 127 is the vector's scale (a JavaScript number;
+ * the scale array stores it as fp32); every element divided by that scale
+ * (in fp64) and rounded to the nearest integer, ties to even, is stored in
+ * an Int8Array.  The page's arithmetic is JavaScript's: Math.max turns the
+ * maximum into NaN when an element is NaN, and the Int8Array store turns NaN
+ * into 0. */
+static double js_max(double a, double b)
+{
+    if (isnan(a) || isnan(b)) return NAN;
+    return a > b ? a : b;
+}
+
+static int8_t js_to_int8(double v)
+{
+    if (!isfinite(v)) return 0;
+    double t = fmod(trunc(v), 256.0);        /* ToInt8: truncate, wrap mod 2^8 */
+    if (t < 0) t += 256.0;
+    return (int8_t)(t >= 128.0 ? t - 256.0 : t);
+}
+
+int oracle_store_int8(const float *v, int64_t n, int8_t *q, float *scale_out)
+{
+    if (!v || !q || !scale_out || n < 0) return -1;
+    double maximum = 1e-12;
+    for (int64_t i = 0; i < n; i++) maximum = js_max(maximum, fabs((double)v[i]));
+    double scale = maximum / 127.0;
+    *scale_out = (float)scale;
+    for (int64_t i = 0; i < n; i++) q[i] = js_to_int8(nearbyint((double)v[i] / scale));
+    return 0;
+}
+
+/* --------------------------------------------------------------- O16 -- */
+/* [P1] §7: a key dot against an int8 cache row multiplies the cached
+ * integers by the row's scale: y = scale[r] * sum_j K[r][j] * x[j]. */
+int oracle_int8_dot(const int8_t *K, const float *scales, int64_t R, int64_t d,
+                    const float *x, int64_t row_begin, int64_t row_count, double *y,
+                    double *mag)
+{
+    if (!K || !scales || !x || R < 0 || d < 0 || row_begin < 0 || row_count < 0 ||
+        row_begin + row_count > R)
+        return -1;
+    for (int64_t i = 0; i < row_count; i++) {
+        int64_t r = row_begin + i;
+        double acc = 0.0, amag = 0.0;
+        for (int64_t j = 0; j < d; j++) {
+            acc += (double)K[r * d + j] * (double)x[j];
+            amag += fabs((double)K[r * d + j] * (double)x[j]);
+        }
+        if (y) y[i] = (double)scales[r] * acc;
+        if (mag) mag[i] = fabs((double)scales[r]) * amag;
+    }
+    return 0;
+}
+
+/* --------------------------------------------------------------- O17 -- */
+/* [P1] §8 "Hadamard MLP", from the normalized block input n[hidden] on:
+ * z = n zero-padded to H; z *= d1; normalized FWHT; z = silu(d2 * z);
+ * normalized FWHT; z *= d3; block output = resid + z[0 .. hidden); the update
+ * subtracts u when u is given.  Float32Array stores round every array write
+ * to fp32; products, silu and the 1/sqrt(H) scale are formed in fp64 first
+ * (JavaScript numbers).  silu(t) = t / (1 + exp(-t)).  mag[i] bounds what
+ * the output's rounding scales with: |resid| + |u| + |d3| / sqrt(H) * sum |silu|. */
+static void normalized_fwht(float *z, int64_t H)
+{
+    oracle_fwht(z, H);
+    double scale = 1.0 / sqrt((double)H);
+    for (int64_t i = 0; i < H; i++) z[i] = (float)((double)z[i] * scale);
+}
+
+int oracle_hadamard_mlp(const float *n, int64_t hidden, int64_t H, const float *d1,
+                        const float *d2, const float *d3, const float *resid,
+                        const float *u, float *out, double *mag)
+{
+    if (!n || !d1 || !d2 || !d3 || !resid || !out || hidden < 0 || H < 1 || hidden > H ||
+        !is_pow2(H))
+        return -1;
+    float *z = (float *)malloc(sizeof(float) * (size_t)H);
+    if (!z) return -1;
+    for (int64_t i = 0; i < H; i++) z[i] = i < hidden ? n[i] : 0.0f;
+    for (int64_t i = 0; i < H; i++) z[i] = (float)((double)z[i] * (double)d1[i]);
+    normalized_fwht(z, H);
+    double l1 = 0.0;
+    for (int64_t i = 0; i < H; i++) {
+        double t = (double)d2[i] * (double)z[i];
+        z[i] = (float)(t / (1.0 + exp(-t)));
+        l1 += fabs((double)z[i]);
+    }
+    normalized_fwht(z, H);
+    for (int64_t i = 0; i < H; i++) z[i] = (float)((double)z[i] * (double)d3[i]);
+    for (int64_t i = 0; i < hidden; i++) {
+        float block = (float)((double)resid[i] + (double)z[i]);
+        out[i] = u ? (float)((double)block - (double)u[i]) : block;
+        if (mag)
+            mag[i] = fabs((double)resid[i]) + (u ? fabs((double)u[i]) : 0.0) +
+                     fabs((double)d3[i]) / sqrt((double)H) * l1;
+    }
+    free(z);
+    return 0;
+}

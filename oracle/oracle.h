@@ -9,7 +9,8 @@
  * Sources (web pages, cited by title and section):
  *   [P1] "Inference engine, part 2: kernels and token step" — §1 Fast
  *        Walsh–Hadamard transform, §2 Prepare an activation for CQ, §3 Dot
- *        packed rows directly, "Row gather".
+ *        packed rows directly, "Row gather", §7 (per-vector int8
+ *        quantization, scaled key dots), §8 (Hadamard MLP).
  *   [P3] "Inference engine, part 1: loader and tokenizer" — §3 Decode FP16
  *        control tensors, §4 Retain packed matrices.
  *   [P4] "attention + tokenizer + sampling: the path to real text
@@ -125,6 +126,33 @@ int32_t oracle_sample_u(const float *vals, const int32_t *ids, int64_t k,
  * then O13.  *state must be nonzero. */
 int32_t oracle_sample(const float *vals, const int32_t *ids, int64_t k,
                       double temperature, uint32_t *state);
+
+/* O14: I8 matvec ([P4] "Step 4 done"): y[i] = sum_c w[r][c] *
+ * e8m0(s[r][c / G]) * x[c] for r = row_begin + i, with ceil(C / G) scale
+ * bytes per row (G = 16 on the page); mag likewise with absolute values. */
+int oracle_i8_matvec(const int8_t *w, int64_t R, int64_t C, const uint8_t *s, int64_t G,
+                     const float *x, int64_t row_begin, int64_t row_count, double *y,
+                     double *mag);
+
+/* O15: storeInt8 ([P1] §7): scale = max(1e-12, max |v|) / 127 in fp64,
+ * stored as fp32 in *scale; q[i] = v[i] / scale (fp64) rounded to the
+ * nearest integer, ties to even, as an Int8Array stores it (NaN -> 0; a NaN
+ * element makes the scale NaN). */
+int oracle_store_int8(const float *v, int64_t n, int8_t *q, float *scale);
+
+/* O16: scaled int8 dot ([P1] §7): y[i] = scales[r] * sum_j K[r][j] * x[j],
+ * r = row_begin + i, fp64; mag = |scales[r]| * sum |K x|. */
+int oracle_int8_dot(const int8_t *K, const float *scales, int64_t R, int64_t d,
+                    const float *x, int64_t row_begin, int64_t row_count, double *y,
+                    double *mag);
+
+/* O17: Hadamard MLP ([P1] §8) from the normalized input n[hidden]: pad to H
+ * (a power of two), times d1, normalized FWHT, silu(d2 * z), normalized FWHT,
+ * times d3; out[i] = resid[i] + z[i] (minus u[i] when u is not NULL), for
+ * i < hidden.  mag (may be NULL): |resid| + |u| + |d3| / sqrt(H) * sum|silu|. */
+int oracle_hadamard_mlp(const float *n, int64_t hidden, int64_t H, const float *d1,
+                        const float *d2, const float *d3, const float *resid,
+                        const float *u, float *out, double *mag);
 
 #ifdef __cplusplus
 }

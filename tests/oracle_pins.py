@@ -471,4 +471,180 @@ def pin_sample_degenerate_cases():
         assert s2 == oracle.xorshift32(s)
         assert tok == oracle.sample_u(vals, ids, 1.0, s2 / 2**32)
 
+# ------------------------------------------------ I8 matvec (O14) --------
+def _i8_case(rng, R, C, G):
+    w = rng.integers(-128, 128, (R, C)).astype(np.int8)
+    s = rng.integers(118, 133, (R, (C + G - 1) // G)).astype(np.uint8)
+    x = rng.standard_normal(C).astype(np.float32)
+    return w, s, x
+
+
+def pin_i8_matvec_dense():
+    """numpy dense product with the E8M0 scales expanded by np.repeat
+    (groups of G columns, the last one ragged)."""
+    rng = np.random.default_rng(31)
+    for R, C, G in ((37, 80, 16), (5, 96, 32), (9, 50, 16), (4, 33, 7), (3, 64, 64)):
+        w, s, x = _i8_case(rng, R, C, G)
+        scale = np.ldexp(1.0, s.astype(np.int64) - 127)
+        wf = w.astype(np.float64) * np.repeat(scale, G, axis=1)[:, :C]
+        ref = wf @ x.astype(np.float64)
+        y, mag = oracle.i8_matvec(w, R, C, s, G, x)
+        assert np.allclose(y, ref, rtol=1e-12, atol=1e-12), (R, C, G)
+        assert np.allclose(mag, np.abs(wf) @ np.abs(x.astype(np.float64)), rtol=1e-12)
+        y2, _ = oracle.i8_matvec(w, R, C, s, G, x, 2, R - 3)
+        assert np.array_equal(y2, y[2:R - 1])
+
+
+def pin_i8_matvec_one_hot():
+    """x = e_c: y[r] = w[r][c] * 2^(s[r][c // G] - 127) exactly, every int8 value."""
+    R, C, G = 256, 48, 16
+    rng = np.random.default_rng(32)
+    w = np.arange(-128, 128, dtype=np.int64).astype(np.int8)[:, None].repeat(C, axis=1)
+    w = np.ascontiguousarray(np.roll(w, 5, axis=1))
+    s = rng.integers(100, 150, (R, C // G)).astype(np.uint8)
+    for c in (0, 15, 16, 47):
+        x = np.zeros(C, np.float32)
+        x[c] = 1.0
+        y, _ = oracle.i8_matvec(w, R, C, s, G, x)
+        expect = [math.ldexp(float(w[r, c]), int(s[r, c // G]) - 127) for r in range(R)]
+        assert np.array_equal(y, np.array(expect)), c
+
+
+# ------------------------------------------ storeInt8 (O15) -------------
+def pin_store_int8_exact_ties():
+    """Largest magnitude 127 makes the scale exactly 1: the codes are the
+    inputs rounded half to even (0.5 -> 0, 1.5 -> 2, 2.5 -> 2, -63.5 -> -64)."""
+    v = np.array([127, 0.5, 1.5, 2.5, -2.5, -63.5, 63.5, -0.5, 3.25, -126.5], np.float32)
+    q, sc = oracle.store_int8(v)
+    assert sc == np.float32(1.0)
+    assert q.tolist() == [127, 0, 2, 2, -2, -64, 64, 0, 3, -126]
+    # largest magnitude negative: -127 and scale 1 again
+    q, sc = oracle.store_int8(-v)
+    assert sc == np.float32(1.0) and q[0] == -127 and q[2] == -2
+
+
+def pin_store_int8_properties():
+    """Codes lie in [-127, 127]; the largest magnitude gets +-127 with its
+    sign; every code is within half a step of v / scale; the scale is the
+    largest magnitude over 127 rounded to fp32."""
+    rng = np.random.default_rng(33)
+    vecs = [rng.standard_normal(128), rng.uniform(-1, 1, 64) * 1e-3, -np.abs(rng.standard_normal(33)) * 50,
+            rng.standard_cauchy(256), np.r_[rng.standard_normal(63), -400.0]]
+    for v in vecs:
+        v = v.astype(np.float32)
+        q, sc = oracle.store_int8(v)
+        a = np.abs(v.astype(np.float64))
+        assert sc == np.float32(a.max() / 127.0)
+        assert np.all(np.abs(q.astype(np.int64)) <= 127)
+        i = int(np.argmax(a))
+        assert q[i] == (127 if v[i] > 0 else -127)
+        assert np.all(np.abs(v.astype(np.float64) / (a.max() / 127.0) - q) <= 0.5 + 1e-9)
+
+
+def pin_store_int8_floor_and_specials():
+    """The 1e-12 floor: an all-zero vector gets scale 1e-12/127 and zero codes;
+    a vector below the floor is coded against it.  A NaN makes the maximum
+    NaN (JavaScript's Math.max), hence every code 0 (Int8Array stores NaN as
+    0); an infinite element makes every finite code 0."""
+    q, sc = oracle.store_int8(np.zeros(8, np.float32))
+    assert sc == np.float32(1e-12 / 127) and not q.any()
+    q, sc = oracle.store_int8(np.array([2.5e-13, -5e-13], np.float32))
+    assert sc == np.float32(1e-12 / 127)
+    assert q.tolist() == [round(float(np.float32(2.5e-13)) * 127 / 1e-12),
+                          -round(float(np.float32(5e-13)) * 127 / 1e-12)]
+    q, sc = oracle.store_int8(np.array([1.0, np.nan, -3.0], np.float32))
+    assert math.isnan(sc) and not q.any()
+    q, sc = oracle.store_int8(np.array([1.0, np.inf, -3.0], np.float32))
+    assert math.isinf(sc) and not q.any()
+
+
+# ------------------------------------------- scaled int8 dot (O16) --------
+def pin_int8_dot_dense():
+    rng = np.random.default_rng(34)
+    K = rng.integers(-127, 128, (70, 128)).astype(np.int8)
+    scales = rng.uniform(1e-3, 2.0, 70).astype(np.float32)
+    x = rng.standard_normal(128).astype(np.float32)
+    y, mag = oracle.int8_dot(K, scales, x)
+    ref = scales.astype(np.float64) * (K.astype(np.float64) @ x.astype(np.float64))
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-15)
+    ref_mag = scales.astype(np.float64) * (np.abs(K.astype(np.float64)) @ np.abs(x.astype(np.float64)))
+    assert np.allclose(mag, ref_mag, rtol=1e-12)
+    y2, _ = oracle.int8_dot(K, scales, x, 10, 20)
+    assert np.array_equal(y2, y[10:30])
+
+
+def pin_int8_quantize_then_dot():
+    """storeInt8 then the scaled dot reproduces dot(v, x) within the
+    quantization bound sum_j |x_j| * scale / 2."""
+    rng = np.random.default_rng(35)
+    V = rng.standard_normal((16, 64)).astype(np.float32)
+    x = rng.standard_normal(64).astype(np.float32)
+    q, sc = oracle.store_int8(V)
+    y, _ = oracle.int8_dot(q, sc, x)
+    exact = V.astype(np.float64) @ x.astype(np.float64)
+    bound = np.abs(x.astype(np.float64)).sum() * sc.astype(np.float64) / 2 * (1 + 1e-6)
+    assert np.all(np.abs(y - exact) <= bound)
+
+
+# ------------------------------------------------ Hadamard MLP (O17) -----
+def _hmlp_exact_case(rng, hidden, H):
+    n = rng.integers(-3, 4, hidden).astype(np.float32)
+    d1 = rng.choice([-1.0, 1.0, 2.0, 0.5], H).astype(np.float32)
+    resid = rng.integers(-8, 9, hidden).astype(np.float32)
+    z = np.zeros(H)
+    z[:hidden] = n
+    z1 = (scipy.linalg.hadamard(H) / math.sqrt(H)) @ (d1.astype(np.float64) * z)
+    return n, d1, resid, z1
+
+
+def pin_hadamard_mlp_closed_forms():
+    """Inputs whose every fp32 stage is exact (small integers, H = 16 or 64
+    so 1/sqrt(H) is a power of two):
+      d2 = 0: silu(0) = 0, the block output is the residual;
+      d2 = 2^12 * sign(z1): silu(t) = t for t >= 40 in fp64, and with
+        d3 = 2^-12 the output is resid + (H_n |H_n (d1 * pad(n))|)[:hidden]
+        (H_n the normalized Sylvester matrix from scipy);
+      d2 = -2^12 * sign(z1): silu of a large negative argument is -0, the
+        block output is the residual again;
+      with u: the update is that output minus u."""
+    rng = np.random.default_rng(36)
+    for hidden, H in ((10, 16), (48, 64)):
+        n, d1, resid, z1 = _hmlp_exact_case(rng, hidden, H)
+        sign = np.where(z1 >= 0, 1.0, -1.0)
+        ones = np.ones(H, np.float32)
+        out, _ = oracle.hadamard_mlp(n, H, d1, np.zeros(H, np.float32), ones, resid)
+        assert np.array_equal(out, resid)
+        nz = np.abs(z1) > 0
+        d2 = (sign * 4096.0 * nz).astype(np.float32)
+        d3 = np.full(H, 2.0 ** -12, np.float32)
+        out, _ = oracle.hadamard_mlp(n, H, d1, d2, d3, resid)
+        Hn = scipy.linalg.hadamard(H) / math.sqrt(H)
+        expect = resid.astype(np.float64) + (Hn @ (np.abs(z1) * nz))[:hidden]
+        assert np.array_equal(out.astype(np.float64), expect), (hidden, H)
+        u = rng.integers(-4, 5, hidden).astype(np.float32)
+        out_u, _ = oracle.hadamard_mlp(n, H, d1, d2, d3, resid, u)
+        assert np.array_equal(out_u.astype(np.float64), expect - u)
+        out, _ = oracle.hadamard_mlp(n, H, d1, -d2, d3, resid)
+        assert np.array_equal(out, resid)
+
+
+def pin_hadamard_mlp_matrix_form():
+    """Random inputs against the float64 matrix form with scipy's Hadamard
+    matrix and numpy's exp, within fp32 rounding of the stages."""
+    rng = np.random.default_rng(37)
+    for hidden, H in ((100, 128), (512, 2048), (64, 64)):
+        n = rng.standard_normal(hidden).astype(np.float32)
+        d1, d2, d3 = (rng.uniform(-2, 2, H).astype(np.float32) for _ in range(3))
+        resid = rng.standard_normal(hidden).astype(np.float32)
+        u = rng.standard_normal(hidden).astype(np.float32)
+        out, mag = oracle.hadamard_mlp(n, H, d1, d2, d3, resid, u)
+        Hn = scipy.linalg.hadamard(H) / math.sqrt(H)
+        z = np.zeros(H)
+        z[:hidden] = n
+        t = d2 * (Hn @ (d1 * z))
+        s_ = t / (1 + np.exp(-t))
+        ref = resid + (d3 * (Hn @ s_))[:hidden] - u
+        assert np.all(np.abs(out - ref) <= 1e-5 * mag + 1e-6), (hidden, H, np.abs(out - ref).max())
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -42,6 +42,21 @@ MUTANTS = {
     "sample_no_temperature": ("exp(((double)vals[i] - (double)vals[0]) / temperature);\n        if",
                               "exp(((double)vals[i] - (double)vals[0]));\n        if"),
     "sample_cdf_off_by_one": ("if (target < run) return ids[i];", "if (target <= run) return ids[i > 0 ? i - 1 : 0];"),
+    "i8_group_fixed_16": ("(double)oracle_e8m0(s[r * ns + c / G])", "(double)oracle_e8m0(s[r * ns + c / 16])"),
+    "i8_scale_dropped": ("double term = (double)w[r * C + c] * (double)oracle_e8m0(s[r * ns + c / G]) *",
+                         "double term = (double)w[r * C + c] * 1.0 *"),
+    "int8_ties_away": ("q[i] = js_to_int8(nearbyint((double)v[i] / scale));",
+                       "q[i] = js_to_int8(round((double)v[i] / scale));"),
+    "int8_signed_max": ("maximum = js_max(maximum, fabs((double)v[i]));", "maximum = js_max(maximum, (double)v[i]);"),
+    "int8_scale_128": ("double scale = maximum / 127.0;", "double scale = maximum / 128.0;"),
+    "int8_no_floor": ("double maximum = 1e-12;", "double maximum = 0.0;"),
+    "int8_dot_scale_dropped": ("if (y) y[i] = (double)scales[r] * acc;", "if (y) y[i] = acc;"),
+    "hmlp_silu_sign": ("z[i] = (float)(t / (1.0 + exp(-t)));", "z[i] = (float)(t / (1.0 + exp(t)));"),
+    "hmlp_pad_ones": ("z[i] = i < hidden ? n[i] : 0.0f;", "z[i] = i < hidden ? n[i] : 1.0f;"),
+    "hmlp_no_d3": ("z[i] = (float)((double)z[i] * (double)d3[i]);", ""),
+    "hmlp_unnormalized": ("double scale = 1.0 / sqrt((double)H);", "double scale = 1.0;"),
+    "hmlp_u_added": ("out[i] = u ? (float)((double)block - (double)u[i]) : block;",
+                     "out[i] = u ? (float)((double)block + (double)u[i]) : block;"),
 }
 
 
