@@ -153,6 +153,30 @@ def build_cases(torch, bqd, synth, hot):
     cases.append(Case("f8_head_246272x4096_matvec",
                       [lambda w=w: bqd.f8_matvec(w, sh, xh, out=yh) for w in whs],
                       head_bytes, hd.R))
+    # -- beyond the step: the I8 head (E8M0 scales per 16 columns) and the
+    # int8 key cache (quantize 4096 vectors of 128, score one query)
+    log("generating I8 head 246272x4096 G16 (seed 5)")
+    i8 = synth.make_i8(**synth.I8_HEAD, seed=5)
+    wi0 = T(i8.w)
+    wis = [wi0] + [wi0.clone() for _ in range(kh - 1)]
+    si, xi = T(i8.scale), T(i8.x)
+    yi = torch.empty(1, i8.R, device=dev)
+    i8_bytes = i8.R * i8.C + i8.scale.size + 4 * i8.C + 4 * i8.R
+    extras.append(Case("i8_head_246272x4096_g16_matvec",
+                       [lambda w=w: bqd.i8_matvec(w, si, xi, i8.G, out=yi) for w in wis],
+                       i8_bytes, i8.R))
+    kv = synth.make_kv(**synth.KV, seed=6)
+    nkv, dkv = kv.v.shape
+    vk, xk = T(kv.v), T(kv.x)
+    qk = torch.empty(nkv, dkv, dtype=torch.int8, device=dev)
+    sk = torch.empty(nkv, device=dev)
+    yk = torch.empty(1, nkv, device=dev)
+    extras.append(Case("kv_int8_4096x128_quantize",
+                       [lambda: bqd.kv_quantize_int8(vk, q=qk, scales=sk)],
+                       4 * nkv * dkv + nkv * dkv + 4 * nkv, nkv))
+    extras.append(Case("kv_int8_4096x128_dot",
+                       [lambda: bqd.kv_int8_dot(qk, sk, xk, out=yk)],
+                       nkv * dkv + 4 * nkv + 4 * dkv + 4 * nkv, nkv))
     data = dict(c4=c4, c3=c3, head=hd, head_logits=yh)
     return cases, extras, data
 
@@ -360,8 +384,10 @@ def main():
             rows_per_s=round(c.rows / (ms.mean() * 1e-3), 1) if c.rows else None)
         if c in cases:
             per_case[c.name] = rec
-        else:
+        elif c.name.startswith("cq4_"):
             extras[c.name] = dict(rec, note="not part of the step: the same stage as two calls")
+        else:
+            extras[c.name] = dict(rec, note="not part of the step: a neighbouring format of the pages")
     # Beyond the step: top-k (k = 64) and a temperature draw over the head's
     # logits, timed the same way (the sampler's state advances on the GPU).
     logits = data["head_logits"].reshape(-1)

@@ -16,6 +16,10 @@ Step 1):
 * ``cq_prepare_matvec(m, x)`` both in one call (the page's cqMatvec(matrix, x))
 * ``cq_gather_rows(m, rows)`` dense rows: decode x norm, normalized FWHT
 * ``f8_matvec(w, scale, x)``  E4M3 weights with E8M0 block scales
+* ``i8_matvec(w, scale, x, G)`` int8 weights with E8M0 scales per G columns
+  ("attention + tokenizer + sampling", Step 4)
+* ``kv_quantize_int8(v)``     storeInt8 per vector ("Inference engine, part 2" §7)
+* ``kv_int8_dot(K, scales, x)`` the scaled key dot against an int8 cache
 """
 from __future__ import annotations
 
@@ -25,7 +29,7 @@ import os
 import torch
 
 __all__ = ["BqdError", "CqMatrix", "cq_prepare", "cq_matvec", "cq_prepare_matvec",
-           "cq_gather_rows", "f8_matvec",
+           "cq_gather_rows", "f8_matvec", "i8_matvec", "kv_quantize_int8", "kv_int8_dot",
            "logits_sample", "logits_sample_workspace_bytes",
            "dbg_cq_unpack", "dbg_f16_decode", "dbg_f8_decode", "dbg_e8m0_decode", "lib",
            "LIB_PATH", "EXPORTS"]
@@ -34,7 +38,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbqd.so")
 
 # Every symbol include/bqd.h declares.
-EXPORTS = ("cq_prepare", "cq_matvec", "cq_prepare_matvec", "cq_gather_rows", "f8_matvec", "logits_sample",
+EXPORTS = ("cq_prepare", "cq_matvec", "cq_prepare_matvec", "cq_gather_rows", "f8_matvec",
+           "i8_matvec", "kv_quantize_int8", "kv_int8_dot", "logits_sample",
            "logits_sample_workspace_bytes", "bqd_dbg_cq_unpack", "bqd_dbg_f16_decode",
            "bqd_dbg_f8_decode", "bqd_dbg_e8m0_decode", "bqd_status_string")
 
@@ -71,6 +76,9 @@ def lib():
                 ("cq_prepare_matvec", [S, P, P, P, I64, I64, I64, P]),
                 ("cq_gather_rows", [S, P, I64, P, P]),
                 ("f8_matvec", [P, I64, I64, P, I64, I64, P, P, I64, P]),
+                ("i8_matvec", [P, I64, I64, P, I64, P, P, I64, P]),
+                ("kv_quantize_int8", [P, I64, I64, P, P, P]),
+                ("kv_int8_dot", [P, P, I64, I64, P, P, I64, P]),
                 ("bqd_dbg_cq_unpack", [S, I64, P, P]),
                 ("bqd_dbg_f16_decode", [P, I64, P, P]),
                 ("bqd_dbg_f8_decode", [P, I64, P, P]),
@@ -230,6 +238,61 @@ def f8_matvec(w: torch.Tensor, scale: torch.Tensor, x: torch.Tensor, out: torch.
     if out.numel() != batch * R:
         raise ValueError("out has the wrong size")
     _call("f8_matvec", _ptr(w), R, C, _ptr(scale), SR, SC, _ptr(x), _ptr(out), batch,
+          _stream(x, stream))
+    return out
+
+
+def i8_matvec(w: torch.Tensor, scale: torch.Tensor, x: torch.Tensor, G: int = 16,
+              out: torch.Tensor = None, stream=None):
+    """w int8 [R][C], scale uint8 E8M0 [R][ceil(C/G)], x float32 [batch][C] -> [batch][R]."""
+    w = _dev(w, torch.int8, "w")
+    scale = _dev(scale, torch.uint8, "scale")
+    x = _dev(x, torch.float32, "x")
+    R, C = w.shape
+    if scale.shape != (R, (C + G - 1) // G):
+        raise ValueError("scale must be [R][ceil(C/G)]")
+    if x.shape[-1] != C:
+        raise ValueError("x must have C columns")
+    batch = x.numel() // C
+    out = torch.empty(x.shape[:-1] + (R,), dtype=torch.float32, device=x.device) if out is None \
+        else _dev(out, torch.float32, "out")
+    if out.numel() != batch * R:
+        raise ValueError("out has the wrong size")
+    _call("i8_matvec", _ptr(w), R, C, _ptr(scale), int(G), _ptr(x), _ptr(out), batch,
+          _stream(x, stream))
+    return out
+
+
+def kv_quantize_int8(v: torch.Tensor, q: torch.Tensor = None, scales: torch.Tensor = None,
+                     stream=None):
+    """v float32 [n][d] -> (q int8 [n][d], scales float32 [n]), storeInt8 per row."""
+    v = _dev(v, torch.float32, "v")
+    n, d = v.shape
+    q = torch.empty((n, d), dtype=torch.int8, device=v.device) if q is None else \
+        _dev(q, torch.int8, "q")
+    scales = torch.empty(n, dtype=torch.float32, device=v.device) if scales is None else \
+        _dev(scales, torch.float32, "scales")
+    if q.numel() != n * d or scales.numel() != n:
+        raise ValueError("q or scales has the wrong size")
+    _call("kv_quantize_int8", _ptr(v), n, d, _ptr(q), _ptr(scales), _stream(v, stream))
+    return q, scales
+
+
+def kv_int8_dot(K: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, out: torch.Tensor = None,
+                stream=None):
+    """K int8 [R][d], scales float32 [R], x float32 [batch][d] -> [batch][R]."""
+    K = _dev(K, torch.int8, "K")
+    scales = _dev(scales, torch.float32, "scales")
+    x = _dev(x, torch.float32, "x")
+    R, d = K.shape
+    if scales.numel() != R or x.shape[-1] != d:
+        raise ValueError("scales must have R entries and x d columns")
+    batch = x.numel() // d
+    out = torch.empty(x.shape[:-1] + (R,), dtype=torch.float32, device=x.device) if out is None \
+        else _dev(out, torch.float32, "out")
+    if out.numel() != batch * R:
+        raise ValueError("out has the wrong size")
+    _call("kv_int8_dot", _ptr(K), _ptr(scales), R, d, _ptr(x), _ptr(out), batch,
           _stream(x, stream))
     return out
 

@@ -47,6 +47,27 @@ int f8_matvec(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int6
   return launch_f8_matvec(w, R, C, scale, SR, SC, x, y, batch, as_stream(stream));
 }
 
+int i8_matvec(const int8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t G,
+              const float* x, float* y, int64_t batch, void* stream) {
+  int rc = check_i8(w, R, C, scale, G, x, y, batch);
+  if (rc || batch == 0 || R == 0) return rc;
+  return launch_i8_matvec(w, R, C, scale, G, x, y, batch, as_stream(stream));
+}
+
+int kv_quantize_int8(const float* v, int64_t n_vec, int64_t d, int8_t* q, float* scales,
+                     void* stream) {
+  int rc = check_kv_quantize(v, n_vec, d, q, scales);
+  if (rc || n_vec == 0) return rc;
+  return launch_kv_quantize_int8(v, n_vec, d, q, scales, as_stream(stream));
+}
+
+int kv_int8_dot(const int8_t* K, const float* scales, int64_t R, int64_t d, const float* x,
+                float* y, int64_t batch, void* stream) {
+  int rc = check_kv_dot(K, scales, R, d, x, y, batch);
+  if (rc || batch == 0 || R == 0) return rc;
+  return launch_kv_int8_dot(K, scales, R, d, x, y, batch, as_stream(stream));
+}
+
 int bqd_dbg_cq_unpack(const bqd_cq_matrix* m, int64_t row, uint8_t* idx, void* stream) {
   int rc = check_unpack(m, row, idx);
   if (rc) return rc;

@@ -121,6 +121,39 @@ int check_f8(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64
   return BQD_OK;
 }
 
+int check_i8(const int8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t G,
+             const float* x, const float* y, int64_t batch) {
+  if (R < 0 || R >= kMaxRows || C < 1 || C >= kMaxColumns || G < 1 || G > C || batch < 0)
+    return BQD_EINVAL;
+  const int64_t ns = (C + G - 1) / G;
+  if (!mul_ok(R, C) || !mul_ok(R, ns) || !mul_ok(batch, C, 4) || !mul_ok(batch, R, 4))
+    return BQD_EOVERFLOW;
+  if (batch == 0 || R == 0) return BQD_OK;
+  if (!w || !scale || !x || !y) return BQD_ENULL;
+  if (!aligned(x, 4) || !aligned(y, 4)) return BQD_EALIGN;
+  return BQD_OK;
+}
+
+int check_kv_quantize(const float* v, int64_t n_vec, int64_t d, const int8_t* q,
+                      const float* scales) {
+  if (n_vec < 0 || n_vec >= kMaxRows || d < 0 || d >= kMaxColumns) return BQD_EINVAL;
+  if (!mul_ok(n_vec, d, 4)) return BQD_EOVERFLOW;
+  if (n_vec == 0) return BQD_OK;
+  if (!scales || (d > 0 && (!v || !q))) return BQD_ENULL;
+  if (!aligned(v, 4) || !aligned(scales, 4)) return BQD_EALIGN;
+  return BQD_OK;
+}
+
+int check_kv_dot(const int8_t* K, const float* scales, int64_t R, int64_t d, const float* x,
+                 const float* y, int64_t batch) {
+  if (R < 0 || R >= kMaxRows || d < 1 || d >= kMaxColumns || batch < 0) return BQD_EINVAL;
+  if (!mul_ok(R, d) || !mul_ok(batch, d, 4) || !mul_ok(batch, R, 4)) return BQD_EOVERFLOW;
+  if (batch == 0 || R == 0) return BQD_OK;
+  if (!K || !scales || !x || !y) return BQD_ENULL;
+  if (!aligned(scales, 4) || !aligned(x, 4) || !aligned(y, 4)) return BQD_EALIGN;
+  return BQD_OK;
+}
+
 int check_unpack(const bqd_cq_matrix* m, int64_t row, const uint8_t* idx) {
   int rc = check_cq(m);
   if (rc) return rc;

@@ -20,6 +20,12 @@ int check_prepare_matvec(const bqd_cq_matrix* m, const float* x, const float* pr
 int check_gather(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, const float* out);
 int check_f8(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
              int64_t SC, const float* x, const float* y, int64_t batch);
+int check_i8(const int8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t G,
+             const float* x, const float* y, int64_t batch);
+int check_kv_quantize(const float* v, int64_t n_vec, int64_t d, const int8_t* q,
+                      const float* scales);
+int check_kv_dot(const int8_t* K, const float* scales, int64_t R, int64_t d, const float* x,
+                 const float* y, int64_t batch);
 int check_unpack(const bqd_cq_matrix* m, int64_t row, const uint8_t* idx);
 int check_decode(const void* codes, int64_t n, const float* out, int code_size);
 int64_t sample_workspace_need(int64_t n, int64_t k);  // or BQD_EINVAL

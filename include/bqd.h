@@ -6,13 +6,14 @@
  *        tutorial): §1 "Fast Walsh–Hadamard transform", §2 "Prepare an
  *        activation for CQ", §3 "Dot packed rows directly", "Row gather",
  *        §6 (row-range matvec, one prepared activation reused for several
- *        matrices);
+ *        matrices), §7 (per-vector int8 quantization, key dots), §8
+ *        (Hadamard MLP);
  *   [P3] "Inference engine, part 1: loader and tokenizer": §2 "Make bounds
  *        checks boring", §3 "Decode FP16 control tensors", §4 "Retain packed
  *        matrices" (the CQ record);
  *   [P4] "attention + tokenizer + sampling: the path to real text (milestone
  *        6)": "Step 1 done: F8 kernel" (E4M3 decode, E8M0 block scales),
- *        "Step 4 done" (the vector decode), work item 3 and "Step 3 done"
+ *        "Step 4 done" (the vector decode, the I8 matvec), work item 3 and "Step 3 done"
  *        (head logits, top-k / temperature sampling, a deterministic
  *        softmax + xorshift sampler).
  *
@@ -138,6 +139,42 @@ int cq_gather_rows(const bqd_cq_matrix *m, const int32_t *rows, int64_t n,
 int f8_matvec(const uint8_t *w, int64_t R, int64_t C, const uint8_t *scale,
               int64_t SR, int64_t SC, const float *x, float *y, int64_t batch,
               void *stream);
+
+/* [P4] "Step 4 done" (the I8 matvec: int8 weights widened, one E8M0 scale
+ * per group of consecutive columns; the page's groups are 16 wide):
+ *   y[b][r] = sum over c < C of w[r][c] * e8m0(scale[r][c / G]) * x[b][c],
+ * with ceil(C / G) scale bytes per row and e8m0 as in f8_matvec.
+ * Accumulation is fp32 (same tolerance as cq_matvec).
+ *   w:     int8 [R][C]          scale: E8M0 bytes [R][ceil(C / G)]
+ *   x:     fp32 [batch][C]      y:     fp32 [batch][R]
+ * Requires 0 <= R < 2^30, 1 <= C < 2^28, 1 <= G <= C, batch >= 0.  Rows of
+ * a multiple of 16 bytes, 16-byte aligned, with G a multiple of 16 take the
+ * streaming kernel; anything else a generic one.
+ * Errors: BQD_EINVAL, BQD_ENULL, BQD_EALIGN, BQD_EOVERFLOW, BQD_EHIP. */
+int i8_matvec(const int8_t *w, int64_t R, int64_t C, const uint8_t *scale, int64_t G,
+              const float *x, float *y, int64_t batch, void *stream);
+
+/* [P1] §7 "Per-vector int8 quantization" (storeInt8), for each of n_vec
+ * vectors of d floats: maximum = max(1e-12, largest |v|) (NaN if any
+ * element is NaN), scale = maximum / 127 formed in fp64 and stored as fp32
+ * in scales[i]; q[i][j] = v[i][j] / scale (fp64) rounded to the nearest
+ * integer, ties to even (0 where that quotient is NaN).  Codes are bit-exact
+ * with that arithmetic and lie in [-127, 127].
+ *   v: fp32 [n_vec][d]    q: int8 [n_vec][d]    scales: fp32 [n_vec]
+ * Requires 0 <= n_vec < 2^30, 0 <= d < 2^28.
+ * Errors: BQD_EINVAL, BQD_ENULL, BQD_EALIGN, BQD_EOVERFLOW, BQD_EHIP. */
+int kv_quantize_int8(const float *v, int64_t n_vec, int64_t d, int8_t *q, float *scales,
+                     void *stream);
+
+/* [P1] §7 key dot against an int8 cache: for b < batch and r < R,
+ *   y[b][r] = scales[r] * sum over j < d of K[r][j] * x[b][j]
+ * (fp32 accumulation; same tolerance as cq_matvec).
+ *   K: int8 [R][d] (rows as kv_quantize_int8 writes them)   scales: fp32 [R]
+ *   x: fp32 [batch][d]                                       y: fp32 [batch][R]
+ * Requires 0 <= R < 2^30, 1 <= d < 2^28, batch >= 0.
+ * Errors: BQD_EINVAL, BQD_ENULL, BQD_EALIGN, BQD_EOVERFLOW, BQD_EHIP. */
+int kv_int8_dot(const int8_t *K, const float *scales, int64_t R, int64_t d, const float *x,
+                float *y, int64_t batch, void *stream);
 
 /* Bytes of device workspace logits_sample needs: ceil(n / 4096) * k * 8.
  * Returns BQD_EINVAL (negative) for n or k outside logits_sample's range. */

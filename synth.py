@@ -16,6 +16,10 @@ Layouts (all host numpy arrays, C-contiguous):
 * FP8 head ("attention + tokenizer + sampling: the path to real text",
   "Step 1 done: F8 kernel"): ``w`` uint8 E4M3 codes ``[R][C]``, ``scale``
   uint8 E8M0 exponents ``[SR][SC]``, activation float32 ``[batch][C]``.
+* I8 matvec (same thread, "Step 4 done"): ``w`` int8 ``[R][C]``, ``scale``
+  uint8 E8M0 exponents ``[R][ceil(C / G)]``, activation float32 ``[batch][C]``.
+* Int8 key cache ("Inference engine, part 2", section 7): key vectors float32
+  ``[n][d]`` (to be quantized per vector), queries float32 ``[batch][d]``.
 
 Recipe (per case, a fresh ``numpy.random.default_rng(seed)``; draw order is
 fixed): 1. packed bytes or F8 weight bytes, uniform over all 256 byte values;
@@ -88,6 +92,22 @@ class F8Case:
     x: np.ndarray           # float32 [batch][C]
 
 
+@dataclasses.dataclass
+class I8Case:
+    R: int
+    C: int
+    G: int
+    w: np.ndarray           # int8 [R][C]
+    scale: np.ndarray       # uint8 [R][ceil(C / G)]
+    x: np.ndarray           # float32 [batch][C]
+
+
+@dataclasses.dataclass
+class KvCase:
+    v: np.ndarray           # float32 [n][d] key vectors to quantize
+    x: np.ndarray           # float32 [batch][d] queries
+
+
 def _random_bytes(rng: np.random.Generator, shape) -> np.ndarray:
     return rng.integers(0, 256, size=shape, dtype=np.uint8)
 
@@ -113,6 +133,27 @@ def make_f8(R: int, C: int, SR: int, SC: int, seed: int, batch: int = 1,
     return F8Case(R, C, SR, SC, w, scale, x)
 
 
+def make_i8(R: int, C: int, G: int, seed: int, batch: int = 1, exp_range=(120, 130)) -> I8Case:
+    """Weight bytes uniform over all 256 int8 values, E8M0 exponents uniform in
+    exp_range, activations N(0, 1); draw order: weights, scales, activations."""
+    rng = np.random.default_rng(seed)
+    w = _random_bytes(rng, (R, C)).view(np.int8)
+    ns = (C + G - 1) // G
+    scale = rng.integers(exp_range[0], exp_range[1] + 1, size=(R, ns), dtype=np.int64).astype(np.uint8)
+    x = rng.standard_normal((batch, C), dtype=np.float32)
+    return I8Case(R, C, G, w, scale, x)
+
+
+def make_kv(n: int, d: int, seed: int, batch: int = 1) -> KvCase:
+    """Key vectors N(0, 1) with a per-vector magnitude spread (each vector
+    times 2^k, k uniform in [-4, 4]), then the queries N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal((n, d), dtype=np.float32)
+    v *= np.ldexp(np.float32(1), rng.integers(-4, 5, (n, 1))).astype(np.float32)
+    x = rng.standard_normal((batch, d), dtype=np.float32)
+    return KvCase(v, x)
+
+
 # The five workloads.  Each is a list of (name, builder) pairs; a builder takes
 # no arguments and returns a case.  Seeds restart per case.
 C1 = CqShape(output=256, input=200, input_padded=256, group=64, bits=2)
@@ -123,6 +164,10 @@ C4 = CqShape(output=16384, input=4096, input_padded=4096, group=256, bits=4)
 HEAD = dict(R=246272, C=4096, SR=1924, SC=32)
 WKV = dict(R=512, C=4096, SR=4, SC=32)
 C3_GATHER_IDS = 4096
+# Beyond the five: an I8 head of the same shape as the F8 one with E8M0 scales
+# per 16 columns, and an int8 key cache of 4096 vectors of 128.
+I8_HEAD = dict(R=246272, C=4096, G=16)
+KV = dict(n=4096, d=128)
 
 
 def config_cases(i: int, batch8: bool = True):

@@ -124,6 +124,42 @@ def test_cq_prepare_matvec_argument_errors():
     assert L.cq_prepare_matvec(None, X, P, Y, 1, 0, 1, None) == ENULL
 
 
+@pytest.mark.parametrize("args,code", [
+    (dict(R=-1), EINVAL), (dict(C=0), EINVAL), (dict(G=0), EINVAL), (dict(G=4097), EINVAL),
+    (dict(batch=-1), EINVAL), (dict(R=1 << 30), EINVAL), (dict(C=1 << 28), EINVAL),
+    (dict(w=0), ENULL), (dict(scale=0), ENULL), (dict(x=0), ENULL), (dict(y=0), ENULL),
+    (dict(x=FAKE + 1), EALIGN), (dict(y=FAKE + 2), EALIGN),
+    (dict(batch=0), OK), (dict(R=0), OK),
+])
+def test_i8_matvec_rejects(args, code):
+    a = dict(w=FAKE, R=512, C=4096, scale=FAKE, G=16, x=FAKE, y=FAKE, batch=1)
+    a.update(args)
+    rc = bqd.lib().i8_matvec(a["w"], a["R"], a["C"], a["scale"], a["G"], a["x"], a["y"],
+                             a["batch"], None)
+    assert rc == code
+
+
+def test_kv_int8_argument_errors():
+    L = bqd.lib()
+    assert L.kv_quantize_int8(FAKE, -1, 128, FAKE, FAKE, None) == EINVAL
+    assert L.kv_quantize_int8(FAKE, 4, -1, FAKE, FAKE, None) == EINVAL
+    assert L.kv_quantize_int8(0, 4, 128, FAKE, FAKE, None) == ENULL
+    assert L.kv_quantize_int8(FAKE, 4, 128, 0, FAKE, None) == ENULL
+    assert L.kv_quantize_int8(FAKE, 4, 128, FAKE, 0, None) == ENULL
+    assert L.kv_quantize_int8(FAKE + 2, 4, 128, FAKE, FAKE, None) == EALIGN
+    assert L.kv_quantize_int8(FAKE, 4, 128, FAKE, FAKE + 1, None) == EALIGN
+    assert L.kv_quantize_int8(0, 0, 128, 0, 0, None) == OK
+    assert L.kv_int8_dot(FAKE, FAKE, -1, 128, FAKE, FAKE, 1, None) == EINVAL
+    assert L.kv_int8_dot(FAKE, FAKE, 4, 0, FAKE, FAKE, 1, None) == EINVAL
+    assert L.kv_int8_dot(FAKE, FAKE, 4, 128, FAKE, FAKE, -1, None) == EINVAL
+    assert L.kv_int8_dot(0, FAKE, 4, 128, FAKE, FAKE, 1, None) == ENULL
+    assert L.kv_int8_dot(FAKE, 0, 4, 128, FAKE, FAKE, 1, None) == ENULL
+    assert L.kv_int8_dot(FAKE, FAKE + 1, 4, 128, FAKE, FAKE, 1, None) == EALIGN
+    assert L.kv_int8_dot(FAKE, FAKE, 4, 128, FAKE + 2, FAKE, 1, None) == EALIGN
+    assert L.kv_int8_dot(FAKE, FAKE, 4, 128, FAKE, FAKE, 0, None) == OK
+    assert L.kv_int8_dot(0, 0, 0, 128, 0, 0, 1, None) == OK
+
+
 def test_cq_gather_argument_errors():
     L = bqd.lib()
     m = cq()

@@ -448,6 +448,99 @@ def test_f8_unaligned_weight_pointer():
 
 
 # -------------------------------------------------------------- empty calls
+# ----------------------------------------------------------------------- I8
+I8_CASES = [
+    (37, 80, 16, 1), (300, 4096, 16, 1), (100, 2048, 32, 3), (65, 128, 16, 2), (33, 16, 16, 1),
+    (17, 8192, 64, 1), (10, 100, 7, 2), (513, 1024, 16, 1), (3, 4096, 4096, 1),
+]
+
+
+@pytest.mark.parametrize("R,C,G,batch", I8_CASES)
+def test_i8_matvec_shapes(R, C, G, batch):
+    case = synth.make_i8(R, C, G, seed=600 + R, batch=batch)
+    got = bqd.i8_matvec(to_dev(case.w), to_dev(case.scale), to_dev(case.x), G).cpu().numpy()
+    ref, mag = oracle.i8_matvec(case.w, R, C, case.scale, G, case.x)
+    assert_tol(got, ref, mag, f"i8_matvec {R}x{C} G{G} batch {batch}")
+
+
+def test_i8_matvec_one_hot_all_codes():
+    """x = e_c: y[r] = w[r][c] * 2^(s - 127) exactly, every int8 value, through
+    the streaming kernel (C = 4096) and the generic one (C = 80)."""
+    for C, G in ((4096, 16), (80, 16)):
+        case = synth.make_i8(256, C, G, seed=7)
+        case.w[:, :] = np.arange(-128, 128, dtype=np.int64).astype(np.int8)[:, None]
+        for c in (0, 17, C - 1):
+            x = np.zeros((1, C), np.float32)
+            x[0, c] = 1.0
+            got = bqd.i8_matvec(to_dev(case.w), to_dev(case.scale), to_dev(x), G).cpu().numpy()[0]
+            ref, _ = oracle.i8_matvec(case.w, 256, C, case.scale, G, x[0])
+            assert np.array_equal(got, ref.astype(np.float32)), (C, c)
+
+
+def test_i8_matvec_unaligned_weights():
+    case = synth.make_i8(40, 4096, 16, seed=8)
+    buf = torch.zeros(case.w.size + 1, dtype=torch.int8, device=DEV)
+    buf[1:] = to_dev(case.w).reshape(-1)
+    got = bqd.i8_matvec(buf[1:].reshape(40, 4096), to_dev(case.scale), to_dev(case.x)).cpu().numpy()
+    ref, mag = oracle.i8_matvec(case.w, 40, 4096, case.scale, 16, case.x)
+    assert_tol(got, ref, mag, "i8_matvec unaligned")
+
+
+def test_i8_head_sampled_rows(cache):
+    """The I8 head at full size in the benchmark's launch configuration; the
+    oracle checks 16 row blocks (first, ragged last, random)."""
+    if "i8_head" not in cache:
+        print("[case] building i8 head 246272x4096 G16", flush=True)
+        cache["i8_head"] = synth.make_i8(**synth.I8_HEAD, seed=5)
+    case = cache["i8_head"]
+    got = bqd.i8_matvec(to_dev(case.w), to_dev(case.scale), to_dev(case.x), case.G).cpu().numpy()[0]
+    rng = np.random.default_rng(0)
+    starts = np.r_[0, case.R - 200, rng.integers(0, case.R - 128, 14)]
+    for st in starts:
+        n = 200 if st == case.R - 200 else 128
+        ref, mag = oracle.i8_matvec(case.w, case.R, case.C, case.scale, case.G, case.x[0], int(st), n)
+        assert_tol(got[st:st + n], ref, mag, f"i8 head rows [{st}, +{n})")
+
+
+# ------------------------------------------------------------- int8 key cache
+def check_kv_quantize(v):
+    v = np.ascontiguousarray(v, np.float32)
+    q, sc = bqd.kv_quantize_int8(to_dev(v))
+    qr, scr = oracle.store_int8(v)
+    assert np.array_equal(q.cpu().numpy(), qr)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), np.asarray(scr, np.float32).view(np.uint32))
+    return q, sc
+
+
+def test_kv_quantize_workload():
+    case = synth.make_kv(**synth.KV, seed=6)
+    check_kv_quantize(case.v)
+
+
+@pytest.mark.parametrize("d", [1, 63, 64, 65, 300, 4096])
+def test_kv_quantize_ragged(d):
+    rng = np.random.default_rng(d)
+    check_kv_quantize(rng.standard_normal((9, d)).astype(np.float32) * 3)
+
+
+def test_kv_quantize_special_vectors():
+    rows = [np.zeros(16), np.r_[127, 0.5, 1.5, 2.5, -2.5, -63.5, 63.5, -0.5, np.zeros(8)],
+            np.r_[1.0, np.nan, -3.0, np.zeros(13)], np.r_[1.0, np.inf, -3.0, np.zeros(13)],
+            np.r_[-np.inf, 2.0, np.zeros(14)], np.full(16, 3e-13), np.full(16, -1e30),
+            np.r_[-400.0, np.linspace(-1, 1, 15)]]
+    check_kv_quantize(np.stack(rows).astype(np.float32))
+
+
+@pytest.mark.parametrize("R,d,batch", [(4096, 128, 1), (300, 64, 2), (77, 100, 1), (40, 4096, 3), (5, 1, 1)])
+def test_kv_int8_dot(R, d, batch):
+    case = synth.make_kv(R, d, seed=700 + d, batch=batch)
+    q, sc = check_kv_quantize(case.v)
+    got = bqd.kv_int8_dot(q, sc, to_dev(case.x)).cpu().numpy().reshape(batch, R)
+    for b in range(batch):
+        ref, mag = oracle.int8_dot(q.cpu().numpy(), sc.cpu().numpy(), case.x[b])
+        assert_tol(got[b], ref, mag, f"kv_int8_dot {R}x{d} vector {b}")
+
+
 def test_empty_problems_are_no_ops():
     case = small_case(0)
     m = dev_matrix(case)
