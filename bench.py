@@ -177,6 +177,13 @@ def build_cases(torch, bqd, synth, hot):
     extras.append(Case("kv_int8_4096x128_dot",
                        [lambda: bqd.kv_int8_dot(qk, sk, xk, out=yk)],
                        nkv * dkv + 4 * nkv + 4 * dkv + 4 * nkv, nkv))
+    hm = synth.make_hmlp(**synth.HMLP, seed=7)
+    hn, hd1, hd2, hd3, hr, hu = (T(a) for a in (hm.n, hm.d1, hm.d2, hm.d3, hm.resid, hm.u))
+    ho = torch.empty_like(hn)
+    H = synth.HMLP["H"]
+    extras.append(Case("hadamard_mlp_512_to_2048",
+                       [lambda: bqd.hadamard_mlp(hn, H, hd1, hd2, hd3, hr, hu, out=ho)],
+                       4 * (3 * H + 4 * hn.numel()), hn.numel()))
     data = dict(c4=c4, c3=c3, head=hd, head_logits=yh)
     return cases, extras, data
 

@@ -20,6 +20,7 @@ Step 1):
   ("attention + tokenizer + sampling", Step 4)
 * ``kv_quantize_int8(v)``     storeInt8 per vector ("Inference engine, part 2" §7)
 * ``kv_int8_dot(K, scales, x)`` the scaled key dot against an int8 cache
+* ``hadamard_mlp(n, H, d1, d2, d3, resid, u)`` the Hadamard MLP (§8)
 """
 from __future__ import annotations
 
@@ -29,7 +30,7 @@ import os
 import torch
 
 __all__ = ["BqdError", "CqMatrix", "cq_prepare", "cq_matvec", "cq_prepare_matvec",
-           "cq_gather_rows", "f8_matvec", "i8_matvec", "kv_quantize_int8", "kv_int8_dot",
+           "cq_gather_rows", "f8_matvec", "i8_matvec", "kv_quantize_int8", "kv_int8_dot", "hadamard_mlp",
            "logits_sample", "logits_sample_workspace_bytes",
            "dbg_cq_unpack", "dbg_f16_decode", "dbg_f8_decode", "dbg_e8m0_decode", "lib",
            "LIB_PATH", "EXPORTS"]
@@ -39,7 +40,7 @@ LIB_PATH = os.path.join(_HERE, "libbqd.so")
 
 # Every symbol include/bqd.h declares.
 EXPORTS = ("cq_prepare", "cq_matvec", "cq_prepare_matvec", "cq_gather_rows", "f8_matvec",
-           "i8_matvec", "kv_quantize_int8", "kv_int8_dot", "logits_sample",
+           "i8_matvec", "kv_quantize_int8", "kv_int8_dot", "hadamard_mlp", "logits_sample",
            "logits_sample_workspace_bytes", "bqd_dbg_cq_unpack", "bqd_dbg_f16_decode",
            "bqd_dbg_f8_decode", "bqd_dbg_e8m0_decode", "bqd_status_string")
 
@@ -79,6 +80,7 @@ def lib():
                 ("i8_matvec", [P, I64, I64, P, I64, P, P, I64, P]),
                 ("kv_quantize_int8", [P, I64, I64, P, P, P]),
                 ("kv_int8_dot", [P, P, I64, I64, P, P, I64, P]),
+                ("hadamard_mlp", [P, I64, I64, P, P, P, P, P, P, I64, P]),
                 ("bqd_dbg_cq_unpack", [S, I64, P, P]),
                 ("bqd_dbg_f16_decode", [P, I64, P, P]),
                 ("bqd_dbg_f8_decode", [P, I64, P, P]),
@@ -294,6 +296,29 @@ def kv_int8_dot(K: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, out: tor
         raise ValueError("out has the wrong size")
     _call("kv_int8_dot", _ptr(K), _ptr(scales), R, d, _ptr(x), _ptr(out), batch,
           _stream(x, stream))
+    return out
+
+
+def hadamard_mlp(n: torch.Tensor, H: int, d1: torch.Tensor, d2: torch.Tensor, d3: torch.Tensor,
+                 resid: torch.Tensor, u: torch.Tensor = None, out: torch.Tensor = None,
+                 stream=None):
+    """n, resid, u float32 [batch][hidden]; d1, d2, d3 float32 [H] -> out [batch][hidden]."""
+    n = _dev(n, torch.float32, "n")
+    d1, d2, d3 = (_dev(t, torch.float32, nm) for t, nm in ((d1, "d1"), (d2, "d2"), (d3, "d3")))
+    resid = _dev(resid, torch.float32, "resid")
+    hidden = n.shape[-1]
+    batch = n.numel() // hidden if hidden else (n.shape[0] if n.dim() > 1 else 1)
+    if resid.shape != n.shape or (u is not None and u.shape != n.shape):
+        raise ValueError("resid and u must have n's shape")
+    if d1.numel() != H or d2.numel() != H or d3.numel() != H:
+        raise ValueError("d1, d2, d3 must have H entries")
+    if u is not None:
+        u = _dev(u, torch.float32, "u")
+    out = torch.empty_like(n) if out is None else _dev(out, torch.float32, "out")
+    if out.numel() != n.numel():
+        raise ValueError("out has the wrong size")
+    _call("hadamard_mlp", _ptr(n), hidden, int(H), _ptr(d1), _ptr(d2), _ptr(d3), _ptr(resid),
+          None if u is None else _ptr(u), _ptr(out), batch, _stream(n, stream))
     return out
 
 

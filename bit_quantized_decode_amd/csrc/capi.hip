@@ -68,6 +68,14 @@ int kv_int8_dot(const int8_t* K, const float* scales, int64_t R, int64_t d, cons
   return launch_kv_int8_dot(K, scales, R, d, x, y, batch, as_stream(stream));
 }
 
+int hadamard_mlp(const float* n, int64_t hidden, int64_t H, const float* d1, const float* d2,
+                 const float* d3, const float* resid, const float* u, float* out, int64_t batch,
+                 void* stream) {
+  int rc = check_hadamard_mlp(n, hidden, H, d1, d2, d3, resid, u, out, batch);
+  if (rc || batch == 0 || hidden == 0) return rc;
+  return launch_hadamard_mlp(n, hidden, H, d1, d2, d3, resid, u, out, batch, as_stream(stream));
+}
+
 int bqd_dbg_cq_unpack(const bqd_cq_matrix* m, int64_t row, uint8_t* idx, void* stream) {
   int rc = check_unpack(m, row, idx);
   if (rc) return rc;

@@ -46,7 +46,6 @@ __device__ __forceinline__ float scale_store(float v, double scale) {
 // Elements per lane of the wavefront transform: a wavefront spans one group
 // (64 * E = group) for groups of 64 and more, else 64 / group whole groups.
 inline int lane_elems(int64_t group) { return group >= 64 ? (int)(group / 64) : 1; }
-constexpr int ilog2_c(int v) { return v <= 1 ? 0 : 1 + ilog2_c(v / 2); }
 
 // ------------------------------------------------------------------ prepare
 // One wavefront per (vector, span of 64*E padded columns).

@@ -5,6 +5,9 @@
 
 namespace bqd {
 
+// log2 of a power of two, at compile time.
+constexpr int ilog2_c(int v) { return v <= 1 ? 0 : 1 + ilog2_c(v / 2); }
+
 // ---------------------------------------------------------------------------
 // Codebook index decode.  A 32-column chunk of a row occupies exactly BITS
 // dwords (4*BITS bytes) of the little-endian bit stream; index k sits at bit

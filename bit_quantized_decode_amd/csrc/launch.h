@@ -25,6 +25,9 @@ int launch_kv_quantize_int8(const float* v, int64_t n_vec, int64_t d, int8_t* q,
                             hipStream_t s);
 int launch_kv_int8_dot(const int8_t* K, const float* scales, int64_t R, int64_t d, const float* x,
                        float* y, int64_t batch, hipStream_t s);
+int launch_hadamard_mlp(const float* n, int64_t hidden, int64_t H, const float* d1,
+                        const float* d2, const float* d3, const float* resid, const float* u,
+                        float* out, int64_t batch, hipStream_t s);
 int launch_f16_decode(const uint16_t* codes, int64_t n, float* out, hipStream_t s);
 int launch_f8_decode(const uint8_t* codes, int64_t n, float* out, hipStream_t s);
 int launch_e8m0_decode(const uint8_t* codes, int64_t n, float* out, hipStream_t s);

@@ -154,6 +154,21 @@ int check_kv_dot(const int8_t* K, const float* scales, int64_t R, int64_t d, con
   return BQD_OK;
 }
 
+int check_hadamard_mlp(const float* n, int64_t hidden, int64_t H, const float* d1,
+                       const float* d2, const float* d3, const float* resid, const float* u,
+                       const float* out, int64_t batch) {
+  if (!is_pow2(H) || H > kMaxHadamard || hidden < 0 || hidden > H) return BQD_EINVAL;
+  if (batch < 0 || batch >= kMaxBatchBlocks) return BQD_EINVAL;
+  if (!mul_ok(batch, hidden, 4)) return BQD_EOVERFLOW;
+  if (batch == 0) return BQD_OK;
+  if (!d1 || !d2 || !d3) return BQD_ENULL;
+  if (hidden > 0 && (!n || !resid || !out)) return BQD_ENULL;
+  if (!aligned(n, 4) || !aligned(d1, 4) || !aligned(d2, 4) || !aligned(d3, 4) ||
+      !aligned(resid, 4) || !aligned(u, 4) || !aligned(out, 4))
+    return BQD_EALIGN;
+  return BQD_OK;
+}
+
 int check_unpack(const bqd_cq_matrix* m, int64_t row, const uint8_t* idx) {
   int rc = check_cq(m);
   if (rc) return rc;

@@ -26,6 +26,9 @@ int check_kv_quantize(const float* v, int64_t n_vec, int64_t d, const int8_t* q,
                       const float* scales);
 int check_kv_dot(const int8_t* K, const float* scales, int64_t R, int64_t d, const float* x,
                  const float* y, int64_t batch);
+int check_hadamard_mlp(const float* n, int64_t hidden, int64_t H, const float* d1,
+                       const float* d2, const float* d3, const float* resid, const float* u,
+                       const float* out, int64_t batch);
 int check_unpack(const bqd_cq_matrix* m, int64_t row, const uint8_t* idx);
 int check_decode(const void* codes, int64_t n, const float* out, int code_size);
 int64_t sample_workspace_need(int64_t n, int64_t k);  // or BQD_EINVAL
@@ -39,5 +42,7 @@ constexpr int64_t kMaxColumns = (int64_t)1 << 28;   // exclusive
 constexpr int64_t kMaxGroup = 1024;
 constexpr int64_t kMaxSampleLogits = (int64_t)1 << 20;  // inclusive
 constexpr int64_t kMaxSampleK = 64;
+constexpr int64_t kMaxHadamard = 16384;               // inclusive
+constexpr int64_t kMaxBatchBlocks = (int64_t)1 << 31;  // exclusive (one workgroup each)
 
 }  // namespace bqd

@@ -176,6 +176,26 @@ int kv_quantize_int8(const float *v, int64_t n_vec, int64_t d, int8_t *q, float 
 int kv_int8_dot(const int8_t *K, const float *scales, int64_t R, int64_t d, const float *x,
                 float *y, int64_t batch, void *stream);
 
+/* [P1] §8 "Hadamard MLP", from the normalized block input on (the page's
+ * zcrms normalization is not defined there and stays with the caller).  For
+ * each of `batch` vectors, with z of H = a power of two >= hidden elements:
+ *   z = n zero-padded to H;  z *= d1;  normalized FWHT;  z = silu(d2 * z);
+ *   normalized FWHT;  z *= d3;  out = resid + z[0 .. hidden)  (- u if u);
+ * where the normalized FWHT is the transform of cq_prepare over all H
+ * elements times 1/sqrt(H), silu(t) = t / (1 + exp(-t)), and every stored
+ * value rounds to fp32 while products, silu and the scale are formed in fp64
+ * (the page's Float32Array / JavaScript-number arithmetic).  The fp64 exp is
+ * the device library's, so a silu value may differ from another exp's in
+ * its last bit; outputs are held to 1e-5 * m + 1e-6 per element, m =
+ * |resid| + |u| + |d3| / sqrt(H) * sum |silu|.
+ *   n, resid, u, out: fp32 [batch][hidden] (u may be NULL)
+ *   d1, d2, d3:       fp32 [H], shared by the batch
+ * Requires H a power of two in [1, 16384], 0 <= hidden <= H, 0 <= batch < 2^31.
+ * Errors: BQD_EINVAL, BQD_ENULL, BQD_EALIGN, BQD_EOVERFLOW, BQD_EHIP. */
+int hadamard_mlp(const float *n, int64_t hidden, int64_t H, const float *d1, const float *d2,
+                 const float *d3, const float *resid, const float *u, float *out, int64_t batch,
+                 void *stream);
+
 /* Bytes of device workspace logits_sample needs: ceil(n / 4096) * k * 8.
  * Returns BQD_EINVAL (negative) for n or k outside logits_sample's range. */
 int64_t logits_sample_workspace_bytes(int64_t n, int64_t k);

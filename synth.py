@@ -20,6 +20,8 @@ Layouts (all host numpy arrays, C-contiguous):
   uint8 E8M0 exponents ``[R][ceil(C / G)]``, activation float32 ``[batch][C]``.
 * Int8 key cache ("Inference engine, part 2", section 7): key vectors float32
   ``[n][d]`` (to be quantized per vector), queries float32 ``[batch][d]``.
+* Hadamard MLP (same page, section 8): normalized input, residual and u
+  float32 ``[batch][hidden]``, diagonal scales d1, d2, d3 float32 ``[H]``.
 
 Recipe (per case, a fresh ``numpy.random.default_rng(seed)``; draw order is
 fixed): 1. packed bytes or F8 weight bytes, uniform over all 256 byte values;
@@ -108,6 +110,16 @@ class KvCase:
     x: np.ndarray           # float32 [batch][d] queries
 
 
+@dataclasses.dataclass
+class HmlpCase:
+    n: np.ndarray           # float32 [batch][hidden] normalized block input
+    d1: np.ndarray          # float32 [H]
+    d2: np.ndarray          # float32 [H]
+    d3: np.ndarray          # float32 [H]
+    resid: np.ndarray       # float32 [batch][hidden]
+    u: np.ndarray           # float32 [batch][hidden]
+
+
 def _random_bytes(rng: np.random.Generator, shape) -> np.ndarray:
     return rng.integers(0, 256, size=shape, dtype=np.uint8)
 
@@ -154,6 +166,17 @@ def make_kv(n: int, d: int, seed: int, batch: int = 1) -> KvCase:
     return KvCase(v, x)
 
 
+def make_hmlp(hidden: int, H: int, seed: int, batch: int = 1) -> HmlpCase:
+    """Hadamard MLP inputs: the normalized input, then d1, d2, d3, the
+    residual and u, all N(0, 1) float32, in that draw order."""
+    rng = np.random.default_rng(seed)
+    n = rng.standard_normal((batch, hidden), dtype=np.float32)
+    d1, d2, d3 = (rng.standard_normal(H, dtype=np.float32) for _ in range(3))
+    resid = rng.standard_normal((batch, hidden), dtype=np.float32)
+    u = rng.standard_normal((batch, hidden), dtype=np.float32)
+    return HmlpCase(n, d1, d2, d3, resid, u)
+
+
 # The five workloads.  Each is a list of (name, builder) pairs; a builder takes
 # no arguments and returns a case.  Seeds restart per case.
 C1 = CqShape(output=256, input=200, input_padded=256, group=64, bits=2)
@@ -168,6 +191,9 @@ C3_GATHER_IDS = 4096
 # per 16 columns, and an int8 key cache of 4096 vectors of 128.
 I8_HEAD = dict(R=246272, C=4096, G=16)
 KV = dict(n=4096, d=128)
+# The Hadamard MLP of a 512-wide block ("Inference engine, part 2", sections 7
+# and 8) padded to 2048.
+HMLP = dict(hidden=512, H=2048)
 
 
 def config_cases(i: int, batch8: bool = True):

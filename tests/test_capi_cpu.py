@@ -160,6 +160,28 @@ def test_kv_int8_argument_errors():
     assert L.kv_int8_dot(0, 0, 0, 128, 0, 0, 1, None) == OK
 
 
+def test_hadamard_mlp_argument_errors():
+    L = bqd.lib()
+
+    def call(n=FAKE, hidden=512, H=2048, d1=FAKE, d2=FAKE, d3=FAKE, resid=FAKE, u=0, out=FAKE,
+             batch=1):
+        return L.hadamard_mlp(n, hidden, H, d1, d2, d3, resid, u, out, batch, None)
+
+    assert call(H=3000) == EINVAL
+    assert call(H=32768) == EINVAL
+    assert call(H=0) == EINVAL
+    assert call(hidden=4096) == EINVAL
+    assert call(hidden=-1) == EINVAL
+    assert call(batch=-1) == EINVAL
+    assert call(batch=1 << 31) == EINVAL
+    assert call(d2=0) == ENULL
+    assert call(n=0) == ENULL
+    assert call(out=0) == ENULL
+    assert call(resid=FAKE + 2) == EALIGN
+    assert call(u=FAKE + 1) == EALIGN
+    assert call(batch=0) == OK
+
+
 def test_cq_gather_argument_errors():
     L = bqd.lib()
     m = cq()

@@ -541,6 +541,48 @@ def test_kv_int8_dot(R, d, batch):
         assert_tol(got[b], ref, mag, f"kv_int8_dot {R}x{d} vector {b}")
 
 
+# ------------------------------------------------------------- Hadamard MLP
+HMLP_CASES = [(512, 2048, 1, True), (10, 16, 3, True), (48, 64, 2, False), (100, 128, 1, True),
+              (200, 256, 2, False), (300, 512, 1, True), (1000, 1024, 1, False),
+              (4096, 8192, 1, True), (10000, 16384, 2, True), (1, 1, 2, False), (64, 4096, 1, True)]
+
+
+@pytest.mark.parametrize("hidden,H,batch,with_u", HMLP_CASES)
+def test_hadamard_mlp(hidden, H, batch, with_u):
+    case = synth.make_hmlp(hidden, H, seed=800 + H, batch=batch)
+    u = to_dev(case.u) if with_u else None
+    got = bqd.hadamard_mlp(to_dev(case.n), H, to_dev(case.d1), to_dev(case.d2), to_dev(case.d3),
+                           to_dev(case.resid), u).cpu().numpy()
+    same = 0
+    for b in range(batch):
+        ref, mag = oracle.hadamard_mlp(case.n[b], H, case.d1, case.d2, case.d3, case.resid[b],
+                                       case.u[b] if with_u else None)
+        ratio = np.abs(got[b].astype(np.float64) - ref) / (1e-5 * mag + 1e-6)
+        assert ratio.max() <= 1.0, (hidden, H, b, ratio.max())
+        same += int(np.sum(got[b].view(np.uint32) == ref.view(np.uint32)))
+    print(f"[tol] hadamard_mlp {hidden}/{H}: max ratio {ratio.max():.3g}; "
+          f"{same} of {batch * hidden} outputs bit-identical", flush=True)
+
+
+def test_hadamard_mlp_exact_closed_form():
+    """The pin's exact construction on the GPU: integer inputs, d2 = 2^12 sign(z1),
+    d3 = 2^-12, so every stage is exact and the result is bit-identical."""
+    rng = np.random.default_rng(36)
+    hidden, H = 48, 64
+    n = rng.integers(-3, 4, hidden).astype(np.float32)
+    d1 = rng.choice([-1.0, 1.0, 2.0, 0.5], H).astype(np.float32)
+    resid = rng.integers(-8, 9, hidden).astype(np.float32)
+    z = np.zeros(H)
+    z[:hidden] = n
+    z1 = (scipy.linalg.hadamard(H) / math.sqrt(H)) @ (d1.astype(np.float64) * z)
+    d2 = (np.where(z1 >= 0, 1.0, -1.0) * 4096.0 * (np.abs(z1) > 0)).astype(np.float32)
+    d3 = np.full(H, 2.0 ** -12, np.float32)
+    got = bqd.hadamard_mlp(to_dev(n[None]), H, to_dev(d1), to_dev(d2), to_dev(d3),
+                           to_dev(resid[None])).cpu().numpy()[0]
+    ref, _ = oracle.hadamard_mlp(n, H, d1, d2, d3, resid)
+    assert bits_eq(got, ref)
+
+
 def test_empty_problems_are_no_ops():
     case = small_case(0)
     m = dev_matrix(case)
