@@ -177,6 +177,22 @@ def build_cases(torch, bqd, synth, hot):
     extras.append(Case("kv_int8_4096x128_dot",
                        [lambda: bqd.kv_int8_dot(qk, sk, xk, out=yk)],
                        nkv * dkv + 4 * nkv + 4 * dkv + 4 * nkv, nkv))
+    # three CQ4 2048 x 512 matrices (group 128) on one activation: one
+    # fused launch, against three separate prepare+matvec calls
+    tri = [synth.make_cq(synth.C2_3.__class__(2048, 512, 512, 128, 4), seed=20 + j) for j in range(3)]
+    tri_m = [bqd.CqMatrix(T(c.packed), T(c.norms.view(np.int16)), T(c.codebook), output=2048,
+                          input=512, input_padded=512, group=128, bits=4) for c in tri]
+    tri_x = T(tri[0].x[0])
+    tri_p = torch.empty(512, device=dev)
+    tri_y = [torch.empty(2048, device=dev) for _ in range(3)]
+    tri_bytes = 3 * 2048 * (256 + 8) + 4 * 512 + 4 * 512 + 3 * 4 * 2048
+    extras.append(Case("cq4_3x2048x512_prepare_matvec_multi",
+                       [lambda: bqd.cq_prepare_matvec_multi(tri_m, tri_x, prepared=tri_p, outs=tri_y)],
+                       tri_bytes, 3 * 2048))
+    extras.append(Case("cq4_3x2048x512_prepare_matvec_separate",
+                       [lambda: [bqd.cq_prepare_matvec(m, tri_x[None], prepared=tri_p[None], out=y[None])
+                                 for m, y in zip(tri_m, tri_y)]],
+                       tri_bytes, 3 * 2048))
     hm = synth.make_hmlp(**synth.HMLP, seed=7)
     hn, hd1, hd2, hd3, hr, hu = (T(a) for a in (hm.n, hm.d1, hm.d2, hm.d3, hm.resid, hm.u))
     ho = torch.empty_like(hn)
@@ -391,6 +407,8 @@ def main():
             rows_per_s=round(c.rows / (ms.mean() * 1e-3), 1) if c.rows else None)
         if c in cases:
             per_case[c.name] = rec
+        elif c.name.startswith("cq4_3x"):
+            extras[c.name] = dict(rec, note="not part of the step: several matrices on one activation")
         elif c.name.startswith("cq4_"):
             extras[c.name] = dict(rec, note="not part of the step: the same stage as two calls")
         else:

@@ -14,6 +14,8 @@ Step 1):
 * ``cq_prepare(m, x)``        zero-pad, per-group FWHT, times 1/sqrt(group)
 * ``cq_matvec(m, prepared)``  packed-row codebook dot with fp16 group norms
 * ``cq_prepare_matvec(m, x)`` both in one call (the page's cqMatvec(matrix, x))
+* ``cq_matvec_multi(ms, prepared)`` / ``cq_prepare_matvec_multi(ms, x)``
+  several matrices (row ranges) on one activation, §6
 * ``cq_gather_rows(m, rows)`` dense rows: decode x norm, normalized FWHT
 * ``f8_matvec(w, scale, x)``  E4M3 weights with E8M0 block scales
 * ``i8_matvec(w, scale, x, G)`` int8 weights with E8M0 scales per G columns
@@ -30,6 +32,7 @@ import os
 import torch
 
 __all__ = ["BqdError", "CqMatrix", "cq_prepare", "cq_matvec", "cq_prepare_matvec",
+           "cq_matvec_multi", "cq_prepare_matvec_multi",
            "cq_gather_rows", "f8_matvec", "i8_matvec", "kv_quantize_int8", "kv_int8_dot", "hadamard_mlp",
            "logits_sample", "logits_sample_workspace_bytes",
            "dbg_cq_unpack", "dbg_f16_decode", "dbg_f8_decode", "dbg_e8m0_decode", "lib",
@@ -39,7 +42,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbqd.so")
 
 # Every symbol include/bqd.h declares.
-EXPORTS = ("cq_prepare", "cq_matvec", "cq_prepare_matvec", "cq_gather_rows", "f8_matvec",
+EXPORTS = ("cq_prepare", "cq_matvec", "cq_prepare_matvec", "cq_matvec_multi",
+           "cq_prepare_matvec_multi", "cq_gather_rows", "f8_matvec",
            "i8_matvec", "kv_quantize_int8", "kv_int8_dot", "hadamard_mlp", "logits_sample",
            "logits_sample_workspace_bytes", "bqd_dbg_cq_unpack", "bqd_dbg_f16_decode",
            "bqd_dbg_f8_decode", "bqd_dbg_e8m0_decode", "bqd_status_string")
@@ -75,6 +79,8 @@ def lib():
                 ("cq_prepare", [S, P, P, I64, P]),
                 ("cq_matvec", [S, P, P, I64, I64, I64, P]),
                 ("cq_prepare_matvec", [S, P, P, P, I64, I64, I64, P]),
+                ("cq_matvec_multi", [S, I64, P, P, P, P, P]),
+                ("cq_prepare_matvec_multi", [S, I64, P, P, P, P, P, P]),
                 ("cq_gather_rows", [S, P, I64, P, P]),
                 ("f8_matvec", [P, I64, I64, P, I64, I64, P, P, I64, P]),
                 ("i8_matvec", [P, I64, I64, P, I64, P, P, I64, P]),
@@ -209,6 +215,45 @@ def cq_prepare_matvec(m: CqMatrix, x: torch.Tensor, prepared: torch.Tensor = Non
     _call("cq_prepare_matvec", m.ref, _ptr(x), _ptr(prepared), _ptr(out), batch, int(row_begin),
           row_count, _stream(x, stream))
     return prepared, out
+
+
+def _multi_args(ms, ranges, outs, device):
+    n = len(ms)
+    ranges = [(0, m.output) for m in ms] if ranges is None else [(int(a), int(b)) for a, b in ranges]
+    if len(ranges) != n:
+        raise ValueError("one row range per matrix")
+    outs = [torch.empty(rc, dtype=torch.float32, device=device) for _, rc in ranges] \
+        if outs is None else [_dev(o, torch.float32, "out") for o in outs]
+    for o, (_, rc) in zip(outs, ranges):
+        if o.numel() != rc:
+            raise ValueError("an output has the wrong size")
+    descs = (_CqStruct * n)(*[m._s for m in ms])
+    rb = (ctypes.c_int64 * n)(*[a for a, _ in ranges])
+    rcs = (ctypes.c_int64 * n)(*[b for _, b in ranges])
+    ys = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
+    return n, descs, rb, rcs, ys, outs
+
+
+def cq_matvec_multi(ms, prepared: torch.Tensor, ranges=None, outs=None, stream=None):
+    """Several CqMatrix objects (row ranges [(row_begin, row_count)]) on one
+    prepared vector float32 [input_padded] -> list of float32 [row_count]."""
+    prepared = _dev(prepared, torch.float32, "prepared")
+    n, descs, rb, rcs, ys, outs = _multi_args(ms, ranges, outs, prepared.device)
+    _call("cq_matvec_multi", descs, n, rb, rcs, _ptr(prepared), ys, _stream(prepared, stream))
+    return outs
+
+
+def cq_prepare_matvec_multi(ms, x: torch.Tensor, prepared: torch.Tensor = None, ranges=None,
+                            outs=None, stream=None):
+    """cq_matvec_multi on the raw activation x float32 [input]; returns
+    (prepared float32 [input_padded], list of outputs)."""
+    x = _dev(x, torch.float32, "x")
+    prepared = torch.empty(ms[0].input_padded, dtype=torch.float32, device=x.device) \
+        if prepared is None else _dev(prepared, torch.float32, "prepared")
+    n, descs, rb, rcs, ys, outs = _multi_args(ms, ranges, outs, x.device)
+    _call("cq_prepare_matvec_multi", descs, n, rb, rcs, _ptr(x), _ptr(prepared), ys,
+          _stream(x, stream))
+    return prepared, outs
 
 
 def cq_gather_rows(m: CqMatrix, rows: torch.Tensor, out: torch.Tensor = None, stream=None):

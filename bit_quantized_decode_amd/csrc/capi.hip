@@ -33,6 +33,25 @@ int cq_prepare_matvec(const bqd_cq_matrix* m, const float* x, float* prepared, f
                                   as_stream(stream));
 }
 
+int cq_matvec_multi(const bqd_cq_matrix* ms, int64_t n, const int64_t* row_begin,
+                    const int64_t* row_count, const float* prepared, float* const* ys,
+                    void* stream) {
+  int64_t rb[kMaxMulti], rc[kMaxMulti];
+  int rc0 = check_matvec_multi(ms, n, row_begin, row_count, false, nullptr, prepared, ys, rb, rc);
+  if (rc0) return rc0;
+  return launch_cq_matvec_multi(ms, n, rb, rc, false, nullptr, const_cast<float*>(prepared), ys,
+                                as_stream(stream));
+}
+
+int cq_prepare_matvec_multi(const bqd_cq_matrix* ms, int64_t n, const int64_t* row_begin,
+                            const int64_t* row_count, const float* x, float* prepared,
+                            float* const* ys, void* stream) {
+  int64_t rb[kMaxMulti], rc[kMaxMulti];
+  int rc0 = check_matvec_multi(ms, n, row_begin, row_count, true, x, prepared, ys, rb, rc);
+  if (rc0) return rc0;
+  return launch_cq_matvec_multi(ms, n, rb, rc, true, x, prepared, ys, as_stream(stream));
+}
+
 int cq_gather_rows(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, float* out,
                    void* stream) {
   int rc = check_gather(m, rows, n, out);

@@ -456,12 +456,37 @@ __device__ __forceinline__ uint32_t ring_word(const typename RingLoad<BPL>::T& v
   if constexpr (BPL == 4) return v; else return v[t];
 }
 
-template <int BPL, int S, int E>
-__global__ __launch_bounds__(kRingThreads) void cq_matvec_ring(
-    const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
-    const float* __restrict__ codebook, const float* __restrict__ act,
-    float* __restrict__ prepared_out, float* __restrict__ y, int64_t row_bytes, int log2_group,
-    int rows, int input, double scale, int x_vec) {
+// One launch can cover several matrices of the same shape class that read
+// one activation ([P1] §6: one prepared vector for phiPre, phiPost and
+// phiResidual, each a row range of its matrix): workgroups [end[k-1], end[k])
+// belong to matrix k.
+// The arguments are one kernel-argument block: the shared fields, then one
+// entry per matrix, contiguous, so a single-matrix launch reads its
+// arguments in one scalar round trip from two cache lines, and a
+// several-matrix launch reads every entry in one round trip too.
+constexpr int kRingMaxMats = 4;
+struct RingMat {
+  const uint8_t* packed;     // first row of the range
+  const uint16_t* norms;     // its norms
+  const float* codebook;
+  float* y;                  // [rows]
+  int64_t row_bytes;
+  int32_t rows;
+  int32_t block_end;         // one past this matrix's last workgroup
+};
+struct RingArgs {
+  const float* act;          // prepared vector, or the raw input (fused prepare)
+  float* prepared_out;       // fused prepare: workgroup 0 stores the prepared vector
+  int32_t log2_group;
+  int32_t input;             // unpadded width (fused prepare)
+  int32_t x_vec;             // fused prepare: unpadded, 16-byte aligned input
+  int32_t pad;
+  double scale;              // 1 / sqrt(group)
+  RingMat m[kRingMaxMats];
+};
+
+template <int BPL, int S, int E, bool MULTI>
+__global__ __launch_bounds__(kRingThreads) void cq_matvec_ring(const RingArgs args) {
   constexpr int C = 128 * S * BPL;   // input_padded
   constexpr int CPL = 2 * BPL;       // columns per lane
   constexpr int AST = CPL + 4;       // padded floats per lane chunk in LDS
@@ -472,9 +497,43 @@ __global__ __launch_bounds__(kRingThreads) void cq_matvec_ring(
   __shared__ __align__(16) float tab[kPairTableFloats];
   __shared__ __align__(16) float act_s[64 * S * AST];
   __shared__ float part[S][RPB];
+  // this workgroup's matrix: entry 0 for a single matrix; otherwise every
+  // entry is read in the same round trip (the values are made opaque so the
+  // selection cannot turn into a second, dependent load)
+  const float* __restrict__ act = args.act;
+  float* __restrict__ prepared_out = args.prepared_out;
+  RingMat mat = args.m[0];
+  int block0 = 0;
+  int log2_group = args.log2_group;
+  if constexpr (MULTI) {
+    RingMat mk[kRingMaxMats];
+#pragma unroll
+    for (int k = 1; k < kRingMaxMats; ++k) mk[k] = args.m[k];
+    asm volatile("" : "+s"(mat.packed), "+s"(mat.norms), "+s"(mat.codebook), "+s"(mat.y),
+                 "+s"(mat.row_bytes), "+s"(mat.rows), "+s"(mat.block_end), "+s"(log2_group));
+    int prev_end = mat.block_end;
+#pragma unroll
+    for (int k = 1; k < kRingMaxMats; ++k) {
+      asm volatile("" : "+s"(mk[k].packed), "+s"(mk[k].norms), "+s"(mk[k].codebook), "+s"(mk[k].y),
+                   "+s"(mk[k].row_bytes), "+s"(mk[k].rows), "+s"(prev_end));
+      if ((int)blockIdx.x >= prev_end) {
+        mat = mk[k];
+        block0 = prev_end;
+      }
+      prev_end = mk[k].block_end;
+    }
+  }
+  const uint8_t* __restrict__ packed = mat.packed;
+  const uint16_t* __restrict__ norms = mat.norms;
+  const float* __restrict__ codebook = mat.codebook;
+  float* __restrict__ y = mat.y;
+  const int64_t row_bytes = mat.row_bytes;
+  const int rows = mat.rows;
+  const int input = args.input, x_vec = args.x_vec;
+  const double scale = args.scale;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sl = wave % S, rs = wave / S;
-  const int wg0 = (int)blockIdx.x * RPB;
+  const int wg0 = ((int)blockIdx.x - block0) * RPB;
   const int row0 = wg0 + rs * kRingRows;
   // loads in the order they are needed: codebook (table), activations,
   // norms, then the first DR rows of weights
@@ -1141,32 +1200,60 @@ RingShape ring_shape(const bqd_cq_matrix* m) {
   return r;
 }
 
+// The ring kernel over up to kRingMaxMats row ranges of matrices that share
+// the ring shape r, input width and group (ms[0] gives those).
 template <int BPL, int S, int E>
-int launch_ring_t(const bqd_cq_matrix* m, const float* act, float* prepared_out, float* y,
-                  int64_t row_begin, int64_t row_count, hipStream_t s) {
+int launch_ring_t(const bqd_cq_matrix* const* ms, const int64_t* row_begin,
+                  const int64_t* row_count, float* const* ys, int n, const float* act,
+                  float* prepared_out, hipStream_t s) {
   constexpr int RPB = (16 / S) * kRingRows;
-  const int64_t grid = (row_count + RPB - 1) / RPB;
-  const int x_vec = E > 0 && m->input == m->input_padded && is_aligned(act, 16);
-  hipLaunchKernelGGL((cq_matvec_ring<BPL, S, E>), dim3((unsigned)grid), dim3(kRingThreads), 0, s,
-                     m->packed + row_begin * m->row_bytes,
-                     m->norms + row_begin * (m->input_padded / m->group), m->codebook, act,
-                     prepared_out, y, m->row_bytes, ilog2(m->group), (int)row_count,
-                     (int)m->input, 1.0 / std::sqrt((double)m->group), x_vec);
+  const bqd_cq_matrix* m0 = ms[0];
+  RingArgs a{};
+  int64_t blocks = 0;
+  for (int k = 0; k < kRingMaxMats; ++k) a.m[k].block_end = INT32_MAX;
+  for (int k = 0; k < n; ++k) {
+    const bqd_cq_matrix* m = ms[k];
+    blocks += (row_count[k] + RPB - 1) / RPB;
+    a.m[k] = RingMat{m->packed + row_begin[k] * m->row_bytes,
+                     m->norms + row_begin[k] * (m->input_padded / m->group), m->codebook, ys[k],
+                     m->row_bytes, (int32_t)row_count[k], (int32_t)blocks};
+  }
+  a.act = act;
+  a.prepared_out = prepared_out;
+  a.log2_group = ilog2(m0->group);
+  a.input = (int32_t)m0->input;
+  a.x_vec = E > 0 && m0->input == m0->input_padded && is_aligned(act, 16);
+  a.scale = 1.0 / std::sqrt((double)m0->group);
+  if (n == 1)
+    hipLaunchKernelGGL((cq_matvec_ring<BPL, S, E, false>), dim3((unsigned)blocks),
+                       dim3(kRingThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((cq_matvec_ring<BPL, S, E, true>), dim3((unsigned)blocks),
+                       dim3(kRingThreads), 0, s, a);
   return launch_status();
 }
 
 // E: 0 for a prepared activation, else the transform's elements per lane.
 template <int E>
-int launch_ring(const bqd_cq_matrix* m, RingShape r, const float* act, float* prepared_out,
-                float* y, int64_t row_begin, int64_t row_count, hipStream_t s) {
-  if (r.bpl == 4) return launch_ring_t<4, 1, E>(m, act, prepared_out, y, row_begin, row_count, s);
-  if (r.bpl == 8) return launch_ring_t<8, 1, E>(m, act, prepared_out, y, row_begin, row_count, s);
+int launch_ring(const bqd_cq_matrix* const* ms, const int64_t* row_begin, const int64_t* row_count,
+                float* const* ys, int n, RingShape r, const float* act, float* prepared_out,
+                hipStream_t s) {
+#define RING_ARGS ms, row_begin, row_count, ys, n, act, prepared_out, s
+  if (r.bpl == 4) return launch_ring_t<4, 1, E>(RING_ARGS);
+  if (r.bpl == 8) return launch_ring_t<8, 1, E>(RING_ARGS);
   switch (r.s) {
-    case 1: return launch_ring_t<16, 1, E>(m, act, prepared_out, y, row_begin, row_count, s);
-    case 2: return launch_ring_t<16, 2, E>(m, act, prepared_out, y, row_begin, row_count, s);
-    case 4: return launch_ring_t<16, 4, E>(m, act, prepared_out, y, row_begin, row_count, s);
+    case 1: return launch_ring_t<16, 1, E>(RING_ARGS);
+    case 2: return launch_ring_t<16, 2, E>(RING_ARGS);
+    case 4: return launch_ring_t<16, 4, E>(RING_ARGS);
   }
+#undef RING_ARGS
   return BQD_EINVAL;  // unreachable: ring_shape() only returns instantiated shapes
+}
+
+template <int E>
+int launch_ring1(const bqd_cq_matrix* m, RingShape r, const float* act, float* prepared_out,
+                 float* y, int64_t row_begin, int64_t row_count, hipStream_t s) {
+  return launch_ring<E>(&m, &row_begin, &row_count, &y, 1, r, act, prepared_out, s);
 }
 
 int run_b1(const bqd_cq_matrix* m, FastShape f, const float* prepared, float* y,
@@ -1249,7 +1336,7 @@ int launch_cq_matvec(const bqd_cq_matrix* m, const float* prepared, float* y, in
   if (batch == 1) {
     const RingShape r = ring_shape(m);
     if (r.bpl && is_aligned(prepared, 16))
-      return launch_ring<0>(m, r, prepared, nullptr, y, row_begin, row_count, s);
+      return launch_ring1<0>(m, r, prepared, nullptr, y, row_begin, row_count, s);
   }
   if (!fast_ok(m)) return launch_generic(m, prepared, y, batch, row_begin, row_count, s);
   const int64_t n_chunk = m->input_padded / 32;
@@ -1298,15 +1385,70 @@ int launch_cq_prepare_matvec(const bqd_cq_matrix* m, const float* x, float* prep
     const RingShape r = ring_shape(m);
     if (r.bpl) {
       switch (lane_elems(m->group)) {
-        case 1: return launch_ring<1>(m, r, x, prepared, y, row_begin, row_count, s);
-        case 2: return launch_ring<2>(m, r, x, prepared, y, row_begin, row_count, s);
-        case 4: return launch_ring<4>(m, r, x, prepared, y, row_begin, row_count, s);
+        case 1: return launch_ring1<1>(m, r, x, prepared, y, row_begin, row_count, s);
+        case 2: return launch_ring1<2>(m, r, x, prepared, y, row_begin, row_count, s);
+        case 4: return launch_ring1<4>(m, r, x, prepared, y, row_begin, row_count, s);
       }
     }
   }
   const int rc = launch_cq_prepare(m, x, prepared, batch, s);
   if (rc || row_count == 0) return rc;
   return launch_cq_matvec(m, prepared, y, batch, row_begin, row_count, s);
+}
+
+// [P1] §6: several matrices, each a row range, on one activation.  Matrices
+// on a common ring shape share launches (up to kRingMaxMats each); with
+// `x` the first launch also prepares the activation in every workgroup and
+// stores it, later ones read it back.  Anything else: the prepare (with x),
+// then one cq_matvec per matrix.  Arguments arrive validated: one vector,
+// equal input_padded and group (and input with x).
+int launch_cq_matvec_multi(const bqd_cq_matrix* ms, int64_t n, const int64_t* row_begin,
+                           const int64_t* row_count, bool with_x, const float* x,
+                           float* prepared, float* const* ys, hipStream_t s) {
+  const bqd_cq_matrix* sel[64];
+  int64_t rb[64], rc[64];
+  float* yy[64];
+  int k_n = 0;
+  for (int64_t k = 0; k < n; ++k) {
+    if (row_count[k] == 0) continue;
+    sel[k_n] = &ms[k];
+    rb[k_n] = row_begin[k];
+    rc[k_n] = row_count[k];
+    yy[k_n] = ys[k];
+    ++k_n;
+  }
+  RingShape r = k_n ? ring_shape(sel[0]) : RingShape{0, 0};
+  for (int k = 1; k < k_n && r.bpl; ++k) {
+    const RingShape rk = ring_shape(sel[k]);
+    if (rk.bpl != r.bpl || rk.s != r.s) r = {0, 0};
+  }
+  const int e = lane_elems(ms[0].group);
+  if (r.bpl && is_aligned(prepared, 16) && (!with_x || e <= 4)) {
+    for (int k0 = 0; k0 < k_n; k0 += kRingMaxMats) {
+      const int nk = std::min(kRingMaxMats, k_n - k0);
+      int rc2 = BQD_EINVAL;
+      if (with_x && k0 == 0) {
+        switch (e) {
+          case 1: rc2 = launch_ring<1>(sel, rb, rc, yy, nk, r, x, prepared, s); break;
+          case 2: rc2 = launch_ring<2>(sel, rb, rc, yy, nk, r, x, prepared, s); break;
+          case 4: rc2 = launch_ring<4>(sel, rb, rc, yy, nk, r, x, prepared, s); break;
+        }
+      } else {
+        rc2 = launch_ring<0>(sel + k0, rb + k0, rc + k0, yy + k0, nk, r, prepared, nullptr, s);
+      }
+      if (rc2) return rc2;
+    }
+    if (k_n) return BQD_OK;
+  }
+  if (with_x) {
+    const int rc2 = launch_cq_prepare(&ms[0], x, prepared, 1, s);
+    if (rc2) return rc2;
+  }
+  for (int k = 0; k < k_n; ++k) {
+    const int rc2 = launch_cq_matvec(sel[k], prepared, yy[k], 1, rb[k], rc[k], s);
+    if (rc2) return rc2;
+  }
+  return BQD_OK;
 }
 
 // ------------------------------------------------------------- unpack probe

@@ -13,6 +13,9 @@ int launch_cq_matvec(const bqd_cq_matrix* m, const float* prepared, float* y, in
                      int64_t row_begin, int64_t row_count, hipStream_t s);
 int launch_cq_prepare_matvec(const bqd_cq_matrix* m, const float* x, float* prepared, float* y,
                              int64_t batch, int64_t row_begin, int64_t row_count, hipStream_t s);
+int launch_cq_matvec_multi(const bqd_cq_matrix* ms, int64_t n, const int64_t* row_begin,
+                           const int64_t* row_count, bool with_x, const float* x,
+                           float* prepared, float* const* ys, hipStream_t s);
 int launch_cq_gather(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, float* out,
                      hipStream_t s);
 int launch_cq_unpack(const bqd_cq_matrix* m, int64_t row, uint8_t* idx, hipStream_t s);

@@ -96,6 +96,43 @@ int check_prepare_matvec(const bqd_cq_matrix* m, const float* x, const float* pr
   return BQD_OK;
 }
 
+int check_matvec_multi(const bqd_cq_matrix* ms, int64_t n, const int64_t* row_begin,
+                       const int64_t* row_count, bool with_x, const float* x,
+                       const float* prepared, float* const* ys, int64_t* rb, int64_t* rc) {
+  if (!ms || !ys) return BQD_ENULL;
+  if (n < 1 || n > kMaxMulti) return BQD_EINVAL;
+  for (int64_t k = 0; k < n; ++k) {
+    rb[k] = row_begin ? row_begin[k] : 0;
+    rc[k] = row_count ? row_count[k] : ms[k].output - rb[k];
+    int rc_k = check_matvec(&ms[k], prepared, ys[k], 1, rb[k], rc[k]);
+    if (rc_k) return rc_k;
+    if (ms[k].input_padded != ms[0].input_padded || ms[k].group != ms[0].group ||
+        (with_x && ms[k].input != ms[0].input))
+      return BQD_EINVAL;
+  }
+  if (with_x) {
+    int rcp = check_prepare(&ms[0], x, prepared, 1);
+    if (rcp) return rcp;
+  }
+  if (!prepared) return BQD_ENULL;
+  if (!aligned(prepared, 4)) return BQD_EALIGN;
+  // no output may overlap the activation it reads (or, with x, the input)
+  const char* pa = (const char*)prepared;
+  const char* pb = pa + ms[0].input_padded * 4;
+  for (int64_t k = 0; k < n; ++k) {
+    if (rc[k] == 0) continue;
+    const char* ya = (const char*)ys[k];
+    const char* yb = ya + rc[k] * 4;
+    if (ya < pb && pa < yb) return BQD_EINVAL;
+    if (x) {
+      const char* xa = (const char*)x;
+      const char* xb = xa + ms[0].input * 4;
+      if (ya < xb && xa < yb) return BQD_EINVAL;
+    }
+  }
+  return BQD_OK;
+}
+
 int check_gather(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, const float* out) {
   int rc = check_cq(m);
   if (rc) return rc;

@@ -17,6 +17,11 @@ int check_matvec(const bqd_cq_matrix* m, const float* prepared, const float* y, 
                  int64_t row_begin, int64_t row_count);
 int check_prepare_matvec(const bqd_cq_matrix* m, const float* x, const float* prepared,
                          const float* y, int64_t batch, int64_t row_begin, int64_t row_count);
+// Several matrices on one vector: n in [1, kMaxMulti]; row_begin / row_count
+// may be NULL (0 / the rest of each matrix) and are resolved into rb / rc.
+int check_matvec_multi(const bqd_cq_matrix* ms, int64_t n, const int64_t* row_begin,
+                       const int64_t* row_count, bool with_x, const float* x,
+                       const float* prepared, float* const* ys, int64_t* rb, int64_t* rc);
 int check_gather(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, const float* out);
 int check_f8(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
              int64_t SC, const float* x, const float* y, int64_t batch);
@@ -42,7 +47,8 @@ constexpr int64_t kMaxColumns = (int64_t)1 << 28;   // exclusive
 constexpr int64_t kMaxGroup = 1024;
 constexpr int64_t kMaxSampleLogits = (int64_t)1 << 20;  // inclusive
 constexpr int64_t kMaxSampleK = 64;
-constexpr int64_t kMaxHadamard = 16384;               // inclusive
+constexpr int64_t kMaxHadamard = 16384;
+constexpr int64_t kMaxMulti = 64;               // inclusive
 constexpr int64_t kMaxBatchBlocks = (int64_t)1 << 31;  // exclusive (one workgroup each)
 
 }  // namespace bqd

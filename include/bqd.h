@@ -113,6 +113,32 @@ int cq_matvec(const bqd_cq_matrix *m, const float *prepared, float *y,
 int cq_prepare_matvec(const bqd_cq_matrix *m, const float *x, float *prepared, float *y,
                       int64_t batch, int64_t row_begin, int64_t row_count, void *stream);
 
+/* [P1] §6: several matrices on one activation vector (phiPre, phiPost and
+ * phiResidual from one normalized input), each restricted to a row range:
+ * for k < n, ys[k][i] for i < row_count[k] is row row_begin[k] + i of
+ * cq_matvec(&ms[k], prepared, ...) at batch 1, bit for bit.  Matrices of
+ * one shape class share kernel launches (up to 4 per launch on the batch-1
+ * 4-bit shapes of cq_prepare_matvec); the rest take one launch each.
+ *   ms:        host array of n descriptors, equal input_padded and group
+ *   row_begin, row_count: host arrays of n (NULL: 0, and the rest of each matrix)
+ *   prepared:  fp32 [input_padded] (the output of cq_prepare)
+ *   ys:        host array of n device pointers, ys[k] fp32 [row_count[k]]
+ * Requires 1 <= n <= 64.  Errors: as cq_matvec for every matrix, BQD_EINVAL
+ * for unequal shapes or an output overlapping prepared, BQD_ENULL. */
+int cq_matvec_multi(const bqd_cq_matrix *ms, int64_t n, const int64_t *row_begin,
+                    const int64_t *row_count, const float *prepared, float *const *ys,
+                    void *stream);
+
+/* cq_matvec_multi on the raw activation x (fp32 [ms[0].input]; all
+ * matrices of equal input too): prepared receives cq_prepare's output and
+ * the outputs are those of cq_prepare followed by cq_matvec_multi, bit for
+ * bit.  On the fused shapes of cq_prepare_matvec the prepare runs inside the
+ * first launch.  Errors: those of cq_prepare and cq_matvec_multi, and
+ * BQD_EINVAL when an output overlaps x. */
+int cq_prepare_matvec_multi(const bqd_cq_matrix *ms, int64_t n, const int64_t *row_begin,
+                            const int64_t *row_count, const float *x, float *prepared,
+                            float *const *ys, void *stream);
+
 /* [P1] "Row gather": for i < n, out[i][c] for c < input is the dense row
  * rows[i]: per group, codebook value times norm (fp32 product), the
  * unnormalized transform as in cq_prepare, times 1/sqrt(group), keeping the

@@ -182,6 +182,37 @@ def test_hadamard_mlp_argument_errors():
     assert call(batch=0) == OK
 
 
+def test_cq_matvec_multi_argument_errors():
+    L = bqd.lib()
+    P = FAKE << 4
+
+    def call(mats, rb=None, rc=None, ys=None, prepared=P, x=None):
+        n = len(mats)
+        arr = (bqd._CqStruct * max(n, 1))(*mats)
+        rbs = None if rb is None else (ctypes.c_int64 * n)(*rb)
+        rcs = None if rc is None else (ctypes.c_int64 * n)(*rc)
+        yv = (ctypes.c_void_p * max(n, 1))(*(ys or [FAKE << (8 + k) for k in range(n)]))
+        if x is None:
+            return L.cq_matvec_multi(arr, n, rbs, rcs, prepared, yv, None)
+        return L.cq_prepare_matvec_multi(arr, n, rbs, rcs, x, prepared, yv, None)
+
+    m = cq()
+    assert call([]) == EINVAL
+    assert call([m] * 65) == EINVAL
+    assert call([m, cq(group=32)]) == EINVAL                       # unequal groups
+    assert call([m, cq(input_padded=512, row_bytes=128)]) == EINVAL  # unequal widths
+    assert call([m, m], rb=[0, 10], rc=[256, 247]) == EINVAL        # range past the end
+    assert call([m, cq(codebook=0)]) == ENULL
+    assert call([m], prepared=0) == ENULL
+    assert call([m], prepared=P + 2) == EALIGN
+    assert call([m], ys=[P + 64]) == EINVAL                         # output overlaps prepared
+    assert call([m], x=FAKE + 1) == EALIGN
+    assert call([m, cq(input=100)], x=FAKE) == EINVAL               # unequal inputs, with x
+    assert call([m], x=FAKE, ys=[FAKE + 8]) == EINVAL               # output overlaps x
+    assert call([m, m], rb=[256, 0], rc=[0, 0]) == OK                # nothing to do
+    assert L.cq_matvec_multi(None, 1, None, None, P, (ctypes.c_void_p * 1)(FAKE), None) == ENULL
+
+
 def test_cq_gather_argument_errors():
     L = bqd.lib()
     m = cq()

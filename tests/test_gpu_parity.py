@@ -317,6 +317,44 @@ def test_prepare_matvec_workload_and_batches(cache):
     assert bits_eq(p.cpu().numpy(), oracle.cq_prepare(h, case.x)) and y.numel() == 0
 
 
+# Several matrices on one activation ([P1] §6): shared launches on the ring
+# shapes (more than eight matrices take two), row ranges, empty ranges,
+# different codebooks, and shapes that fall back to one launch each.
+MULTI_CASES = [
+    ([synth.CqShape(2048, 512, 512, 128, 4), synth.CqShape(300, 512, 512, 128, 4),
+      synth.CqShape(65, 512, 512, 128, 4)], [(0, 2048), (10, 200), (64, 1)]),
+    ([synth.CqShape(130 + 7 * k, 4000, 4096, 256, 4) for k in range(10)], None),
+    ([synth.CqShape(200, 256, 256, 64, 2), synth.CqShape(100, 256, 256, 64, 4),
+      synth.CqShape(50, 256, 256, 64, 3)], [(0, 200), (5, 90), (0, 0)]),
+    ([synth.CqShape(40, 8192, 8192, 1024, 4), synth.CqShape(33, 8192, 8192, 1024, 4)], None),
+]
+
+
+@pytest.mark.parametrize("k", range(len(MULTI_CASES)))
+@pytest.mark.parametrize("fused", [False, True])
+def test_matvec_multi(k, fused):
+    shapes, ranges = MULTI_CASES[k]
+    cases = [synth.make_cq(sh, seed=950 + 10 * k + j) for j, sh in enumerate(shapes)]
+    x = cases[0].x
+    ms = [dev_matrix(c) for c in cases]
+    ranges = ranges or [(0, sh.output) for sh in shapes]
+    print(f"[case] multi {len(shapes)} matrices {shapes[0]} fused={fused}", flush=True)
+    p_ref = oracle.cq_prepare(host_matrix(cases[0]), x)
+    if fused:
+        p, outs = bqd.cq_prepare_matvec_multi(ms, to_dev(x[0]), ranges=ranges)
+        assert bits_eq(p.cpu().numpy(), p_ref[0])
+    else:
+        p = bqd.cq_prepare(ms[0], to_dev(x))[0]
+        outs = bqd.cq_matvec_multi(ms, p, ranges=ranges)
+    for c, m, (rb, rc), o in zip(cases, ms, ranges, outs):
+        got = o.cpu().numpy()
+        single = bqd.cq_matvec(m, p[None], row_begin=rb, row_count=rc).cpu().numpy()[0]
+        assert bits_eq(got, single)
+        if rc:
+            ref, mag = oracle.cq_matvec(host_matrix(c), p_ref[0], rb, rc)
+            assert_tol(got, ref, mag, f"multi {c.shape} [{rb}, +{rc})")
+
+
 def test_matvec_unaligned_packed_uses_generic_path():
     case = synth.make_cq(synth.CqShape(50, 512, 512, 128, 4), seed=5)
     s = case.shape
