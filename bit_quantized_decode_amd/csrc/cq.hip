@@ -1092,6 +1092,218 @@ void cq_matvec_mfma(const uint8_t* __restrict__ packed, const uint16_t* __restri
   }
 }
 
+// 4-bit rows on the matrix cores with each weight's two bf16 halves side by
+// side in K: a 32-deep K block holds 16 weights as (hi, lo) pairs, and the
+// matching operand rows hold each activation column twice, so one product
+// sums (hi + lo) * x over 16 weights.  The pair table then returns, for a
+// packed byte, both weights' (hi, lo) halves as one 8-byte read landing in
+// two consecutive operand registers: two reads, two byte permutes and one
+// product per 16 weights of a row (the split-table layout above needs eight
+// 4-byte reads and two products per 32).  The activation operands go from
+// memory straight to registers: eight whole-line loads per lane (each load
+// instruction reads one 128-byte line per vector), rearranged with lane swaps,
+// so the only workgroup barrier before the first product is the table's.  A
+// CU reads all activations of its rows (8 x 4096 floats = 128 KiB) besides
+// its ~128 KiB of weights; both go through the same per-CU memory path, and
+// scattered 16-byte activation reads (32 lines per load instruction) cost
+// ~3 us more than the line-wise ones.
+//
+// Lanes and columns: lane l = (r16, q) owns tile row r16 and, in the span's
+// 128 bytes, the 16-byte chunks 16 q and 64 + 16 q (each weight load reads
+// 64 consecutive bytes of 16 rows).  K block t (0..15) takes bytes 2t, 2t + 1
+// of the first chunk (t < 8) or of the second: columns c(q, t) + 0..3 with
+// c = 32 q + 4 t (t < 8) or 128 + 32 q + 4 (t - 8).  The operand lane
+// (r16, q) holds, for vector r16 % 8, the high (r16 < 8) or low bf16 half of
+// x at those four columns, each duplicated into both halves of a register.
+constexpr int kPair4RowBytes = 32 * 8;                       // 32 copies of two packed halves
+constexpr int kPair4TableBytes = 256 * kPair4RowBytes;       // 64 KiB
+constexpr int kMfma4LdsBytes = kPair4TableBytes + kRedBytes + 2 * kMaxBlockRows;
+constexpr int kMfma4Tiles = 4;  // 16-row tiles per wavefront and round
+constexpr int kMfma4Ahead = 1;  // tiles requested ahead of the one decoded
+
+template <int T, int AHEAD>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void cq_matvec_mfma4(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
+                     const float* __restrict__ codebook, const float* __restrict__ prepared,
+                     float* __restrict__ y, int input_padded, int64_t row_bytes, int log2_group,
+                     int rows, int64_t y_stride, int nb, int rg_n) {
+  static_assert(T <= kMfmaTiles && AHEAD <= T, "LDS sized for kMfmaTiles");
+  __shared__ __align__(16) uint8_t smem[kMfma4LdsBytes];
+  float* red = reinterpret_cast<float*>(smem + kPair4TableBytes);  // [span][row][vector]
+  uint16_t* nrm_lds = reinterpret_cast<uint16_t*>(smem + kPair4TableBytes + kRedBytes);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, l = tid & 63, r16 = l & 15, q = l >> 4;
+  const int n_spans = input_padded >> 8;
+  const int span = wave % n_spans, rg = wave / n_spans;
+  const int block_rows = 16 * T * rg_n;
+  const int n_tiles = (rows + 15) >> 4;
+  const int n_groups = input_padded >> log2_group;
+  const int g = (256 * span) >> log2_group;
+  const int grid = (int)gridDim.x;
+  // round `it`: local tile T r + i is global tile ((it T + i) rg_n + r) grid + blockIdx
+  auto tile_of = [&](int it, int lt) {
+    return ((it * T + lt % T) * rg_n + lt / T) * grid + (int)blockIdx.x;
+  };
+  const int block_norms = block_rows * n_groups;
+  const int tile_norms = 16 * n_groups;
+  const uint8_t* lane_bytes = packed + 128 * span + 16 * q;
+
+  // Loads in the order they are needed: the codebook (table), the activation
+  // operands, the round's norms, then the first two tiles' weights.
+  constexpr int kSlots = kPair4TableBytes / 16;  // 16-byte table slots
+  const int nthreads = (int)blockDim.x;
+  const float cbv = codebook[l & 15];  // lane l: codebook[l % 16]
+  const int v = r16 & 7, part = r16 >> 3;
+  // Activations in whole lines: load i gives lane (q, part, v) the float4 of
+  // vector v at span column 32 i + 8 q + 4 part (4-column chunk 8 i + 2 q + part).
+  float4 xa[8];
+  {
+    const float* xv = prepared + (int64_t)(v < nb ? v : 0) * input_padded + 256 * span + 8 * q + 4 * part;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xa[i] = *reinterpret_cast<const float4*>(xv + 32 * i);
+  }
+  int it = 0;  // tile_of(0, 0) < n_tiles: the grid has at most n_tiles workgroups
+  auto load_norm = [&](int it) {
+    const int t = min(tid, block_norms - 1);
+    const int64_t e = min((int64_t)tile_of(it, t / tile_norms) * tile_norms + t % tile_norms,
+                          (int64_t)rows * n_groups - 1);
+    return norms[e];
+  };
+  uint16_t nv = load_norm(it);
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4_t d[T][2];
+  auto load_tile = [&](int it, int i) {
+    const int r = min(16 * tile_of(it, T * rg + i) + r16, rows - 1);
+    const uint8_t* p = lane_bytes + (int64_t)r * row_bytes;
+    d[i][0] = stream_load(reinterpret_cast<const u32x4_nt*>(p));
+    d[i][1] = stream_load(reinterpret_cast<const u32x4_nt*>(p + 64));
+  };
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) load_tile(it, i);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // The table: slot t (16 bytes) is copies 2 (t % 16), + 1 of row b = t / 16,
+  // each (pack(codebook[b % 16]), pack(codebook[b / 16])) with pack(w) =
+  // bf16(w) | bf16(w - bf16(w)) << 16.  A wavefront's 64 slots share t / 256.
+  for (int t = tid; t < kSlots; t += nthreads) {
+    const float ca = __shfl(cbv, (t >> 4) & 15);
+    const float cb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cbv), t >> 8));
+    uint32_t hp, lp;
+    bf16_split_pair(ca, cb, &hp, &lp);  // hp = hi(ca) | hi(cb) << 16, lp likewise
+    const uint32_t pa = (hp & 0xffffu) | (lp << 16);
+    const uint32_t pb = (hp >> 16) | (lp & 0xffff0000u);
+    const u32x4_t e = {pa, pb, pa, pb};
+    *reinterpret_cast<u32x4_t*>(smem + 16 * t) = e;
+  }
+  // Activation operands, packed: K block t holds the chosen bf16 half of x
+  // at the span's 4-column chunk 8 q + (t % 8) + 32 (t / 8) as two pairs; each
+  // product's operand register j then duplicates the half of column j with
+  // one byte permute.  From the whole-line loads: split every float4 into
+  // (hi, lo) pairs, then for h = 0, 1 transpose loads 4 h + j (j = 0..3)
+  // against the 16-lane rows q with the two lane swaps, which leaves in slot j
+  // of row q the chunk 8 (4 h + q) + 2 j + part; the chunk of the other parity
+  // comes from lane l ^ 8 (same q and v), which sends the half this lane takes.
+  uint32_t bxp[16][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t sl[4][4];  // [slot j][hi pair 0, hi pair 1, lo pair 0, lo pair 1]
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 f = xa[4 * h + j];
+      bf16_split_pair(f.x, f.y, &sl[j][0], &sl[j][2]);
+      bf16_split_pair(f.z, f.w, &sl[j][1], &sl[j][3]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {  // rows 2, 3 of slot j trade with rows 0, 1 of slot j + 2
+        const auto r = __builtin_amdgcn_permlane32_swap(sl[j][e], sl[j + 2][e], false, false);
+        sl[j][e] = r[0];
+        sl[j + 2][e] = r[1];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; j += 2) {  // rows 1, 3 of slot j trade with rows 0, 2 of slot j + 1
+        const auto r = __builtin_amdgcn_permlane16_swap(sl[j][e], sl[j + 1][e], false, false);
+        sl[j][e] = r[0];
+        sl[j + 1][e] = r[1];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t own = part ? sl[j][2 + e] : sl[j][e];
+        const uint32_t give = part ? sl[j][e] : sl[j][2 + e];
+        const uint32_t got = __float_as_uint(lane_xor<8>(__uint_as_float(give)));
+        bxp[8 * h + 2 * j][e] = part ? got : own;      // chunk parity 0
+        bxp[8 * h + 2 * j + 1][e] = part ? own : got;  // chunk parity 1
+      }
+    }
+  }
+
+  const uint32_t lane_off = 8u * (uint32_t)(l & 31);  // this lane's table copy
+  while (true) {
+    if (tid < block_norms) nrm_lds[tid] = nv;
+    __syncthreads();  // table and norms written; the previous partials read
+    const bool more = tile_of(it + 1, 0) < n_tiles;
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      // AHEAD tiles ahead: this round's, then the next round's first ones
+      if (i + AHEAD < T) {
+        load_tile(it, i + AHEAD);
+      } else if (more) {
+        if (i + AHEAD == T) nv = load_norm(it + 1);
+        load_tile(it + 1, i + AHEAD - T);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // keep the packed operands packed (32 registers, not 64): their
+      // duplicates are made per product
+#pragma unroll
+      for (int t = 0; t < 16; ++t) asm volatile("" : "+v"(bxp[t][0]), "+v"(bxp[t][1]));
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const uint32_t w = d[i][t >> 3][(t >> 1) & 3];  // dword holding bytes 2t, 2t + 1
+        const uint32_t b0 = 2u * (t & 1);                // byte position of 2t in it
+        const uint32_t a0 = __builtin_amdgcn_perm(w, lane_off, 0x0c0c0400u | ((4u + b0) << 8));
+        const uint32_t a1 = __builtin_amdgcn_perm(w, lane_off, 0x0c0c0400u | ((5u + b0) << 8));
+        const f32x2_t e0 = *reinterpret_cast<const f32x2_t*>(smem + a0);
+        const f32x2_t e1 = *reinterpret_cast<const f32x2_t*>(smem + a1);
+        const u32x4_t a = {__float_as_uint(e0[0]), __float_as_uint(e0[1]), __float_as_uint(e1[0]),
+                           __float_as_uint(e1[1])};
+        const u32x4_t bx = {__builtin_amdgcn_perm(bxp[t][0], bxp[t][0], 0x01000100u),
+                            __builtin_amdgcn_perm(bxp[t][0], bxp[t][0], 0x03020302u),
+                            __builtin_amdgcn_perm(bxp[t][1], bxp[t][1], 0x01000100u),
+                            __builtin_amdgcn_perm(bxp[t][1], bxp[t][1], 0x03020302u)};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                      __builtin_bit_cast(bf16x8_t, bx), acc, 0, 0, 0);
+      }
+      // acc[k]: row 16 T rg + 16 i + 4 q + k of the block, operand column r16;
+      // times its norm, then column v (high halves) + column v + 8 (low halves)
+      const int row = 16 * T * rg + 16 * i + 4 * q;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float s = acc[k] * f16_to_f32(nrm_lds[(row + k) * n_groups + g]);
+        const float vv = s + dpp<kRowRor8, 0xf, false>(0.0f, s);
+        if (r16 < 8) red[(span * block_rows + row + k) * kRedStride + r16] = vv;
+      }
+    }
+    __syncthreads();
+    for (int o = tid; o < block_rows * nb; o += (int)blockDim.x) {
+      const int vec = o / block_rows, row = o - vec * block_rows;
+      float sum = 0.0f;
+#pragma unroll
+      for (int s2 = 0; s2 < kMfmaMaxSpans; ++s2)
+        if (s2 < n_spans) sum += red[(s2 * block_rows + row) * kRedStride + vec];
+      const int r = 16 * tile_of(it, row >> 4) + (row & 15);
+      if (r < rows) y[vec * y_stride + r] = sum;
+    }
+    if (!more) break;
+    ++it;
+  }
+}
+
 namespace {
 
 constexpr int kMaxGrid = 4096;
@@ -1309,12 +1521,34 @@ int launch_mfma_b(const bqd_cq_matrix* m, const float* prepared, float* y, int64
   return launch_status();
 }
 
+// 4-bit rows that load as 16-byte chunks take the paired-halves kernel.
+int launch_mfma4(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t y_stride, int nb,
+                 int64_t row_begin, int64_t row_count, hipStream_t s) {
+  constexpr int T = kMfma4Tiles, AHEAD = kMfma4Ahead;
+  const int n_spans = (int)(m->input_padded / 256);
+  const int64_t tiles = (row_count + 16 * T - 1) / (16 * T);
+  const int64_t rg_need = (tiles + cu_count() - 1) / cu_count();
+  const int rg = (int)std::max<int64_t>(1, std::min<int64_t>(rg_need, kMfmaMaxSpans / n_spans));
+  const int64_t block_rows = 16 * T * rg;
+  const int64_t grid = std::min<int64_t>(std::min<int64_t>((row_count + block_rows - 1) / block_rows,
+                                                           cu_count()), (row_count + 15) / 16);
+  hipLaunchKernelGGL((cq_matvec_mfma4<T, AHEAD>), dim3((unsigned)grid), dim3((unsigned)(64 * n_spans * rg)),
+                     0, s, m->packed + row_begin * m->row_bytes,
+                     m->norms + row_begin * (m->input_padded / m->group), m->codebook, prepared, y,
+                     (int)m->input_padded, m->row_bytes, ilog2(m->group), (int)row_count, y_stride,
+                     nb, rg);
+  return launch_status();
+}
+
 int run_mfma(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t y_stride, int nb,
              int64_t row_begin, int64_t row_count, hipStream_t s) {
   switch (m->bits) {
     case 2: return launch_mfma_b<2>(m, prepared, y, y_stride, nb, row_begin, row_count, s);
     case 3: return launch_mfma_b<3>(m, prepared, y, y_stride, nb, row_begin, row_count, s);
-    case 4: return launch_mfma_b<4>(m, prepared, y, y_stride, nb, row_begin, row_count, s);
+    case 4:
+      if (m->row_bytes % 16 == 0 && is_aligned(m->packed, 16))
+        return launch_mfma4(m, prepared, y, y_stride, nb, row_begin, row_count, s);
+      return launch_mfma_b<4>(m, prepared, y, y_stride, nb, row_begin, row_count, s);
     case 5: return launch_mfma_b<5>(m, prepared, y, y_stride, nb, row_begin, row_count, s);
   }
   return BQD_EINVAL;
