@@ -66,8 +66,11 @@ __global__ __launch_bounds__(kI8Threads) void i8_matvec_generic(
 // group (G a multiple of 16): its partial dot is multiplied by the group's
 // power-of-two scale (exact).  The row then reduces across lanes with DPP
 // and, for ROWSCALE, is multiplied by the row's fp32 scale.
+// Where NJ <= 4 (and no row scale, which would spill) the kernel keeps to
+// 128 registers, 4 wavefronts per SIMD, as the F8 kernel does.
 template <int NJ, int LPR, int U, bool ROWSCALE>
-__global__ __launch_bounds__(kI8Threads) void i8_matvec_fast(
+__global__ __launch_bounds__(kI8Threads)
+__attribute__((amdgpu_waves_per_eu(NJ <= 4 && !ROWSCALE ? 4 : 1))) void i8_matvec_fast(
     const int8_t* __restrict__ w, const uint8_t* __restrict__ gscale,
     const float* __restrict__ rscale, const float* __restrict__ x, float* __restrict__ y,
     int64_t R, int64_t C, int64_t G) {
