@@ -46,7 +46,10 @@ EXPORTS = ("cq_prepare", "cq_matvec", "cq_prepare_matvec", "cq_matvec_multi",
            "cq_prepare_matvec_multi", "cq_gather_rows", "f8_matvec",
            "i8_matvec", "kv_quantize_int8", "kv_int8_dot", "hadamard_mlp", "logits_sample",
            "logits_sample_workspace_bytes", "bqd_dbg_cq_unpack", "bqd_dbg_f16_decode",
-           "bqd_dbg_f8_decode", "bqd_dbg_e8m0_decode", "bqd_status_string")
+           "bqd_dbg_f8_decode", "bqd_dbg_e8m0_decode", "bqd_dbg_read_stream",
+           "bqd_status_string")
+
+READ_STREAM_WORDS = 2048  # BQD_READ_STREAM_WORDS
 
 _lib = None
 
@@ -91,6 +94,7 @@ def lib():
                 ("bqd_dbg_f16_decode", [P, I64, P, P]),
                 ("bqd_dbg_f8_decode", [P, I64, P, P]),
                 ("bqd_dbg_e8m0_decode", [P, I64, P, P]),
+                ("bqd_dbg_read_stream", [P, I64, P, P]),
                 ("logits_sample", [P, I64, I64, ctypes.c_float, P, P, I64, P, P, P, P])):
             fn = getattr(L, name)
             fn.argtypes = args
@@ -419,3 +423,16 @@ def dbg_f8_decode(codes, stream=None):
 
 def dbg_e8m0_decode(codes, stream=None):
     return _decode("bqd_dbg_e8m0_decode", codes, torch.uint8, stream)
+
+
+def dbg_read_stream(buf, out=None, stream=None):
+    """Read every byte of ``buf`` (a contiguous device tensor, 16-byte aligned,
+    nbytes a multiple of 16) once; returns ``out`` (int32 [READ_STREAM_WORDS])
+    whose XOR is the XOR of the buffer's 32-bit words."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf: a contiguous device tensor")
+    if out is None:
+        out = torch.empty(READ_STREAM_WORDS, dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _call("bqd_dbg_read_stream", _ptr(buf), nbytes, _ptr(out), _stream(buf, stream))
+    return out

@@ -17,7 +17,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libbqd.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-HIP_SOURCES = ["cq.hip", "f8.hip", "i8.hip", "mlp.hip", "sample.hip", "capi.hip"]
+HIP_SOURCES = ["cq.hip", "f8.hip", "i8.hip", "mlp.hip", "sample.hip", "stream.hip", "capi.hip"]
 HOST_SOURCES = ["validate.cpp"]
 ARCH = "gfx950"
 # Packed fp32 VALU instructions are turned off for every device pass.

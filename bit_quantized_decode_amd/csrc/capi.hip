@@ -119,6 +119,12 @@ int bqd_dbg_e8m0_decode(const uint8_t* codes, int64_t n, float* out, void* strea
   return launch_e8m0_decode(codes, n, out, as_stream(stream));
 }
 
+int bqd_dbg_read_stream(const void* buf, int64_t bytes, uint32_t* out, void* stream) {
+  int rc = check_read_stream(buf, bytes, out);
+  if (rc || bytes == 0) return rc;
+  return launch_read_stream(buf, bytes, out, as_stream(stream));
+}
+
 int64_t logits_sample_workspace_bytes(int64_t n, int64_t k) {
   return sample_workspace_need(n, k);
 }

@@ -34,6 +34,7 @@ int launch_hadamard_mlp(const float* n, int64_t hidden, int64_t H, const float* 
 int launch_f16_decode(const uint16_t* codes, int64_t n, float* out, hipStream_t s);
 int launch_f8_decode(const uint8_t* codes, int64_t n, float* out, hipStream_t s);
 int launch_e8m0_decode(const uint8_t* codes, int64_t n, float* out, hipStream_t s);
+int launch_read_stream(const void* buf, int64_t bytes, uint32_t* out, hipStream_t s);
 int launch_logits_sample(const float* logits, int64_t n, int64_t k, float temperature,
                          uint32_t* state, void* workspace, int32_t* token, int32_t* topk_ids,
                          float* topk_logits, hipStream_t s);

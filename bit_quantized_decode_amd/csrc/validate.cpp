@@ -222,6 +222,14 @@ int check_decode(const void* codes, int64_t n, const float* out, int code_size) 
   return BQD_OK;
 }
 
+int check_read_stream(const void* buf, int64_t bytes, const uint32_t* out) {
+  if (bytes < 0 || bytes % 16 != 0 || bytes >= (int64_t(1) << 46)) return BQD_EINVAL;
+  if (bytes == 0) return BQD_OK;
+  if (!buf || !out) return BQD_ENULL;
+  if (!aligned(buf, 16) || !aligned(out, 4)) return BQD_EALIGN;
+  return BQD_OK;
+}
+
 int64_t sample_workspace_need(int64_t n, int64_t k) {
   if (n < 1 || n > kMaxSampleLogits || k < 1 || k > kMaxSampleK || k > n) return BQD_EINVAL;
   return (n + 4095) / 4096 * k * 8;

@@ -36,6 +36,7 @@ int check_hadamard_mlp(const float* n, int64_t hidden, int64_t H, const float* d
                        const float* out, int64_t batch);
 int check_unpack(const bqd_cq_matrix* m, int64_t row, const uint8_t* idx);
 int check_decode(const void* codes, int64_t n, const float* out, int code_size);
+int check_read_stream(const void* buf, int64_t bytes, const uint32_t* out);
 int64_t sample_workspace_need(int64_t n, int64_t k);  // or BQD_EINVAL
 int check_sample(const float* logits, int64_t n, int64_t k, float temperature,
                  const uint32_t* state, const void* workspace, int64_t workspace_bytes,

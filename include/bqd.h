@@ -261,6 +261,19 @@ int bqd_dbg_f16_decode(const uint16_t *codes, int64_t n, float *out, void *strea
 int bqd_dbg_f8_decode(const uint8_t *codes, int64_t n, float *out, void *stream);
 int bqd_dbg_e8m0_decode(const uint8_t *codes, int64_t n, float *out, void *stream);
 
+/* Measurement probe: reads bytes bytes of buf once (nontemporal 16-byte
+ * loads, the layout of the head kernels, no other work) and writes the XOR
+ * of every 32-bit word read, split over out[0 .. BQD_READ_STREAM_WORDS) (one
+ * word per workgroup, zeros after the last; the XOR of all of out is the XOR
+ * of the buffer's words).  Its duration is the plain-read reference for the
+ * decode kernels' bandwidth.
+ *   buf: device, 16-byte aligned, bytes a multiple of 16, 0 <= bytes < 2^46
+ *   out: device uint32 [BQD_READ_STREAM_WORDS], 4-byte aligned
+ * Errors: BQD_EINVAL (bytes), BQD_ENULL, BQD_EALIGN, BQD_EHIP.  bytes == 0
+ * returns BQD_OK without a launch. */
+#define BQD_READ_STREAM_WORDS 2048
+int bqd_dbg_read_stream(const void *buf, int64_t bytes, uint32_t *out, void *stream);
+
 /* A static, human-readable name for a status code. */
 const char *bqd_status_string(int status);
 

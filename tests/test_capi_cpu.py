@@ -245,6 +245,14 @@ def test_probe_argument_errors():
     assert L.bqd_dbg_f8_decode(0, 4, FAKE, None) == ENULL
     assert L.bqd_dbg_e8m0_decode(FAKE, -1, FAKE, None) == EINVAL
     assert L.bqd_dbg_f8_decode(FAKE, 0, FAKE, None) == OK
+    assert L.bqd_dbg_read_stream(FAKE, 24, FAKE, None) == EINVAL
+    assert L.bqd_dbg_read_stream(FAKE, -16, FAKE, None) == EINVAL
+    assert L.bqd_dbg_read_stream(FAKE, 1 << 46, FAKE, None) == EINVAL
+    assert L.bqd_dbg_read_stream(0, 16, FAKE, None) == ENULL
+    assert L.bqd_dbg_read_stream(FAKE, 16, 0, None) == ENULL
+    assert L.bqd_dbg_read_stream(FAKE + 8, 16, FAKE, None) == EALIGN
+    assert L.bqd_dbg_read_stream(FAKE, 16, FAKE + 2, None) == EALIGN
+    assert L.bqd_dbg_read_stream(0, 0, 0, None) == OK
     m = cq()
     assert L.bqd_dbg_cq_unpack(ctypes.byref(m), 256, FAKE, None) == EINVAL
     assert L.bqd_dbg_cq_unpack(ctypes.byref(m), 0, 0, None) == ENULL

@@ -109,6 +109,20 @@ def test_probe_f8_all_codes():
         assert bits_eq(got, ref), np.flatnonzero(got.view(np.uint32) != ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("nbytes", [16, 1008, 16384, 16384 * 64 + 48, 4096 * 2048 * 16 + 4096 * 5 + 32])
+def test_read_stream_reads_every_word(nbytes):
+    # The bandwidth probe: the XOR of its per-workgroup words is the XOR of
+    # every 32-bit word of the buffer (whole steps, the ragged tail, and a
+    # buffer beyond one step per workgroup).
+    rng = np.random.default_rng(nbytes)
+    words = rng.integers(0, 2**32, nbytes // 4, dtype=np.uint32)
+    buf = to_dev(words.view(np.int32))
+    out = torch.full((bqd.READ_STREAM_WORDS,), -1, dtype=torch.int32, device=DEV)
+    bqd.dbg_read_stream(buf, out)
+    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(words)
+
+
 def test_probe_e8m0_all_codes():
     codes = np.arange(256, dtype=np.uint8)
     got = bqd.dbg_e8m0_decode(to_dev(codes)).cpu().numpy()
