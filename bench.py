@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 (vector)
+HEAD_STAGE = "f8_head_246272x4096_matvec"
 METRIC = "weight-stream GB/s & % of HBM peak, CQ/F8 decode matvec; rows/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "f8_head_246272x4096_hbm_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_quantized_decode_amd", "csrc", f) for f in ("f8.hip", "device.h")]
@@ -151,7 +152,7 @@ def build_cases(torch, bqd, synth, hot):
     sh, xh = T(hd.scale), T(hd.x)
     yh = torch.empty(1, hd.R, device=dev)
     head_bytes = hd.R * hd.C + hd.SR * hd.SC + 4 * hd.C + 4 * hd.R
-    cases.append(Case("f8_head_246272x4096_matvec",
+    cases.append(Case(HEAD_STAGE,
                       [lambda w=w: bqd.f8_matvec(w, sh, xh, out=yh) for w in whs],
                       head_bytes, hd.R))
     # -- beyond the step: the I8 head (E8M0 scales per 16 columns) and the
@@ -388,14 +389,21 @@ def main():
     stream = torch.cuda.current_stream()
     period = max(len(c.calls) for c in cases)  # weight copies rotate with this period
 
-    # One graph per rotation index: the whole step (every stage, in order).
+    # One graph per rotation index: the whole step (every stage, in order),
+    # and the same step without the head (the head's in-step duration is the
+    # difference of the two).
     log(f"capturing {period} step graphs")
     step_graphs = [capture(torch, lambda k=k: [c.calls[k % len(c.calls)]() for c in cases])
                    for k in range(period)]
-    # Per stage: one graph of `period` back-to-back launches over the copies.
+    head_case = next(c for c in cases if c.name == HEAD_STAGE)
+    rest = [c for c in cases if c is not head_case]
+    rest_graphs = [capture(torch, lambda k=k: [c.calls[k % len(c.calls)]() for c in rest])
+                   for k in range(period)]
+    # Per stage (the head aside): one graph of `period` back-to-back launches
+    # over the copies.
     stage_graphs = {c.name: capture(torch, lambda c=c: [c.calls[k % len(c.calls)]()
                                                        for k in range(period)])
-                    for c in cases + extra_cases}
+                    for c in rest + extra_cases}
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
@@ -409,22 +417,44 @@ def main():
     torch.cuda.synchronize()
     step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
 
-    # Kernel durations: HIP events on the launch stream bracket replays of
+    # The head inside the step: HIP events on the launch stream bracket runs
+    # of 3 * period replays of the whole step and of the step without the
+    # head, alternated; each difference per step is one sample.
+    def replays_ms(graphs, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            graphs[i % period].replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    replays_ms(rest_graphs, period)
+    head_samples = []
+    for _ in range(8):
+        full_ms = replays_ms(step_graphs, 3 * period)
+        head_samples.append(full_ms - replays_ms(rest_graphs, 3 * period))
+    head_ms = np.array(head_samples)
+
+    # The other stages: HIP events on the launch stream bracket replays of
     # each stage's graph of `period` back-to-back launches.
     reps = max(4, args.steps // period)
     per_case = {}
     extras = {}
     for c in cases + extra_cases:
-        g = stage_graphs[c.name]
-        g.replay()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(reps)]
-        for e0, e1 in ev:
-            e0.record(stream)
+        if c is head_case:
+            ms = head_ms
+        else:
+            g = stage_graphs[c.name]
             g.replay()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) / period
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(reps)]
+            for e0, e1 in ev:
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) / period
         c.ms = ms
         gbs = c.nbytes / (ms.mean() * 1e-3) / 1e9
         rec = dict(
@@ -433,8 +463,11 @@ def main():
             us_p90=round(float(np.percentile(ms, 90) * 1e3), 3), bytes=c.nbytes,
             gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4),
             rows_per_s=round(c.rows / (ms.mean() * 1e-3), 1) if c.rows else None)
-        if c in cases:
-            per_case[c.name] = rec
+        if c is head_case:
+            per_case[c.name] = dict(rec, timing="in the step: the step minus the step without the "
+                                                "head, 8 samples of 3 x 16 replays each")
+        elif c in cases:
+            per_case[c.name] = dict(rec, timing="16 back-to-back launches per graph replay")
         elif c.name.startswith("cq4_3x"):
             extras[c.name] = dict(rec, note="not part of the step: several matrices on one activation")
         elif c.name.startswith("cq4_"):
@@ -464,7 +497,7 @@ def main():
     total_bytes = sum(c.nbytes for c in cases)
     total_rows = sum(c.rows for c in cases)
     value = total_bytes / (step_ms * 1e-3) / 1e9
-    head = per_case["f8_head_246272x4096_matvec"]
+    head = per_case[HEAD_STAGE]
     roofline = dict(bound="hbm", kernel="f8_matvec_fast (F8 head 246272x4096)",
                     achieved=head["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(head["gbs"] / HBM_PEAK_GBS, 4), traffic=measured_traffic(),
