@@ -6,8 +6,9 @@
 // each group, multiply by 1/sqrt(group)), §3 (dot packed rows directly: per
 // row and group, the fp16 norm times the sum of codebook[index] * prepared),
 // "Row gather" (each group's codebook values scaled by the group norm, the
-// normalized transform, the columns below the unpadded width) and §6 (a row range of a matrix).  The record
-// layout is that of "Inference engine, part 1: loader and tokenizer", §4.
+// normalized transform, the columns below the unpadded width) and §6 (a row
+// range of a matrix).  The record layout is that of "Inference engine, part 1:
+// loader and tokenizer", §4.
 #include <algorithm>
 #include <atomic>
 #include <cmath>
