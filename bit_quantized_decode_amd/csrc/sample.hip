@@ -14,23 +14,33 @@
 // get small distinct keys (below every real key, whose low half is at least
 // 2^32 - 2^20); they are never selected, since k <= n real logits compete.
 //
-// Two launches.  Blocks of 4096 logits: each wavefront sorts four runs of 64
-// keys across its lanes (a bitonic network on lane exchanges, no barriers),
-// merges them into its top 64, and the wavefronts' lists merge in LDS down to
-// the block's top 64, of which the first k go to the caller's workspace.  One
-// block then merges the blocks' lists the same way, takes the first k, and
+// Two launches.  Blocks of 1024 R logits (R = 1, 2 or 4: the smallest that
+// leaves at most 256 blocks, so that the work spreads over many CUs): each
+// wavefront sorts R runs of 64 keys across its lanes (a bitonic network on
+// lane exchanges, no barriers), merges them into its top 64, and the
+// wavefronts' lists merge in LDS down to the block's top 64, of which the
+// first k go to the caller's workspace.
+//
+// One block then selects the first k of the blocks' lists.  Pruning: with H
+// the k-th largest of the lists' first keys, at least k keys are >= H, so
+// every one of the first k overall is >= H, and in each (descending) list the
+// keys >= H are a prefix.  The block reads the first 8 keys of every list,
+// keeps those >= H (typically a few per list), sorts and merges them; where a
+// list may hold more than 8 such keys, or more than 1024 survive, or there are
+// fewer than k lists, it merges every list in full instead.  Either way it
 // draws the token in fp64.  Keys carry the index, so the logits are re-read
 // for the k values (copied bit for bit).
 #include <math.h>
 
 #include "cq_device.h"
 #include "launch.h"
+#include "validate.h"
 
 namespace bqd {
 
 constexpr int kSampleThreads = 1024;
-constexpr int kChunk = 4096;          // logits per first-stage block (4 per thread)
 constexpr int kMaxCandidates = 16384; // second-stage capacity (16 per thread)
+constexpr int kPeek = 8;              // keys read per list by the pruned selection
 constexpr int kMaxK = 64;
 
 // Unsigned key of a logit: the order of values, NaN below everything, -0 = +0.
@@ -126,23 +136,36 @@ __device__ void block_merge_lists(uint64_t* lists, int n_lists) {
   __syncthreads();
 }
 
-// Stage 1: block b keeps the first k keys of logits [4096 b, 4096 b + 4096)
+// The 64 largest of R sorted runs of the wavefront (R = 1, 2 or 4),
+// descending: lane l holds the l-th largest.
+template <int R>
+__device__ __forceinline__ uint64_t wave_top_of_runs(const uint64_t (&run)[R]) {
+  const int l = threadIdx.x & 63;
+  if constexpr (R == 1) return run[0];
+  if constexpr (R == 2) return wave_merge_desc(run[0], key_from_lane(run[1], 63 - l));
+  const uint64_t m01 = wave_merge_desc(run[0], key_from_lane(run[1], 63 - l));
+  const uint64_t m23 = wave_merge_desc(run[2], key_from_lane(run[3], 63 - l));
+  return wave_merge_desc(m01, key_from_lane(m23, 63 - l));
+}
+
+// Stage 1: block b keeps the first k keys of logits [C b, C b + C), C = 1024 R,
 // in workspace slots [k b, k b + k).
+template <int R>
 __global__ __launch_bounds__(kSampleThreads) void topk_chunk_kernel(
     const float* __restrict__ logits, int64_t n, int k, uint64_t* __restrict__ ws) {
-  __shared__ uint64_t lists[kChunk / 4];  // one list of 64 per wavefront
+  static_assert(R == 1 || R == 2 || R == 4, "runs per wavefront");
+  constexpr int kChunk = kSampleThreads * R;
+  __shared__ uint64_t lists[kSampleThreads];  // one list of 64 per wavefront
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
-  uint64_t run[4];
+  uint64_t run[R];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {  // run r: chunk elements 256 wave + 64 r + lane
-    const int t = 256 * wave + 64 * r + l;
+  for (int r = 0; r < R; ++r) {  // run r: chunk elements 64 R wave + 64 r + lane
+    const int t = 64 * R * wave + 64 * r + l;
     const int64_t i = (int64_t)blockIdx.x * kChunk + t;
     run[r] = i < n ? cand_key(logits[i], (uint32_t)i) : (uint64_t)(i - n);  // padding < kChunk
   }
-  wave_sort_desc<4>(run);
-  const uint64_t m01 = wave_merge_desc(run[0], key_from_lane(run[1], 63 - l));
-  const uint64_t m23 = wave_merge_desc(run[2], key_from_lane(run[3], 63 - l));
-  lists[64 * wave + l] = wave_merge_desc(m01, key_from_lane(m23, 63 - l));
+  wave_sort_desc<R>(run);
+  lists[64 * wave + l] = wave_top_of_runs<R>(run);
   block_merge_lists(lists, kSampleThreads / 64);
   if ((int)threadIdx.x < k) ws[(int64_t)blockIdx.x * k + threadIdx.x] = lists[threadIdx.x];
 }
@@ -157,15 +180,80 @@ __global__ __launch_bounds__(kSampleThreads) void topk_final_kernel(
   __shared__ float sel_v[kMaxK];
   __shared__ int32_t sel_i[kMaxK];
   __shared__ double weight[kMaxK];
-  for (int c = threadIdx.x; c < 64 * n_lists; c += kSampleThreads) {
-    const int b = c >> 6, j = c & 63;
-    const uint64_t v = j < k ? ws[(int64_t)b * k + j] : 0;
-    // padding (a short chunk's, or past k): distinct keys below every real
-    // key, decreasing along the list so that each list stays sorted
-    lists[c] = v < (uint64_t)kMaxCandidates ? (uint64_t)(kMaxCandidates - 1 - c) : v;
+  __shared__ uint64_t thr;
+  __shared__ int n_keep, full_merge;
+  const int t = threadIdx.x, wave = t >> 6, l = t & 63;
+  // The first kPeek keys of list t (all requested together).  A list holds k
+  // keys; its padding keys (a short chunk's) are below every real key.
+  const bool has = t < n_lists;
+  uint64_t pk[kPeek];
+#pragma unroll
+  for (int q = 0; q < kPeek; ++q) pk[q] = (has && q < k) ? ws[(int64_t)t * k + q] : 0;
+  lists[t] = has ? pk[0] : 0;  // the lists' first keys (n_lists <= 256)
+  __syncthreads();
+  if (wave == 0) {  // H = the k-th largest first key
+    uint64_t h[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) h[r] = lists[64 * r + l];
+    wave_sort_desc<4>(h);
+    const uint64_t top = wave_top_of_runs<4>(h);
+    if (l == k - 1) thr = top;
   }
-  block_merge_lists(lists, n_lists);
-  const int t = threadIdx.x;
+  __syncthreads();
+  const uint64_t H = n_lists >= k ? thr : 0;
+  int c = 0;  // keys >= H among the first kPeek of list t: a prefix
+#pragma unroll
+  for (int q = 0; q < kPeek; ++q) c += (has && q < k && pk[q] >= H) ? 1 : 0;
+  // exclusive prefix of the counts over the lists (wavefront 0 on 4 per lane)
+  __syncthreads();
+  lists[t] = (uint64_t)c;
+  __syncthreads();
+  if (wave == 0) {
+    const int c0 = (int)lists[4 * l], c1 = (int)lists[4 * l + 1], c2 = (int)lists[4 * l + 2],
+              c3 = (int)lists[4 * l + 3];
+    const int s = c0 + c1 + c2 + c3;
+    int incl = s;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (l >= d) incl += o;
+    }
+    const int excl = incl - s;
+    lists[4 * l] = (uint64_t)excl;
+    lists[4 * l + 1] = (uint64_t)(excl + c0);
+    lists[4 * l + 2] = (uint64_t)(excl + c0 + c1);
+    lists[4 * l + 3] = (uint64_t)(excl + c0 + c1 + c2);
+    if (l == 63) n_keep = incl;
+    if (l == 0) full_merge = n_lists < k;
+  }
+  __syncthreads();
+  if (c == kPeek && kPeek < k) full_merge = 1;  // list t may hold more keys >= H
+  const int off = (int)lists[t];
+  __syncthreads();
+  if (!full_merge && n_keep <= kSampleThreads) {
+    // the survivors in slots [0, n_keep), distinct small keys after them;
+    // each wavefront sorts its 64 slots, then the 16 lists merge
+    const int kept = n_keep;
+    if (t >= kept) lists[t] = (uint64_t)t;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kPeek; ++q)
+      if (q < c) lists[off + q] = pk[q];
+    __syncthreads();
+    uint64_t v[1] = {lists[t]};
+    wave_sort_desc<1>(v);
+    lists[t] = v[0];
+    block_merge_lists(lists, kSampleThreads / 64);
+  } else {
+    for (int c2 = t; c2 < 64 * n_lists; c2 += kSampleThreads) {
+      const int b = c2 >> 6, j = c2 & 63;
+      const uint64_t v = j < k ? ws[(int64_t)b * k + j] : 0;
+      // padding (a short chunk's, or past k): distinct keys below every real
+      // key, decreasing along the list so that each list stays sorted
+      lists[c2] = v < (uint64_t)kMaxCandidates ? (uint64_t)(kMaxCandidates - 1 - c2) : v;
+    }
+    block_merge_lists(lists, n_lists);
+  }
   if (t < k) {
     const int32_t i = (int32_t)(0xffffffffu - (uint32_t)lists[t]);
     sel_i[t] = i;
@@ -211,10 +299,18 @@ __global__ __launch_bounds__(kSampleThreads) void topk_final_kernel(
 int launch_logits_sample(const float* logits, int64_t n, int64_t k, float temperature,
                          uint32_t* state, void* workspace, int32_t* token, int32_t* topk_ids,
                          float* topk_logits, hipStream_t s) {
-  const int64_t chunks = (n + kChunk - 1) / kChunk;
+  const int64_t chunk = sample_chunk(n);
+  const int64_t chunks = (n + chunk - 1) / chunk;
   uint64_t* ws = reinterpret_cast<uint64_t*>(workspace);
-  hipLaunchKernelGGL(topk_chunk_kernel, dim3((unsigned)chunks), dim3(kSampleThreads), 0, s,
-                     logits, n, (int)k, ws);
+  if (chunk == 1024)
+    hipLaunchKernelGGL(topk_chunk_kernel<1>, dim3((unsigned)chunks), dim3(kSampleThreads), 0, s,
+                       logits, n, (int)k, ws);
+  else if (chunk == 2048)
+    hipLaunchKernelGGL(topk_chunk_kernel<2>, dim3((unsigned)chunks), dim3(kSampleThreads), 0, s,
+                       logits, n, (int)k, ws);
+  else
+    hipLaunchKernelGGL(topk_chunk_kernel<4>, dim3((unsigned)chunks), dim3(kSampleThreads), 0, s,
+                       logits, n, (int)k, ws);
   int rc = launch_status();
   if (rc) return rc;
   hipLaunchKernelGGL(topk_final_kernel, dim3(1), dim3(kSampleThreads), 0, s, logits, ws,

@@ -232,7 +232,8 @@ int check_read_stream(const void* buf, int64_t bytes, const uint32_t* out) {
 
 int64_t sample_workspace_need(int64_t n, int64_t k) {
   if (n < 1 || n > kMaxSampleLogits || k < 1 || k > kMaxSampleK || k > n) return BQD_EINVAL;
-  return (n + 4095) / 4096 * k * 8;
+  const int64_t chunk = sample_chunk(n);
+  return (n + chunk - 1) / chunk * k * 8;
 }
 
 int check_sample(const float* logits, int64_t n, int64_t k, float temperature,

@@ -48,6 +48,12 @@ constexpr int64_t kMaxColumns = (int64_t)1 << 28;   // exclusive
 constexpr int64_t kMaxGroup = 1024;
 constexpr int64_t kMaxSampleLogits = (int64_t)1 << 20;  // inclusive
 constexpr int64_t kMaxSampleK = 64;
+// Logits per first-stage sampler workgroup: the smallest of 1024, 2048 and
+// 4096 that leaves at most 256 workgroups (256 lists of candidates for the
+// second stage) for n <= kMaxSampleLogits.
+constexpr int64_t sample_chunk(int64_t n) {
+  return n <= 256 * 1024 ? 1024 : (n <= 256 * 2048 ? 2048 : 4096);
+}
 constexpr int64_t kMaxHadamard = 16384;
 constexpr int64_t kMaxMulti = 64;               // inclusive
 constexpr int64_t kMaxBatchBlocks = (int64_t)1 << 31;  // exclusive (one workgroup each)

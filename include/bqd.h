@@ -222,7 +222,8 @@ int hadamard_mlp(const float *n, int64_t hidden, int64_t H, const float *d1, con
                  const float *d3, const float *resid, const float *u, float *out, int64_t batch,
                  void *stream);
 
-/* Bytes of device workspace logits_sample needs: ceil(n / 4096) * k * 8.
+/* Bytes of device workspace logits_sample needs: ceil(n / C) * k * 8, where
+ * C = 1024 for n <= 262144, 2048 for n <= 524288, else 4096.
  * Returns BQD_EINVAL (negative) for n or k outside logits_sample's range. */
 int64_t logits_sample_workspace_bytes(int64_t n, int64_t k);
 

@@ -258,7 +258,7 @@ def test_probe_argument_errors():
     assert L.bqd_dbg_cq_unpack(ctypes.byref(m), 0, 0, None) == ENULL
 
 
-SAMPLE_NEED = (246272 + 4095) // 4096 * 64 * 8  # workspace bytes for n = 246272, k = 64
+SAMPLE_NEED = (246272 + 1023) // 1024 * 64 * 8  # workspace bytes for n = 246272, k = 64
 
 
 @pytest.mark.parametrize("args,code", [
@@ -284,7 +284,10 @@ def test_logits_sample_workspace_bytes():
     L = bqd.lib()
     assert L.logits_sample_workspace_bytes(246272, 64) == SAMPLE_NEED
     assert L.logits_sample_workspace_bytes(1, 1) == 8
-    assert L.logits_sample_workspace_bytes(4097, 3) == 2 * 3 * 8
+    assert L.logits_sample_workspace_bytes(4097, 3) == 5 * 3 * 8  # blocks of 1024
+    assert L.logits_sample_workspace_bytes(256 * 1024, 2) == 256 * 2 * 8
+    assert L.logits_sample_workspace_bytes(256 * 1024 + 1, 2) == 129 * 2 * 8  # of 2048
+    assert L.logits_sample_workspace_bytes(512 * 1024 + 1, 2) == 129 * 2 * 8  # of 4096
     assert L.logits_sample_workspace_bytes(1 << 20, 64) == 256 * 64 * 8
     for n, k in ((0, 1), (10, 11), (100, 0), (100, 65), ((1 << 20) + 1, 1)):
         assert L.logits_sample_workspace_bytes(n, k) == EINVAL

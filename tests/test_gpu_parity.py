@@ -752,8 +752,10 @@ def test_sample_head_sized(kind, k, T):
     check_sample(_logits(kind, 246272, 90 + k), k, T, seed=0x9E3779B9 + k, calls=4)
 
 
-@pytest.mark.parametrize("n,k", [(1, 1), (5, 5), (64, 64), (4095, 7), (4096, 64), (4097, 64),
-                                 (8191, 3), (65536 + 17, 33), (1 << 20, 64)])
+@pytest.mark.parametrize("n,k", [(1, 1), (5, 5), (64, 64), (1023, 5), (1025, 64), (4095, 7),
+                                 (4096, 64), (4097, 64), (8191, 3), (65536 + 17, 33),
+                                 (256 * 1024, 64), (256 * 1024 + 1, 9), (512 * 1024 + 1, 64),
+                                 (1 << 20, 64)])
 def test_sample_ragged_sizes(n, k):
     check_sample(_logits("normal", n, n), k, 0.8, seed=12345 + n)
     check_sample(_logits("ties", n, n + 1), k, 1.3, seed=777 + n)
