@@ -1151,7 +1151,7 @@ void cq_matvec_mfma4(const uint8_t* __restrict__ packed, const uint16_t* __restr
   const uint8_t* lane_bytes = packed + 128 * span + 16 * q;
 
   // Loads in the order they are needed: the codebook (table), the activation
-  // operands, the round's norms, then the first two tiles' weights.
+  // operands, the round's norms, then the first AHEAD tiles' weights.
   constexpr int kSlots = kPair4TableBytes / 16;  // 16-byte table slots
   const int nthreads = (int)blockDim.x;
   const float cbv = codebook[l & 15];  // lane l: codebook[l % 16]
@@ -1160,7 +1160,8 @@ void cq_matvec_mfma4(const uint8_t* __restrict__ packed, const uint16_t* __restr
   // vector v at span column 32 i + 8 q + 4 part (4-column chunk 8 i + 2 q + part).
   float4 xa[8];
   {
-    const float* xv = prepared + (int64_t)(v < nb ? v : 0) * input_padded + 256 * span + 8 * q + 4 * part;
+    const float* xv =
+        prepared + (int64_t)(v < nb ? v : 0) * input_padded + 256 * span + 8 * q + 4 * part;
 #pragma unroll
     for (int i = 0; i < 8; ++i) xa[i] = *reinterpret_cast<const float4*>(xv + 32 * i);
   }
