@@ -68,6 +68,9 @@ def parse_args():
                          "under profiles/ (no GPU needed)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for counter runs: 8 F8 head launches, then 8 plain 1 GiB device copies")
+    ap.add_argument("--stage-probe", metavar="STAGE",
+                    help="for counter runs: 4 replays of one stage's graph of 16 launches "
+                         "(a step stage or an extra, by its name in the JSON line)")
     return ap.parse_args()
 
 
@@ -317,6 +320,22 @@ def traffic_probe(torch, bqd, synth):
     print(json.dumps({"f8_head_bytes": hd.R * hd.C + hd.SR * hd.SC, "copy_bytes": n}), flush=True)
 
 
+def stage_probe(torch, bqd, synth, name, hot):
+    """A fixed launch sequence for rocprofv3 --pmc runs on one stage: its
+    graph of 16 launches (rotating weight copies), replayed 4 times."""
+    cases, extra_cases, _ = build_cases(torch, bqd, synth, hot)
+    by_name = {c.name: c for c in cases + extra_cases}
+    if name not in by_name:
+        raise SystemExit(f"bench.py: no stage {name!r}; stages: {', '.join(sorted(by_name))}")
+    c = by_name[name]
+    period = 16
+    g = capture(torch, lambda: [c.calls[k % len(c.calls)]() for k in range(period)])
+    for _ in range(4):
+        g.replay()
+    torch.cuda.synchronize()
+    print(json.dumps({"stage": name, "launches": 4 * period + period, "bytes": c.nbytes}), flush=True)
+
+
 def _dispatch_kib(out_dir, counter):
     """Median per-dispatch value of `counter` for the head kernel and for the
     1 GiB copy, from a rocprofv3 --pmc csv directory."""
@@ -383,6 +402,9 @@ def main():
     bqd.lib()
     if args.traffic_probe:
         traffic_probe(torch, bqd, synth)
+        return
+    if args.stage_probe:
+        stage_probe(torch, bqd, synth, args.stage_probe, args.hot)
         return
     cases, extra_cases, data = build_cases(torch, bqd, synth, args.hot)
     torch.cuda.synchronize()

@@ -48,11 +48,20 @@ __global__ __launch_bounds__(kF8Threads) void f8_matvec_generic(
 // scale (exact), then the row reduces across lanes with DPP.  Where NJ <= 4
 // the kernel keeps to 128 registers (4 wavefronts per SIMD): the extra
 // wavefronts hide more load latency (~3% on the 246272 x 4096 head).
-template <int NJ, int LPR, int U>
+//
+// The scale row of weight row r is floor(r SR / R).  Where SR divides R
+// (EXACT: R / SR rows per block) it is r / (R / SR), formed as
+// (r * magic) >> shift with the launcher's magic = ceil(2^shift / (R / SR)),
+// shift = 31 + ceil(log2(R / SR)), exact for every r < 2^31 (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994,
+// Theorem 4.2); a 64-bit division per row otherwise (~80 instructions, a
+// large share of the loop's work on the head).
+template <int NJ, int LPR, int U, bool EXACT>
 __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(NJ <= 4 ? 4 : 1)))
 void f8_matvec_fast(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ scale, const float* __restrict__ x,
-    float* __restrict__ y, int64_t R, int64_t C, int64_t SR, int64_t SC, int64_t cols_per_block) {
+    float* __restrict__ y, int R, int64_t C, int64_t SR, int64_t SC, int64_t cols_per_block,
+    uint32_t blk_magic, int blk_shift) {
   constexpr int SLOTS = kF8Threads / LPR;
   const int tid = threadIdx.x;
   const int slot = tid / LPR;
@@ -66,16 +75,19 @@ void f8_matvec_fast(
 #pragma unroll
     for (int k = 0; k < 16; ++k) act[j][k] = x[c + k];
   }
-  const int64_t n_steps = (R + SLOTS - 1) / SLOTS;
-  for (int64_t s0 = (int64_t)blockIdx.x * U; s0 < n_steps; s0 += (int64_t)gridDim.x * U) {
+  // rows < 2^30: 32-bit row arithmetic
+  const int n_steps = (R + SLOTS - 1) / SLOTS;
+  for (int s0 = (int)blockIdx.x * U; s0 < n_steps; s0 += (int)gridDim.x * U) {
     uint4 d[U][NJ];
     uint32_t sb[U][NJ];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      int64_t r = (s0 + u) * SLOTS + slot;
+      int r = (s0 + u) * SLOTS + slot;
       r = r < R ? r : R - 1;  // in-bounds load; the result is dropped
-      const uint4* wr = reinterpret_cast<const uint4*>(w + r * C);
-      const uint8_t* srow = scale + ((r * SR) / R) * SC;
+      const uint4* wr = reinterpret_cast<const uint4*>(w + (int64_t)r * C);
+      const int64_t sr = EXACT ? (int64_t)(((uint64_t)(uint32_t)r * blk_magic) >> blk_shift)
+                               : ((int64_t)r * SR) / R;
+      const uint8_t* srow = scale + sr * SC;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const u32x4_nt t = stream_load(reinterpret_cast<const u32x4_nt*>(wr + q + LPR * j));
@@ -99,7 +111,7 @@ void f8_matvec_fast(
         acc += part * e8m0_to_f32(sb[u][j]);
       }
       acc = group_sum<LPR>(acc);
-      const int64_t r = (s0 + u) * SLOTS + slot;
+      const int r = (s0 + u) * SLOTS + slot;
       if (q == LPR - 1 && r < R) y[r] = acc;
     }
   }
@@ -118,8 +130,18 @@ int launch_f8_fast(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale,
   constexpr int SLOTS = kF8Threads / LPR;
   const int64_t n_steps = (R + SLOTS - 1) / SLOTS;
   const int64_t grid = std::min<int64_t>((n_steps + U - 1) / U, kMaxGrid);
-  hipLaunchKernelGGL((f8_matvec_fast<NJ, LPR, U>), dim3((unsigned)grid), dim3(kF8Threads), 0, s,
-                     w, scale, x, y, R, C, SR, SC, C / SC);
+  if (R % SR == 0) {
+    // rows per scale block d: magic = ceil(2^(31 + l) / d), 2^l >= d > 2^(l - 1)
+    const uint64_t d = (uint64_t)(R / SR);
+    int l = 0;
+    while ((uint64_t(1) << l) < d) ++l;
+    const uint64_t magic = ((uint64_t(1) << (31 + l)) + d - 1) / d;  // < 2^32
+    hipLaunchKernelGGL((f8_matvec_fast<NJ, LPR, U, true>), dim3((unsigned)grid), dim3(kF8Threads),
+                       0, s, w, scale, x, y, (int)R, C, SR, SC, C / SC, (uint32_t)magic, 31 + l);
+  } else {
+    hipLaunchKernelGGL((f8_matvec_fast<NJ, LPR, U, false>), dim3((unsigned)grid), dim3(kF8Threads),
+                       0, s, w, scale, x, y, (int)R, C, SR, SC, C / SC, 0u, 0);
+  }
   return launch_status();
 }
 
