@@ -469,6 +469,9 @@ def test_f8_head_sampled_rows(cache):
     (10, 7, 3, 2, 1), (130, 260, 3, 5, 2), (64, 128, 1, 1, 1), (257, 4096, 3, 32, 1),
     (300, 1024, 3, 8, 3), (129, 2048, 2, 16, 1), (77, 8192, 1, 64, 1), (40, 768, 4, 3, 1),
     (33, 128, 33, 8, 1),
+    # scale blocks of a whole number of rows that is not a power of two (125): the scale row by
+    # multiply and shift, up to row 10^6 on a grid-stride launch
+    (12000, 2048, 96, 16, 1), (1000000, 256, 8000, 16, 1),
 ])
 def test_f8_shapes(R, C, SR, SC, batch):
     check_f8(synth.make_f8(R, C, SR, SC, seed=R * 7 + C, batch=batch))
