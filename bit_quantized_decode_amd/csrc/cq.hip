@@ -27,7 +27,8 @@ int cu_count() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
   int n = cache[dev].load(std::memory_order_relaxed);
   if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
       n = 256;
     cache[dev].store(n, std::memory_order_relaxed);
   }
@@ -318,7 +319,8 @@ struct ActLayout {
 };
 
 template <int BITS, int NJ, int LPR, int U, bool CONTIG>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NJ > 2 ? 2 : 4, NJ > 2 ? 2 : 4)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(NJ > 2 ? 2 : 4, NJ > 2 ? 2 : 4)))
 void cq_matvec_b1(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
                   const float* __restrict__ codebook, const float* __restrict__ prepared,
                   float* __restrict__ y, int64_t input_padded, int64_t row_bytes, int log2_group,
@@ -572,11 +574,13 @@ __global__ __launch_bounds__(kRingThreads) void cq_matvec_ring(const RingArgs ar
   const int n_groups = C >> log2_group;
   uint16_t nb[kRingRows];
 #pragma unroll
-  for (int k = 0; k < kRingRows; ++k) nb[k] = norms[(int64_t)min(row0 + k, rows - 1) * n_groups + g];
+  for (int k = 0; k < kRingRows; ++k)
+    nb[k] = norms[(int64_t)min(row0 + k, rows - 1) * n_groups + g];
   V d[kRingRows];
   const uint8_t* base = packed + sl * 64 * BPL + lane * BPL;
   auto issue = [&](int k) {
-    d[k] = stream_load(reinterpret_cast<const V*>(base + (int64_t)min(row0 + k, rows - 1) * row_bytes));
+    d[k] = stream_load(
+        reinterpret_cast<const V*>(base + (int64_t)min(row0 + k, rows - 1) * row_bytes));
   };
 #pragma unroll
   for (int k = 0; k < DR; ++k) issue(k);
@@ -633,7 +637,8 @@ __global__ __launch_bounds__(kRingThreads) void cq_matvec_ring(const RingArgs ar
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         // byte b of the dword: columns 8 t + 2 b (low nibble) and + 1
-        const uint32_t adr = __builtin_amdgcn_perm(ring_word<BPL>(d[k], t), lane_off, 0x0c0c0400u | ((4u + b) << 8));
+        const uint32_t adr = __builtin_amdgcn_perm(ring_word<BPL>(d[k], t), lane_off,
+                                                   0x0c0c0400u | ((4u + b) << 8));
         const float2 c = *reinterpret_cast<const float2*>(tb + adr);
         p0 += c.x * a[8 * t + 2 * b];
         p1 += c.y * a[8 * t + 2 * b + 1];
@@ -700,7 +705,8 @@ __global__ __launch_bounds__(kThreads) void cq_matvec_nb(
   const int n4 = (int)(input_padded >> 2);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const float4* src = reinterpret_cast<const float4*>(prepared + (int64_t)(b < nb ? b : nb - 1) * input_padded);
+    const float4* src =
+        reinterpret_cast<const float4*>(prepared + (int64_t)(b < nb ? b : nb - 1) * input_padded);
     for (int i = tid; i < n4; i += kThreads)
       *reinterpret_cast<float4*>(act_lds + L::offset(4 * i)) = src[i];
     __syncthreads();
@@ -1067,8 +1073,10 @@ void cq_matvec_mfma(const uint8_t* __restrict__ packed, const uint16_t* __restri
           }
         }
         const bf16x8_t bo = __builtin_bit_cast(bf16x8_t, bx[j]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ahi), bo, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, alo), bo, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ahi), bo, acc,
+                                                      0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, alo), bo, acc,
+                                                      0, 0, 0);
       }
       // acc[k]: row 16 T rg + 16 i + 4 q + k of the block, operand column r16;
       // times its norm, then column v (high halves) + column v + 8 (low halves)
@@ -1279,7 +1287,8 @@ void cq_matvec_mfma4(const uint8_t* __restrict__ packed, const uint16_t* __restr
                             __builtin_amdgcn_perm(bxp[t][1], bxp[t][1], 0x01000100u),
                             __builtin_amdgcn_perm(bxp[t][1], bxp[t][1], 0x03020302u)};
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                      __builtin_bit_cast(bf16x8_t, bx), acc, 0, 0, 0);
+                                                      __builtin_bit_cast(bf16x8_t, bx), acc,
+                                                      0, 0, 0);
       }
       // acc[k]: row 16 T rg + 16 i + 4 q + k of the block, operand column r16;
       // times its norm, then column v (high halves) + column v + 8 (low halves)
@@ -1342,11 +1351,12 @@ int launch_b1(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t r
   const int64_t n_steps = (row_count + SLOTS - 1) / SLOTS;
   const int per_cu = NJ > 2 ? 2 : kB1BlocksPerCu;  // the kernel's occupancy
   const int64_t grid = std::min<int64_t>((n_steps + U - 1) / U, (int64_t)cu_count() * per_cu);
-  constexpr bool CONTIG = false;  // measured faster: each load instruction reads 64 consecutive chunks
+  // measured faster: each load instruction reads 64 consecutive chunks
+  constexpr bool CONTIG = false;
   const size_t lds = sizeof(float) * ActLayout<NJ, LPR, CONTIG>::floats(m->input_padded);
-  hipLaunchKernelGGL((cq_matvec_b1<BITS, NJ, LPR, U, CONTIG>), dim3((unsigned)grid), dim3(kThreads), lds, s,
-                     m->packed, m->norms, m->codebook, prepared, y, m->input_padded, m->row_bytes,
-                     ilog2(m->group), row_begin, row_count);
+  hipLaunchKernelGGL((cq_matvec_b1<BITS, NJ, LPR, U, CONTIG>), dim3((unsigned)grid),
+                     dim3(kThreads), lds, s, m->packed, m->norms, m->codebook, prepared, y,
+                     m->input_padded, m->row_bytes, ilog2(m->group), row_begin, row_count);
   return launch_status();
 }
 
@@ -1358,7 +1368,8 @@ int launch_nb(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t y
   const int64_t n_steps = (row_count + SLOTS - 1) / SLOTS;
   // persistent: every workgroup loads all its activations once, so the
   // grid is kept to what the CUs hold at once (2 per CU at 128+ VGPRs)
-  const int64_t grid = std::min<int64_t>((n_steps + U - 1) / U, (int64_t)cu_count() * kNbBlocksPerCu);
+  const int64_t grid =
+      std::min<int64_t>((n_steps + U - 1) / U, (int64_t)cu_count() * kNbBlocksPerCu);
   const size_t lds = sizeof(float) * ActLayout<1, LPR, false>::floats(m->input_padded);
   hipLaunchKernelGGL((cq_matvec_nb<BITS, 1, LPR, 4, U>), dim3((unsigned)grid), dim3(kThreads), lds,
                      s, m->packed, m->norms, m->codebook, prepared, y, m->input_padded,
@@ -1513,10 +1524,12 @@ int launch_mfma_b(const bqd_cq_matrix* m, const float* prepared, float* y, int64
   const int rg = (int)std::max<int64_t>(1, std::min<int64_t>(rg_need, kMfmaMaxSpans / n_spans));
   const int64_t block_rows = 16 * T * rg;
   // every workgroup has a first tile: grid <= n_tiles
-  const int64_t grid = std::min<int64_t>(std::min<int64_t>((row_count + block_rows - 1) / block_rows,
-                                                           cu_count()), (row_count + 15) / 16);
-  hipLaunchKernelGGL((cq_matvec_mfma<BITS, T>), dim3((unsigned)grid), dim3((unsigned)(64 * n_spans * rg)),
-                     0, s, m->packed + row_begin * m->row_bytes,
+  const int64_t blocks = (row_count + block_rows - 1) / block_rows;
+  const int64_t grid =
+      std::min<int64_t>(std::min<int64_t>(blocks, cu_count()), (row_count + 15) / 16);
+  hipLaunchKernelGGL((cq_matvec_mfma<BITS, T>), dim3((unsigned)grid),
+                     dim3((unsigned)(64 * n_spans * rg)), 0, s,
+                     m->packed + row_begin * m->row_bytes,
                      m->norms + row_begin * (m->input_padded / m->group), m->codebook, prepared, y,
                      (int)m->input_padded, m->row_bytes, ilog2(m->group), (int)row_count, y_stride,
                      nb, rg);
@@ -1532,10 +1545,12 @@ int launch_mfma4(const bqd_cq_matrix* m, const float* prepared, float* y, int64_
   const int64_t rg_need = (tiles + cu_count() - 1) / cu_count();
   const int rg = (int)std::max<int64_t>(1, std::min<int64_t>(rg_need, kMfmaMaxSpans / n_spans));
   const int64_t block_rows = 16 * T * rg;
-  const int64_t grid = std::min<int64_t>(std::min<int64_t>((row_count + block_rows - 1) / block_rows,
-                                                           cu_count()), (row_count + 15) / 16);
-  hipLaunchKernelGGL((cq_matvec_mfma4<T, AHEAD>), dim3((unsigned)grid), dim3((unsigned)(64 * n_spans * rg)),
-                     0, s, m->packed + row_begin * m->row_bytes,
+  const int64_t blocks = (row_count + block_rows - 1) / block_rows;
+  const int64_t grid =
+      std::min<int64_t>(std::min<int64_t>(blocks, cu_count()), (row_count + 15) / 16);
+  hipLaunchKernelGGL((cq_matvec_mfma4<T, AHEAD>), dim3((unsigned)grid),
+                     dim3((unsigned)(64 * n_spans * rg)), 0, s,
+                     m->packed + row_begin * m->row_bytes,
                      m->norms + row_begin * (m->input_padded / m->group), m->codebook, prepared, y,
                      (int)m->input_padded, m->row_bytes, ilog2(m->group), (int)row_count, y_stride,
                      nb, rg);
@@ -1558,7 +1573,8 @@ int run_mfma(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t y_
 
 int launch_generic(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t batch,
                    int64_t row_begin, int64_t row_count, hipStream_t s) {
-  const int64_t grid = std::min<int64_t>((row_count + kWavesPerBlock - 1) / kWavesPerBlock, kMaxGrid);
+  const int64_t grid =
+      std::min<int64_t>((row_count + kWavesPerBlock - 1) / kWavesPerBlock, kMaxGrid);
   hipLaunchKernelGGL(cq_matvec_generic, dim3((unsigned)grid), dim3(kThreads), 0, s, m->packed,
                      m->norms, m->codebook, prepared, y, m->input_padded, m->row_bytes,
                      (int)m->bits, ilog2(m->group), row_begin, row_count, batch);

@@ -140,7 +140,8 @@ int launch_i8_fast(const int8_t* w, int64_t R, int64_t C, const uint8_t* gscale,
 
 // Lane layout for rows of n_chunk 16-byte chunks (as the F8 head's), or 0.
 int i8_layout(int64_t n_chunk) {
-  if (n_chunk >= 1 && n_chunk <= 64 && (n_chunk & (n_chunk - 1)) == 0) return (int)(n_chunk * 16 + 1);
+  if (n_chunk >= 1 && n_chunk <= 64 && (n_chunk & (n_chunk - 1)) == 0)
+    return (int)(n_chunk * 16 + 1);
   if (n_chunk == 128) return 64 * 16 + 2;
   if (n_chunk == 256) return 64 * 16 + 4;
   if (n_chunk == 512) return 64 * 16 + 8;

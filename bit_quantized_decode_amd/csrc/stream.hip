@@ -60,8 +60,8 @@ __global__ __launch_bounds__(kReadThreads) void read_stream_kernel(const u32x4_n
 int launch_read_stream(const void* buf, int64_t bytes, uint32_t* out, hipStream_t s) {
   const int64_t n16 = bytes / 16;
   const int64_t per_block = (int64_t)kReadThreads * kReadLoads;
-  const int64_t grid =
-      std::max<int64_t>(1, std::min<int64_t>(BQD_READ_STREAM_WORDS, (n16 + per_block - 1) / per_block));
+  const int64_t blocks = (n16 + per_block - 1) / per_block;
+  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(BQD_READ_STREAM_WORDS, blocks));
   hipLaunchKernelGGL(read_stream_kernel, dim3((unsigned)grid), dim3(kReadThreads), 0, s,
                      static_cast<const u32x4_nt*>(buf), n16, out);
   return launch_status();
