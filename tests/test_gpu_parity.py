@@ -472,6 +472,8 @@ def test_f8_head_sampled_rows(cache):
     # scale blocks of a whole number of rows that is not a power of two (125): the scale row by
     # multiply and shift, up to row 10^6 on a grid-stride launch
     (12000, 2048, 96, 16, 1), (1000000, 256, 8000, 16, 1),
+    # rows wider than the fast kernel's widest lane layout (8192 columns): the generic kernel
+    (64, 16384, 2, 64, 2),
 ])
 def test_f8_shapes(R, C, SR, SC, batch):
     check_f8(synth.make_f8(R, C, SR, SC, seed=R * 7 + C, batch=batch))
@@ -507,6 +509,7 @@ def test_f8_unaligned_weight_pointer():
 I8_CASES = [
     (37, 80, 16, 1), (300, 4096, 16, 1), (100, 2048, 32, 3), (65, 128, 16, 2), (33, 16, 16, 1),
     (17, 8192, 64, 1), (10, 100, 7, 2), (513, 1024, 16, 1), (3, 4096, 4096, 1),
+    (40, 16384, 16, 2),
 ]
 
 
