@@ -659,6 +659,79 @@ def test_empty_problems_are_no_ops():
 
 
 # ------------------------------------------------------------- graph replay
+def test_graph_replay_matches_eager_beyond_the_path(cache):
+    """The entry points beyond the five workloads captured in one HIP graph:
+    the fused prepare + matvec, several matrices in one launch, the I8 matvec,
+    storeInt8 and the key dot, the Hadamard MLP and the sampler.  Every
+    replay, with eager fills and synchronizations between replays, equals the
+    eager result bitwise; the sampler's state is reset before each replay and
+    then holds the eager state after one draw."""
+    c4 = workload(cache, "cq4_16384x4096_b8")
+    m4 = dev_matrix(c4)
+    x1 = to_dev(c4.x[:1])
+    shapes = [synth.CqShape(2048, 512, 512, 128, 4), synth.CqShape(300, 512, 512, 128, 4)]
+    cases = [synth.make_cq(sh, seed=880 + k) for k, sh in enumerate(shapes)]
+    ms = [dev_matrix(c) for c in cases]
+    xm = to_dev(cases[0].x[0])
+    i8 = synth.make_i8(300, 4096, 16, seed=881)
+    w8, s8, x8 = to_dev(i8.w), to_dev(i8.scale), to_dev(i8.x)
+    kv = synth.make_kv(1000, 128, seed=882)
+    v, xq = to_dev(kv.v), to_dev(kv.x)
+    hm = synth.make_hmlp(512, 2048, seed=883)
+    hn, d1, d2, d3, hr, hu = (to_dev(a) for a in (hm.n, hm.d1, hm.d2, hm.d3, hm.resid, hm.u))
+    logits = to_dev(_logits("normal", 50000, 884))
+    seed = 0x1234567
+    state = _state_tensor(seed)
+    ws = torch.empty(bqd.logits_sample_workspace_bytes(50000, 16), dtype=torch.uint8, device=DEV)
+    p1 = torch.empty(1, c4.shape.input_padded, device=DEV)
+    y1 = torch.empty(1, c4.shape.output, device=DEV)
+    pm = torch.empty(512, device=DEV)
+    ym = [torch.empty(sh.output, device=DEV) for sh in shapes]
+    yi = torch.empty(1, i8.R, device=DEV)
+    q = torch.empty(1000, 128, dtype=torch.int8, device=DEV)
+    qs = torch.empty(1000, device=DEV)
+    yk = torch.empty(1, 1000, device=DEV)
+    ho = torch.empty_like(hn)
+    sampled = []
+
+    def work():
+        bqd.cq_prepare_matvec(m4, x1, prepared=p1, out=y1)
+        bqd.cq_prepare_matvec_multi(ms, xm, prepared=pm, outs=ym)
+        bqd.i8_matvec(w8, s8, x8, G=16, out=yi)
+        bqd.kv_quantize_int8(v, q=q, scales=qs)
+        bqd.kv_int8_dot(q, qs, xq, out=yk)
+        bqd.hadamard_mlp(hn, 2048, d1, d2, d3, hr, hu, out=ho)
+        sampled.append(bqd.logits_sample(logits, 16, 0.9, state, ws))
+
+    outs = lambda: [p1, y1, pm, *ym, yi, q, qs, yk, ho]
+    work()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs()]
+    ref_draw = [t.clone() for t in sampled[-1]]
+    ref_state = state.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    draw = sampled[-1]
+    for _ in range(4):
+        for t in outs() + list(draw):
+            t.fill_(-1)
+        state.copy_(_state_tensor(seed))
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, r in zip(outs(), ref):
+            assert torch.equal(t, r)
+        for t, r in zip(draw, ref_draw):
+            assert torch.equal(t, r)
+        assert torch.equal(state, ref_state)
+
+
 def test_graph_replay_matches_eager(cache):
     """The path captured in a HIP graph: every replay, with eager work and
     synchronizations between replays, equals the eager result bitwise."""
