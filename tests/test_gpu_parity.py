@@ -93,6 +93,8 @@ SMALL = [
     synth.CqShape(11, 96, 96, 32, 2), synth.CqShape(3, 250, 256, 128, 5, row_bytes=161),
     # matrix-core batch path: groups >= 256, whole 256-column spans, ragged row tiles
     synth.CqShape(37, 700, 768, 256, 2), synth.CqShape(20, 4096, 4096, 1024, 4, row_bytes=2052),
+    # rows wider than every fast layout (16384 columns): the generic kernels
+    synth.CqShape(7, 16000, 16384, 1024, 4),
 ]
 
 
