@@ -286,14 +286,14 @@ __global__ __launch_bounds__(kThreads) void cq_matvec_generic(
 // ------------------------------------------------------ fast matvec, batch 1
 // Rows whose padded width is a multiple of 32 columns, groups of >= 32 and
 // dword-aligned rows.  A 32-column chunk is BITS dwords; LPR lanes share a
-// row and each owns NJ chunks: chunks q*NJ .. q*NJ+NJ-1 when CONTIG (one
-// contiguous span, so one group norm per row once groups span it), else
-// chunks q + LPR*j (each load instruction of a wavefront then reads 64
-// consecutive chunks).  Every lane keeps the prepared activations of its
-// chunks in registers for the whole kernel (the same columns for every row).
-// They are staged once per workgroup through LDS: coalesced global loads,
-// then 16-byte LDS reads from a layout padded by 4 floats per lane span so
-// that the 16 lanes of a read phase hit distinct banks.  The codebook is
+// row and lane q owns the NJ chunks q + LPR*j, so each load instruction of a
+// wavefront reads 64 consecutive chunks (measured faster than each lane
+// owning NJ adjacent chunks, which would share one group norm).  Every lane
+// keeps the prepared activations of its chunks in registers for the whole
+// kernel (the same columns for every row).  They are staged once per
+// workgroup through LDS: coalesced global loads, then 16-byte LDS reads from
+// a layout padded by 4 floats per chunk so that the 16 lanes of a read phase
+// hit distinct banks.  The codebook is
 // looked up in LDS (2^BITS distinct words in distinct banks: conflict free),
 // each chunk partial is multiplied by its group norm, and the LPR lanes of a
 // row reduce with DPP.  The codebook lookups are the LDS's limit and their
@@ -301,31 +301,22 @@ __global__ __launch_bounds__(kThreads) void cq_matvec_generic(
 // wavefronts per SIMD; 2 for rows of 8192 columns, whose activations alone
 // take 128) and the grid is persistent, each workgroup walking steps of
 // SLOTS*U rows.
-template <int NJ, int LPR, bool CONTIG>
+// LDS layout of the staged activations: each 32-column chunk padded to 36 floats.
 struct ActLayout {
-  static constexpr int kUnit = CONTIG ? 32 * NJ : 32;  // floats read contiguously by a lane
-  static constexpr int kStride = kUnit + 4;            // padded LDS stride of a unit
+  static constexpr int kStride = 32 + 4;  // padded LDS stride of a chunk
   // LDS float offset of float f of the padded row
-  __device__ static int offset(int f) {
-    const int c = f >> 5;  // chunk
-    const int unit = CONTIG ? c / NJ : c;
-    const int within = CONTIG ? (c % NJ) * 32 + (f & 31) : (f & 31);
-    return unit * kStride + within;
-  }
-  static int64_t floats(int64_t input_padded) {
-    const int64_t n_chunk = input_padded / 32;
-    return (CONTIG ? n_chunk / NJ : n_chunk) * kStride;
-  }
+  __device__ static int offset(int f) { return (f >> 5) * kStride + (f & 31); }
+  static int64_t floats(int64_t input_padded) { return input_padded / 32 * kStride; }
 };
 
-template <int BITS, int NJ, int LPR, int U, bool CONTIG>
+template <int BITS, int NJ, int LPR, int U>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(NJ > 2 ? 2 : 4, NJ > 2 ? 2 : 4)))
 void cq_matvec_b1(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
                   const float* __restrict__ codebook, const float* __restrict__ prepared,
                   float* __restrict__ y, int64_t input_padded, int64_t row_bytes, int log2_group,
                   int64_t row_begin, int64_t row_count) {
-  typedef ActLayout<NJ, LPR, CONTIG> L;
+  typedef ActLayout L;
   constexpr int SLOTS = kThreads / LPR;  // rows per step
   extern __shared__ float act_lds[];
   __shared__ float cb[32];
@@ -336,9 +327,7 @@ void cq_matvec_b1(const uint8_t* __restrict__ packed, const uint16_t* __restrict
   const int rows = (int)row_count;  // < 2^30, validated
   const int n_steps = (rows + SLOTS - 1) / SLOTS;
   const int stride = (int)gridDim.x * U;
-  auto chunk_of = [&](int j) { return CONTIG ? q * NJ + j : q + LPR * j; };
-  // one norm per row when the lane's chunks lie in one group
-  const bool one_norm = CONTIG && (32 * NJ) <= (1 << log2_group);
+  auto chunk_of = [&](int j) { return q + LPR * j; };
   const uint8_t* lane_base = packed + row_begin * row_bytes + 4 * BITS * chunk_of(0);
   const uint16_t* norm_base = norms + row_begin * n_groups;
   int gidx[NJ];
@@ -376,19 +365,13 @@ void cq_matvec_b1(const uint8_t* __restrict__ packed, const uint16_t* __restrict
       const uint32_t* pc = reinterpret_cast<const uint32_t*>(lane_base + (int64_t)i * row_bytes);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const int off = CONTIG ? BITS * j : BITS * LPR * j;
+        const int off = BITS * LPR * j;
 #pragma unroll
         for (int t = 0; t < BITS; ++t) d[u][j][t] = stream_load(pc + off + t);
       }
       const uint16_t* nr = norm_base + (int64_t)i * n_groups;
-      if (one_norm) {
-        const uint16_t n0 = nr[gidx[0]];
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) nb[u][j] = n0;
-      } else {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) nb[u][j] = nr[gidx[j]];
-      }
+      for (int j = 0; j < NJ; ++j) nb[u][j] = nr[gidx[j]];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -685,7 +668,7 @@ __global__ __launch_bounds__(kThreads) void cq_matvec_nb(
   constexpr int SLOTS = LPR <= kThreads ? kThreads / LPR : 1;  // rows per step
   constexpr int WPS = LPR > kWave ? LPR / kWave : 1;            // wavefronts per row
   constexpr int RED = LPR > kWave ? kWavesPerBlock * U * NB : 1;
-  typedef ActLayout<NJ, LPR, false> L;
+  typedef ActLayout L;
   extern __shared__ float act_lds[];  // one padded activation row at a time
   __shared__ float cb[32];
   __shared__ float red[RED];
@@ -1351,10 +1334,8 @@ int launch_b1(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t r
   const int64_t n_steps = (row_count + SLOTS - 1) / SLOTS;
   const int per_cu = NJ > 2 ? 2 : kB1BlocksPerCu;  // the kernel's occupancy
   const int64_t grid = std::min<int64_t>((n_steps + U - 1) / U, (int64_t)cu_count() * per_cu);
-  // measured faster: each load instruction reads 64 consecutive chunks
-  constexpr bool CONTIG = false;
-  const size_t lds = sizeof(float) * ActLayout<NJ, LPR, CONTIG>::floats(m->input_padded);
-  hipLaunchKernelGGL((cq_matvec_b1<BITS, NJ, LPR, U, CONTIG>), dim3((unsigned)grid),
+  const size_t lds = sizeof(float) * ActLayout::floats(m->input_padded);
+  hipLaunchKernelGGL((cq_matvec_b1<BITS, NJ, LPR, U>), dim3((unsigned)grid),
                      dim3(kThreads), lds, s, m->packed, m->norms, m->codebook, prepared, y,
                      m->input_padded, m->row_bytes, ilog2(m->group), row_begin, row_count);
   return launch_status();
@@ -1370,7 +1351,7 @@ int launch_nb(const bqd_cq_matrix* m, const float* prepared, float* y, int64_t y
   // grid is kept to what the CUs hold at once (2 per CU at 128+ VGPRs)
   const int64_t grid =
       std::min<int64_t>((n_steps + U - 1) / U, (int64_t)cu_count() * kNbBlocksPerCu);
-  const size_t lds = sizeof(float) * ActLayout<1, LPR, false>::floats(m->input_padded);
+  const size_t lds = sizeof(float) * ActLayout::floats(m->input_padded);
   hipLaunchKernelGGL((cq_matvec_nb<BITS, 1, LPR, 4, U>), dim3((unsigned)grid), dim3(kThreads), lds,
                      s, m->packed, m->norms, m->codebook, prepared, y, m->input_padded,
                      m->row_bytes, ilog2(m->group), row_begin, row_count, y_stride, nb);
