@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 (vector)
 HEAD_STAGE = "f8_head_246272x4096_matvec"
+STAGE_LAUNCHES = 16  # back-to-back launches per timed stage graph
 METRIC = "weight-stream GB/s & % of HBM peak, CQ/F8 decode matvec; rows/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "f8_head_246272x4096_hbm_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_quantized_decode_amd", "csrc", f) for f in ("f8.hip", "device.h")]
@@ -328,12 +329,12 @@ def stage_probe(torch, bqd, synth, name, hot):
     if name not in by_name:
         raise SystemExit(f"bench.py: no stage {name!r}; stages: {', '.join(sorted(by_name))}")
     c = by_name[name]
-    period = 16
-    g = capture(torch, lambda: [c.calls[k % len(c.calls)]() for k in range(period)])
+    n = STAGE_LAUNCHES
+    g = capture(torch, lambda: [c.calls[k % len(c.calls)]() for k in range(n)])
     for _ in range(4):
         g.replay()
     torch.cuda.synchronize()
-    print(json.dumps({"stage": name, "launches": 4 * period + period, "bytes": c.nbytes}), flush=True)
+    print(json.dumps({"stage": name, "launches": 5 * n, "bytes": c.nbytes}), flush=True)
 
 
 def _dispatch_kib(out_dir, counter):
@@ -421,10 +422,10 @@ def main():
     rest = [c for c in cases if c is not head_case]
     rest_graphs = [capture(torch, lambda k=k: [c.calls[k % len(c.calls)]() for c in rest])
                    for k in range(period)]
-    # Per stage (the head aside): one graph of `period` back-to-back launches
-    # over the copies.
+    # Per stage (the head aside): one graph of STAGE_LAUNCHES back-to-back
+    # launches over the copies.
     stage_graphs = {c.name: capture(torch, lambda c=c: [c.calls[k % len(c.calls)]()
-                                                       for k in range(period)])
+                                                       for k in range(STAGE_LAUNCHES)])
                     for c in rest + extra_cases}
 
     log(f"warmup {args.warmup} steps")
@@ -440,8 +441,8 @@ def main():
     step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
 
     # The head inside the step: HIP events on the launch stream bracket runs
-    # of 3 * period replays of the whole step and of the step without the
-    # head, alternated; each difference per step is one sample.
+    # of 48 replays of the whole step and of the step without the head,
+    # alternated; each difference per step is one sample.
     def replays_ms(graphs, n):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -454,13 +455,13 @@ def main():
     replays_ms(rest_graphs, period)
     head_samples = []
     for _ in range(8):
-        full_ms = replays_ms(step_graphs, 3 * period)
-        head_samples.append(full_ms - replays_ms(rest_graphs, 3 * period))
+        full_ms = replays_ms(step_graphs, 3 * STAGE_LAUNCHES)
+        head_samples.append(full_ms - replays_ms(rest_graphs, 3 * STAGE_LAUNCHES))
     head_ms = np.array(head_samples)
 
     # The other stages: HIP events on the launch stream bracket replays of
-    # each stage's graph of `period` back-to-back launches.
-    reps = max(4, args.steps // period)
+    # each stage's graph of STAGE_LAUNCHES back-to-back launches.
+    reps = max(4, args.steps // STAGE_LAUNCHES)
     per_case = {}
     extras = {}
     for c in cases + extra_cases:
@@ -476,7 +477,7 @@ def main():
                 g.replay()
                 e1.record(stream)
             torch.cuda.synchronize()
-            ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) / period
+            ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) / STAGE_LAUNCHES
         c.ms = ms
         gbs = c.nbytes / (ms.mean() * 1e-3) / 1e9
         rec = dict(
@@ -503,7 +504,7 @@ def main():
     ws = torch.empty(bqd.logits_sample_workspace_bytes(logits.numel(), 64), dtype=torch.uint8,
                      device="cuda")
     g = capture(torch, lambda: [bqd.logits_sample(logits, 64, 0.8, state, ws)
-                                for _ in range(period)])
+                                for _ in range(STAGE_LAUNCHES)])
     g.replay()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
@@ -512,7 +513,7 @@ def main():
         g.replay()
         e1.record(stream)
     torch.cuda.synchronize()
-    ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) / period
+    ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) / STAGE_LAUNCHES
     extras["head_logits_sample_k64"] = dict(
         us_mean=round(float(ms.mean() * 1e3), 3), logits=logits.numel(), k=64, temperature=0.8,
         note="not part of the step: the sampler over the head's logits")
