@@ -842,6 +842,22 @@ def test_sample_ragged_sizes(n, k):
     check_sample(_logits("ties", n, n + 1), k, 1.3, seed=777 + n)
 
 
+@pytest.mark.parametrize("n,k", [(40, 40), (246272, 64)])
+def test_sample_zeros_and_nans_in_top_k(n, k):
+    """Zeros of both signs at the top and NaNs (with payloads) inside the k:
+    the values whose keys drop the sign or the payload come back bit for bit."""
+    rng = np.random.default_rng(n)
+    x = -np.abs(rng.standard_normal(n)).astype(np.float32) - np.float32(0.5)
+    pos = rng.choice(n, 30 if n > 64 else 12, replace=False)
+    x[pos[:len(pos) // 2]] = np.float32(-0.0)
+    x[pos[len(pos) // 2:]] = np.float32(0.0)
+    if n <= k:  # every logit is a candidate: NaNs with distinct payloads rank last
+        nan_bits = np.array([0x7fc00001, 0xffc00002, 0x7f800003, 0x7fffffff], np.uint32)
+        x[rng.choice(np.setdiff1d(np.arange(n), pos), 4, replace=False)] = nan_bits.view(np.float32)
+    check_sample(x, k, 0.9, seed=4242 + n)
+    check_sample(x, k, 0.0, seed=99 + n)
+
+
 def test_sample_chain_of_twenty():
     """Twenty draws on one device state continue the oracle's sequence."""
     check_sample(_logits("normal", 50000, 5), 16, 1.0, seed=1, calls=20)
