@@ -56,7 +56,13 @@ __global__ __launch_bounds__(kF8Threads) void f8_matvec_generic(
 // Montgomery, "Division by invariant integers using multiplication", 1994,
 // Theorem 4.2); a 64-bit division per row otherwise (~80 instructions, a
 // large share of the loop's work on the head).
-template <int NJ, int LPR, int U, bool EXACT>
+//
+// SHARE: an iteration's U rows of a lane, (s0 + u) SLOTS + slot with s0 a
+// multiple of U, lie in one aligned block of U SLOTS rows; where R / SR is a
+// multiple of U SLOTS that block is inside one scale block, so the row's
+// block scales are read once per iteration instead of once per row (a third
+// fewer load instructions on the head, ~1.5% faster).
+template <int NJ, int LPR, int U, bool EXACT, bool SHARE>
 __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(NJ <= 4 ? 4 : 1)))
 void f8_matvec_fast(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ scale, const float* __restrict__ x,
@@ -92,7 +98,7 @@ void f8_matvec_fast(
       for (int j = 0; j < NJ; ++j) {
         const u32x4_nt t = stream_load(reinterpret_cast<const u32x4_nt*>(wr + q + LPR * j));
         d[u][j] = make_uint4(t.x, t.y, t.z, t.w);
-        sb[u][j] = srow[scol[j]];
+        sb[u][j] = (SHARE && u > 0) ? sb[0][j] : srow[scol[j]];
       }
     }
 #pragma unroll
@@ -136,11 +142,17 @@ int launch_f8_fast(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale,
     int l = 0;
     while ((uint64_t(1) << l) < d) ++l;
     const uint64_t magic = ((uint64_t(1) << (31 + l)) + d - 1) / d;  // < 2^32
-    hipLaunchKernelGGL((f8_matvec_fast<NJ, LPR, U, true>), dim3((unsigned)grid), dim3(kF8Threads),
-                       0, s, w, scale, x, y, (int)R, C, SR, SC, C / SC, (uint32_t)magic, 31 + l);
+    if (d % (U * SLOTS) == 0)
+      hipLaunchKernelGGL((f8_matvec_fast<NJ, LPR, U, true, true>), dim3((unsigned)grid),
+                         dim3(kF8Threads), 0, s, w, scale, x, y, (int)R, C, SR, SC, C / SC,
+                         (uint32_t)magic, 31 + l);
+    else
+      hipLaunchKernelGGL((f8_matvec_fast<NJ, LPR, U, true, false>), dim3((unsigned)grid),
+                         dim3(kF8Threads), 0, s, w, scale, x, y, (int)R, C, SR, SC, C / SC,
+                         (uint32_t)magic, 31 + l);
   } else {
-    hipLaunchKernelGGL((f8_matvec_fast<NJ, LPR, U, false>), dim3((unsigned)grid), dim3(kF8Threads),
-                       0, s, w, scale, x, y, (int)R, C, SR, SC, C / SC, 0u, 0);
+    hipLaunchKernelGGL((f8_matvec_fast<NJ, LPR, U, false, false>), dim3((unsigned)grid),
+                       dim3(kF8Threads), 0, s, w, scale, x, y, (int)R, C, SR, SC, C / SC, 0u, 0);
   }
   return launch_status();
 }

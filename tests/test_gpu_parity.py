@@ -476,6 +476,10 @@ def test_f8_head_sampled_rows(cache):
     (12000, 2048, 96, 16, 1), (1000000, 256, 8000, 16, 1),
     # rows wider than the fast kernel's widest lane layout (8192 columns): the generic kernel
     (64, 16384, 2, 64, 2),
+    # scale blocks of a multiple of an iteration's aligned rows (U * SLOTS = 64, 32, 8 for 8, 16
+    # and 64 lanes per row): one scale read per iteration; 12 rows per block (not a multiple of 8)
+    (8192, 128, 64, 8, 1), (4096, 256, 64, 16, 2), (24576, 4096, 96, 32, 1),
+    (4800, 4096, 400, 32, 1),
 ])
 def test_f8_shapes(R, C, SR, SC, batch):
     check_f8(synth.make_f8(R, C, SR, SC, seed=R * 7 + C, batch=batch))
