@@ -60,8 +60,8 @@ __global__ __launch_bounds__(kF8Threads) void f8_matvec_generic(
 // SHARE: an iteration's U rows of a lane, (s0 + u) SLOTS + slot with s0 a
 // multiple of U, lie in one aligned block of U SLOTS rows; where R / SR is a
 // multiple of U SLOTS that block is inside one scale block, so the row's
-// block scales are read once per iteration instead of once per row (a third
-// fewer load instructions on the head, ~1.5% faster).
+// block scales are read once per iteration instead of once per row (a fifth
+// fewer vector memory reads on the head, ~1.5% faster).
 template <int NJ, int LPR, int U, bool EXACT, bool SHARE>
 __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(NJ <= 4 ? 4 : 1)))
 void f8_matvec_fast(
