@@ -62,24 +62,43 @@ __global__ __launch_bounds__(kF8Threads) void f8_matvec_generic(
 // multiple of U SLOTS that block is inside one scale block, so the row's
 // block scales are read once per iteration instead of once per row (a fifth
 // fewer vector memory reads on the head, ~1.5% faster).
+//
+// The workgroup stages x in LDS once (float4 loads where x is 16-byte
+// aligned, x_vec) and each wavefront takes its lanes' activations from there:
+// one copy of x per workgroup from L2 instead of one per wavefront (~1%).
 template <int NJ, int LPR, int U, bool EXACT, bool SHARE>
 __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(NJ <= 4 ? 4 : 1)))
 void f8_matvec_fast(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ scale, const float* __restrict__ x,
     float* __restrict__ y, int R, int64_t C, int64_t SR, int64_t SC, int64_t cols_per_block,
-    uint32_t blk_magic, int blk_shift) {
+    uint32_t blk_magic, int blk_shift, int x_vec) {
   constexpr int SLOTS = kF8Threads / LPR;
+  constexpr int CX = 16 * LPR * NJ;  // = C
+  __shared__ __align__(16) float xs[CX];
   const int tid = threadIdx.x;
   const int slot = tid / LPR;
   const int q = tid % LPR;
+  if (x_vec) {
+    for (int i = tid; i < CX / 4; i += kF8Threads)
+      reinterpret_cast<float4*>(xs)[i] = reinterpret_cast<const float4*>(x)[i];
+  } else {
+    for (int i = tid; i < CX; i += kF8Threads) xs[i] = x[i];
+  }
+  __syncthreads();
   float act[NJ][16];
   int scol[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int64_t c = 16 * (int64_t)(q + LPR * j);
+    const int c = 16 * (q + LPR * j);
     scol[j] = (int)(c / cols_per_block);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) act[j][k] = x[c + k];
+    for (int k = 0; k < 16; k += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(xs + c + k);
+      act[j][k] = v.x;
+      act[j][k + 1] = v.y;
+      act[j][k + 2] = v.z;
+      act[j][k + 3] = v.w;
+    }
   }
   // rows < 2^30: 32-bit row arithmetic
   const int n_steps = (R + SLOTS - 1) / SLOTS;
@@ -136,6 +155,7 @@ int launch_f8_fast(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale,
   constexpr int SLOTS = kF8Threads / LPR;
   const int64_t n_steps = (R + SLOTS - 1) / SLOTS;
   const int64_t grid = std::min<int64_t>((n_steps + U - 1) / U, kMaxGrid);
+  const int x_vec = is_aligned(x, 16) ? 1 : 0;
   if (R % SR == 0) {
     // rows per scale block d: magic = ceil(2^(31 + l) / d), 2^l >= d > 2^(l - 1)
     const uint64_t d = (uint64_t)(R / SR);
@@ -145,14 +165,15 @@ int launch_f8_fast(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale,
     if (d % (U * SLOTS) == 0)
       hipLaunchKernelGGL((f8_matvec_fast<NJ, LPR, U, true, true>), dim3((unsigned)grid),
                          dim3(kF8Threads), 0, s, w, scale, x, y, (int)R, C, SR, SC, C / SC,
-                         (uint32_t)magic, 31 + l);
+                         (uint32_t)magic, 31 + l, x_vec);
     else
       hipLaunchKernelGGL((f8_matvec_fast<NJ, LPR, U, true, false>), dim3((unsigned)grid),
                          dim3(kF8Threads), 0, s, w, scale, x, y, (int)R, C, SR, SC, C / SC,
-                         (uint32_t)magic, 31 + l);
+                         (uint32_t)magic, 31 + l, x_vec);
   } else {
     hipLaunchKernelGGL((f8_matvec_fast<NJ, LPR, U, false, false>), dim3((unsigned)grid),
-                       dim3(kF8Threads), 0, s, w, scale, x, y, (int)R, C, SR, SC, C / SC, 0u, 0);
+                       dim3(kF8Threads), 0, s, w, scale, x, y, (int)R, C, SR, SC, C / SC, 0u, 0,
+                       x_vec);
   }
   return launch_status();
 }

@@ -510,6 +510,23 @@ def test_f8_unaligned_weight_pointer():
     assert_tol(got, ref, mag, "unaligned f8")
 
 
+def test_f8_activation_not_16_byte_aligned():
+    """x at a 4-byte (not 16-byte) offset: the fast kernel stages it in LDS one
+    float at a time; every lane layout, batch 2 (the second vector 4 bytes
+    further on as well)."""
+    for R, C, SR, SC in ((256, 4096, 2, 32), (96, 1024, 3, 8), (64, 128, 1, 1), (80, 8192, 5, 64)):
+        case = synth.make_f8(R, C, SR, SC, seed=R + C, batch=2)
+        buf = torch.zeros(2 * C + 4, dtype=torch.float32, device=DEV)
+        buf[1:1 + 2 * C] = to_dev(case.x).reshape(-1)
+        x = buf[1:1 + 2 * C].view(2, C)
+        assert x.data_ptr() % 16 == 4
+        got = bqd.f8_matvec(to_dev(case.w), to_dev(case.scale), x).cpu().numpy()
+        ref, mag = oracle.f8_matvec(case.w, R, C, case.scale, SR, SC, case.x)
+        assert_tol(got, ref, mag, f"f8 x at +4 bytes {R}x{C}")
+        aligned = bqd.f8_matvec(to_dev(case.w), to_dev(case.scale), to_dev(case.x)).cpu().numpy()
+        assert bits_eq(got, aligned), (R, C)
+
+
 # -------------------------------------------------------------- empty calls
 # ----------------------------------------------------------------------- I8
 I8_CASES = [
