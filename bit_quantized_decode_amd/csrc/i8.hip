@@ -73,20 +73,37 @@ __global__ __launch_bounds__(kI8Threads)
 __attribute__((amdgpu_waves_per_eu(NJ <= 4 && !ROWSCALE ? 4 : 1))) void i8_matvec_fast(
     const int8_t* __restrict__ w, const uint8_t* __restrict__ gscale,
     const float* __restrict__ rscale, const float* __restrict__ x, float* __restrict__ y,
-    int64_t R, int64_t C, int64_t G) {
+    int64_t R, int64_t C, int64_t G, int x_vec) {
   constexpr int SLOTS = kI8Threads / LPR;
+  constexpr int CX = 16 * LPR * NJ;  // = C
+  __shared__ __align__(16) float xs[CX];
   const int tid = threadIdx.x;
   const int slot = tid / LPR;
   const int q = tid % LPR;
   const int64_t ns = ROWSCALE ? 0 : (C + G - 1) / G;
+  // x staged in LDS once per workgroup (float4 loads where it is 16-byte
+  // aligned), then each lane's activations read from there
+  if (x_vec) {
+    for (int i = tid; i < CX / 4; i += kI8Threads)
+      reinterpret_cast<float4*>(xs)[i] = reinterpret_cast<const float4*>(x)[i];
+  } else {
+    for (int i = tid; i < CX; i += kI8Threads) xs[i] = x[i];
+  }
+  __syncthreads();
   float act[NJ][16];
   int64_t scol[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int64_t c = 16 * (int64_t)(q + LPR * j);
+    const int c = 16 * (q + LPR * j);
     scol[j] = ROWSCALE ? 0 : c / G;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) act[j][k] = x[c + k];
+    for (int k = 0; k < 16; k += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(xs + c + k);
+      act[j][k] = v.x;
+      act[j][k + 1] = v.y;
+      act[j][k + 2] = v.z;
+      act[j][k + 3] = v.w;
+    }
   }
   const int64_t n_steps = (R + SLOTS - 1) / SLOTS;
   for (int64_t s0 = (int64_t)blockIdx.x * U; s0 < n_steps; s0 += (int64_t)gridDim.x * U) {
@@ -134,7 +151,8 @@ int launch_i8_fast(const int8_t* w, int64_t R, int64_t C, const uint8_t* gscale,
   const int64_t n_steps = (R + SLOTS - 1) / SLOTS;
   const int64_t grid = std::min<int64_t>((n_steps + U - 1) / U, kI8MaxGrid);
   hipLaunchKernelGGL((i8_matvec_fast<NJ, LPR, U, ROWSCALE>), dim3((unsigned)grid),
-                     dim3(kI8Threads), 0, s, w, gscale, rscale, x, y, R, C, G);
+                     dim3(kI8Threads), 0, s, w, gscale, rscale, x, y, R, C, G,
+                     is_aligned(x, 16) ? 1 : 0);
   return launch_status();
 }
 

@@ -567,6 +567,23 @@ def test_i8_matvec_unaligned_weights():
     assert_tol(got, ref, mag, "i8_matvec unaligned")
 
 
+def test_i8_matvec_activation_not_16_byte_aligned():
+    """x 4 bytes off 16-byte alignment: the fast kernel stages it in LDS one
+    float at a time; the result equals the aligned call's bit for bit."""
+    for R, C, G in ((40, 4096, 16), (33, 1024, 32), (20, 128, 16)):
+        case = synth.make_i8(R, C, G, seed=R + C)
+        xf = np.ascontiguousarray(case.x, np.float32).reshape(-1)
+        buf = torch.zeros(xf.size + 4, dtype=torch.float32, device=DEV)
+        buf[1:1 + xf.size] = to_dev(xf)
+        x = buf[1:1 + xf.size].view(case.x.shape)
+        assert x.data_ptr() % 16 == 4
+        got = bqd.i8_matvec(to_dev(case.w), to_dev(case.scale), x, G).cpu().numpy()
+        ref, mag = oracle.i8_matvec(case.w, R, C, case.scale, G, case.x)
+        assert_tol(got, ref, mag, f"i8 x at +4 bytes {R}x{C}")
+        aligned = bqd.i8_matvec(to_dev(case.w), to_dev(case.scale), to_dev(case.x), G).cpu().numpy()
+        assert bits_eq(got, aligned), (R, C)
+
+
 def test_i8_head_sampled_rows(cache):
     """The I8 head at full size in the benchmark's launch configuration; the
     oracle checks 16 row blocks (first, ragged last, random)."""
