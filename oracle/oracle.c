@@ -9,36 +9,27 @@
 #include <string.h>
 
 /* ---------------------------------------------------------------- O1 -- */
-/* [P3] §3 "Decode FP16 control tensors": rebuild the fp32 bit pattern from
- * sign, 5-bit exponent and 10-bit mantissa.  Zero exponent: signed zero, or a
- * subnormal renormalized by shifting the mantissa up until its leading one
- * reaches the hidden-bit position; all-ones exponent: infinity or NaN with the
- * mantissa carried over; otherwise rebias the exponent from 15 to 127. */
+/* [P3] §3 "Decode FP16 control tensors", written from the IEEE 754 binary16
+ * format rather than from bit surgery.  A code is a sign s (bit 15), a
+ * biased exponent E (bits 10..14, bias 15) and a fraction F (bits 0..9):
+ *   E = 0       value (-1)^s * F * 2^-24          (zero or subnormal)
+ *   E = 1..30   value (-1)^s * (1024 + F) * 2^(E - 25)
+ *   E = 31      infinity when F = 0, otherwise NaN.
+ * The magnitude is formed with ldexp in double; every binary16 value is
+ * exactly representable in binary32, so the final conversion is exact. */
 float oracle_f16(uint16_t h)
 {
-    uint32_t sign = ((uint32_t)h & 0x8000u) << 16;
-    int32_t exponent = (h >> 10) & 0x1f;
-    uint32_t mantissa = h & 0x3ffu;
-    uint32_t bits32;
-    if (exponent == 0) {
-        if (mantissa == 0) {
-            bits32 = sign;
-        } else {
-            int32_t e = 127 - 15 + 1;
-            while ((mantissa & 0x400u) == 0) {
-                mantissa <<= 1;
-                e--;
-            }
-            bits32 = sign | ((uint32_t)e << 23) | ((mantissa & 0x3ffu) << 13);
-        }
-    } else if (exponent == 0x1f) {
-        bits32 = sign | 0x7f800000u | (mantissa << 13);
-    } else {
-        bits32 = sign | ((uint32_t)(exponent - 15 + 127) << 23) | (mantissa << 13);
-    }
-    float f;
-    memcpy(&f, &bits32, sizeof f);
-    return f;
+    int negative = (h >> 15) & 1;
+    int E = (h >> 10) & 31;
+    int F = h & 1023;
+    double magnitude;
+    if (E == 31)
+        magnitude = F == 0 ? HUGE_VAL : NAN;
+    else if (E == 0)
+        magnitude = ldexp((double)F, -24);
+    else
+        magnitude = ldexp((double)(1024 + F), E - 25);
+    return (float)(negative ? -magnitude : magnitude);
 }
 
 /* ------------------------------------------------------------ O3 core -- */

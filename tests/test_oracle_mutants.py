@@ -28,8 +28,10 @@ MUTANTS = {
                              "tg[k] = m->codebook[oracle_cq_index(m, row, g * m->group + k)];"),
     "dense_dropped_column": ("for (int64_t c = 0; c < m->input; c++) acc +=",
                              "for (int64_t c = 1; c < m->input; c++) acc +="),
-    "f16_bias": ("(exponent - 15 + 127) << 23", "(exponent - 16 + 127) << 23"),
-    "f16_subnormal_bias": ("int32_t e = 127 - 15 + 1;", "int32_t e = 127 - 15;"),
+    "f16_bias": ("ldexp((double)(1024 + F), E - 25)", "ldexp((double)(1024 + F), E - 26)"),
+    "f16_subnormal_bias": ("ldexp((double)F, -24)", "ldexp((double)F, -25)"),
+    "f16_hidden_bit_dropped": ("ldexp((double)(1024 + F), E - 25)", "ldexp((double)F, E - 25)"),
+    "f16_sign_dropped": ("return (float)(negative ? -magnitude : magnitude);", "return (float)magnitude;"),
     "e4m3_subnormal_exp": ("v = ldexp((double)mant / 8.0, 1 - 7);", "v = ldexp((double)mant / 8.0, 0 - 7);"),
     "e4m3_no_clamp": ("if (v > 448.0) v = 448.0;", ""),
     "e4m3_sign_dropped": ("return (float)(s ? -v : v);", "return (float)v;"),
