@@ -17,6 +17,39 @@ bool mul_ok(int64_t a, int64_t b, int64_t c = 1) {
   return true;
 }
 
+// A byte range [p, p + bytes) of a call's buffer; null or empty ranges take
+// no part in the overlap test.
+struct Span {
+  const void* p;
+  int64_t bytes;
+};
+
+bool spans_meet(const Span& a, const Span& b) {
+  if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + (uintptr_t)b.bytes && b0 < a0 + (uintptr_t)a.bytes;
+}
+
+// Every workgroup reads its inputs while others already store outputs, so an
+// output that shares a byte with another output or with any input would make
+// the result depend on scheduling: such calls are refused (BQD_EINVAL).
+bool outputs_overlap(const Span* outs, int n_out, const Span* ins, int n_in) {
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = i + 1; j < n_out; ++j)
+      if (spans_meet(outs[i], outs[j])) return true;
+    for (int j = 0; j < n_in; ++j)
+      if (spans_meet(outs[i], ins[j])) return true;
+  }
+  return false;
+}
+
+// The three arrays a CQ matrix reads (its shape already validated).
+void cq_spans(const bqd_cq_matrix* m, Span* s) {
+  s[0] = {m->packed, m->output * m->row_bytes};
+  s[1] = {m->norms, m->output * (m->input_padded / m->group) * 2};
+  s[2] = {m->codebook, (int64_t)4 << m->bits};
+}
+
 }  // namespace
 
 int check_cq_shape(const bqd_cq_matrix* m) {
@@ -52,14 +85,9 @@ int check_prepare(const bqd_cq_matrix* m, const float* x, const float* prepared,
   if (batch == 0) return BQD_OK;
   if (!prepared || (m->input > 0 && !x)) return BQD_ENULL;
   if (!aligned(x, 4) || !aligned(prepared, 4)) return BQD_EALIGN;
-  // x and prepared must not overlap
-  if (x) {
-    const char* xa = (const char*)x;
-    const char* xb = xa + batch * m->input * 4;
-    const char* pa = (const char*)prepared;
-    const char* pb = pa + batch * m->input_padded * 4;
-    if (xa < pb && pa < xb) return BQD_EINVAL;
-  }
+  const Span out[1] = {{prepared, batch * m->input_padded * 4}};
+  const Span in[1] = {{x, batch * m->input * 4}};
+  if (outputs_overlap(out, 1, in, 1)) return BQD_EINVAL;
   return BQD_OK;
 }
 
@@ -73,6 +101,11 @@ int check_matvec(const bqd_cq_matrix* m, const float* prepared, const float* y, 
   if (batch == 0 || row_count == 0) return BQD_OK;
   if (!prepared || !y) return BQD_ENULL;
   if (!aligned(prepared, 4) || !aligned(y, 4)) return BQD_EALIGN;
+  Span in[4];
+  cq_spans(m, in);
+  in[3] = {prepared, batch * m->input_padded * 4};
+  const Span out[1] = {{y, batch * row_count * 4}};
+  if (outputs_overlap(out, 1, in, 4)) return BQD_EINVAL;
   return BQD_OK;
 }
 
@@ -81,18 +114,13 @@ int check_prepare_matvec(const bqd_cq_matrix* m, const float* x, const float* pr
   int rc = check_prepare(m, x, prepared, batch);
   if (rc) return rc;
   rc = check_matvec(m, prepared, y, batch, row_begin, row_count);
-  if (rc || batch == 0 || row_count == 0) return rc;
-  // y must overlap neither input
-  const char* ya = (const char*)y;
-  const char* yb = ya + batch * row_count * 4;
-  const char* pa = (const char*)prepared;
-  const char* pb = pa + batch * m->input_padded * 4;
-  if (ya < pb && pa < yb) return BQD_EINVAL;
-  if (x) {
-    const char* xa = (const char*)x;
-    const char* xb = xa + batch * m->input * 4;
-    if (ya < xb && xa < yb) return BQD_EINVAL;
-  }
+  if (rc || batch == 0) return rc;
+  // the prepared vectors are an output here as well
+  Span in[4];
+  cq_spans(m, in);
+  in[3] = {x, batch * m->input * 4};
+  const Span out[2] = {{prepared, batch * m->input_padded * 4}, {y, batch * row_count * 4}};
+  if (outputs_overlap(out, 2, in, 4)) return BQD_EINVAL;
   return BQD_OK;
 }
 
@@ -103,6 +131,10 @@ int check_matvec_multi(const bqd_cq_matrix* ms, int64_t n, const int64_t* row_be
   if (n < 1 || n > kMaxMulti) return BQD_EINVAL;
   for (int64_t k = 0; k < n; ++k) {
     rb[k] = row_begin ? row_begin[k] : 0;
+    // the begin is range-checked before the default count subtracts it
+    const int rs = check_cq_shape(&ms[k]);
+    if (rs) return rs;
+    if (rb[k] < 0 || rb[k] > ms[k].output) return BQD_EINVAL;
     rc[k] = row_count ? row_count[k] : ms[k].output - rb[k];
     int rc_k = check_matvec(&ms[k], prepared, ys[k], 1, rb[k], rc[k]);
     if (rc_k) return rc_k;
@@ -116,20 +148,25 @@ int check_matvec_multi(const bqd_cq_matrix* ms, int64_t n, const int64_t* row_be
   }
   if (!prepared) return BQD_ENULL;
   if (!aligned(prepared, 4)) return BQD_EALIGN;
-  // no output may overlap the activation it reads (or, with x, the input)
-  const char* pa = (const char*)prepared;
-  const char* pb = pa + ms[0].input_padded * 4;
+  // No output may overlap another output or anything a launch reads: the
+  // activation (with x, the raw input too) and every matrix's arrays.  With
+  // x the prepared vector is an output; without it, an input.
+  Span outs[kMaxMulti + 1];
+  Span ins[3 * kMaxMulti + 2];
+  int n_out = 0, n_in = 0;
   for (int64_t k = 0; k < n; ++k) {
-    if (rc[k] == 0) continue;
-    const char* ya = (const char*)ys[k];
-    const char* yb = ya + rc[k] * 4;
-    if (ya < pb && pa < yb) return BQD_EINVAL;
-    if (x) {
-      const char* xa = (const char*)x;
-      const char* xb = xa + ms[0].input * 4;
-      if (ya < xb && xa < yb) return BQD_EINVAL;
-    }
+    outs[n_out++] = {ys[k], rc[k] * 4};
+    cq_spans(&ms[k], ins + n_in);
+    n_in += 3;
   }
+  const Span pspan = {prepared, ms[0].input_padded * 4};
+  if (with_x) {
+    outs[n_out++] = pspan;
+    ins[n_in++] = {x, ms[0].input * 4};
+  } else {
+    ins[n_in++] = pspan;
+  }
+  if (outputs_overlap(outs, n_out, ins, n_in)) return BQD_EINVAL;
   return BQD_OK;
 }
 
@@ -141,6 +178,11 @@ int check_gather(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, const f
   if (n == 0) return BQD_OK;
   if (!rows || (m->input > 0 && !out)) return BQD_ENULL;
   if (!aligned(rows, 4) || !aligned(out, 4)) return BQD_EALIGN;
+  Span in[4];
+  cq_spans(m, in);
+  in[3] = {rows, n * 4};
+  const Span o[1] = {{out, n * m->input * 4}};
+  if (outputs_overlap(o, 1, in, 4)) return BQD_EINVAL;
   return BQD_OK;
 }
 
@@ -155,6 +197,9 @@ int check_f8(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64
   if (batch == 0 || R == 0) return BQD_OK;
   if (!w || !scale || !x || !y) return BQD_ENULL;
   if (!aligned(x, 4) || !aligned(y, 4)) return BQD_EALIGN;
+  const Span in[3] = {{w, R * C}, {scale, SR * SC}, {x, batch * C * 4}};
+  const Span out[1] = {{y, batch * R * 4}};
+  if (outputs_overlap(out, 1, in, 3)) return BQD_EINVAL;
   return BQD_OK;
 }
 
@@ -168,6 +213,9 @@ int check_i8(const int8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_
   if (batch == 0 || R == 0) return BQD_OK;
   if (!w || !scale || !x || !y) return BQD_ENULL;
   if (!aligned(x, 4) || !aligned(y, 4)) return BQD_EALIGN;
+  const Span in[3] = {{w, R * C}, {scale, R * ns}, {x, batch * C * 4}};
+  const Span out[1] = {{y, batch * R * 4}};
+  if (outputs_overlap(out, 1, in, 3)) return BQD_EINVAL;
   return BQD_OK;
 }
 
@@ -178,6 +226,9 @@ int check_kv_quantize(const float* v, int64_t n_vec, int64_t d, const int8_t* q,
   if (n_vec == 0) return BQD_OK;
   if (!scales || (d > 0 && (!v || !q))) return BQD_ENULL;
   if (!aligned(v, 4) || !aligned(scales, 4)) return BQD_EALIGN;
+  const Span in[1] = {{v, n_vec * d * 4}};
+  const Span out[2] = {{q, n_vec * d}, {scales, n_vec * 4}};
+  if (outputs_overlap(out, 2, in, 1)) return BQD_EINVAL;
   return BQD_OK;
 }
 
@@ -188,6 +239,9 @@ int check_kv_dot(const int8_t* K, const float* scales, int64_t R, int64_t d, con
   if (batch == 0 || R == 0) return BQD_OK;
   if (!K || !scales || !x || !y) return BQD_ENULL;
   if (!aligned(scales, 4) || !aligned(x, 4) || !aligned(y, 4)) return BQD_EALIGN;
+  const Span in[3] = {{K, R * d}, {scales, R * 4}, {x, batch * d * 4}};
+  const Span out[1] = {{y, batch * R * 4}};
+  if (outputs_overlap(out, 1, in, 3)) return BQD_EINVAL;
   return BQD_OK;
 }
 
@@ -203,6 +257,10 @@ int check_hadamard_mlp(const float* n, int64_t hidden, int64_t H, const float* d
   if (!aligned(n, 4) || !aligned(d1, 4) || !aligned(d2, 4) || !aligned(d3, 4) ||
       !aligned(resid, 4) || !aligned(u, 4) || !aligned(out, 4))
     return BQD_EALIGN;
+  const int64_t vec = batch * hidden * 4;
+  const Span in[6] = {{n, vec}, {d1, H * 4}, {d2, H * 4}, {d3, H * 4}, {resid, vec}, {u, vec}};
+  const Span o[1] = {{out, vec}};
+  if (outputs_overlap(o, 1, in, 6)) return BQD_EINVAL;
   return BQD_OK;
 }
 
@@ -247,6 +305,11 @@ int check_sample(const float* logits, int64_t n, int64_t k, float temperature,
   if (!aligned(logits, 4) || !aligned(state, 4) || !aligned(workspace, 4) || !aligned(token, 4) ||
       !aligned(topk_ids, 4) || !aligned(topk_logits, 4))
     return BQD_EALIGN;
+  // the generator state is read and written: it counts as an output
+  const Span in[1] = {{logits, n * 4}};
+  const Span out[5] = {{state, 4}, {workspace, need}, {token, 4}, {topk_ids, k * 4},
+                       {topk_logits, k * 4}};
+  if (outputs_overlap(out, 5, in, 1)) return BQD_EINVAL;
   return BQD_OK;
 }
 

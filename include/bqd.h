@@ -26,6 +26,11 @@
  *    work and return; results are valid once the stream has reached them.
  *  - Arrays are dense, C order, with the element types stated.  Pointers must
  *    be aligned to their element size (float/int32: 4 bytes, fp16: 2 bytes).
+ *  - No output array may share a byte with another output or with any array
+ *    the call reads (activations, weights, scales, norms, codebook, ids):
+ *    workgroups read inputs while others already store outputs, so such a
+ *    call is refused with BQD_EINVAL rather than giving scheduling-dependent
+ *    results.  Inputs may overlap one another.
  *  - Every argument is validated on the host before anything is enqueued; a
  *    call that returns an error has enqueued nothing.  Return value: BQD_OK
  *    or one of the negative codes below.  A zero-sized problem (no rows, no
@@ -93,7 +98,8 @@ int cq_prepare(const bqd_cq_matrix *m, const float *x, float *prepared,
  *   prepared: fp32 [batch][m->input_padded]   (the output of cq_prepare)
  *   y:        fp32 [batch][row_count]
  * Errors: BQD_EINVAL (shape fields, batch < 0, row range outside
- * [0, output]), BQD_ENULL, BQD_EALIGN, BQD_EOVERFLOW, BQD_EHIP. */
+ * [0, output], y overlapping prepared or the matrix's arrays), BQD_ENULL,
+ * BQD_EALIGN, BQD_EOVERFLOW, BQD_EHIP. */
 int cq_matvec(const bqd_cq_matrix *m, const float *prepared, float *y,
               int64_t batch, int64_t row_begin, int64_t row_count, void *stream);
 
@@ -108,8 +114,8 @@ int cq_matvec(const bqd_cq_matrix *m, const float *prepared, float *y,
  *   x:        fp32 [batch][m->input]
  *   prepared: fp32 [batch][m->input_padded]   (written; must not overlap x or y)
  *   y:        fp32 [batch][row_count]         (must not overlap x)
- * Errors: those of cq_prepare and cq_matvec, and BQD_EINVAL when y overlaps
- * x or prepared. */
+ * Errors: those of cq_prepare and cq_matvec, and BQD_EINVAL when y or
+ * prepared overlaps x, each other or the matrix's arrays. */
 int cq_prepare_matvec(const bqd_cq_matrix *m, const float *x, float *prepared, float *y,
                       int64_t batch, int64_t row_begin, int64_t row_count, void *stream);
 
@@ -124,7 +130,8 @@ int cq_prepare_matvec(const bqd_cq_matrix *m, const float *x, float *prepared, f
  *   prepared:  fp32 [input_padded] (the output of cq_prepare)
  *   ys:        host array of n device pointers, ys[k] fp32 [row_count[k]]
  * Requires 1 <= n <= 64.  Errors: as cq_matvec for every matrix, BQD_EINVAL
- * for unequal shapes or an output overlapping prepared, BQD_ENULL. */
+ * for unequal shapes or an output overlapping another output, prepared or
+ * any matrix's arrays, BQD_ENULL. */
 int cq_matvec_multi(const bqd_cq_matrix *ms, int64_t n, const int64_t *row_begin,
                     const int64_t *row_count, const float *prepared, float *const *ys,
                     void *stream);

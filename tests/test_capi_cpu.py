@@ -297,3 +297,69 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(TypeError):
         bqd.f8_matvec(torch.zeros(4, 16, dtype=torch.uint8), torch.zeros(1, 1, dtype=torch.uint8),
                       torch.zeros(16))
+
+
+# Disjoint fake device buffers, 4 GiB apart; an overlap is made by pointing an
+# output into one of them.  Every call below must fail validation (EINVAL)
+# before anything is enqueued.
+A, B, C_, D, E, F, G_ = ((k + 1) << 32 for k in range(7))
+
+
+def test_f8_i8_kv_outputs_overlapping_inputs_are_refused():
+    L = bqd.lib()
+    f8 = lambda w=A, s=B, x=C_, y=D: L.f8_matvec(w, 512, 4096, s, 4, 32, x, y, 1, None)
+    assert f8(y=C_ + 4096) == EINVAL         # y inside x
+    assert f8(y=C_ - 64) == EINVAL           # y runs into x
+    assert f8(y=A + 1024) == EINVAL          # y inside the weights
+    assert f8(y=B) == EINVAL                 # y on the scales
+    i8 = lambda w=A, s=B, x=C_, y=D: L.i8_matvec(w, 512, 4096, s, 16, x, y, 1, None)
+    assert i8(y=C_ + 16) == EINVAL
+    assert i8(y=A + 512 * 4096 - 4) == EINVAL  # the last weight bytes
+    assert i8(y=B + 100) == EINVAL
+    kd = lambda k=A, s=B, x=C_, y=D: L.kv_int8_dot(k, s, 64, 128, x, y, 1, None)
+    assert kd(y=C_ + 4) == EINVAL
+    assert kd(y=B) == EINVAL
+    assert kd(y=A + 64 * 128 - 4) == EINVAL
+    kq = lambda v=A, q=B, s=C_: L.kv_quantize_int8(v, 64, 128, q, s, None)
+    assert kq(q=A + 128) == EINVAL           # codes into the vectors
+    assert kq(s=A) == EINVAL                 # scales onto the vectors
+    assert kq(s=B + 64 * 128 - 4) == EINVAL  # scales onto the codes
+
+
+def test_cq_outputs_overlapping_inputs_are_refused():
+    L = bqd.lib()
+    m = cq(packed=A, norms=B, codebook=C_)
+    mv = lambda p=D, y=E, mm=m: L.cq_matvec(ctypes.byref(mm), p, y, 1, 0, 256, None)
+    assert mv(y=D + 512) == EINVAL           # y inside prepared
+    assert mv(y=A + 64) == EINVAL            # y inside the packed rows
+    assert mv(y=B + 2044) == EINVAL          # y over the last norms
+    assert mv(y=C_ + 12) == EINVAL           # y on the codebook
+    pm = lambda x=F, p=D, y=E: L.cq_prepare_matvec(ctypes.byref(m), x, p, y, 1, 0, 256, None)
+    assert pm(p=A) == EINVAL                 # prepared written over the packed rows
+    assert pm(p=B + 100) == EINVAL
+    assert pm(y=D + 8) == EINVAL             # y inside prepared
+    g = lambda ids=F, out=G_: L.cq_gather_rows(ctypes.byref(m), ids, 4, out, None)
+    assert g(out=F + 12) == EINVAL           # out over the ids
+    assert g(out=A) == EINVAL
+    assert g(out=C_ - 8) == EINVAL           # out runs into the codebook
+    mats = (bqd._CqStruct * 2)(m, cq(packed=F, norms=G_, codebook=C_))
+    multi = lambda ys: L.cq_matvec_multi(mats, 2, None, None, D, (ctypes.c_void_p * 2)(*ys), None)
+    assert multi([E, E + 512]) == EINVAL     # the two outputs overlap
+    assert multi([E, G_ + 40]) == EINVAL     # an output over the second matrix's norms
+    assert multi([E, D + 4]) == EINVAL       # an output over prepared
+
+
+def test_mlp_and_sampler_outputs_overlapping_inputs_are_refused():
+    L = bqd.lib()
+    mlp = lambda n=A, d1=B, d2=C_, d3=D, r=E, u=0, out=F: L.hadamard_mlp(
+        n, 512, 2048, d1, d2, d3, r, u, out, 2, None)
+    assert mlp(out=A + 2048) == EINVAL       # out over the second input vector
+    assert mlp(out=C_ + 4 * 2047) == EINVAL  # out over the last d2 entry
+    assert mlp(out=E) == EINVAL              # out over resid
+    assert mlp(u=G_, out=G_ + 4) == EINVAL   # out over u
+    smp = lambda logits=A, state=B, ws=C_, tok=D, ids=E, vals=F: L.logits_sample(
+        logits, 246272, 64, 0.7, state, ws, SAMPLE_NEED, tok, ids, vals, None)
+    assert smp(ws=A + 4096) == EINVAL        # workspace over the logits
+    assert smp(tok=E + 8) == EINVAL          # token inside the ids
+    assert smp(vals=C_ + SAMPLE_NEED - 4) == EINVAL  # values over the workspace's end
+    assert smp(state=A + 4 * 246271) == EINVAL  # state on the last logit
