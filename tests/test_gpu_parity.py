@@ -3,12 +3,13 @@
 Bit-exact: index decode, fp16 / E4M3 / E8M0 value decode, prepare, gather,
 and the one-hot cases whose sums are exact.  fp32 dots: per output
 |gpu - oracle| <= 1e-4 * sum|w*x| + 1e-6 (sum|w*x| from the oracle).
-Sizes: the five workloads at full size (the head's outputs sampled by row
-blocks the oracle computes one by one), plus small shapes that cover every
+Sizes: the five workloads at full size (every output, the heads' 246272 rows
+included, against the oracle), plus small shapes that cover every
 bit width, every fast-kernel lane layout, ragged row counts, padded rows and
 the generic (unaligned / odd-width) path.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -184,13 +185,17 @@ def test_prepare_small(i):
 
 # ------------------------------------------------------------------- matvec
 def check_matvec(case, row_begin=0, row_count=None):
+    """The oracle's reference starts from its own prepared vectors (O3 on the
+    raw activations); the GPU's prepared vectors must equal them bit for bit
+    for every vector of the batch before they feed the GPU matvec."""
     s = case.shape
     row_count = s.output - row_begin if row_count is None else row_count
     m, h = dev_matrix(case), host_matrix(case)
     p_dev = bqd.cq_prepare(m, to_dev(case.x))
-    p = p_dev.cpu().numpy()
+    p_ref = oracle.cq_prepare(h, case.x)
+    assert bits_eq(p_dev.cpu().numpy(), p_ref), (s, "prepared vectors differ from the oracle's")
     got = bqd.cq_matvec(m, p_dev, row_begin=row_begin, row_count=row_count).cpu().numpy()
-    ref, mag = oracle.cq_matvec(h, p, row_begin, row_count)
+    ref, mag = oracle.cq_matvec(h, p_ref, row_begin, row_count)
     assert_tol(got, ref, mag, f"cq_matvec {s} rows [{row_begin}, +{row_count})")
     return got
 
@@ -455,14 +460,37 @@ def test_f8_wkv(cache):
     check_f8(workload(cache, "f8_wkv_512x4096"))
 
 
-def test_f8_head_sampled_rows(cache):
+def oracle_all_rows(fn, R):
+    """fn(row_begin, row_count) -> (y, mag) over all R rows, the rows split in
+    contiguous chunks over host threads (the oracle's ctypes calls release
+    the GIL); each chunk is an unmodified oracle call on its row range."""
+    import threading
+    n = max(1, min(32, len(os.sched_getaffinity(0))))
+    per = (R + n - 1) // n
+    chunks = [(a, min(per, R - a)) for a in range(0, R, per)]
+    res = [None] * len(chunks)
+
+    def run(i, a, c):
+        res[i] = fn(a, c)
+
+    ts = [threading.Thread(target=run, args=(i, a, c)) for i, (a, c) in enumerate(chunks)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    return (np.concatenate([r[0] for r in res], axis=-1), np.concatenate([r[1] for r in res], axis=-1))
+
+
+def test_f8_head_all_rows(cache):
+    """The head at full size in the benchmark's launch configuration, every one
+    of its 246272 rows against the oracle."""
     case = workload(cache, "f8_head_246272x4096")
-    rng = np.random.default_rng(1)
-    starts = rng.integers(0, case.R // 128, 14) * 128
-    blocks = [(0, 256), (case.R - 200, 200)] + [(int(s0), 128) for s0 in starts]
-    print("[case] f8 head full launch, sampled oracle rows", flush=True)
-    got = check_f8(case, blocks)
+    print("[case] f8 head full launch, all rows against the oracle", flush=True)
     w, s, x = dev_f8(case)
+    got = bqd.f8_matvec(w, s, x).cpu().numpy()
+    ref, mag = oracle_all_rows(lambda a, c: oracle.f8_matvec(
+        case.w, case.R, case.C, case.scale, case.SR, case.SC, case.x[0], a, c), case.R)
+    assert_tol(got[0], ref, mag, f"f8 head {case.R}x{case.C}, all rows")
     again = bqd.f8_matvec(w, s, x).cpu().numpy()
     assert bits_eq(got, again)
 
@@ -584,20 +612,17 @@ def test_i8_matvec_activation_not_16_byte_aligned():
         assert bits_eq(got, aligned), (R, C)
 
 
-def test_i8_head_sampled_rows(cache):
-    """The I8 head at full size in the benchmark's launch configuration; the
-    oracle checks 16 row blocks (first, ragged last, random)."""
+def test_i8_head_all_rows(cache):
+    """The I8 head at full size in the benchmark's launch configuration, every
+    row against the oracle."""
     if "i8_head" not in cache:
         print("[case] building i8 head 246272x4096 G16", flush=True)
         cache["i8_head"] = synth.make_i8(**synth.I8_HEAD, seed=5)
     case = cache["i8_head"]
     got = bqd.i8_matvec(to_dev(case.w), to_dev(case.scale), to_dev(case.x), case.G).cpu().numpy()[0]
-    rng = np.random.default_rng(0)
-    starts = np.r_[0, case.R - 200, rng.integers(0, case.R - 128, 14)]
-    for st in starts:
-        n = 200 if st == case.R - 200 else 128
-        ref, mag = oracle.i8_matvec(case.w, case.R, case.C, case.scale, case.G, case.x[0], int(st), n)
-        assert_tol(got[st:st + n], ref, mag, f"i8 head rows [{st}, +{n})")
+    ref, mag = oracle_all_rows(lambda a, c: oracle.i8_matvec(
+        case.w, case.R, case.C, case.scale, case.G, case.x[0], a, c), case.R)
+    assert_tol(got, ref, mag, f"i8 head {case.R}x{case.C}, all rows")
 
 
 # ------------------------------------------------------------- int8 key cache
