@@ -388,7 +388,7 @@ def logits_sample(logits: torch.Tensor, k: int, temperature: float, state: torch
     n = logits.numel()
     need = logits_sample_workspace_bytes(n, k)
     if workspace is None:
-        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=logits.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
     workspace = _dev(workspace, torch.uint8, "workspace")
     token = torch.empty(1, dtype=torch.int32, device=logits.device)
     ids = torch.empty(k, dtype=torch.int32, device=logits.device)

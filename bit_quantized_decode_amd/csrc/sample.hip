@@ -14,22 +14,30 @@
 // get small distinct keys (below every real key, whose low half is at least
 // 2^32 - 2^20); they are never selected, since k <= n real logits compete.
 //
-// Two launches.  Blocks of 1024 R logits (R = 1, 2 or 4: the smallest that
-// leaves at most 256 blocks, so that the work spreads over many CUs): each
-// wavefront sorts R runs of 64 keys across its lanes (a bitonic network on
-// lane exchanges, no barriers), merges them into its top 64, and the
+// Two launches.  First, blocks of 1024 R logits (R = 1, 2 or 4: the smallest
+// that leaves at most 256 blocks, so that the work spreads over many CUs):
+// each wavefront sorts R runs of 64 keys across its lanes (a bitonic network
+// on lane exchanges, no barriers), merges them into its top 64, and the
 // wavefronts' lists merge in LDS down to the block's top 64, of which the
-// first k go to the caller's workspace.
+// first k go to the caller's workspace.  (One launch, with the last block to
+// finish selecting, measured slower here: the device-scope release every
+// block needs before counting itself done cost ~4 us across 241 blocks, more
+// than the kernel boundary.)
 //
-// One block then selects the first k of the blocks' lists.  Pruning: with H
+// Then one block selects the first k of the blocks' lists.  Pruning: with H
 // the k-th largest of the lists' first keys, at least k keys are >= H, so
 // every one of the first k overall is >= H, and in each (descending) list the
-// keys >= H are a prefix.  The block reads the first 8 keys of every list,
-// keeps those >= H (typically a few per list), sorts and merges them; where a
-// list may hold more than 8 such keys, or more than 1024 survive, or there are
-// fewer than k lists, it merges every list in full instead.  Either way it
-// draws the token in fp64.  Keys carry the index, so the logits are re-read
-// for the k values (copied bit for bit).
+// keys >= H are a prefix.  The block reads the first 8 keys of every list and
+// keeps those >= H (typically a few per list).  H itself and, for up to 256
+// survivors, their order come from counting: with distinct keys, a key's rank
+// is the number of larger ones, each count split over the block's 16
+// wavefronts, with no sorting network.  More survivors are sorted and merged;
+// where a list may hold more than 8 such keys, or more than 1024 survive, or
+// there are fewer than k lists, every list is merged in full instead.  The
+// token is drawn in fp64 in one wavefront's registers.  The k values are
+// rebuilt from the keys (the order map is invertible except for the sign of
+// zero and NaN payloads; those few are re-read from the logits), so they are
+// copied bit for bit.
 #include <math.h>
 
 #include "cq_device.h"
@@ -42,6 +50,8 @@ constexpr int kSampleThreads = 1024;
 constexpr int kMaxCandidates = 16384; // second-stage capacity (16 per thread)
 constexpr int kPeek = 8;              // keys read per list by the pruned selection
 constexpr int kMaxK = 64;
+constexpr int kRankMax = 256;         // survivors ranked by counting (more: sorted)
+constexpr int kTopSlot = kSampleThreads;  // LDS slot of the counted top k
 
 // Unsigned key of a logit: the order of values, NaN below everything, -0 = +0.
 __device__ __forceinline__ uint32_t value_key(float v) {
@@ -148,14 +158,13 @@ __device__ __forceinline__ uint64_t wave_top_of_runs(const uint64_t (&run)[R]) {
   return wave_merge_desc(m01, key_from_lane(m23, 63 - l));
 }
 
-// Stage 1: block b keeps the first k keys of logits [C b, C b + C), C = 1024 R,
-// in workspace slots [k b, k b + k).
+// Stage 1: the block's top 64 keys of logits [C b, C b + C), C = 1024 R,
+// descending in lists[0 .. 64); every thread of the workgroup calls it.
 template <int R>
-__global__ __launch_bounds__(kSampleThreads) void topk_chunk_kernel(
-    const float* __restrict__ logits, int64_t n, int k, uint64_t* __restrict__ ws) {
+__device__ __forceinline__ void block_top64(const float* __restrict__ logits, int64_t n,
+                                            uint64_t* lists) {
   static_assert(R == 1 || R == 2 || R == 4, "runs per wavefront");
   constexpr int kChunk = kSampleThreads * R;
-  __shared__ uint64_t lists[kSampleThreads];  // one list of 64 per wavefront
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
   uint64_t run[R];
 #pragma unroll
@@ -167,37 +176,78 @@ __global__ __launch_bounds__(kSampleThreads) void topk_chunk_kernel(
   wave_sort_desc<R>(run);
   lists[64 * wave + l] = wave_top_of_runs<R>(run);
   block_merge_lists(lists, kSampleThreads / 64);
-  if ((int)threadIdx.x < k) ws[(int64_t)blockIdx.x * k + threadIdx.x] = lists[threadIdx.x];
 }
 
-// Stage 2: the blocks' lists (k keys each, padded to 64) merged, the first k
-// kept, then the draw.
-__global__ __launch_bounds__(kSampleThreads) void topk_final_kernel(
-    const float* __restrict__ logits, const uint64_t* __restrict__ ws, int n_lists, int k,
-    float temperature, uint32_t* __restrict__ state, int32_t* __restrict__ token,
-    int32_t* __restrict__ topk_ids, float* __restrict__ topk_vals) {
-  __shared__ uint64_t lists[kMaxCandidates];
-  __shared__ float sel_v[kMaxK];
-  __shared__ int32_t sel_i[kMaxK];
-  __shared__ double weight[kMaxK];
+// The logit a key was made from, bit for bit: the inverse of value_key, or
+// a re-read where the key does not determine the bits (zeros, NaNs).
+__device__ __forceinline__ float key_logit(uint64_t key, const float* __restrict__ logits) {
+  const uint32_t vk = (uint32_t)(key >> 32);
+  if (vk == 0u || vk == 0x80000000u) return logits[0xffffffffu - (uint32_t)key];
+  return __uint_as_float((vk & 0x80000000u) ? (vk & 0x7fffffffu) : ~vk);
+}
+
+// The number of keys among keys[b0, b1) larger than `mine` (b0, b1 even;
+// keys 16-byte aligned in LDS, read two at a time, eight reads in flight;
+// every lane of a wavefront reads the same address).
+__device__ __forceinline__ int count_above(const uint64_t* keys, int b0, int b1, uint64_t mine) {
+  const ulonglong2* p = reinterpret_cast<const ulonglong2*>(keys);
+  int above = 0, u = b0 / 2;
+  const int end = b1 / 2;
+  for (; u + 8 <= end; u += 8) {
+    ulonglong2 r[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = p[u + j];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) above += (r[j].x > mine ? 1 : 0) + (r[j].y > mine ? 1 : 0);
+  }
+  for (; u < end; ++u) {
+    const ulonglong2 two = p[u];
+    above += (two.x > mine ? 1 : 0) + (two.y > mine ? 1 : 0);
+  }
+  return above;
+}
+
+// Ranks of keys[0, m) (m <= 256, keys distinct, a zero key at keys[m] when m
+// is odd) counted by all 1024 threads: thread t counts, for key t % 256, the
+// larger keys in quarter t / 256 of the range.  Returns, in thread i < m, the
+// rank of keys[i] (the number of larger keys).  Every thread calls it.
+__device__ __forceinline__ int block_rank(const uint64_t* keys, int m, int (*part)[256]) {
+  const int t = threadIdx.x, i = t & 255, q = t >> 8;
+  const int even = (m + 1) & ~1, span = ((m + 7) / 8) * 2;
+  const int b0 = q * span, b1 = min(b0 + span, even);
+  part[q][i] = (i < m && b0 < b1) ? count_above(keys, b0, b1, keys[i]) : 0;
+  __syncthreads();
+  return t < m ? part[0][t] + part[1][t] + part[2][t] + part[3][t] : 0;
+}
+
+// Stage 2 (one block): the blocks' lists (k keys each, padded to 64) merged,
+// the first k kept, then the draw.  `lists` is the workgroup's LDS buffer of
+// kMaxCandidates keys.
+__device__ void select_and_draw(const float* __restrict__ logits, const uint64_t* ws,
+                                int n_lists, int k, float temperature,
+                                uint32_t* __restrict__ state, int32_t* __restrict__ token,
+                                int32_t* __restrict__ topk_ids, float* __restrict__ topk_vals,
+                                uint64_t* lists) {
   __shared__ uint64_t thr;
   __shared__ int n_keep, full_merge;
+  __shared__ int part[4][256];
   const int t = threadIdx.x, wave = t >> 6, l = t & 63;
+  // the generator state, requested first so that its latency overlaps the
+  // selection
+  const uint32_t state_in = wave == 0 ? *state : 0u;
   // The first kPeek keys of list t (all requested together).  A list holds k
   // keys; its padding keys (a short chunk's) are below every real key.
   const bool has = t < n_lists;
   uint64_t pk[kPeek];
 #pragma unroll
   for (int q = 0; q < kPeek; ++q) pk[q] = (has && q < k) ? ws[(int64_t)t * k + q] : 0;
-  lists[t] = has ? pk[0] : 0;  // the lists' first keys (n_lists <= 256)
+  lists[t] = has ? pk[0] : 0;  // the lists' first keys (n_lists <= 256), zeros after
   __syncthreads();
-  if (wave == 0) {  // H = the k-th largest first key
-    uint64_t h[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) h[r] = lists[64 * r + l];
-    wave_sort_desc<4>(h);
-    const uint64_t top = wave_top_of_runs<4>(h);
-    if (l == k - 1) thr = top;
+  // H = the k-th largest first key: the one with exactly k - 1 larger (keys
+  // are distinct)
+  if (n_lists >= k) {
+    const int rank = block_rank(lists, n_lists, part);
+    if (has && rank == k - 1) thr = pk[0];
   }
   __syncthreads();
   const uint64_t H = n_lists >= k ? thr : 0;
@@ -230,7 +280,22 @@ __global__ __launch_bounds__(kSampleThreads) void topk_final_kernel(
   if (c == kPeek && kPeek < k) full_merge = 1;  // list t may hold more keys >= H
   const int off = (int)lists[t];
   __syncthreads();
-  if (!full_merge && n_keep <= kSampleThreads) {
+  int top_at = 0;  // where the first k keys end up in LDS
+  if (!full_merge && n_keep <= kRankMax) {
+    // the survivors in slots [0, n_keep) (a zero key after an odd count); each
+    // one's rank is the number of larger survivors, and ranks below k are the
+    // first k in order
+    const int kept = n_keep;
+#pragma unroll
+    for (int q = 0; q < kPeek; ++q)
+      if (q < c) lists[off + q] = pk[q];
+    if (t == kept) lists[t] = 0;
+    __syncthreads();
+    const int rank = block_rank(lists, kept, part);
+    if (t < kept && rank < k) lists[kTopSlot + rank] = lists[t];
+    __syncthreads();
+    top_at = kTopSlot;
+  } else if (!full_merge && n_keep <= kSampleThreads) {
     // the survivors in slots [0, n_keep), distinct small keys after them;
     // each wavefront sorts its 64 slots, then the 16 lists merge
     const int kept = n_keep;
@@ -254,46 +319,69 @@ __global__ __launch_bounds__(kSampleThreads) void topk_final_kernel(
     }
     block_merge_lists(lists, n_lists);
   }
+  if (wave != 0) return;
+  // Wavefront 0: lane t holds candidate t (t < k); the draw stays in registers.
+  const uint64_t key = t < k ? lists[top_at + t] : 0;
+  const int32_t id = (int32_t)(0xffffffffu - (uint32_t)key);
+  const float v = t < k ? key_logit(key, logits) : 0.0f;
   if (t < k) {
-    const int32_t i = (int32_t)(0xffffffffu - (uint32_t)lists[t]);
-    sel_i[t] = i;
-    sel_v[t] = logits[i];
-    topk_ids[t] = i;
-    topk_vals[t] = sel_v[t];
+    topk_ids[t] = id;
+    topk_vals[t] = v;
   }
-  __syncthreads();
-  const float top = sel_v[0];
+  const float top = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(v)));
   const bool draw = temperature > 0.0f && k > 1 && isfinite(top);
-  if (draw && t < k) {  // the softmax weights in fp64, one per lane
-    const float v = sel_v[t];
-    weight[t] = (v != v) ? 0.0 : exp(((double)v - (double)top) / (double)temperature);
-  }
-  __syncthreads();
-  if (t == 0) {
-    // one xorshift step (13, 17, 5), u = state / 2^32, then the inverse of the
-    // cumulative softmax: sums in list order, in fp64
-    uint32_t s = *state;
-    s ^= s << 13;
-    s ^= s >> 17;
-    s ^= s << 5;
-    *state = s;
-    int32_t tok = sel_i[0];
-    if (draw) {
-      double S = 0.0;
-      for (int j = 0; j < k; ++j) S += weight[j];
-      const double target = ((double)s / 4294967296.0) * S;
-      double run = 0.0;
-      tok = sel_i[k - 1];
-      for (int j = 0; j < k; ++j) {
-        run += weight[j];
-        if (target < run) {
-          tok = sel_i[j];
-          break;
-        }
-      }
+  // one xorshift step (13, 17, 5), u = state / 2^32
+  uint32_t s = __builtin_amdgcn_readfirstlane(state_in);
+  s ^= s << 13;
+  s ^= s >> 17;
+  s ^= s << 5;
+  int32_t tok = __builtin_amdgcn_readfirstlane(id);
+  if (draw) {
+    // the softmax weights in fp64, one per lane (NaN values and lanes past k
+    // weigh 0), then the running sums in list order: lane j receives
+    // w_0 + ... + w_j, each sum formed as one fp64 add on the previous one
+    const double w = (t < k && v == v) ? exp(((double)v - (double)top) / (double)temperature)
+                                       : 0.0;
+    const uint64_t wb = __builtin_bit_cast(uint64_t, w);
+    const uint32_t wlo = (uint32_t)wb, whi = (uint32_t)(wb >> 32);
+    double run = 0.0, mine = 0.0;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+      const uint64_t bj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(whi, j) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane(wlo, j);
+      run += __builtin_bit_cast(double, bj);
+      if (t == j) mine = run;
     }
+    // S = run (the zeros past k leave it unchanged); the token is the first
+    // candidate whose running sum exceeds u * S, else the last one
+    const double target = ((double)s / 4294967296.0) * run;
+    const uint64_t over = __ballot(t < k && target < mine);
+    const int pick = over ? __ffsll((unsigned long long)over) - 1 : k - 1;
+    tok = __builtin_amdgcn_readlane(id, pick);
+  }
+  if (t == 0) {
+    *state = s;
     *token = tok;
   }
+}
+
+// Stage 1: block b keeps the first k keys of its logits in workspace slots
+// [k b, k b + k).
+template <int R>
+__global__ __launch_bounds__(kSampleThreads) void topk_chunk_kernel(
+    const float* __restrict__ logits, int64_t n, int k, uint64_t* __restrict__ ws) {
+  __shared__ uint64_t lists[kSampleThreads];  // one list of 64 per wavefront
+  block_top64<R>(logits, n, lists);
+  if ((int)threadIdx.x < k) ws[(int64_t)blockIdx.x * k + threadIdx.x] = lists[threadIdx.x];
+}
+
+// Stage 2: one block selects from the n_lists lists and draws.
+__global__ __launch_bounds__(kSampleThreads) void topk_select_kernel(
+    const float* __restrict__ logits, const uint64_t* __restrict__ ws, int n_lists, int k,
+    float temperature, uint32_t* __restrict__ state, int32_t* __restrict__ token,
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_vals) {
+  __shared__ uint64_t lists[kMaxCandidates];
+  select_and_draw(logits, ws, n_lists, k, temperature, state, token, topk_ids, topk_vals, lists);
 }
 
 int launch_logits_sample(const float* logits, int64_t n, int64_t k, float temperature,
@@ -302,19 +390,17 @@ int launch_logits_sample(const float* logits, int64_t n, int64_t k, float temper
   const int64_t chunk = sample_chunk(n);
   const int64_t chunks = (n + chunk - 1) / chunk;
   uint64_t* ws = reinterpret_cast<uint64_t*>(workspace);
+  const dim3 grid((unsigned)chunks), block(kSampleThreads);
   if (chunk == 1024)
-    hipLaunchKernelGGL(topk_chunk_kernel<1>, dim3((unsigned)chunks), dim3(kSampleThreads), 0, s,
-                       logits, n, (int)k, ws);
+    hipLaunchKernelGGL(topk_chunk_kernel<1>, grid, block, 0, s, logits, n, (int)k, ws);
   else if (chunk == 2048)
-    hipLaunchKernelGGL(topk_chunk_kernel<2>, dim3((unsigned)chunks), dim3(kSampleThreads), 0, s,
-                       logits, n, (int)k, ws);
+    hipLaunchKernelGGL(topk_chunk_kernel<2>, grid, block, 0, s, logits, n, (int)k, ws);
   else
-    hipLaunchKernelGGL(topk_chunk_kernel<4>, dim3((unsigned)chunks), dim3(kSampleThreads), 0, s,
-                       logits, n, (int)k, ws);
+    hipLaunchKernelGGL(topk_chunk_kernel<4>, grid, block, 0, s, logits, n, (int)k, ws);
   int rc = launch_status();
   if (rc) return rc;
-  hipLaunchKernelGGL(topk_final_kernel, dim3(1), dim3(kSampleThreads), 0, s, logits, ws,
-                     (int)chunks, (int)k, temperature, state, token, topk_ids, topk_logits);
+  hipLaunchKernelGGL(topk_select_kernel, dim3(1), block, 0, s, logits, ws, (int)chunks, (int)k,
+                     temperature, state, token, topk_ids, topk_logits);
   return launch_status();
 }
 

@@ -230,7 +230,8 @@ int hadamard_mlp(const float *n, int64_t hidden, int64_t H, const float *d1, con
                  void *stream);
 
 /* Bytes of device workspace logits_sample needs: ceil(n / C) * k * 8, where
- * C = 1024 for n <= 262144, 2048 for n <= 524288, else 4096.
+ * C = 1024 for n <= 262144, 2048 for n <= 524288, else 4096 (the per-block
+ * candidate lists of the first of its two launches).
  * Returns BQD_EINVAL (negative) for n or k outside logits_sample's range. */
 int64_t logits_sample_workspace_bytes(int64_t n, int64_t k);
 
@@ -248,7 +249,9 @@ int64_t logits_sample_workspace_bytes(int64_t n, int64_t k);
  *   The same state and logits give the same token; successive calls on one
  *   state continue the generator's sequence.  A zero state stays zero.
  *   logits:      fp32 [n]                 state: uint32 [1], read and written
- *   workspace:   logits_sample_workspace_bytes(n, k) bytes, 4-byte aligned
+ *   workspace:   logits_sample_workspace_bytes(n, k) bytes, 4-byte aligned,
+ *                no initial contents needed; calls that share a workspace
+ *                must not overlap in time.
  *   token:       int32 [1]                topk_ids: int32 [k]   topk_logits: fp32 [k]
  * All pointers are device pointers.  Requires 1 <= n <= 2^20,
  * 1 <= k <= min(64, n), 0 <= temperature < inf.
