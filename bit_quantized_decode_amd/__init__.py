@@ -34,7 +34,7 @@ import torch
 __all__ = ["BqdError", "CqMatrix", "cq_prepare", "cq_matvec", "cq_prepare_matvec",
            "cq_matvec_multi", "cq_prepare_matvec_multi",
            "cq_gather_rows", "f8_matvec", "i8_matvec", "kv_quantize_int8", "kv_int8_dot", "hadamard_mlp",
-           "logits_sample", "logits_sample_workspace_bytes",
+           "logits_sample", "logits_sample_workspace_bytes", "logits_sample_noalloc",
            "dbg_cq_unpack", "dbg_f16_decode", "dbg_f8_decode", "dbg_e8m0_decode", "lib",
            "LIB_PATH", "EXPORTS"]
 
@@ -45,7 +45,7 @@ LIB_PATH = os.path.join(_HERE, "libbqd.so")
 EXPORTS = ("cq_prepare", "cq_matvec", "cq_prepare_matvec", "cq_matvec_multi",
            "cq_prepare_matvec_multi", "cq_gather_rows", "f8_matvec",
            "i8_matvec", "kv_quantize_int8", "kv_int8_dot", "hadamard_mlp", "logits_sample",
-           "logits_sample_workspace_bytes", "bqd_dbg_cq_unpack", "bqd_dbg_f16_decode",
+           "logits_sample_workspace_bytes", "logits_sample_noalloc", "bqd_dbg_cq_unpack", "bqd_dbg_f16_decode",
            "bqd_dbg_f8_decode", "bqd_dbg_e8m0_decode", "bqd_dbg_read_stream",
            "bqd_status_string")
 
@@ -95,7 +95,8 @@ def lib():
                 ("bqd_dbg_f8_decode", [P, I64, P, P]),
                 ("bqd_dbg_e8m0_decode", [P, I64, P, P]),
                 ("bqd_dbg_read_stream", [P, I64, P, P]),
-                ("logits_sample", [P, I64, I64, ctypes.c_float, P, P, I64, P, P, P, P])):
+                ("logits_sample", [P, I64, I64, ctypes.c_float, P, P, I64, P, P, P, P]),
+                ("logits_sample_noalloc", [P, I64, I64, ctypes.c_float, P, P, P, P, P])):
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = I
@@ -397,6 +398,24 @@ def logits_sample(logits: torch.Tensor, k: int, temperature: float, state: torch
           _ptr(workspace), workspace.numel(), _ptr(token), _ptr(ids), _ptr(vals),
           _stream(logits, stream))
     return token, ids, vals
+
+
+def logits_sample_noalloc(logits: torch.Tensor, k: int, temperature: float, state: torch.Tensor,
+                          token: torch.Tensor, topk_ids: torch.Tensor, topk_logits: torch.Tensor,
+                          stream=None):
+    """logits_sample into caller-given outputs (token int32 [1], topk_ids
+    int32 [k], topk_logits float32 [k]), with the library's static scratch as
+    the workspace: the call allocates no device memory."""
+    logits = _dev(logits, torch.float32, "logits")
+    state = _dev(state, (torch.int32, torch.uint32), "state")
+    token = _dev(token, torch.int32, "token")
+    topk_ids = _dev(topk_ids, torch.int32, "topk_ids")
+    topk_logits = _dev(topk_logits, torch.float32, "topk_logits")
+    if token.numel() < 1 or topk_ids.numel() < k or topk_logits.numel() < k:
+        raise ValueError("token needs 1 element, topk_ids and topk_logits k each")
+    _call("logits_sample_noalloc", _ptr(logits), logits.numel(), int(k), float(temperature),
+          _ptr(state), _ptr(token), _ptr(topk_ids), _ptr(topk_logits), _stream(logits, stream))
+    return token, topk_ids, topk_logits
 
 
 def dbg_cq_unpack(m: CqMatrix, row: int, stream=None):

@@ -139,6 +139,19 @@ int logits_sample(const float* logits, int64_t n, int64_t k, float temperature, 
                               topk_logits, as_stream(stream));
 }
 
+int logits_sample_noalloc(const float* logits, int64_t n, int64_t k, float temperature,
+                          uint32_t* state, int32_t* token, int32_t* topk_ids, float* topk_logits,
+                          void* stream) {
+  int rc = check_sample_noalloc(logits, n, k, temperature, state, token, topk_ids, topk_logits,
+                                sample_scratch_bytes());
+  if (rc) return rc;
+  void* ws = nullptr;
+  rc = sample_scratch(&ws);
+  if (rc) return rc;
+  return launch_logits_sample(logits, n, k, temperature, state, ws, token, topk_ids,
+                              topk_logits, as_stream(stream));
+}
+
 const char* bqd_status_string(int status) {
   switch (status) {
     case BQD_OK: return "ok";

@@ -39,6 +39,11 @@ int launch_logits_sample(const float* logits, int64_t n, int64_t k, float temper
                          uint32_t* state, void* workspace, int32_t* token, int32_t* topk_ids,
                          float* topk_logits, hipStream_t s);
 
+// The allocation-free sampler's device scratch: its size, and its address on
+// the current device (looked up once per device).
+int64_t sample_scratch_bytes();
+int sample_scratch(void** out);
+
 inline int launch_status() {
   return hipGetLastError() == hipSuccess ? BQD_OK : BQD_EHIP;
 }

@@ -40,6 +40,8 @@
 // copied bit for bit.
 #include <math.h>
 
+#include <mutex>
+
 #include "cq_device.h"
 #include "launch.h"
 #include "validate.h"
@@ -402,6 +404,41 @@ int launch_logits_sample(const float* logits, int64_t n, int64_t k, float temper
   hipLaunchKernelGGL(topk_select_kernel, dim3(1), block, 0, s, logits, ws, (int)chunks, (int)k,
                      temperature, state, token, topk_ids, topk_logits);
   return launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant.  Its workspace is this file-scope device array,
+// sized for the largest call (n = 2^20 logits: 256 blocks of lists of k = 64
+// keys): 128 KiB.  Each GPU holds its own copy for the life of the process.
+// Nothing in it needs clearing: every first-stage block writes its list
+// before the second stage, a later launch on the stream, reads it.  Calls on
+// one GPU share the array: calls that overlap in time race.
+constexpr int64_t kScratchBytes = (int64_t)256 * kMaxSampleK * (int64_t)sizeof(uint64_t);
+static_assert(kMaxSampleLogits / 4096 <= 256, "the largest call has at most 256 blocks");
+static __device__ __align__(256) uint64_t scratch[kScratchBytes / sizeof(uint64_t)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int64_t sample_scratch_bytes() { return kScratchBytes; }
+
+// The device address of `scratch` on the current device, looked up once per
+// device with that device current (the host-side name of the array is not a
+// device address).
+int sample_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BQD_EHIP;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BQD_EHIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return BQD_OK;
 }
 
 }  // namespace bqd

@@ -313,4 +313,20 @@ int check_sample(const float* logits, int64_t n, int64_t k, float temperature,
   return BQD_OK;
 }
 
+int check_sample_noalloc(const float* logits, int64_t n, int64_t k, float temperature,
+                         const uint32_t* state, const int32_t* token, const int32_t* topk_ids,
+                         const float* topk_logits, int64_t scratch_bytes) {
+  const int64_t need = sample_workspace_need(n, k);
+  if (need < 0 || need > scratch_bytes) return BQD_EINVAL;
+  if (!(temperature >= 0.0f) || temperature > 3.4e38f) return BQD_EINVAL;  // NaN, < 0, inf
+  if (!logits || !state || !token || !topk_ids || !topk_logits) return BQD_ENULL;
+  if (!aligned(logits, 4) || !aligned(state, 4) || !aligned(token, 4) || !aligned(topk_ids, 4) ||
+      !aligned(topk_logits, 4))
+    return BQD_EALIGN;
+  const Span in[1] = {{logits, n * 4}};
+  const Span out[4] = {{state, 4}, {token, 4}, {topk_ids, k * 4}, {topk_logits, k * 4}};
+  if (outputs_overlap(out, 4, in, 1)) return BQD_EINVAL;
+  return BQD_OK;
+}
+
 }  // namespace bqd

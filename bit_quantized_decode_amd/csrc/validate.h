@@ -41,6 +41,12 @@ int64_t sample_workspace_need(int64_t n, int64_t k);  // or BQD_EINVAL
 int check_sample(const float* logits, int64_t n, int64_t k, float temperature,
                  const uint32_t* state, const void* workspace, int64_t workspace_bytes,
                  const int32_t* token, const int32_t* topk_ids, const float* topk_logits);
+// logits_sample_noalloc: check_sample's rules for everything but the
+// workspace, which is the library's scratch of scratch_bytes (a call needing
+// more is refused with BQD_EINVAL).
+int check_sample_noalloc(const float* logits, int64_t n, int64_t k, float temperature,
+                         const uint32_t* state, const int32_t* token, const int32_t* topk_ids,
+                         const float* topk_logits, int64_t scratch_bytes);
 
 // Largest sizes the kernels index with their 32-bit row / column counters.
 constexpr int64_t kMaxRows = (int64_t)1 << 30;      // exclusive

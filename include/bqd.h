@@ -261,6 +261,23 @@ int logits_sample(const float *logits, int64_t n, int64_t k, float temperature,
                   uint32_t *state, void *workspace, int64_t workspace_bytes,
                   int32_t *token, int32_t *topk_ids, float *topk_logits, void *stream);
 
+/* logits_sample without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same kernels and results, bit for bit, with
+ * the workspace taken from a static device array inside the library, 131,072
+ * bytes (the need of the largest call: n = 2^20, k = 64) held by each GPU the
+ * library runs on until the process ends.  The call allocates nothing.  Its
+ * address is looked up on the first call on each device (with that device
+ * current).  All calls on one GPU share that array: calls that overlap in
+ * time on one GPU (different streams, no ordering between them) race and
+ * may return wrong results; calls ordered on one stream are safe.  Arguments
+ * and errors as logits_sample (a call needing more scratch than the array
+ * holds is refused with BQD_EINVAL; none can within the documented ranges),
+ * plus BQD_EHIP if the array's device address cannot be found. */
+int logits_sample_noalloc(const float *logits, int64_t n, int64_t k, float temperature,
+                          uint32_t *state, int32_t *token, int32_t *topk_ids,
+                          float *topk_logits, void *stream);
+
 /* Test probes: run the very device decode routines the kernels use.
  * bqd_dbg_cq_unpack: idx[c] = index(row, c) for c < input_padded (uint8).
  * bqd_dbg_f16_decode: out[i] = fp16 codes[i] as fp32 (the norm decode).

@@ -127,6 +127,10 @@ int main() {
       for (int64_t ws : {kSmall, (int64_t)0, (int64_t)1 << 20, kBig})
         for (float t : {-1.0f, 0.0f, 0.7f, std::numeric_limits<float>::infinity(),
                         std::numeric_limits<float>::quiet_NaN()})
+          note(check_sample_noalloc(X, n, k, t, fake<uint32_t>((uintptr_t)10 << 32),
+                                    fake<int32_t>((uintptr_t)12 << 32),
+                                    fake<int32_t>((uintptr_t)13 << 32),
+                                    fake<float>((uintptr_t)14 << 32), ws)),
           note(check_sample(X, n, k, t, fake<uint32_t>((uintptr_t)10 << 32),
                             fake<void>((uintptr_t)11 << 32), ws, fake<int32_t>((uintptr_t)12 << 32),
                             fake<int32_t>((uintptr_t)13 << 32), fake<float>((uintptr_t)14 << 32)));

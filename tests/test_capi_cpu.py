@@ -280,6 +280,25 @@ def test_logits_sample_rejects(args, code):
     assert rc == code
 
 
+@pytest.mark.parametrize("args,code", [
+    (dict(n=0), EINVAL), (dict(n=(1 << 20) + 1), EINVAL), (dict(k=0), EINVAL),
+    (dict(k=65), EINVAL), (dict(n=10, k=11), EINVAL), (dict(temperature=-1.0), EINVAL),
+    (dict(temperature=float("nan")), EINVAL),
+    (dict(logits=0), ENULL), (dict(state=0), ENULL), (dict(token=0), ENULL),
+    (dict(ids=0), ENULL), (dict(vals=0), ENULL),
+    (dict(logits=FAKE + 2), EALIGN), (dict(token=FAKE + 3), EALIGN), (dict(vals=FAKE + 1), EALIGN),
+    (dict(vals=(1 << 32) + 400), EINVAL),   # the values written over the logits
+    (dict(token=(3 << 32) + 8), EINVAL),    # the token inside the ids
+])
+def test_logits_sample_noalloc_rejects(args, code):
+    a = dict(logits=1 << 32, n=246272, k=64, temperature=0.7, state=2 << 32, token=4 << 32,
+             ids=3 << 32, vals=5 << 32)
+    a.update(args)
+    rc = bqd.lib().logits_sample_noalloc(a["logits"], a["n"], a["k"], a["temperature"],
+                                         a["state"], a["token"], a["ids"], a["vals"], None)
+    assert rc == code
+
+
 def test_logits_sample_workspace_bytes():
     L = bqd.lib()
     assert L.logits_sample_workspace_bytes(246272, 64) == SAMPLE_NEED
