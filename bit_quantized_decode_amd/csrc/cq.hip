@@ -137,62 +137,127 @@ __global__ __launch_bounds__(kThreads) void cq_gather_generic(
 }
 
 // Groups of 8 and more: lane l owns E = 8 or 16 consecutive columns, which lie
-// in one group (one norm) and in E * BITS / 8 whole bytes of the row; all the
-// lane's loads are issued together before any is used.  Rows whose visible
+// in one group (one norm) and in E * BITS / 8 whole bytes of the row.  Work
+// items are (id, span of 64 E columns); persistent wavefronts take items
+// wv, wv + n_waves, ... (at most 64 each).  Lane j loads the id of the
+// wavefront's j-th item up front; then the row bytes and norms of up to
+// kGatherAhead items are requested together, and the items are decoded,
+// transformed and stored one after another, so one item's stores drain while
+// the next is computed.  LOG2G > 0 fixes the group at compile time (the
+// transform's stage choices fold away); 0 takes log2_group.  WORDS: the lane's
+// bytes are whole dwords at dword addresses (rows of a multiple of 4 bytes,
+// packed 4-byte aligned, E * BITS / 8 a multiple of 4).  Rows whose visible
 // columns fill the lane are stored as float4s when the output rows are
-// 16-byte aligned.
-template <int BITS, int E>
+// 16-byte aligned; every output store is nontemporal.
+constexpr int kGatherAhead = 8;
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+
+template <int BITS, int E, bool WORDS>
+struct GatherLoad {
+  static constexpr int kBytes = E * BITS / 8;
+  static constexpr int kRegs = WORDS ? kBytes / 4 : kBytes;  // dwords, or one byte each
+  uint32_t reg[kRegs];
+  uint32_t norm_bits;
+  __device__ __forceinline__ uint32_t byte(int k) const {
+    if constexpr (WORDS) return (reg[k >> 2] >> (8 * (k & 3))) & 0xffu;
+    else return reg[k];
+  }
+};
+
+template <int BITS, int E, bool WORDS>
+__device__ __forceinline__ void gather_request(GatherLoad<BITS, E, WORDS>& g, const uint8_t* prow,
+                                               const uint16_t* nrow, int cl, int log2_group) {
+  const uint8_t* pb = prow + (int64_t)cl * BITS / 8;
+  if constexpr (WORDS) {
+    const uint32_t* pw = reinterpret_cast<const uint32_t*>(pb);
+#pragma unroll
+    for (int k = 0; k < GatherLoad<BITS, E, WORDS>::kRegs; ++k) g.reg[k] = pw[k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < GatherLoad<BITS, E, WORDS>::kRegs; ++k) g.reg[k] = pb[k];
+  }
+  g.norm_bits = nrow[cl >> log2_group];
+}
+
+template <int BITS, int E, int LOG2G, bool WORDS>
 __global__ __launch_bounds__(kThreads) void cq_gather_kernel(
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
     const float* __restrict__ codebook, const int32_t* __restrict__ rows, float* __restrict__ out,
-    int64_t output, int64_t input, int64_t input_padded, int64_t row_bytes, int log2_group,
-    int64_t spans, int64_t n_waves, double scale, bool vec_store) {
-  constexpr int kBytes = E * BITS / 8;
+    int64_t output, int64_t input, int64_t input_padded, int64_t row_bytes, int log2_group_rt,
+    int64_t spans, int64_t items, int64_t n_waves, double scale, bool vec_store) {
+  const int log2_group = LOG2G > 0 ? LOG2G : log2_group_rt;
   __shared__ float cb[32];
-  if (threadIdx.x < (1 << BITS)) cb[threadIdx.x] = codebook[threadIdx.x];
-  __syncthreads();
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wv = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-  if (wv >= n_waves) return;  // whole wavefront
-  const int64_t i = wv / spans;
-  const int64_t c0 = (wv % spans) * (64 * E) + lane * E;
-  const int64_t r = rows[i];
-  float* o = out + i * input + c0;
-  if (r < 0 || r >= output) {  // an id outside the table: a NaN row
+  // lane j: the id of this wavefront's j-th item (requested with the codebook);
+  // item = id index * spans + span, and one span per id is the common case
+  const int64_t my_item = wv + lane * n_waves;
+  const int32_t my_id = my_item < items ? rows[spans == 1 ? my_item : my_item / spans] : 0;
+  if (threadIdx.x < (1 << BITS)) cb[threadIdx.x] = codebook[threadIdx.x];
+  __syncthreads();
+  if (wv >= items) return;  // whole wavefront, after the barrier
+  const int n_mine = (int)((items - wv + n_waves - 1) / n_waves);  // <= 64
+  const int64_t nrow_stride = input_padded >> log2_group;
+  // columns fit in 32 bits (input_padded < 2^28)
+  const int in = (int)input, in_pad = (int)input_padded;
+  for (int base = 0; base < n_mine; base += kGatherAhead) {
+    // request this round's items: row bytes and norm of the lane's columns
+    // (an id outside the table, or columns past the stored row, load row 0 /
+    // column 0 and use nothing)
+    GatherLoad<BITS, E, WORDS> g[kGatherAhead];
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (c0 + e < input) o[e] = __uint_as_float(0x7fc00000u);
-    return;
-  }
-  // input_padded is a multiple of the group, so a lane's E columns are all
-  // inside the stored row or all past it
-  const bool live = c0 < input_padded;
-  const int64_t cl = live ? c0 : 0;  // past the row: load column 0, use nothing
-  const uint8_t* pb = packed + r * row_bytes + cl * BITS / 8;
-  uint32_t byte[kBytes];
+    for (int q = 0; q < kGatherAhead; ++q) {
+      if (base + q < n_mine) {
+        const int64_t it = wv + (int64_t)(base + q) * n_waves;
+        const int64_t r = __builtin_amdgcn_readlane(my_id, base + q);
+        const int64_t rs = r >= 0 && r < output ? r : 0;
+        const int c0 = (spans == 1 ? 0 : (int)(it % spans)) * (64 * E) + lane * E;
+        gather_request<BITS, E, WORDS>(g[q], packed + rs * row_bytes, norms + rs * nrow_stride,
+                                       c0 < in_pad ? c0 : 0, log2_group);
+      }
+    }
 #pragma unroll
-  for (int k = 0; k < kBytes; ++k) byte[k] = pb[k];
-  const float nrm = f16_to_f32(norms[r * (input_padded >> log2_group) + (cl >> log2_group)]);
-  float v[E];
+    for (int q = 0; q < kGatherAhead; ++q) {
+      if (base + q >= n_mine) break;
+      const int64_t it = wv + (int64_t)(base + q) * n_waves;
+      const int64_t r = __builtin_amdgcn_readlane(my_id, base + q);
+      const int c0 = (spans == 1 ? 0 : (int)(it % spans)) * (64 * E) + lane * E;
+      float* o = out + (spans == 1 ? it : it / spans) * input + c0;
+      if (r < 0 || r >= output) {  // an id outside the table: a NaN row
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int bit = BITS * e, k = bit >> 3, sh = bit & 7;
-    uint32_t w = byte[k];
-    if (sh + BITS > 8) w |= byte[k + 1] << 8;
-    const float c = cb[(w >> sh) & ((1u << BITS) - 1u)] * nrm;
-    v[e] = live ? c : 0.0f;
-  }
-  wave_fwht<E>(v, lane, log2_group);
-  if (vec_store && c0 + E <= input) {
+        for (int e = 0; e < E; ++e)
+          if (c0 + e < in) o[e] = __uint_as_float(0x7fc00000u);
+        continue;
+      }
+      // input_padded is a multiple of the group, so a lane's E columns are all
+      // inside the stored row or all past it
+      const bool live = c0 < in_pad;
+      const float nrm = f16_to_f32((uint16_t)g[q].norm_bits);
+      float v[E];
 #pragma unroll
-    for (int e = 0; e < E; e += 4)
-      *reinterpret_cast<float4*>(o + e) =
-          make_float4(scale_store(v[e], scale), scale_store(v[e + 1], scale),
-                      scale_store(v[e + 2], scale), scale_store(v[e + 3], scale));
-  } else {
+      for (int e = 0; e < E; ++e) {
+        const int bit = BITS * e, k = bit >> 3, sh = bit & 7;
+        uint32_t w = g[q].byte(k);
+        if (sh + BITS > 8) w |= g[q].byte(k + 1) << 8;
+        const float c = cb[(w >> sh) & ((1u << BITS) - 1u)] * nrm;
+        v[e] = live ? c : 0.0f;
+      }
+      wave_fwht<E>(v, lane, log2_group);
+      // nontemporal stores: the rows stream out to memory as they are made
+      // instead of waiting in the L2 for the kernel's end
+      if (vec_store && c0 + E <= in) {
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (c0 + e < input) o[e] = scale_store(v[e], scale);
+        for (int e = 0; e < E; e += 4) {
+          const f32x4_nt q = {scale_store(v[e], scale), scale_store(v[e + 1], scale),
+                              scale_store(v[e + 2], scale), scale_store(v[e + 3], scale)};
+          __builtin_nontemporal_store(q, reinterpret_cast<f32x4_nt*>(o + e));
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (c0 + e < in) __builtin_nontemporal_store(scale_store(v[e], scale), o + e);
+      }
+    }
   }
 }
 
@@ -210,18 +275,39 @@ int launch_gather_generic(const bqd_cq_matrix* m, const int32_t* rows, int64_t n
   return launch_status();
 }
 
+// Persistent wavefronts per CU for the gather: enough items each to overlap
+// one item's loads with the previous item's arithmetic and stores.
+constexpr int kGatherWavesPerCu = 16;
+
+template <int BITS, int E, int LOG2G, bool WORDS>
+int launch_gather_kernel(const bqd_cq_matrix* m, const int32_t* rows, int64_t items,
+                         int64_t spans, float* out, hipStream_t s) {
+  // at most 64 items per wavefront (one id per lane)
+  int64_t n_waves = std::max<int64_t>((int64_t)cu_count() * kGatherWavesPerCu, (items + 63) / 64);
+  n_waves = std::min(n_waves, items);
+  const int64_t grid = (n_waves + kWavesPerBlock - 1) / kWavesPerBlock;
+  const bool vec_store = m->input % 4 == 0 && is_aligned(out, 16);
+  hipLaunchKernelGGL((cq_gather_kernel<BITS, E, LOG2G, WORDS>), dim3((unsigned)grid),
+                     dim3(kThreads), 0, s, m->packed, m->norms, m->codebook, rows, out,
+                     m->output, m->input, m->input_padded, m->row_bytes, ilog2(m->group),
+                     spans, items, n_waves, 1.0 / std::sqrt((double)m->group), vec_store);
+  return launch_status();
+}
+
 template <int BITS, int E>
 int launch_gather_fast(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, float* out,
                        hipStream_t s) {
+  // spans past the last visible column store nothing and are not launched
   const int64_t spans = (m->input + 64 * E - 1) / (64 * E);
-  const int64_t n_waves = spans * n;
-  const int64_t grid = (n_waves + kWavesPerBlock - 1) / kWavesPerBlock;
-  const bool vec_store = m->input % 4 == 0 && is_aligned(out, 16);
-  hipLaunchKernelGGL((cq_gather_kernel<BITS, E>), dim3((unsigned)grid), dim3(kThreads), 0, s,
-                     m->packed, m->norms, m->codebook, rows, out, m->output, m->input,
-                     m->input_padded, m->row_bytes, ilog2(m->group), spans, n_waves,
-                     1.0 / std::sqrt((double)m->group), vec_store);
-  return launch_status();
+  const int64_t items = spans * n;
+  constexpr bool kWholeWords = (E * BITS / 8) % 4 == 0;
+  const bool words = kWholeWords && m->row_bytes % 4 == 0 && is_aligned(m->packed, 4);
+  if (words && E == 8 && m->group == 128)
+    return launch_gather_kernel<BITS, E, 7, kWholeWords>(m, rows, items, spans, out, s);
+  if (words && E == 8 && m->group == 256)
+    return launch_gather_kernel<BITS, E, 8, kWholeWords>(m, rows, items, spans, out, s);
+  if (words) return launch_gather_kernel<BITS, E, 0, kWholeWords>(m, rows, items, spans, out, s);
+  return launch_gather_kernel<BITS, E, 0, false>(m, rows, items, spans, out, s);
 }
 
 template <int E>

@@ -133,18 +133,22 @@ __device__ __forceinline__ float lane_xor(float v) {
 }
 
 // One butterfly stage across lanes l and l ^ D: the lower lane keeps a + b,
-// the upper one a - b, where a is the lower lane's value.
+// the upper one a - b, where a is the lower lane's value.  Both are one fused
+// multiply-add with a per-lane sign: fma(x, +-1, y) forms x * (+-1) exactly
+// and rounds the sum once, so it is the fp32 a + b (lower lane: x = a, y = b)
+// or a - b (upper lane: x = b, y = a) bit for bit, signed zeros and
+// infinities included.
 template <int E, int D>
 __device__ __forceinline__ void lane_stage(float (&v)[E], int lane) {
-  const bool upper = (lane & D) != 0;
+  const float sign = (lane & D) ? -1.0f : 1.0f;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     if constexpr (D >= 16) {
       const float2 p = lane_pair<D>(v[e]);  // (a, b): the lower and the upper element
-      v[e] = upper ? p.x - p.y : p.x + p.y;
+      v[e] = __builtin_fmaf(p.y, sign, p.x);
     } else {
       const float o = lane_xor<D>(v[e]);
-      v[e] = upper ? o - v[e] : v[e] + o;
+      v[e] = __builtin_fmaf(v[e], sign, o);
     }
   }
 }
