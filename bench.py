@@ -60,6 +60,29 @@ def measured_traffic():
     return rec["traffic_bytes"] if rec.get("source_sha256_16") == h else None
 
 
+# CQ stages with an HBM traffic record: the kernel that runs them (a
+# substring of its name in the counter output), the workload, and the bytes
+# the method must move per launch (weights, activations and ids in; outputs).
+STAGE_TRAFFIC = {
+    "cq4_16384x4096_prepare_matvec_b1": dict(
+        kernel="cq_matvec_ring", workload="cq4_16384x4096_b1",
+        what="CQ4 16384 x 4096 (group 256), one vector, prepare fused",
+        reads=16384 * 2048 + 16384 * 16 * 2 + 4 * 4096, writes=4 * 4096 + 4 * 16384),
+    "cq4_16384x4096_matvec_b8": dict(
+        kernel="cq_matvec_mfma4", workload="cq4_16384x4096_b8",
+        what="CQ4 16384 x 4096 (group 256), eight prepared vectors",
+        reads=16384 * 2048 + 16384 * 16 * 2 + 8 * 4 * 4096, writes=8 * 4 * 16384),
+    "cq4_65536x512_prepare_matvec_b1": dict(
+        kernel="cq_matvec_ring", workload="cq4_65536x512_b1",
+        what="CQ4 65536 x 512 (group 128) vocabulary projection, one vector, prepare fused",
+        reads=65536 * 256 + 65536 * 4 * 2 + 4 * 512, writes=4 * 512 + 4 * 65536),
+    "cq4_65536x512_gather_4096": dict(
+        kernel="cq_gather_kernel", workload="cq4_65536x512_gather_4096",
+        what="4096 rows of CQ4 65536 x 512 (group 128) gathered dense",
+        reads=4096 * (256 + 8) + 4 * 4096, writes=4 * 4096 * 512),
+}
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -75,9 +98,12 @@ def parse_args():
     ap.add_argument("--hot", action="store_true", help="one weight copy (cache-resident timing)")
     ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn the two --traffic-probe counter runs into the traffic record "
-                         "under profiles/ (no GPU needed)")
+                         "under profiles/ (no GPU needed); with --stage, a stage's record")
     ap.add_argument("--traffic-probe", action="store_true",
-                    help="for counter runs: 8 F8 head launches, then 8 plain 1 GiB device copies")
+                    help="for counter runs: 8 F8 head launches (with --stage: 4 replays of the "
+                         "stage's graph of 16 launches), then 8 plain 1 GiB device copies")
+    ap.add_argument("--stage", choices=sorted(STAGE_TRAFFIC),
+                    help="the CQ stage of --traffic-probe / --traffic-record")
     ap.add_argument("--stage-probe", metavar="STAGE",
                     help="for counter runs: 4 replays of one stage's graph of 16 launches "
                          "(a step stage or an extra, by its name in the JSON line)")
@@ -92,7 +118,10 @@ class Case:
         self.ms = []
 
 
-def build_cases(torch, bqd, synth, hot):
+def build_cases(torch, bqd, synth, hot, heads=True):
+    """The step's stages and the extras; heads=False leaves out the two
+    1 GB heads (F8 and I8) and the sampler's logits, for counter probes of
+    the CQ stages."""
     dev = "cuda"
     T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     cases = []
@@ -163,30 +192,32 @@ def build_cases(torch, bqd, synth, hot):
                        for k in range(len(mats3))],
                       gather_bytes, n_ids))
 
-    # -- FP8 head 246272 x 4096
-    log("generating F8 head 246272x4096 (seed 4)")
-    hd = synth.make_f8(**synth.HEAD, seed=4)
-    kh = 1 if hot else 2
-    wh0 = T(hd.w)
-    whs = [wh0] + [wh0.clone() for _ in range(kh - 1)]
-    sh, xh = T(hd.scale), T(hd.x)
-    yh = torch.empty(1, hd.R, device=dev)
-    head_bytes = hd.R * hd.C + hd.SR * hd.SC + 4 * hd.C + 4 * hd.R
-    cases.append(Case(HEAD_STAGE,
-                      [lambda w=w: bqd.f8_matvec(w, sh, xh, out=yh) for w in whs],
-                      head_bytes, hd.R))
-    # -- beyond the step: the I8 head (E8M0 scales per 16 columns) and the
-    # int8 key cache (quantize 4096 vectors of 128, score one query)
-    log("generating I8 head 246272x4096 G16 (seed 5)")
-    i8 = synth.make_i8(**synth.I8_HEAD, seed=5)
-    wi0 = T(i8.w)
-    wis = [wi0] + [wi0.clone() for _ in range(kh - 1)]
-    si, xi = T(i8.scale), T(i8.x)
-    yi = torch.empty(1, i8.R, device=dev)
-    i8_bytes = i8.R * i8.C + i8.scale.size + 4 * i8.C + 4 * i8.R
-    extras.append(Case("i8_head_246272x4096_g16_matvec",
-                       [lambda w=w: bqd.i8_matvec(w, si, xi, i8.G, out=yi) for w in wis],
-                       i8_bytes, i8.R))
+    hd = yh = None
+    if heads:
+        # -- FP8 head 246272 x 4096
+        log("generating F8 head 246272x4096 (seed 4)")
+        hd = synth.make_f8(**synth.HEAD, seed=4)
+        kh = 1 if hot else 2
+        wh0 = T(hd.w)
+        whs = [wh0] + [wh0.clone() for _ in range(kh - 1)]
+        sh, xh = T(hd.scale), T(hd.x)
+        yh = torch.empty(1, hd.R, device=dev)
+        head_bytes = hd.R * hd.C + hd.SR * hd.SC + 4 * hd.C + 4 * hd.R
+        cases.append(Case(HEAD_STAGE,
+                          [lambda w=w: bqd.f8_matvec(w, sh, xh, out=yh) for w in whs],
+                          head_bytes, hd.R))
+        # -- beyond the step: the I8 head (E8M0 scales per 16 columns) and the
+        # int8 key cache (quantize 4096 vectors of 128, score one query)
+        log("generating I8 head 246272x4096 G16 (seed 5)")
+        i8 = synth.make_i8(**synth.I8_HEAD, seed=5)
+        wi0 = T(i8.w)
+        wis = [wi0] + [wi0.clone() for _ in range(kh - 1)]
+        si, xi = T(i8.scale), T(i8.x)
+        yi = torch.empty(1, i8.R, device=dev)
+        i8_bytes = i8.R * i8.C + i8.scale.size + 4 * i8.C + 4 * i8.R
+        extras.append(Case("i8_head_246272x4096_g16_matvec",
+                           [lambda w=w: bqd.i8_matvec(w, si, xi, i8.G, out=yi) for w in wis],
+                           i8_bytes, i8.R))
     kv = synth.make_kv(**synth.KV, seed=6)
     nkv, dkv = kv.v.shape
     vk, xk = T(kv.v), T(kv.x)
@@ -439,24 +470,35 @@ def capture(torch, fn):
     return g
 
 
-def traffic_probe(torch, bqd, synth):
-    """A fixed launch sequence for rocprofv3 --pmc runs: the dominant kernel,
-    then a plain device copy of known size to calibrate the byte counters."""
-    hd = synth.make_f8(**synth.HEAD, seed=4)
-    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
-    w, s, x = T(hd.w), T(hd.scale), T(hd.x)
-    y = torch.empty(1, hd.R, device="cuda")
-    for _ in range(8):
-        bqd.f8_matvec(w, s, x, out=y)
-    torch.cuda.synchronize()
-    del w
+def traffic_probe(torch, bqd, synth, stage=None):
+    """A fixed launch sequence for rocprofv3 --pmc runs: the dominant kernel
+    (or a CQ stage's graph of 16 launches over its rotated copies, replayed
+    4 times), then a plain device copy of known size to calibrate the byte
+    counters."""
+    if stage:
+        cases, extra_cases, _ = build_cases(torch, bqd, synth, False, heads=False)
+        c = next(c for c in cases + extra_cases if c.name == stage)
+        g = capture(torch, lambda: [c.calls[k % len(c.calls)]() for k in range(STAGE_LAUNCHES)])
+        for _ in range(4):
+            g.replay()
+        torch.cuda.synchronize()
+        del g, cases, extra_cases
+    else:
+        hd = synth.make_f8(**synth.HEAD, seed=4)
+        T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+        w, s, x = T(hd.w), T(hd.scale), T(hd.x)
+        y = torch.empty(1, hd.R, device="cuda")
+        for _ in range(8):
+            bqd.f8_matvec(w, s, x, out=y)
+        torch.cuda.synchronize()
+        del w
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(7)
     b = torch.empty_like(a)
     for _ in range(8):
         b.copy_(a)
     torch.cuda.synchronize()
-    print(json.dumps({"f8_head_bytes": hd.R * hd.C + hd.SR * hd.SC, "copy_bytes": n}), flush=True)
+    print(json.dumps({"probe": stage or HEAD_STAGE, "copy_bytes": n}), flush=True)
 
 
 def stage_probe(torch, bqd, synth, name, hot):
@@ -475,24 +517,83 @@ def stage_probe(torch, bqd, synth, name, hot):
     print(json.dumps({"stage": name, "launches": 5 * n, "bytes": c.nbytes}), flush=True)
 
 
-def _dispatch_kib(out_dir, counter):
-    """Median per-dispatch value of `counter` for the head kernel and for the
-    1 GiB copy, from a rocprofv3 --pmc csv directory."""
+def _dispatch_kib(out_dir, counter, kernel="f8_matvec_fast"):
+    """Median per-dispatch value of `counter` for the kernel and for the
+    1 GiB copy, from a rocprofv3 --pmc csv directory; also the kernel's full
+    name."""
     import csv
     import glob
     import statistics
-    vals = {"head": [], "copy": []}
+    vals = {"kernel": [], "copy": []}
+    names = set()
     for f in glob.glob(os.path.join(out_dir, "**", "*counter_collection.csv"), recursive=True):
         for row in csv.DictReader(open(f)):
             if row["Counter_Name"] != counter:
                 continue
             name = row["Kernel_Name"]
-            key = "head" if "f8_matvec_fast" in name else "copy" if "copyBuffer" in name else None
+            key = "kernel" if kernel in name else "copy" if "copyBuffer" in name else None
             if key:
-                vals[key].append(float(row["Counter_Value"]))
-    if len(vals["head"]) < 8 or len(vals["copy"]) < 8:
-        raise SystemExit(f"{out_dir}: expected 8 head and 8 copy dispatches for {counter}")
-    return statistics.median(vals["head"]), statistics.median(vals["copy"])
+                vals[key].append((int(row.get("Dispatch_Id") or 0), float(row["Counter_Value"])))
+                if key == "kernel":
+                    names.add(name.split("(")[0])
+    if len(vals["kernel"]) < 8 or len(vals["copy"]) < 8:
+        raise SystemExit(f"{out_dir}: expected 8 {kernel} and 8 copy dispatches for {counter}")
+    # the calibration copies are the probe's last 8 copy dispatches (uploads
+    # and clones of the inputs come earlier)
+    copies = [v for _, v in sorted(vals["copy"])[-8:]]
+    return (statistics.median(v for _, v in vals["kernel"]), statistics.median(copies),
+            sorted(names))
+
+
+def stage_traffic_record(stage, fetch_dir, write_dir, out_dir=None):
+    """HBM bytes per launch of a CQ stage's kernel: FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch, median) each scaled by what the same counter reads for
+    a 1 GiB device copy in the same run; written as JSON and markdown under
+    profiles/."""
+    import hashlib
+    st = STAGE_TRAFFIC[stage]
+    kf, copy_f, names = _dispatch_kib(fetch_dir, "FETCH_SIZE", st["kernel"])
+    kw, copy_w, _ = _dispatch_kib(write_dir, "WRITE_SIZE", st["kernel"])
+    gib_kib = float(1 << 20)
+    fetch_scale, write_scale = round(gib_kib / copy_f, 2), round(gib_kib / copy_w, 2)
+    read_b, write_b = round(kf * 1024 * fetch_scale), round(kw * 1024 * write_scale)
+    srcs = [os.path.join(ROOT, "bit_quantized_decode_amd", "csrc", f)
+            for f in ("cq.hip", "cq_device.h", "device.h")]
+    rec = {
+        "stage": stage, "kernel": names, "workload": st["what"],
+        "source_sha256_16": hashlib.sha256(b"".join(open(f, "rb").read() for f in srcs)).hexdigest()[:16],
+        "fetch_kib_per_dispatch_raw": kf, "write_kib_per_dispatch_raw": kw,
+        "copy_1gib_fetch_kib_raw": copy_f, "copy_1gib_write_kib_raw": copy_w,
+        "fetch_scale": fetch_scale, "write_scale": write_scale,
+        "read_bytes": read_b, "write_bytes": write_b, "traffic_bytes": read_b + write_b,
+        "algorithmic_read_bytes": st["reads"], "algorithmic_write_bytes": st["writes"],
+        "read_over_algorithmic": round(read_b / st["reads"], 4),
+        "write_over_algorithmic": round(write_b / st["writes"], 4),
+    }
+    base = os.path.join(out_dir or os.path.join(ROOT, "profiles"),
+                        f"{st['kernel']}_{st['workload']}_hbm_traffic")
+    with open(base + ".json", "w") as f:
+        json.dump(rec, f, indent=1)
+    cmd = (f"rocprofv3 --pmc {{FETCH_SIZE|WRITE_SIZE}} --output-format csv -d <dir> -o t -- "
+           f"python3 bench.py --traffic-probe --stage {stage}")
+    md = [f"# HBM traffic of `{st['kernel']}`: {st['what']}", "",
+          "Two counter runs of one fixed launch sequence (the stage's graph of 16 launches over its",
+          "16 rotated weight copies, replayed 4 times, then 8 plain 1 GiB device copies), then the",
+          "record (no GPU):", "", "```", cmd,
+          f"python3 bench.py --traffic-record <fetch dir> <write dir> --stage {stage}", "```", "",
+          "Per dispatch (median), KiB as the counters report them:", "",
+          "| kernel | FETCH_SIZE | WRITE_SIZE |", "|---|---:|---:|",
+          f"| `__amd_rocclr_copyBuffer`, 1 GiB copy | {copy_f:,.1f} | {copy_w:,.1f} |",
+          f"| `{', '.join(names)}` | {kf:,.1f} | {kw:,.1f} |", "",
+          f"Scales from the copy: FETCH_SIZE x {fetch_scale}, WRITE_SIZE x {write_scale}.", "",
+          "| | bytes per launch |", "|---|---:|",
+          f"| reads, scaled | {read_b:,} |", f"| algorithmic reads | {st['reads']:,} |",
+          f"| reads / algorithmic | {rec['read_over_algorithmic']} |",
+          f"| writes, scaled | {write_b:,} |", f"| algorithmic writes | {st['writes']:,} |",
+          f"| writes / algorithmic | {rec['write_over_algorithmic']} |", ""]
+    with open(base + ".md", "w") as f:
+        f.write("\n".join(md))
+    print(json.dumps(rec))
 
 
 def traffic_record(fetch_dir, write_dir):
@@ -501,8 +602,8 @@ def traffic_record(fetch_dir, write_dir):
     import hashlib
     import synth
     hd = synth.HEAD
-    head_f, copy_f = _dispatch_kib(fetch_dir, "FETCH_SIZE")
-    head_w, copy_w = _dispatch_kib(write_dir, "WRITE_SIZE")
+    head_f, copy_f, _ = _dispatch_kib(fetch_dir, "FETCH_SIZE")
+    head_w, copy_w, _ = _dispatch_kib(write_dir, "WRITE_SIZE")
     gib_kib = float(1 << 20)
     fetch_scale = round(gib_kib / copy_f, 2)
     write_scale = round(gib_kib / copy_w, 2)
@@ -526,7 +627,10 @@ def traffic_record(fetch_dir, write_dir):
 def main():
     args = parse_args()
     if args.traffic_record:
-        traffic_record(*args.traffic_record)
+        if args.stage:
+            stage_traffic_record(args.stage, *args.traffic_record)
+        else:
+            traffic_record(*args.traffic_record)
         return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -540,7 +644,7 @@ def main():
     torch.cuda.set_device(0)
     bqd.lib()
     if args.traffic_probe:
-        traffic_probe(torch, bqd, synth)
+        traffic_probe(torch, bqd, synth, args.stage)
         return
     if args.stage_probe:
         stage_probe(torch, bqd, synth, args.stage_probe, args.hot)

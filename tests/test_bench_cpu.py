@@ -34,3 +34,30 @@ def test_traffic_is_reported_only_for_the_recorded_sources(tmp_path, monkeypatch
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(other))
     assert bench.measured_traffic() == rec["traffic_bytes"]
 
+
+
+def _counter_csv(d, counter, rows):
+    d.mkdir(parents=True, exist_ok=True)
+    with open(d / "t_counter_collection.csv", "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for i, (name, v) in enumerate(rows):
+            f.write(f"{i + 1},\"{name}\",{counter},{v}\n")
+
+
+def test_stage_traffic_record_scales_by_the_copy(tmp_path):
+    # FETCH_SIZE reading half of a 1 GiB copy's reads scales by 2, WRITE_SIZE
+    # reading it exactly by 1; medians over 8 dispatches of each
+    stage = "cq4_65536x512_gather_4096"
+    kern = "void bqd::cq_gather_kernel<4, 8, 7, true>(unsigned char const*)"
+    copy = "__amd_rocclr_copyBuffer"
+    # uploads of the inputs are earlier, small copies: only the last 8 calibrate
+    _counter_csv(tmp_path / "f", "FETCH_SIZE",
+                 [(copy, 3.0)] * 20 + [(kern, 600.0)] * 8 + [(copy, 524288.0)] * 8)
+    _counter_csv(tmp_path / "w", "WRITE_SIZE", [(kern, 8192.0)] * 8 + [(copy, 1048576.0)] * 8)
+    bench.stage_traffic_record(stage, str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path))
+    rec = json.load(open(tmp_path / "cq_gather_kernel_cq4_65536x512_gather_4096_hbm_traffic.json"))
+    assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
+    assert rec["read_bytes"] == 600 * 1024 * 2 and rec["write_bytes"] == 8192 * 1024
+    assert rec["algorithmic_write_bytes"] == 4 * 4096 * 512
+    assert rec["kernel"] == ["void bqd::cq_gather_kernel<4, 8, 7, true>"]
+    assert (tmp_path / "cq_gather_kernel_cq4_65536x512_gather_4096_hbm_traffic.md").exists()
