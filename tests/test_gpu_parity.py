@@ -896,13 +896,26 @@ def test_sample_head_sized(kind, k, T):
     check_sample(_logits(kind, 246272, 90 + k), k, T, seed=0x9E3779B9 + k, calls=4)
 
 
+# Ragged tails and sizes around the first stage's block counts.
 @pytest.mark.parametrize("n,k", [(1, 1), (5, 5), (64, 64), (1023, 5), (1025, 64), (4095, 7),
-                                 (4096, 64), (4097, 64), (8191, 3), (65536 + 17, 33),
-                                 (256 * 1024, 64), (256 * 1024 + 1, 9), (512 * 1024 + 1, 64),
-                                 (1 << 20, 64)])
+                                 (4096, 64), (4097, 64), (8191, 3), (32768, 64), (32769, 64),
+                                 (65536, 2), (65536 + 17, 33), (131073, 17), (256 * 1024, 64),
+                                 (256 * 1024 + 1, 9), (512 * 1024 + 1, 64), (1 << 20, 64)])
 def test_sample_ragged_sizes(n, k):
     check_sample(_logits("normal", n, n), k, 0.8, seed=12345 + n)
     check_sample(_logits("ties", n, n + 1), k, 1.3, seed=777 + n)
+
+
+@pytest.mark.parametrize("n", [246272, 1 << 20])
+def test_sample_top_keys_crowded_in_one_block(n):
+    """The best 512 logits are the first 512 (a ladder rising with the
+    index), so one first-stage block holds all of the top k: the second stage
+    finds a list whose first 8 keys all pass its bound and merges every list
+    in full."""
+    x = _logits("normal", n, n + 5)
+    x[:512] = (1000 + np.arange(512)).astype(np.float32)
+    check_sample(x, 64, 0.9, seed=31 + n)
+    check_sample(x, 40, 0.0, seed=32 + n)
 
 
 @pytest.mark.parametrize("n,k", [(40, 40), (246272, 64)])
