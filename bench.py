@@ -38,7 +38,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
-# Host cores the GPU machine grants one GPU's job (its affinity mask may show more).
+# Host cores granted to a job on one GPU (the affinity mask may show more).
 CPU_SHARE = 16
 HEAD_STAGE = "f8_head_246272x4096_matvec"
 STAGE_LAUNCHES = 16  # back-to-back launches per timed stage graph
