@@ -28,6 +28,13 @@ MUTANTS = {
                              "tg[k] = m->codebook[oracle_cq_index(m, row, g * m->group + k)];"),
     "dense_dropped_column": ("for (int64_t c = 0; c < m->input; c++) acc +=",
                              "for (int64_t c = 1; c < m->input; c++) acc +="),
+    "dequant_no_transform": ("        oracle_fwht(tg, m->group);\n        for (int64_t k = 0; k < m->group; k++) tg[k] = scale_store",
+                             "        for (int64_t k = 0; k < m->group; k++) tg[k] = scale_store"),
+    "dequant_no_scale": ("for (int64_t k = 0; k < m->group; k++) tg[k] = scale_store(tg[k], m->group);",
+                         "for (int64_t k = 0; k < m->group; k++) tg[k] = tg[k];"),
+    "dequant_norm_of_group_0": ("float norm = oracle_f16(m->norms[row * n_groups + g]);",
+                                "float norm = oracle_f16(m->norms[row * n_groups]);"),
+    "gather_mag_unscaled": ("gmag[i * m->input + k] = s * inv;", "gmag[i * m->input + k] = s;"),
     "f16_bias": ("ldexp((double)(1024 + F), E - 25)", "ldexp((double)(1024 + F), E - 26)"),
     "f16_subnormal_bias": ("ldexp((double)F, -24)", "ldexp((double)F, -25)"),
     "f16_hidden_bit_dropped": ("ldexp((double)(1024 + F), E - 25)", "ldexp((double)F, E - 25)"),
