@@ -35,6 +35,12 @@ MUTANTS = {
     "dequant_norm_of_group_0": ("float norm = oracle_f16(m->norms[row * n_groups + g]);",
                                 "float norm = oracle_f16(m->norms[row * n_groups]);"),
     "gather_mag_unscaled": ("gmag[i * m->input + k] = s * inv;", "gmag[i * m->input + k] = s;"),
+    "matvec_mag_no_norm": ("amag += fabs(norm) * apart;", "amag += apart;"),
+    "matvec_mag_signed": ("apart += fabs(term);", "apart += term;"),
+    "f8_mag_signed": ("(double)oracle_e8m0(s[sr * SC + sc]) * (double)x[c];\n            acc += term;\n            amag += fabs(term);",
+                      "(double)oracle_e8m0(s[sr * SC + sc]) * (double)x[c];\n            acc += term;\n            amag += term;"),
+    "i8_mag_signed": ("(double)oracle_e8m0(s[r * ns + c / G]) *\n                          (double)x[c];\n            acc += term;\n            amag += fabs(term);",
+                      "(double)oracle_e8m0(s[r * ns + c / G]) *\n                          (double)x[c];\n            acc += term;\n            amag += term;"),
     "f16_bias": ("ldexp((double)(1024 + F), E - 25)", "ldexp((double)(1024 + F), E - 26)"),
     "f16_subnormal_bias": ("ldexp((double)F, -24)", "ldexp((double)F, -25)"),
     "f16_hidden_bit_dropped": ("ldexp((double)(1024 + F), E - 25)", "ldexp((double)F, E - 25)"),
