@@ -135,6 +135,22 @@ def pin_fwht_involution():
         assert np.array_equal(oracle.fwht(oracle.fwht(x)), (n * x).astype(np.float32))
 
 
+def pin_fwht_stride_order_rounding():
+    """[P1] §1 runs the strides in ascending order and stores every stage in
+    fp32; both show in the rounding.  x = [1, 2^-24, -1, 2^-24]: the stride-1
+    stage forms 1 + 2^-24 (a tie between 1 and 1 + 2^-23, rounded to the even
+    1), 1 - 2^-24 (exact), -1 + 2^-24 (exact) and -1 - 2^-24 (a tie, -1); the
+    stride-2 stage then gives [2^-24, -2^-24, 2 - 2^-24 -> 2 (a tie, to the
+    even 2), 2].  The strides in the other order, or stages kept exact, give
+    the true transform [2^-23, -2^-23, 2, 2]."""
+    t = np.float32(2.0 ** -24)
+    x = np.array([1, t, -1, t], dtype=np.float32)
+    want = np.array([t, -t, 2, 2], dtype=np.float32)
+    assert np.array_equal(oracle.fwht(x).view(np.uint32), want.view(np.uint32))
+    exact = np.array([2 * t, -2 * t, 2, 2], dtype=np.float32)
+    assert not np.array_equal(want, exact)
+
+
 def pin_crumb_order_golden():
     for row in _read_table("crumb_order.txt"):
         byte = int(row[0], 16)
@@ -193,6 +209,45 @@ def pin_prepare_one_hot():
                 sign = -1.0 if bin((j - g0) & k).count("1") % 2 else 1.0
                 ref[g0 + k] = np.float32(sign * scale)
             assert np.array_equal(p, ref), (g, j)
+
+
+def _round_significand(fr: Fraction, bits: int) -> Fraction:
+    """A positive rational rounded to `bits` significant bits, ties to even
+    (IEEE round-to-nearest for a normal result)."""
+    e = fr.numerator.bit_length() - fr.denominator.bit_length()
+    if Fraction(2) ** e > fr:
+        e -= 1  # now 2^e <= fr < 2^(e + 1)
+    unit = Fraction(2) ** (e - bits + 1)
+    scaled = fr / unit
+    q = scaled.numerator // scaled.denominator
+    rem = scaled - q
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and q % 2 == 1):
+        q += 1
+    return q * unit
+
+
+def pin_prepare_scale_rounds_from_fp64():
+    """[P1] §2 keeps the scale 1/sqrt(g) as a JavaScript number (a double),
+    multiplies in double and stores to a Float32Array: the exact product is
+    rounded to 53 bits, then to 24.  Worked exactly in rationals for g = 128
+    (where the scale is no power of two): a one-hot v at column 0 transforms to
+    v in every column of the group, so every prepared value is v's scaled
+    value.  The v below are ones where a plain fp32 product rounds otherwise."""
+    g = 128
+    s64 = 1.0 / math.sqrt(float(g))  # the library's correctly rounded sqrt and division
+    m = oracle.CqMatrix(1, g, g, g, 4, g // 2, np.zeros((1, g // 2), np.uint8),
+                        np.zeros((1, 1), np.uint16), synth.codebook(4))
+    differs = 0
+    for bits in (0x3F800001, 0x3F800006, 0x3F800008, 0x40490FDB, 0x3DCCCCCD, 0x4479C000):
+        v = np.array([bits], np.uint32).view(np.float32)[0]
+        exact = Fraction(float(v)) * Fraction(s64)
+        want = np.float32(float(_round_significand(_round_significand(exact, 53), 24)))
+        x = np.zeros(g, np.float32)
+        x[0] = v
+        p = oracle.cq_prepare(m, x)
+        assert np.array_equal(p.view(np.uint32), np.full(g, want).view(np.uint32)), hex(bits)
+        differs += np.float32(v) * np.float32(s64) != want
+    assert differs >= 3
 
 
 def pin_prepare_vs_scipy():

@@ -17,7 +17,10 @@ SRC = os.path.join(os.path.dirname(oracle.LIB_PATH), "oracle.c")
 MUTANTS = {
     "butterfly_sign": ("x[base + j + stride] = a - b;", "x[base + j + stride] = b - a;"),
     "fwht_dropped_stage": ("stride < n; stride <<= 1", "stride < n / 2; stride <<= 1"),
+    "fwht_strides_descending": ("for (int64_t stride = 1; stride < n; stride <<= 1) {",
+                                "for (int64_t stride = n >> 1; stride >= 1; stride >>= 1) {"),
     "scale_not_sqrt": ("1.0 / sqrt((double)group)", "1.0 / (double)group"),
+    "scale_in_fp32": ("    return (float)((double)v * scale);", "    return v * (float)scale;"),
     "index_msb_first": ("idx |= bit << j;", "idx |= bit << (m->bits - 1 - j);"),
     "index_wrong_stride": ("int64_t t = m->bits * col + j;", "int64_t t = 4 * col + j;"),
     "matvec_dropped_norm": ("acc += norm * part;", "acc += part;"),
