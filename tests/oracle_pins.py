@@ -321,6 +321,24 @@ def pin_tiny_exact_rationals():
     _ = s
 
 
+def pin_dequantize_row_norm_before_transform():
+    """[P1] Row gather: each codebook value times the group norm (an fp32
+    product), then the transform, then the scale (reading S8); only rounding
+    shows the order.  Worked by hand for g = 4, codebook entries 1, 2^-24, -1
+    at indices 1, 2, 3, indices [1, 2, 3, 2] and norm 3: the products are
+    [3, 3*2^-24, -3, 3*2^-24]; stride 1 gives 3 +- 0.75 ulp(3), which round to
+    3 +- 2^-22, so [3 + 2^-22, 3 - 2^-22, -3 + 2^-22, -3 - 2^-22]; stride 2 is
+    exact, [2^-21, -2^-21, 6, 6]; times 1/2: [2^-22, -2^-22, 3, 3].  The norm
+    applied after the transform would give [3*2^-25, -3*2^-25, 3, 3]."""
+    cb = np.zeros(16, np.float32)
+    cb[1], cb[2], cb[3] = 1.0, 2.0 ** -24, -1.0
+    packed = np.array([[0x21, 0x23]], np.uint8)  # low nibble first: indices 1, 2, 3, 2
+    norms = np.array([[0x4200]], np.uint16)      # fp16 3.0
+    m = oracle.CqMatrix(1, 4, 4, 4, 4, 2, packed, norms, cb)
+    want = np.array([2.0 ** -22, -2.0 ** -22, 3, 3], np.float32)
+    assert np.array_equal(oracle.cq_dequantize_row(m, 0).view(np.uint32), want.view(np.uint32))
+
+
 def pin_dequantize_row_vs_scipy():
     for case in small_cases():
         s = case.shape

@@ -37,6 +37,13 @@ MUTANTS = {
                          "for (int64_t k = 0; k < m->group; k++) tg[k] = tg[k];"),
     "dequant_norm_of_group_0": ("float norm = oracle_f16(m->norms[row * n_groups + g]);",
                                 "float norm = oracle_f16(m->norms[row * n_groups]);"),
+    "dequant_norm_after_transform": (
+        "            tg[k] = m->codebook[oracle_cq_index(m, row, g * m->group + k)] * norm;\n"
+        "        oracle_fwht(tg, m->group);\n"
+        "        for (int64_t k = 0; k < m->group; k++) tg[k] = scale_store(tg[k], m->group);",
+        "            tg[k] = m->codebook[oracle_cq_index(m, row, g * m->group + k)];\n"
+        "        oracle_fwht(tg, m->group);\n"
+        "        for (int64_t k = 0; k < m->group; k++) tg[k] = scale_store(tg[k] * norm, m->group);"),
     "gather_mag_unscaled": ("gmag[i * m->input + k] = s * inv;", "gmag[i * m->input + k] = s;"),
     "matvec_mag_no_norm": ("amag += fabs(norm) * apart;", "amag += apart;"),
     "matvec_mag_signed": ("apart += fabs(term);", "apart += term;"),
