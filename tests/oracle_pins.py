@@ -701,6 +701,24 @@ def pin_hadamard_mlp_closed_forms():
         assert np.array_equal(out, resid)
 
 
+def pin_hadamard_mlp_magnitude_tight():
+    """The MLP's tolerance magnitude |resid| + |u| + |d3| / sqrt(H) * sum|silu|
+    is the exact triangle bound of the output: where every silu value is
+    positive (d2 = 2^12 sign(z1), silu(t) = t) and the output row is the
+    all-ones row of the transform (row 0), the bound is met exactly, so
+    magnitude[0] = |resid[0]| + (out[0] - resid[0]) with every stage exact."""
+    rng = np.random.default_rng(37)
+    for hidden, H in ((10, 16), (48, 64)):
+        n, d1, resid, z1 = _hmlp_exact_case(rng, hidden, H)
+        nz = np.abs(z1) > 0
+        d2 = (np.where(z1 >= 0, 1.0, -1.0) * 4096.0 * nz).astype(np.float32)
+        d3 = np.full(H, 2.0 ** -12, np.float32)
+        out, mag = oracle.hadamard_mlp(n, H, d1, d2, d3, resid)
+        lift = float(out[0]) - float(resid[0])
+        assert lift > 0
+        assert mag[0] == abs(float(resid[0])) + lift, (hidden, H)
+
+
 def pin_hadamard_mlp_matrix_form():
     """Random inputs against the float64 matrix form with scipy's Hadamard
     matrix and numpy's exp, within fp32 rounding of the stages."""

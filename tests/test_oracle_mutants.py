@@ -80,6 +80,7 @@ MUTANTS = {
     "hmlp_pad_ones": ("z[i] = i < hidden ? n[i] : 0.0f;", "z[i] = i < hidden ? n[i] : 1.0f;"),
     "hmlp_no_d3": ("z[i] = (float)((double)z[i] * (double)d3[i]);", ""),
     "hmlp_unnormalized": ("double scale = 1.0 / sqrt((double)H);", "double scale = 1.0;"),
+    "hmlp_mag_l1_unscaled": ("fabs((double)d3[i]) / sqrt((double)H) * l1;", "fabs((double)d3[i]) * l1;"),
     "hmlp_u_added": ("out[i] = u ? (float)((double)block - (double)u[i]) : block;",
                      "out[i] = u ? (float)((double)block + (double)u[i]) : block;"),
 }
