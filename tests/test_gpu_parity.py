@@ -338,6 +338,50 @@ def test_prepare_matvec_workload_and_batches(cache):
     assert bits_eq(p.cpu().numpy(), oracle.cq_prepare(h, case.x)) and y.numel() == 0
 
 
+# cq_prepare_matvec on batches (the prepare, then the matrix-core matvec):
+# the workload's eight vectors, a remainder launch, unpadded widths, row
+# ranges, a single workgroup over four spans, workgroups of several row
+# groups, a single span, and an input that is not a whole number of float4s.
+BATCH_PM_CASES = [
+    (synth.CqShape(300, 2048, 2048, 256, 4), 9, 0, None),
+    (synth.CqShape(1000, 3840, 3840, 256, 4), 8, 0, None),
+    (synth.CqShape(77, 4000, 4096, 256, 4), 3, 5, 70),
+    (synth.CqShape(20, 1000, 1024, 256, 4), 16, 0, None),
+    (synth.CqShape(40000, 512, 512, 256, 4), 8, 3, 39990),
+    (synth.CqShape(33, 252, 256, 256, 4), 5, 0, None),
+    (synth.CqShape(64, 256, 256, 256, 4), 2, 63, 1),
+    (synth.CqShape(21, 1001, 1024, 256, 4), 3, 0, None),
+]
+
+
+def check_prepare_matvec_batch(case, rb=0, rc=None):
+    s = case.shape
+    rc = s.output - rb if rc is None else rc
+    m, h = dev_matrix(case), host_matrix(case)
+    x = to_dev(case.x)
+    p, y = bqd.cq_prepare_matvec(m, x, row_begin=rb, row_count=rc)
+    p_ref = oracle.cq_prepare(h, case.x)
+    assert bits_eq(p.cpu().numpy(), p_ref), (s, "prepared vectors differ from the oracle's")
+    ref, mag = oracle.cq_matvec(h, p_ref, rb, rc)
+    assert_tol(y.cpu().numpy(), ref, mag, f"cq_prepare_matvec {s} batch {len(case.x)}")
+    # the same bits as the two calls it stands for
+    y2 = bqd.cq_matvec(m, bqd.cq_prepare(m, x), row_begin=rb, row_count=rc)
+    assert bits_eq(y.cpu().numpy(), y2.cpu().numpy())
+
+
+@pytest.mark.parametrize("k", range(len(BATCH_PM_CASES)))
+def test_prepare_matvec_batch(k):
+    shape, batch, rb, rc = BATCH_PM_CASES[k]
+    print(f"[case] batch prepare+matvec {shape} batch {batch} rows [{rb}, +{rc})", flush=True)
+    check_prepare_matvec_batch(synth.make_cq(shape, seed=950 + k, batch=batch), rb, rc)
+
+
+def test_prepare_matvec_batch_workload(cache):
+    case = workload(cache, "cq4_16384x4096_b8")
+    print(f"[case] batch prepare+matvec {case.shape} batch {len(case.x)}", flush=True)
+    check_prepare_matvec_batch(case)
+
+
 # Several matrices on one activation ([P1] §6): shared launches on the ring
 # shapes (more than eight matrices take two), row ranges, empty ranges,
 # different codebooks, and shapes that fall back to one launch each.
