@@ -120,14 +120,20 @@ class HmlpCase:
     u: np.ndarray           # float32 [batch][hidden]
 
 
-def _random_bytes(rng: np.random.Generator, shape) -> np.ndarray:
-    return rng.integers(0, 256, size=shape, dtype=np.uint8)
+def _random_bytes(rng: np.random.Generator, shape, wide: bool = False) -> np.ndarray:
+    """Uniform bytes; wide: drawn as full-range 64-bit words (a different
+    stream, ~3x faster for multi-GiB buffers)."""
+    if not wide:
+        return rng.integers(0, 256, size=shape, dtype=np.uint8)
+    n = int(np.prod(shape))
+    words = rng.integers(0, 2**64, size=(n + 7) // 8, dtype=np.uint64)
+    return words.view(np.uint8)[:n].reshape(shape)
 
 
 def make_cq(shape: CqShape, seed: int, batch: int = 1, n_ids: int = 0,
-            norm_range=(0.5, 2.0)) -> CqCase:
+            norm_range=(0.5, 2.0), wide_bytes: bool = False) -> CqCase:
     rng = np.random.default_rng(seed)
-    packed = _random_bytes(rng, (shape.output, shape.stride))
+    packed = _random_bytes(rng, (shape.output, shape.stride), wide_bytes)
     norms = rng.uniform(norm_range[0], norm_range[1],
                         (shape.output, shape.n_groups)).astype(np.float16).view(np.uint16)
     x = rng.standard_normal((batch, shape.input), dtype=np.float32)
@@ -137,19 +143,20 @@ def make_cq(shape: CqShape, seed: int, batch: int = 1, n_ids: int = 0,
 
 
 def make_f8(R: int, C: int, SR: int, SC: int, seed: int, batch: int = 1,
-            exp_range=(120, 130)) -> F8Case:
+            exp_range=(120, 130), wide_bytes: bool = False) -> F8Case:
     rng = np.random.default_rng(seed)
-    w = _random_bytes(rng, (R, C))
+    w = _random_bytes(rng, (R, C), wide_bytes)
     scale = rng.integers(exp_range[0], exp_range[1] + 1, size=(SR, SC), dtype=np.int64).astype(np.uint8)
     x = rng.standard_normal((batch, C), dtype=np.float32)
     return F8Case(R, C, SR, SC, w, scale, x)
 
 
-def make_i8(R: int, C: int, G: int, seed: int, batch: int = 1, exp_range=(120, 130)) -> I8Case:
+def make_i8(R: int, C: int, G: int, seed: int, batch: int = 1, exp_range=(120, 130),
+            wide_bytes: bool = False) -> I8Case:
     """Weight bytes uniform over all 256 int8 values, E8M0 exponents uniform in
     exp_range, activations N(0, 1); draw order: weights, scales, activations."""
     rng = np.random.default_rng(seed)
-    w = _random_bytes(rng, (R, C)).view(np.int8)
+    w = _random_bytes(rng, (R, C), wide_bytes).view(np.int8)
     ns = (C + G - 1) // G
     scale = rng.integers(exp_range[0], exp_range[1] + 1, size=(R, ns), dtype=np.int64).astype(np.uint8)
     x = rng.standard_normal((batch, C), dtype=np.float32)

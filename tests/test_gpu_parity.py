@@ -750,6 +750,83 @@ def test_hadamard_mlp_exact_closed_form():
     assert bits_eq(got, ref)
 
 
+# Buffers past 2 GiB: every byte offset the kernels form is 64-bit.  Weights
+# of more than 2^31 bytes (F8, I8, and CQ4 at batch 1 and 8 plus its row
+# gather), a row range that starts past the mark, and a gather whose output
+# passes 2 GiB; checked on the first rows, the rows around the 2^31-byte mark
+# and the last rows.
+BIG = 1 << 31
+
+
+def ranges_past_2gib(n_rows, row_bytes):
+    mark = BIG // row_bytes
+    return [(0, 64), (mark - 64, 128), (n_rows - 64, 64)]
+
+
+def test_f8_weights_past_2gib():
+    R, C, SR, SC = 540000, 4096, 1000, 32
+    print(f"[case] f8 {R}x{C}, {R * C} weight bytes", flush=True)
+    case = synth.make_f8(R, C, SR, SC, seed=61, wide_bytes=True)
+    assert case.w.nbytes > BIG
+    check_f8(case, ranges_past_2gib(R, C))
+
+
+def test_i8_weights_past_2gib():
+    R, C, G = 540000, 4096, 16
+    print(f"[case] i8 {R}x{C} G{G}, {R * C} weight bytes", flush=True)
+    case = synth.make_i8(R, C, G, seed=62, wide_bytes=True)
+    assert case.w.nbytes > BIG
+    got = bqd.i8_matvec(to_dev(case.w), to_dev(case.scale), to_dev(case.x), G).cpu().numpy()[0]
+    for a, c in ranges_past_2gib(R, C):
+        ref, mag = oracle.i8_matvec(case.w, R, C, case.scale, G, case.x[0], a, c)
+        assert_tol(got[a:a + c], ref, mag, f"i8 {R}x{C} rows [{a}, +{c})")
+
+
+def test_cq_rows_past_2gib():
+    shape = synth.CqShape(1100000, 4096, 4096, 256, 4)
+    print(f"[case] cq4 {shape.output}x{shape.input}, {shape.output * shape.stride} packed bytes",
+          flush=True)
+    case = synth.make_cq(shape, seed=63, batch=8, wide_bytes=True)
+    assert case.packed.nbytes > BIG
+    m, h = dev_matrix(case), host_matrix(case)
+    x = to_dev(case.x)
+    p_ref = oracle.cq_prepare(h, case.x)
+    p1, y1 = bqd.cq_prepare_matvec(m, x[:1])
+    p8, y8 = bqd.cq_prepare_matvec(m, x)
+    assert bits_eq(p1.cpu().numpy(), p_ref[:1]) and bits_eq(p8.cpu().numpy(), p_ref)
+    y1, y8 = y1.cpu().numpy(), y8.cpu().numpy()
+    ranges = ranges_past_2gib(shape.output, shape.stride)
+    for a, c in ranges:
+        ref, mag = oracle.cq_matvec(h, p_ref, a, c)
+        assert_tol(y1[:, a:a + c], ref[:1], mag[:1], f"cq4 batch 1 rows [{a}, +{c})")
+        assert_tol(y8[:, a:a + c], ref, mag, f"cq4 batch 8 rows [{a}, +{c})")
+    # a row range that starts past the mark, at batch 1 and 8
+    a, c = ranges[1][0] + 100, 1000
+    ref, mag = oracle.cq_matvec(h, p_ref, a, c)
+    yr1 = bqd.cq_matvec(m, p1, row_begin=a, row_count=c).cpu().numpy()
+    yr8 = bqd.cq_matvec(m, p8, row_begin=a, row_count=c).cpu().numpy()
+    assert_tol(yr1, ref[:1], mag[:1], f"cq4 batch 1 row range [{a}, +{c})")
+    assert_tol(yr8, ref, mag, f"cq4 batch 8 row range [{a}, +{c})")
+    ids = np.concatenate([np.arange(a, a + c) for a, c in ranges]).astype(np.int32)
+    g = bqd.cq_gather_rows(m, to_dev(ids)).cpu().numpy()
+    assert bits_eq(g, oracle.cq_gather(h, ids)[0])
+
+
+def test_gather_output_past_2gib():
+    case = synth.make_cq(synth.C3, seed=64)
+    s = case.shape
+    n = BIG // (4 * s.input) + 4096
+    print(f"[case] gather of {n} rows of {s.output}x{s.input}, {4 * n * s.input} output bytes",
+          flush=True)
+    ids = np.random.default_rng(64).integers(0, s.output, n).astype(np.int32)
+    m, h = dev_matrix(case), host_matrix(case)
+    g = bqd.cq_gather_rows(m, to_dev(ids))
+    assert g.numel() * 4 > BIG
+    sel = np.concatenate([np.arange(a, a + c) for a, c in ranges_past_2gib(n, 4 * s.input)])
+    got = g[torch.from_numpy(sel).to(DEV)].cpu().numpy()
+    assert bits_eq(got, oracle.cq_gather(h, ids[sel])[0])
+
+
 def test_empty_problems_are_no_ops():
     case = small_case(0)
     m = dev_matrix(case)
