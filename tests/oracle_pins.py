@@ -544,6 +544,38 @@ def pin_sample_degenerate_cases():
         assert s2 == oracle.xorshift32(s)
         assert tok == oracle.sample_u(vals, ids, 1.0, s2 / 2**32)
 
+def pin_sample_special_candidates():
+    """O13 on special candidates: NaNs (which O12 sorts last) carry no weight,
+    so over the u grid they are never drawn and the others keep their softmax
+    shares; an infinite top candidate takes every draw; and large logits draw
+    exactly as the same logits shifted down by 998 (both exact in fp32, so
+    the differences to the top candidate, and every weight, are the same)."""
+    from scipy.special import softmax
+    vals = np.array([1.5, 0.25, -1.0, np.nan, np.nan], np.float32)
+    ids = np.array([7, 3, 9, 1, 2], np.int32)
+    p = softmax(vals[:3].astype(np.float64) / 0.8)
+    M = 20000
+    counts = {int(i): 0 for i in ids}
+    for j in range(M):
+        counts[oracle.sample_u(vals, ids, 0.8, (j + 0.5) / M)] += 1
+    assert counts[1] == 0 and counts[2] == 0, counts
+    for i, pi in zip(ids[:3], p):
+        assert abs(counts[int(i)] - M * pi) <= 1.0 + 1e-9, (i, counts[int(i)], M * pi)
+    top_inf = np.array([np.inf, 2.0, 1.0], np.float32)
+    for u in (0.0, 0.3, 0.999):
+        assert oracle.sample_u(top_inf, ids[:3], 1.0, u) == 7
+    big = np.array([1000.0, 999.5, 999.0, 998.0], np.float32)
+    small = big - np.float32(998.0)
+    ids4 = np.array([5, 6, 7, 8], np.int32)
+    drawn = set()
+    for j in range(200):
+        u = (j + 0.5) / 200
+        t = oracle.sample_u(big, ids4, 0.7, u)
+        assert t == oracle.sample_u(small, ids4, 0.7, u), u
+        drawn.add(t)
+    assert drawn == set(ids4.tolist())
+
+
 # ------------------------------------------------ I8 matvec (O14) --------
 def _i8_case(rng, R, C, G):
     w = rng.integers(-128, 128, (R, C)).astype(np.int8)

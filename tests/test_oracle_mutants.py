@@ -66,6 +66,22 @@ MUTANTS = {
     "topk_nan_first": ("if (na != nb) return na ? 1 : -1;", "if (na != nb) return na ? -1 : 1;"),
     "sample_no_temperature": ("exp(((double)vals[i] - (double)vals[0]) / temperature);\n        if",
                               "exp(((double)vals[i] - (double)vals[0]));\n        if"),
+    "topk_plus_zero_above_minus_zero": (
+        "if (!na && va != vb) return va > vb ? -1 : 1;",
+        "if (!na && (va != vb || signbit(va) != signbit(vb)))\n"
+        "        return (va > vb || (va == vb && !signbit(va))) ? -1 : 1;"),
+    "sample_nan_weighted": ("S += isnan(vals[i]) ? 0.0 : exp(", "S += isnan(vals[i]) ? 1.0 : exp("),
+    "sample_greedy_only_on_nan": ("if (temperature <= 0.0 || k == 1 || !isfinite(vals[0])) return ids[0];",
+                                  "if (temperature <= 0.0 || k == 1 || isnan(vals[0])) return ids[0];"),
+    "sample_top_not_subtracted": (
+        "        S += isnan(vals[i]) ? 0.0 : exp(((double)vals[i] - (double)vals[0]) / temperature);\n"
+        "    double target = u * S, run = 0.0;\n"
+        "    for (int64_t i = 0; i < k; i++) {\n"
+        "        run += isnan(vals[i]) ? 0.0 : exp(((double)vals[i] - (double)vals[0]) / temperature);",
+        "        S += isnan(vals[i]) ? 0.0 : exp((double)vals[i] / temperature);\n"
+        "    double target = u * S, run = 0.0;\n"
+        "    for (int64_t i = 0; i < k; i++) {\n"
+        "        run += isnan(vals[i]) ? 0.0 : exp((double)vals[i] / temperature);"),
     "sample_cdf_off_by_one": ("if (target < run) return ids[i];", "if (target <= run) return ids[i > 0 ? i - 1 : 0];"),
     "i8_group_fixed_16": ("(double)oracle_e8m0(s[r * ns + c / G])", "(double)oracle_e8m0(s[r * ns + c / 16])"),
     "i8_scale_dropped": ("double term = (double)w[r * C + c] * (double)oracle_e8m0(s[r * ns + c / G]) *",
