@@ -383,8 +383,9 @@ def test_prepare_matvec_batch_workload(cache):
 
 
 # Several matrices on one activation ([P1] §6): shared launches on the ring
-# shapes (more than eight matrices take two), row ranges, empty ranges,
-# different codebooks, and shapes that fall back to one launch each.
+# shapes (up to four matrices a launch: ten take three, 64 take sixteen),
+# row ranges, empty ranges, different codebooks, and shapes that fall back
+# to one launch each.
 MULTI_CASES = [
     ([synth.CqShape(2048, 512, 512, 128, 4), synth.CqShape(300, 512, 512, 128, 4),
       synth.CqShape(65, 512, 512, 128, 4)], [(0, 2048), (10, 200), (64, 1)]),
@@ -392,6 +393,8 @@ MULTI_CASES = [
     ([synth.CqShape(200, 256, 256, 64, 2), synth.CqShape(100, 256, 256, 64, 4),
       synth.CqShape(50, 256, 256, 64, 3)], [(0, 200), (5, 90), (0, 0)]),
     ([synth.CqShape(40, 8192, 8192, 1024, 4), synth.CqShape(33, 8192, 8192, 1024, 4)], None),
+    # the most matrices one call takes (64): sixteen shared launches of four
+    ([synth.CqShape(20 + 3 * k, 512, 512, 128, 4) for k in range(64)], None),
 ]
 
 
