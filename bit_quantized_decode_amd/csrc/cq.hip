@@ -50,25 +50,27 @@ __device__ __forceinline__ float scale_store(float v, double scale) {
 inline int lane_elems(int64_t group) { return group >= 64 ? (int)(group / 64) : 1; }
 
 // ------------------------------------------------------------------ prepare
-// One wavefront per (vector, span of 64*E padded columns).
+// One wavefront per (vector, span of 64*E padded columns); the grid is capped
+// (kMaxStrideGrid) and the wavefronts loop over the work.
 template <int E>
 __global__ __launch_bounds__(kThreads) void cq_prepare_kernel(
     const float* __restrict__ x, float* __restrict__ p, int64_t input, int64_t input_padded,
     int log2_group, int64_t spans, int64_t n_waves, double scale) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t wv = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-  if (wv >= n_waves) return;  // whole wavefront
-  const int64_t b = wv / spans;
-  const int64_t c0 = (wv % spans) * (64 * E) + lane * E;
-  const float* xb = x + b * input;
-  float v[E];
+  for (int64_t wv = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; wv < n_waves;
+       wv += (int64_t)gridDim.x * kWavesPerBlock) {  // wavefront-uniform
+    const int64_t b = wv / spans;
+    const int64_t c0 = (wv % spans) * (64 * E) + lane * E;
+    const float* xb = x + b * input;
+    float v[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) v[e] = c0 + e < input ? xb[c0 + e] : 0.0f;
-  wave_fwht<E>(v, lane, log2_group);
-  float* pb = p + b * input_padded;
+    for (int e = 0; e < E; ++e) v[e] = c0 + e < input ? xb[c0 + e] : 0.0f;
+    wave_fwht<E>(v, lane, log2_group);
+    float* pb = p + b * input_padded;
 #pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (c0 + e < input_padded) pb[c0 + e] = scale_store(v[e], scale);
+    for (int e = 0; e < E; ++e)
+      if (c0 + e < input_padded) pb[c0 + e] = scale_store(v[e], scale);
+  }
 }
 
 template <int E>
@@ -76,7 +78,8 @@ int launch_prepare_e(const bqd_cq_matrix* m, const float* x, float* prepared, in
                      hipStream_t s) {
   const int64_t spans = (m->input_padded + 64 * E - 1) / (64 * E);
   const int64_t n_waves = spans * batch;
-  const int64_t grid = (n_waves + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t grid = std::min<int64_t>((n_waves + kWavesPerBlock - 1) / kWavesPerBlock,
+                                         kMaxStrideGrid);
   hipLaunchKernelGGL((cq_prepare_kernel<E>), dim3((unsigned)grid), dim3(kThreads), 0, s, x,
                      prepared, m->input, m->input_padded, ilog2(m->group), spans, n_waves,
                      1.0 / std::sqrt((double)m->group));
@@ -98,7 +101,8 @@ int launch_cq_prepare(const bqd_cq_matrix* m, const float* x, float* prepared, i
 // ------------------------------------------------------------------- gather
 // One wavefront per (id, span of 64*E columns): codebook value times norm
 // (an fp32 product), transform, scale, store the columns below `input`.
-// Generic form: any bit width and group, one index decode per element.
+// Generic form: any bit width and group, one index decode per element; the
+// grid is capped (kMaxStrideGrid) and the wavefronts loop over the work.
 template <int E>
 __global__ __launch_bounds__(kThreads) void cq_gather_generic(
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ norms,
@@ -109,31 +113,32 @@ __global__ __launch_bounds__(kThreads) void cq_gather_generic(
   if (threadIdx.x < (1 << bits)) cb[threadIdx.x] = codebook[threadIdx.x];
   __syncthreads();
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t wv = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-  if (wv >= n_waves) return;  // whole wavefront
-  const int64_t i = wv / spans;
-  const int64_t c0 = (wv % spans) * (64 * E) + lane * E;
-  const int64_t r = rows[i];
-  float* o = out + i * input;
-  if (r < 0 || r >= output) {  // an id outside the table: a NaN row
+  for (int64_t wv = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; wv < n_waves;
+       wv += (int64_t)gridDim.x * kWavesPerBlock) {  // wavefront-uniform
+    const int64_t i = wv / spans;
+    const int64_t c0 = (wv % spans) * (64 * E) + lane * E;
+    const int64_t r = rows[i];
+    float* o = out + i * input;
+    if (r < 0 || r >= output) {  // an id outside the table: a NaN row
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (c0 + e < input) o[c0 + e] = __uint_as_float(0x7fc00000u);
+      continue;
+    }
+    const uint8_t* prow = packed + r * row_bytes;
+    const uint16_t* nrow = norms + r * (input_padded >> log2_group);
+    float v[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int64_t c = c0 + e;
+      v[e] = c < input_padded ? cb[byte_index(prow, bits, c)] * f16_to_f32(nrow[c >> log2_group])
+                              : 0.0f;
+    }
+    wave_fwht<E>(v, lane, log2_group);
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if (c0 + e < input) o[c0 + e] = __uint_as_float(0x7fc00000u);
-    return;
+      if (c0 + e < input) o[c0 + e] = scale_store(v[e], scale);
   }
-  const uint8_t* prow = packed + r * row_bytes;
-  const uint16_t* nrow = norms + r * (input_padded >> log2_group);
-  float v[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int64_t c = c0 + e;
-    v[e] = c < input_padded ? cb[byte_index(prow, bits, c)] * f16_to_f32(nrow[c >> log2_group])
-                            : 0.0f;
-  }
-  wave_fwht<E>(v, lane, log2_group);
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (c0 + e < input) o[c0 + e] = scale_store(v[e], scale);
 }
 
 // Groups of 8 and more: lane l owns E = 8 or 16 consecutive columns, which lie
@@ -267,7 +272,8 @@ int launch_gather_generic(const bqd_cq_matrix* m, const int32_t* rows, int64_t n
   // spans past the last visible column store nothing and are not launched
   const int64_t spans = (m->input + 64 * E - 1) / (64 * E);
   const int64_t n_waves = spans * n;
-  const int64_t grid = (n_waves + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t grid = std::min<int64_t>((n_waves + kWavesPerBlock - 1) / kWavesPerBlock,
+                                         kMaxStrideGrid);
   hipLaunchKernelGGL((cq_gather_generic<E>), dim3((unsigned)grid), dim3(kThreads), 0, s,
                      m->packed, m->norms, m->codebook, rows, out, m->output, m->input,
                      m->input_padded, m->row_bytes, (int)m->bits, ilog2(m->group), spans,
@@ -1492,13 +1498,35 @@ RingShape ring_shape(const bqd_cq_matrix* m) {
   return r;
 }
 
+// Workgroups of one ring launch: times 1024 threads, below the 2^32
+// work-items one dispatch holds (reached only by 512- and 1024-column rows
+// past 137 and 275 GB of weights).
+constexpr int64_t kRingMaxBlocks = ((int64_t)1 << 32) / kRingThreads - 1;
+
 // The ring kernel over up to kRingMaxMats row ranges of matrices that share
-// the ring shape r, input width and group (ms[0] gives those).
+// the ring shape r, input width and group (ms[0] gives those).  Ranges that
+// would need more than kRingMaxBlocks workgroups run one matrix at a time in
+// row chunks (prepared_out is stored by the first launch).
 template <int BPL, int S, int E>
 int launch_ring_t(const bqd_cq_matrix* const* ms, const int64_t* row_begin,
                   const int64_t* row_count, float* const* ys, int n, const float* act,
                   float* prepared_out, hipStream_t s) {
   constexpr int RPB = (16 / S) * kRingRows;
+  int64_t total = 0;
+  for (int k = 0; k < n; ++k) total += (row_count[k] + RPB - 1) / RPB;
+  if (total > kRingMaxBlocks) {
+    constexpr int64_t chunk = kRingMaxBlocks * RPB;
+    for (int k = 0; k < n; ++k) {
+      for (int64_t r0 = 0; r0 < row_count[k]; r0 += chunk) {
+        const int64_t rb = row_begin[k] + r0, rc = std::min(chunk, row_count[k] - r0);
+        float* yk = ys[k] + r0;
+        const int rc2 = launch_ring_t<BPL, S, E>(&ms[k], &rb, &rc, &yk, 1, act, prepared_out, s);
+        if (rc2) return rc2;
+        prepared_out = nullptr;
+      }
+    }
+    return BQD_OK;
+  }
   const bqd_cq_matrix* m0 = ms[0];
   RingArgs a{};
   int64_t blocks = 0;

@@ -218,48 +218,52 @@ int launch_kv_int8_dot(const int8_t* K, const float* scales, int64_t R, int64_t 
 __global__ __launch_bounds__(kI8Threads) void kv_quantize_int8_kernel(
     const float* __restrict__ v, int64_t n_vec, int64_t d, int8_t* __restrict__ q,
     float* __restrict__ scales) {
+  // one wavefront per vector, the grid capped and looping over the vectors
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t i = (int64_t)blockIdx.x * (kI8Threads / kWave) + threadIdx.x / kWave;
-  if (i >= n_vec) return;  // whole wavefront
-  const float* vi = v + i * d;
-  float m = 0.0f;
-  int nan = 0;
-  for (int64_t j = lane; j < d; j += kWave) {
-    const float a = fabsf(vi[j]);
-    nan |= a != a;
-    m = fmaxf(m, a);
-  }
-  // wavefront max: every lane ends with the maximum (DPP within rows, then
-  // the row maxima through the lane swaps)
-  m = fmaxf(m, dpp<kQuadXor1, 0xf, false>(0.0f, m));
-  m = fmaxf(m, dpp<kQuadXor2, 0xf, false>(0.0f, m));
-  m = fmaxf(m, dpp<kRowHalfMirror, 0xf, false>(0.0f, m));
-  m = fmaxf(m, dpp<kRowMirror, 0xf, false>(0.0f, m));
-  {
-    const uint32_t u = __float_as_uint(m);
-    const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    m = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
-    const uint32_t u2 = __float_as_uint(m);
-    const auto r32 = __builtin_amdgcn_permlane32_swap(u2, u2, false, false);
-    m = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
-  }
-  const bool any_nan = __any(nan);
-  double maximum = fmax(1e-12, (double)m);
-  if (any_nan) maximum = __longlong_as_double(0x7ff8000000000000ll);
-  const double scale = maximum / 127.0;
-  if (lane == 0) scales[i] = (float)scale;
-  int8_t* qi = q + i * d;
-  for (int64_t j = lane; j < d; j += kWave) {
-    const double t = rint((double)vi[j] / scale);
-    qi[j] = (t == t && t >= -128.0 && t <= 127.0) ? (int8_t)(int)t : (int8_t)0;
+  const int64_t stride = (int64_t)gridDim.x * (kI8Threads / kWave);
+  for (int64_t i = (int64_t)blockIdx.x * (kI8Threads / kWave) + threadIdx.x / kWave; i < n_vec;
+       i += stride) {  // wavefront-uniform
+    const float* vi = v + i * d;
+    float m = 0.0f;
+    int nan = 0;
+    for (int64_t j = lane; j < d; j += kWave) {
+      const float a = fabsf(vi[j]);
+      nan |= a != a;
+      m = fmaxf(m, a);
+    }
+    // wavefront max: every lane ends with the maximum (DPP within rows, then
+    // the row maxima through the lane swaps)
+    m = fmaxf(m, dpp<kQuadXor1, 0xf, false>(0.0f, m));
+    m = fmaxf(m, dpp<kQuadXor2, 0xf, false>(0.0f, m));
+    m = fmaxf(m, dpp<kRowHalfMirror, 0xf, false>(0.0f, m));
+    m = fmaxf(m, dpp<kRowMirror, 0xf, false>(0.0f, m));
+    {
+      const uint32_t u = __float_as_uint(m);
+      const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+      m = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+      const uint32_t u2 = __float_as_uint(m);
+      const auto r32 = __builtin_amdgcn_permlane32_swap(u2, u2, false, false);
+      m = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+    }
+    const bool any_nan = __any(nan);
+    double maximum = fmax(1e-12, (double)m);
+    if (any_nan) maximum = __longlong_as_double(0x7ff8000000000000ll);
+    const double scale = maximum / 127.0;
+    if (lane == 0) scales[i] = (float)scale;
+    int8_t* qi = q + i * d;
+    for (int64_t j = lane; j < d; j += kWave) {
+      const double t = rint((double)vi[j] / scale);
+      qi[j] = (t == t && t >= -128.0 && t <= 127.0) ? (int8_t)(int)t : (int8_t)0;
+    }
   }
 }
 
 int launch_kv_quantize_int8(const float* v, int64_t n_vec, int64_t d, int8_t* q, float* scales,
                             hipStream_t s) {
   const int64_t waves = kI8Threads / kWave;
-  hipLaunchKernelGGL(kv_quantize_int8_kernel, dim3((unsigned)((n_vec + waves - 1) / waves)),
-                     dim3(kI8Threads), 0, s, v, n_vec, d, q, scales);
+  const int64_t grid = std::min<int64_t>((n_vec + waves - 1) / waves, kMaxStrideGrid);
+  hipLaunchKernelGGL(kv_quantize_int8_kernel, dim3((unsigned)grid), dim3(kI8Threads), 0, s, v,
+                     n_vec, d, q, scales);
   return launch_status();
 }
 

@@ -48,6 +48,11 @@ inline int launch_status() {
   return hipGetLastError() == hipSuccess ? BQD_OK : BQD_EHIP;
 }
 
+// Grid cap of the kernels that loop over their work (grid-stride): 65536
+// workgroups of at most 1024 threads keep a launch below the 2^32 work-items
+// one dispatch can hold, whatever the problem size.
+constexpr int64_t kMaxStrideGrid = 65536;
+
 inline bool is_aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 inline int ilog2(int64_t v) {

@@ -5,6 +5,7 @@
 // Arithmetic as the page's: arrays are Float32Array (every store rounds to
 // fp32), products, silu and the 1/sqrt(H) scale are JavaScript numbers (fp64)
 // rounded once when stored.  silu(t) = t / (1 + exp(-t)).
+#include <algorithm>
 #include <cmath>
 
 #include "cq_device.h"
@@ -46,42 +47,45 @@ __device__ void block_fwht(float (&v)[E], int log2_h, float* lds) {
 
 }  // namespace
 
+// One workgroup per vector; the grid is capped (kMaxStrideGrid) and each
+// workgroup loops over the batch.
 template <int E>
 __global__ __launch_bounds__(1024) void hadamard_mlp_kernel(
     const float* __restrict__ n, int hidden, int log2_h, const float* __restrict__ d1,
     const float* __restrict__ d2, const float* __restrict__ d3, const float* __restrict__ resid,
-    const float* __restrict__ u, float* __restrict__ out, double scale, int pow2) {
+    const float* __restrict__ u, float* __restrict__ out, double scale, int pow2, int64_t batch) {
   extern __shared__ float lds[];
   const int H = 1 << log2_h;
   const int tid = threadIdx.x;
-  const int64_t b = blockIdx.x;
-  const float* nb = n + b * hidden;
-  float v[E];
+  for (int64_t b = blockIdx.x; b < batch; b += gridDim.x) {  // workgroup-uniform
+    const float* nb = n + b * hidden;
+    float v[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i = tid * E + e;
-    // pad, then z *= d1 (the fp32 product is the rounded fp64 product)
-    v[e] = (i < hidden ? nb[i] : 0.0f) * (i < H ? d1[i] : 0.0f);
-  }
-  block_fwht<E>(v, log2_h, lds);
+    for (int e = 0; e < E; ++e) {
+      const int i = tid * E + e;
+      // pad, then z *= d1 (the fp32 product is the rounded fp64 product)
+      v[e] = (i < hidden ? nb[i] : 0.0f) * (i < H ? d1[i] : 0.0f);
+    }
+    block_fwht<E>(v, log2_h, lds);
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i = tid * E + e;
-    const float z = scaled(v[e], scale, pow2);
-    const double t = (double)(i < H ? d2[i] : 0.0f) * (double)z;
-    v[e] = (float)(t / (1.0 + exp(-t)));
-  }
-  block_fwht<E>(v, log2_h, lds);
-  const float* rb = resid + b * hidden;
-  const float* ub = u ? u + b * hidden : nullptr;
-  float* ob = out + b * hidden;
+    for (int e = 0; e < E; ++e) {
+      const int i = tid * E + e;
+      const float z = scaled(v[e], scale, pow2);
+      const double t = (double)(i < H ? d2[i] : 0.0f) * (double)z;
+      v[e] = (float)(t / (1.0 + exp(-t)));
+    }
+    block_fwht<E>(v, log2_h, lds);
+    const float* rb = resid + b * hidden;
+    const float* ub = u ? u + b * hidden : nullptr;
+    float* ob = out + b * hidden;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i = tid * E + e;
-    if (i < hidden) {
-      const float z = scaled(v[e], scale, pow2) * d3[i];
-      const float block = rb[i] + z;
-      ob[i] = ub ? block - ub[i] : block;
+    for (int e = 0; e < E; ++e) {
+      const int i = tid * E + e;
+      if (i < hidden) {
+        const float z = scaled(v[e], scale, pow2) * d3[i];
+        const float block = rb[i] + z;
+        ob[i] = ub ? block - ub[i] : block;
+      }
     }
   }
 }
@@ -97,8 +101,9 @@ int launch_mlp_e(const float* n, int64_t hidden, int64_t H, const float* d1, con
   const size_t lds = H > 64 * E ? (size_t)H * sizeof(float) : 0;
   const double scale = 1.0 / std::sqrt((double)H);
   const int pow2 = (log2_h % 2) == 0;
-  hipLaunchKernelGGL((hadamard_mlp_kernel<E>), dim3((unsigned)batch), dim3((unsigned)threads), lds,
-                     s, n, (int)hidden, log2_h, d1, d2, d3, resid, u, out, scale, pow2);
+  const int64_t grid = std::min<int64_t>(batch, kMaxStrideGrid);
+  hipLaunchKernelGGL((hadamard_mlp_kernel<E>), dim3((unsigned)grid), dim3((unsigned)threads), lds,
+                     s, n, (int)hidden, log2_h, d1, d2, d3, resid, u, out, scale, pow2, batch);
   return launch_status();
 }
 

@@ -203,6 +203,39 @@ KV = dict(n=4096, d=128)
 HMLP = dict(hidden=512, H=2048)
 
 
+# Inputs of many GB drawn on the device by torch's seeded generator (the
+# caller passes the torch module); tests copy back the rows they check.
+def _device_generator(torch, seed: int, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def device_normal(torch, shape, seed: int, device, scale: float = 1.0):
+    """float32 N(0, scale^2)."""
+    g = _device_generator(torch, seed, device)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32) * scale
+
+
+def device_bytes(torch, n: int, seed: int, device):
+    """n uniform bytes."""
+    g = _device_generator(torch, seed, device)
+    return torch.randint(0, 256, (n,), generator=g, device=device, dtype=torch.uint8)
+
+
+def device_ids(torch, n: int, high: int, seed: int, device):
+    """n int32 ids uniform in [0, high)."""
+    g = _device_generator(torch, seed, device)
+    return torch.randint(0, high, (n,), generator=g, device=device, dtype=torch.int32)
+
+
+def device_norms(torch, shape, seed: int, device, lo: float = 0.5, hi: float = 2.0):
+    """fp16 norms uniform in [lo, hi), as their int16 bit patterns."""
+    g = _device_generator(torch, seed, device)
+    return torch.empty(shape, dtype=torch.float16, device=device).uniform_(lo, hi, generator=g) \
+        .view(torch.int16)
+
+
 def config_cases(i: int, batch8: bool = True):
     """Cases of workload ``i`` (1-based), as (name, zero-argument builder)."""
     if i == 1:

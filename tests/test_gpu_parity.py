@@ -830,6 +830,95 @@ def test_gather_output_past_2gib():
     assert bits_eq(got, oracle.cq_gather(h, ids[sel])[0])
 
 
+# Launches that would pass 2^32 work-items (one dispatch's limit): the kernels
+# that take one wavefront or workgroup per unit of work cap their grids and
+# loop (the KV quantize, the Hadamard MLP, the prepare and the gather of
+# groups under 8, each at 2^26 + 7 units), and the batch-1 ring kernel splits
+# a 512-column matrix of 2^29 + 1000 rows (137 GB packed) into launches of at
+# most 2^22 - 1 workgroups.  Inputs are drawn on the device; the first,
+# middle and last units are checked against the oracle.
+HUGE_UNITS = (1 << 26) + 7
+
+
+def _sampled_units(n):
+    sel = np.r_[np.arange(0, 8), np.arange(n // 2 - 4, n // 2 + 4), np.arange(n - 8, n)]
+    return sel, torch.from_numpy(sel).to(DEV)
+
+
+def test_kv_quantize_past_2_32_work_items():
+    print(f"[case] kv quantize of {HUGE_UNITS} vectors of 3", flush=True)
+    v = synth.device_normal(torch, (HUGE_UNITS, 3), seed=71, device=DEV, scale=3.0)
+    q, sc = bqd.kv_quantize_int8(v)
+    sel, idx = _sampled_units(HUGE_UNITS)
+    qr, scr = oracle.store_int8(v[idx].cpu().numpy())
+    assert np.array_equal(q[idx].cpu().numpy(), qr)
+    assert bits_eq(sc[idx].cpu().numpy(), scr)
+
+
+def test_hadamard_mlp_past_2_32_work_items():
+    hidden, H = 3, 4
+    print(f"[case] hadamard mlp {hidden}/{H} on {HUGE_UNITS} vectors", flush=True)
+    rng = np.random.default_rng(72)
+    d1, d2, d3 = (rng.standard_normal(H).astype(np.float32) for _ in range(3))
+    n = synth.device_normal(torch, (HUGE_UNITS, hidden), seed=73, device=DEV)
+    resid = synth.device_normal(torch, (HUGE_UNITS, hidden), seed=74, device=DEV)
+    out = bqd.hadamard_mlp(n, H, to_dev(d1), to_dev(d2), to_dev(d3), resid)
+    sel, idx = _sampled_units(HUGE_UNITS)
+    got, ns, rs = (t[idx].cpu().numpy() for t in (out, n, resid))
+    for b in range(len(sel)):
+        ref, mag = oracle.hadamard_mlp(ns[b], H, d1, d2, d3, rs[b])
+        ratio = np.abs(got[b].astype(np.float64) - ref) / (1e-5 * mag + 1e-6)
+        assert ratio.max() <= 1.0, (sel[b], ratio.max())
+
+
+def test_prepare_past_2_32_work_items():
+    case = synth.make_cq(synth.CqShape(4, 32, 32, 32, 4), seed=75)
+    print(f"[case] prepare of {HUGE_UNITS} vectors of 32", flush=True)
+    m, h = dev_matrix(case), host_matrix(case)
+    x = synth.device_normal(torch, (HUGE_UNITS, 32), seed=76, device=DEV)
+    p = bqd.cq_prepare(m, x)
+    sel, idx = _sampled_units(HUGE_UNITS)
+    assert bits_eq(p[idx].cpu().numpy(), oracle.cq_prepare(h, x[idx].cpu().numpy()))
+
+
+def test_gather_small_groups_past_2_32_work_items():
+    case = synth.make_cq(synth.CqShape(1000, 4, 4, 4, 2), seed=77)
+    print(f"[case] gather of {HUGE_UNITS} rows of 4 (groups of 4)", flush=True)
+    m, h = dev_matrix(case), host_matrix(case)
+    ids = synth.device_ids(torch, HUGE_UNITS, 1000, seed=78, device=DEV)
+    g = bqd.cq_gather_rows(m, ids)
+    sel, idx = _sampled_units(HUGE_UNITS)
+    assert bits_eq(g[idx].cpu().numpy(), oracle.cq_gather(h, ids[idx].cpu().numpy())[0])
+
+
+def test_ring_launch_past_2_32_work_items():
+    rows, C = (1 << 29) + 1000, 512
+    shape = synth.CqShape(rows, C, C, 128, 4)
+    need = rows * (shape.stride + 2 * shape.n_groups + 4)
+    if torch.cuda.get_device_properties(0).total_memory < need + (16 << 30):
+        pytest.skip(f"needs {need >> 30} GiB of device memory")
+    print(f"[case] ring matvec of CQ4 {rows}x{C}, {rows * shape.stride} packed bytes", flush=True)
+    packed = synth.device_bytes(torch, rows * shape.stride, seed=79, device=DEV).view(rows, -1)
+    norms = synth.device_norms(torch, (rows, shape.n_groups), seed=80, device=DEV)
+    cb = synth.codebook(4)
+    m = bqd.CqMatrix(packed, norms, to_dev(cb), output=rows, input=C, input_padded=C, group=128,
+                     bits=4, row_bytes=shape.stride)
+    x = np.random.default_rng(81).standard_normal((1, C)).astype(np.float32)
+    p, y = bqd.cq_prepare_matvec(m, to_dev(x))
+    y2 = bqd.cq_matvec(m, p)
+    chunk = ((1 << 32) // 1024 - 1) * 128  # rows of one launch
+    for a, c in ((0, 64), (chunk - 64, 128), (rows - 64, 64)):
+        hs = oracle.CqMatrix(c, C, C, 128, 4, shape.stride, packed[a:a + c].cpu().numpy(),
+                             norms[a:a + c].cpu().numpy(), cb)
+        p_ref = oracle.cq_prepare(hs, x)
+        assert bits_eq(p.cpu().numpy(), p_ref)
+        ref, mag = oracle.cq_matvec(hs, p_ref)
+        assert_tol(y[:, a:a + c].cpu().numpy(), ref, mag, f"ring rows [{a}, +{c})")
+        assert bits_eq(y2[:, a:a + c].cpu().numpy(), y[:, a:a + c].cpu().numpy())
+    del packed, norms, m, y, y2
+    torch.cuda.empty_cache()
+
+
 def test_empty_problems_are_no_ops():
     case = small_case(0)
     m = dev_matrix(case)
