@@ -148,6 +148,14 @@ class CqMatrix:
         self.output, self.input, self.input_padded = int(output), int(input), int(input_padded)
         self.group, self.bits = int(group), int(bits)
         self.row_bytes = int(row_bytes if row_bytes is not None else packed.shape[-1])
+        # the buffers must hold what the shape fields describe (the C ABI sees
+        # only their addresses); the shape rules themselves are checked there
+        if self.output > 0 and self.row_bytes > 0 and self.packed.numel() < self.output * self.row_bytes:
+            raise ValueError("packed holds fewer than output * row_bytes bytes")
+        if self.group > 0 and self.norms.numel() < self.output * (self.input_padded // self.group):
+            raise ValueError("norms holds fewer than output * (input_padded / group) entries")
+        if 0 <= self.bits <= 16 and self.codebook.numel() < (1 << self.bits):
+            raise ValueError("codebook holds fewer than 2**bits entries")
         self._s = _CqStruct(self.output, self.input, self.input_padded, self.group, self.bits,
                             self.row_bytes, self.packed.data_ptr(), self.norms.data_ptr(),
                             self.codebook.data_ptr())
@@ -243,6 +251,8 @@ def cq_matvec_multi(ms, prepared: torch.Tensor, ranges=None, outs=None, stream=N
     """Several CqMatrix objects (row ranges [(row_begin, row_count)]) on one
     prepared vector float32 [input_padded] -> list of float32 [row_count]."""
     prepared = _dev(prepared, torch.float32, "prepared")
+    if not ms or prepared.numel() != ms[0].input_padded:
+        raise ValueError("prepared must have the matrices' input_padded entries")
     n, descs, rb, rcs, ys, outs = _multi_args(ms, ranges, outs, prepared.device)
     _call("cq_matvec_multi", descs, n, rb, rcs, _ptr(prepared), ys, _stream(prepared, stream))
     return outs
@@ -253,8 +263,12 @@ def cq_prepare_matvec_multi(ms, x: torch.Tensor, prepared: torch.Tensor = None, 
     """cq_matvec_multi on the raw activation x float32 [input]; returns
     (prepared float32 [input_padded], list of outputs)."""
     x = _dev(x, torch.float32, "x")
+    if not ms or x.numel() != ms[0].input:
+        raise ValueError("x must have the matrices' input entries")
     prepared = torch.empty(ms[0].input_padded, dtype=torch.float32, device=x.device) \
         if prepared is None else _dev(prepared, torch.float32, "prepared")
+    if prepared.numel() != ms[0].input_padded:
+        raise ValueError("prepared must have the matrices' input_padded entries")
     n, descs, rb, rcs, ys, outs = _multi_args(ms, ranges, outs, x.device)
     _call("cq_prepare_matvec_multi", descs, n, rb, rcs, _ptr(x), _ptr(prepared), ys,
           _stream(x, stream))
@@ -386,6 +400,8 @@ def logits_sample(logits: torch.Tensor, k: int, temperature: float, state: torch
     Returns (token int32 [1], topk_ids int32 [k], topk_logits float32 [k])."""
     logits = _dev(logits, torch.float32, "logits")
     state = _dev(state, (torch.int32, torch.uint32), "state")
+    if state.numel() < 1:
+        raise ValueError("state needs one element")
     n = logits.numel()
     need = logits_sample_workspace_bytes(n, k)
     if workspace is None:
@@ -411,6 +427,8 @@ def logits_sample_noalloc(logits: torch.Tensor, k: int, temperature: float, stat
     token = _dev(token, torch.int32, "token")
     topk_ids = _dev(topk_ids, torch.int32, "topk_ids")
     topk_logits = _dev(topk_logits, torch.float32, "topk_logits")
+    if state.numel() < 1:
+        raise ValueError("state needs one element")
     if token.numel() < 1 or topk_ids.numel() < k or topk_logits.numel() < k:
         raise ValueError("token needs 1 element, topk_ids and topk_logits k each")
     _call("logits_sample_noalloc", _ptr(logits), logits.numel(), int(k), float(temperature),

@@ -919,6 +919,35 @@ def test_ring_launch_past_2_32_work_items():
     torch.cuda.empty_cache()
 
 
+def test_binding_rejects_buffers_smaller_than_their_shapes():
+    """The C ABI sees addresses only; the binding checks every buffer against
+    the shape fields before any launch."""
+    case = synth.make_cq(synth.CqShape(10, 512, 512, 128, 4), seed=3)
+    m = dev_matrix(case)
+    kw = dict(output=10, input=512, input_padded=512, group=128, bits=4, row_bytes=256)
+    with pytest.raises(ValueError):
+        bqd.CqMatrix(m.packed.reshape(-1)[:-1], m.norms, m.codebook, **kw)
+    with pytest.raises(ValueError):
+        bqd.CqMatrix(m.packed, m.norms.reshape(-1)[:-1], m.codebook, **kw)
+    with pytest.raises(ValueError):
+        bqd.CqMatrix(m.packed, m.norms, m.codebook[:15], **kw)
+    p = torch.zeros(511, device=DEV)
+    with pytest.raises(ValueError):
+        bqd.cq_matvec_multi([m, m], p)
+    with pytest.raises(ValueError):
+        bqd.cq_prepare_matvec_multi([m, m], torch.zeros(500, device=DEV))
+    with pytest.raises(ValueError):
+        bqd.cq_prepare_matvec_multi([m, m], torch.zeros(512, device=DEV), prepared=p)
+    logits = torch.zeros(100, device=DEV)
+    no_state = torch.zeros(0, dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError):
+        bqd.logits_sample(logits, 4, 1.0, no_state)
+    with pytest.raises(ValueError):
+        bqd.logits_sample_noalloc(logits, 4, 1.0, no_state, torch.zeros(1, dtype=torch.int32, device=DEV),
+                                  torch.zeros(4, dtype=torch.int32, device=DEV),
+                                  torch.zeros(4, device=DEV))
+
+
 def test_empty_problems_are_no_ops():
     case = small_case(0)
     m = dev_matrix(case)
