@@ -146,7 +146,7 @@ int logits_sample_noalloc(const float* logits, int64_t n, int64_t k, float tempe
                                 sample_scratch_bytes());
   if (rc) return rc;
   void* ws = nullptr;
-  rc = sample_scratch(&ws);
+  rc = sample_scratch(as_stream(stream), &ws);
   if (rc) return rc;
   return launch_logits_sample(logits, n, k, temperature, state, ws, token, topk_ids,
                               topk_logits, as_stream(stream));

@@ -40,9 +40,9 @@ int launch_logits_sample(const float* logits, int64_t n, int64_t k, float temper
                          float* topk_logits, hipStream_t s);
 
 // The allocation-free sampler's device scratch: its size, and its address on
-// the current device (looked up once per device).
+// the device of stream s (looked up once per device).
 int64_t sample_scratch_bytes();
-int sample_scratch(void** out);
+int sample_scratch(hipStream_t s, void** out);
 
 inline int launch_status() {
   return hipGetLastError() == hipSuccess ? BQD_OK : BQD_EHIP;

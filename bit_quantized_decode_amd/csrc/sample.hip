@@ -425,16 +425,26 @@ void* scratch_ptr[kMaxDevices] = {};
 
 int64_t sample_scratch_bytes() { return kScratchBytes; }
 
-// The device address of `scratch` on the current device, looked up once per
-// device with that device current (the host-side name of the array is not a
-// device address).
-int sample_scratch(void** out) {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BQD_EHIP;
+// The device address of `scratch` on the device that runs stream s (the
+// current device for the null stream), looked up once per device with that
+// device current (the host-side name of the array is not a device address;
+// each GPU holds its own copy).
+int sample_scratch(hipStream_t s, void** out) {
+  int cur = -1, dev = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return BQD_EHIP;
+  if (s == nullptr || s == hipStreamPerThread) {
+    dev = cur;
+  } else if (hipStreamGetDevice(s, &dev) != hipSuccess) {
+    return BQD_EHIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return BQD_EHIP;
   std::lock_guard<std::mutex> lock(scratch_mutex);
   if (!scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return BQD_EHIP;
     void* p = nullptr;
-    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BQD_EHIP;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return BQD_EHIP;
+    if (e != hipSuccess || !p) return BQD_EHIP;
     scratch_ptr[dev] = p;
   }
   *out = scratch_ptr[dev];

@@ -267,8 +267,9 @@ int logits_sample(const float *logits, int64_t n, int64_t k, float temperature,
  * the workspace taken from a static device array inside the library, 131,072
  * bytes (the need of the largest call: n = 2^20, k = 64) held by each GPU the
  * library runs on until the process ends.  The call allocates nothing.  Its
- * address is looked up on the first call on each device (with that device
- * current).  All calls on one GPU share that array: calls that overlap in
+ * address is looked up on the first call on each device: the device of
+ * `stream` (the current device for the null stream), made current for the
+ * lookup and then restored.  All calls on one GPU share that array: calls that overlap in
  * time on one GPU (different streams, no ordering between them) race and
  * may return wrong results; calls ordered on one stream are safe.  Arguments
  * and errors as logits_sample (a call needing more scratch than the array

@@ -66,6 +66,22 @@ def test_no_alloc_matches_workspace_entry_point(kind):
         assert np.array_equal(got[2].numpy().view(np.uint32), oval.view(np.uint32))
 
 
+def test_no_alloc_on_a_stream_of_its_own():
+    """The scratch is found on the device that runs the call's stream; on a
+    created stream the results still equal logits_sample's on that stream."""
+    rng = np.random.default_rng(2025)
+    logits = torch.from_numpy((3.0 * rng.standard_normal(100000)).astype(np.float32)).to(DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for fn in (_no_alloc, _with_workspace):
+        with torch.cuda.stream(side):
+            print(f"[case] {fn.__name__} on a created stream", flush=True)
+            outs.append(fn(logits, 32, 0.9, 99))
+    torch.cuda.synchronize()
+    _same(outs[0], outs[1])
+
+
 def test_no_alloc_rejects_bad_arguments():
     logits = torch.zeros(100, device=DEV)
     state = _state(1)
