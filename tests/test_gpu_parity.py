@@ -830,6 +830,81 @@ def test_gather_output_past_2gib():
     assert bits_eq(got, oracle.cq_gather(h, ids[sel])[0])
 
 
+# Seeded random shapes across the dispatch space: every bit width and group,
+# widths up to 16384 with ragged unpadded inputs, rows padded past their
+# minimum (odd and aligned), batches 1-9 and random row ranges, so the ring,
+# batch-1, 4-vector, matrix-core and generic kernels are all chosen by the
+# launch rules rather than by hand; each against the oracle, the fused call
+# bit-identical to the two it stands for, and a gather of random ids (one out
+# of range).  Then F8 and I8 shapes likewise (row widths of whole 16-byte
+# chunks and ragged ones, scale blocks that divide the row and ones that
+# do not).
+def _random_cq_shape(rng):
+    group = int(2 ** rng.integers(2, 11))
+    n_groups = int(rng.integers(1, max(2, min(16, 16384 // group) + 1)))
+    input_padded = group * n_groups
+    cut = int(rng.integers(0, min(group, 38))) if rng.random() < 0.5 else 0
+    input_ = max(1, input_padded - cut)
+    bits = int(rng.integers(2, 6))
+    pad = int(rng.choice([0, 0, 0, 1, 3, 4, 16]))
+    row_bytes = synth.min_row_bytes(input_padded, bits) + pad
+    output = int(rng.integers(1, 2500))
+    return synth.CqShape(output, input_, input_padded, group, bits, row_bytes)
+
+
+@pytest.mark.parametrize("k", range(120))
+def test_cq_random_shapes(k):
+    rng = np.random.default_rng(7000 + k)
+    shape = _random_cq_shape(rng)
+    batch = int(rng.choice([1, 1, 2, 3, 8, 9]))
+    rb = int(rng.integers(0, shape.output)) if rng.random() < 0.5 else 0
+    rc = int(rng.integers(0, shape.output - rb + 1)) if rng.random() < 0.5 else shape.output - rb
+    print(f"[case] random cq {shape} batch {batch} rows [{rb}, +{rc})", flush=True)
+    case = synth.make_cq(shape, seed=7100 + k, batch=batch, n_ids=16)
+    m, h = dev_matrix(case), host_matrix(case)
+    x = to_dev(case.x)
+    p, y = bqd.cq_prepare_matvec(m, x, row_begin=rb, row_count=rc)
+    p_ref = oracle.cq_prepare(h, case.x)
+    assert bits_eq(p.cpu().numpy(), p_ref)
+    if rc:
+        ref, mag = oracle.cq_matvec(h, p_ref, rb, rc)
+        assert_tol(y.cpu().numpy(), ref, mag, f"random cq {shape} batch {batch}")
+    y2 = bqd.cq_matvec(m, p, row_begin=rb, row_count=rc)
+    assert bits_eq(y.cpu().numpy(), y2.cpu().numpy())
+    ids = np.r_[case.ids, np.int32(shape.output)].astype(np.int32)
+    g = bqd.cq_gather_rows(m, to_dev(ids)).cpu().numpy()
+    g_ref, _ = oracle.cq_gather(h, ids[:-1])
+    assert bits_eq(g[:-1], g_ref) and np.isnan(g[-1]).all()
+
+
+@pytest.mark.parametrize("k", range(60))
+def test_f8_random_shapes(k):
+    rng = np.random.default_rng(7500 + k)
+    R = int(rng.integers(1, 3000))
+    C = int(16 * rng.integers(1, 513)) if rng.random() < 0.6 else int(rng.integers(1, 3000))
+    SR = int(rng.integers(1, min(R, 64) + 1))
+    SC = int(rng.choice([d for d in range(1, min(C, 64) + 1) if C % d == 0])) if rng.random() < 0.6 \
+        else int(rng.integers(1, min(C, 64) + 1))
+    batch = int(rng.choice([1, 1, 2]))
+    print(f"[case] random f8 {R}x{C} scales {SR}x{SC} batch {batch}", flush=True)
+    check_f8(synth.make_f8(R, C, SR, SC, seed=7600 + k, batch=batch))
+
+
+@pytest.mark.parametrize("k", range(40))
+def test_i8_random_shapes(k):
+    rng = np.random.default_rng(7800 + k)
+    R = int(rng.integers(1, 3000))
+    C = int(16 * rng.integers(1, 513)) if rng.random() < 0.6 else int(rng.integers(1, 3000))
+    G = int(16 * rng.integers(1, max(2, min(C // 16, 8) + 1))) if rng.random() < 0.6 and C >= 16 \
+        else int(rng.integers(1, min(C, 100) + 1))
+    batch = int(rng.choice([1, 1, 2]))
+    print(f"[case] random i8 {R}x{C} G{G} batch {batch}", flush=True)
+    case = synth.make_i8(R, C, G, seed=7900 + k, batch=batch)
+    got = bqd.i8_matvec(to_dev(case.w), to_dev(case.scale), to_dev(case.x), G).cpu().numpy()
+    ref, mag = oracle.i8_matvec(case.w, R, C, case.scale, G, case.x)
+    assert_tol(got, ref, mag, f"random i8 {R}x{C} G{G} batch {batch}")
+
+
 # Launches that would pass 2^32 work-items (one dispatch's limit): the kernels
 # that take one wavefront or workgroup per unit of work cap their grids and
 # loop (the KV quantize, the Hadamard MLP, the prepare and the gather of
