@@ -402,11 +402,40 @@ MULTI_CASES = [
 @pytest.mark.parametrize("fused", [False, True])
 def test_matvec_multi(k, fused):
     shapes, ranges = MULTI_CASES[k]
-    cases = [synth.make_cq(sh, seed=950 + 10 * k + j) for j, sh in enumerate(shapes)]
+    print(f"[case] multi {len(shapes)} matrices {shapes[0]} fused={fused}", flush=True)
+    check_multi(shapes, ranges, fused, 950 + 10 * k)
+
+
+@pytest.mark.parametrize("k", range(16))
+def test_matvec_multi_random(k):
+    """Random sets of 1-12 matrices on one activation (mostly on the ring
+    shapes, some other widths), random row ranges, both entry points."""
+    rng = np.random.default_rng(8700 + k)
+    if rng.random() < 0.7:
+        input_padded, bits_choice = int(rng.choice([512, 1024, 2048, 4096, 8192])), [4]
+    else:
+        input_padded, bits_choice = int(256 * rng.integers(1, 9)), [2, 3, 4, 5]
+    group = int(rng.choice([g for g in (8, 16, 32, 64, 128, 256, 512, 1024) if input_padded % g == 0]))
+    input_ = input_padded - (int(rng.integers(0, min(group, 20))) if rng.random() < 0.4 else 0)
+    shapes, ranges = [], []
+    for _ in range(int(rng.integers(1, 13))):
+        bits = int(rng.choice(bits_choice))
+        pad = int(rng.choice([0, 0, 16, 4]))
+        out = int(rng.integers(1, 1500))
+        shapes.append(synth.CqShape(out, input_, input_padded, group, bits,
+                                    synth.min_row_bytes(input_padded, bits) + pad))
+        rb = int(rng.integers(0, out)) if rng.random() < 0.4 else 0
+        ranges.append((rb, int(rng.integers(0, out - rb + 1)) if rng.random() < 0.4 else out - rb))
+    for fused in (False, True):
+        print(f"[case] random multi {len(shapes)} x {shapes[0]} fused={fused}", flush=True)
+        check_multi(shapes, ranges, fused, 8800 + 20 * k)
+
+
+def check_multi(shapes, ranges, fused, seed0):
+    cases = [synth.make_cq(sh, seed=seed0 + j) for j, sh in enumerate(shapes)]
     x = cases[0].x
     ms = [dev_matrix(c) for c in cases]
     ranges = ranges or [(0, sh.output) for sh in shapes]
-    print(f"[case] multi {len(shapes)} matrices {shapes[0]} fused={fused}", flush=True)
     p_ref = oracle.cq_prepare(host_matrix(cases[0]), x)
     if fused:
         p, outs = bqd.cq_prepare_matvec_multi(ms, to_dev(x[0]), ranges=ranges)
@@ -703,12 +732,30 @@ def test_kv_quantize_special_vectors():
 
 @pytest.mark.parametrize("R,d,batch", [(4096, 128, 1), (300, 64, 2), (77, 100, 1), (40, 4096, 3), (5, 1, 1)])
 def test_kv_int8_dot(R, d, batch):
-    case = synth.make_kv(R, d, seed=700 + d, batch=batch)
+    check_kv_dot(synth.make_kv(R, d, seed=700 + d, batch=batch))
+
+
+def check_kv_dot(case):
+    """The GPU's quantized keys (bit-equal to the oracle's) through the GPU key
+    dot, against the oracle's dot on the oracle's own keys."""
+    R, d = case.v.shape
+    batch = case.x.shape[0]
     q, sc = check_kv_quantize(case.v)
+    qr, scr = oracle.store_int8(case.v)
     got = bqd.kv_int8_dot(q, sc, to_dev(case.x)).cpu().numpy().reshape(batch, R)
     for b in range(batch):
-        ref, mag = oracle.int8_dot(q.cpu().numpy(), sc.cpu().numpy(), case.x[b])
+        ref, mag = oracle.int8_dot(qr, scr, case.x[b])
         assert_tol(got[b], ref, mag, f"kv_int8_dot {R}x{d} vector {b}")
+
+
+@pytest.mark.parametrize("k", range(24))
+def test_kv_random_shapes(k):
+    rng = np.random.default_rng(8000 + k)
+    R = int(rng.integers(1, 5000))
+    d = int(rng.integers(1, 4200)) if rng.random() < 0.5 else int(rng.choice([64, 128, 256]))
+    batch = int(rng.choice([1, 1, 2, 3]))
+    print(f"[case] random kv {R}x{d} batch {batch}", flush=True)
+    check_kv_dot(synth.make_kv(R, d, seed=8100 + k, batch=batch))
 
 
 # ------------------------------------------------------------- Hadamard MLP
@@ -719,7 +766,22 @@ HMLP_CASES = [(512, 2048, 1, True), (10, 16, 3, True), (48, 64, 2, False), (100,
 
 @pytest.mark.parametrize("hidden,H,batch,with_u", HMLP_CASES)
 def test_hadamard_mlp(hidden, H, batch, with_u):
-    case = synth.make_hmlp(hidden, H, seed=800 + H, batch=batch)
+    check_mlp(synth.make_hmlp(hidden, H, seed=800 + H, batch=batch), H, with_u)
+
+
+@pytest.mark.parametrize("k", range(24))
+def test_hadamard_mlp_random_shapes(k):
+    rng = np.random.default_rng(8200 + k)
+    H = int(2 ** rng.integers(0, 15))
+    hidden = int(rng.integers(1, H + 1))
+    batch = int(rng.integers(1, 4))
+    with_u = bool(rng.random() < 0.5)
+    print(f"[case] random mlp {hidden}/{H} batch {batch} u={with_u}", flush=True)
+    check_mlp(synth.make_hmlp(hidden, H, seed=8300 + k, batch=batch), H, with_u)
+
+
+def check_mlp(case, H, with_u):
+    batch, hidden = case.n.shape
     u = to_dev(case.u) if with_u else None
     got = bqd.hadamard_mlp(to_dev(case.n), H, to_dev(case.d1), to_dev(case.d2), to_dev(case.d3),
                            to_dev(case.resid), u).cpu().numpy()
@@ -1249,6 +1311,17 @@ def test_sample_zeros_and_nans_in_top_k(n, k):
         x[rng.choice(np.setdiff1d(np.arange(n), pos), 4, replace=False)] = nan_bits.view(np.float32)
     check_sample(x, k, 0.9, seed=4242 + n)
     check_sample(x, k, 0.0, seed=99 + n)
+
+
+@pytest.mark.parametrize("k", range(30))
+def test_sample_random(k):
+    rng = np.random.default_rng(8400 + k)
+    n = int(rng.integers(1, (1 << 20) + 1)) if rng.random() < 0.7 else int(rng.integers(1, 5000))
+    kk = int(rng.integers(1, min(64, n) + 1))
+    T = 0.0 if rng.random() < 0.2 else float(rng.uniform(0.05, 3.0))
+    kind = str(rng.choice(["normal", "ties", "special"]))
+    print(f"[case] random sample n={n} k={kk} T={T:.3f} {kind}", flush=True)
+    check_sample(_logits(kind, n, 8500 + k), kk, T, seed=8600 + k, calls=2)
 
 
 def test_sample_chain_of_twenty():
