@@ -372,6 +372,8 @@ def self_check(data, bqd, state):
     vectors and the gathered rows bit for bit; matvec outputs on sampled rows
     within |gpu - oracle| <= 1e-4 * sum|w*x| + 1e-6, reported as the largest
     ratio of the two sides.  The small configs are checked on every row."""
+    import torch
+
     import oracle
     rng = np.random.default_rng(2026)
     out = data["outputs"]
@@ -444,12 +446,14 @@ def self_check(data, bqd, state):
             res[f"{name}_prepared_b1"] = dict(bit_exact=bits_eq(p_dev.cpu().numpy()[0], pr))
             ref, mag = oracle.cq_matvec(h, pr)
         tol_rec(f"{name}_matvec", ratio(y, ref, mag), len(y))
-    # the sampler's top 64 of the head's logits (ids and values bit for bit)
-    logits = out["yh"].reshape(-1)
+    # the sampler's top 64 (ids and values bit for bit) on seeded logits of the
+    # head's size, an input of its own rather than the head's output
+    import synth
+    lg = synth.make_logits(data["head_logits"].numel(), seed=8)
     st = state.clone()
-    _, ids, vals = bqd.logits_sample(logits, 64, 0.8, st)
-    oid, oval = oracle.topk(logits.cpu().numpy(), 64)
-    res["head_logits_top64"] = dict(checked=64, bit_exact=bool(
+    _, ids, vals = bqd.logits_sample(torch.from_numpy(lg).to(state.device), 64, 0.8, st)
+    oid, oval = oracle.topk(lg, 64)
+    res["logits_top64"] = dict(checked=64, bit_exact=bool(
         np.array_equal(ids.cpu().numpy(), oid) and bits_eq(vals.cpu().numpy(), oval)))
     res["all_ok"] = all(v.get("ok", True) and v.get("bit_exact", True) for v in res.values())
     return res

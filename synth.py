@@ -203,6 +203,11 @@ KV = dict(n=4096, d=128)
 HMLP = dict(hidden=512, H=2048)
 
 
+def make_logits(n: int, seed: int, scale: float = 3.0) -> np.ndarray:
+    """float32 logits N(0, scale^2) (a sampler's input of the head's size)."""
+    return (scale * np.random.default_rng(seed).standard_normal(n)).astype(np.float32)
+
+
 # Inputs of many GB drawn on the device by torch's seeded generator (the
 # caller passes the torch module); tests copy back the rows they check.
 def _device_generator(torch, seed: int, device):

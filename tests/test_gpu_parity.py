@@ -461,7 +461,9 @@ def test_matvec_unaligned_packed_uses_generic_path():
     mo = bqd.CqMatrix(buf[1:], m.norms, m.codebook, output=s.output, input=s.input,
                       input_padded=s.input_padded, group=s.group, bits=s.bits, row_bytes=s.stride)
     p = bqd.cq_prepare(m, to_dev(case.x))
-    ref, mag = oracle.cq_matvec(host_matrix(case), p.cpu().numpy())
+    p_ref = oracle.cq_prepare(host_matrix(case), case.x)
+    assert bits_eq(p.cpu().numpy(), p_ref)
+    ref, mag = oracle.cq_matvec(host_matrix(case), p_ref)
     assert_tol(bqd.cq_matvec(mo, p).cpu().numpy(), ref, mag, "unaligned packed")
     got = bqd.dbg_cq_unpack(mo, 7).cpu().numpy()
     assert np.array_equal(got, oracle.cq_unpack_row(host_matrix(case), 7))
