@@ -37,7 +37,8 @@
  *    vectors, no ids) is valid and enqueues nothing.
  *  - Results are deterministic: a fixed reduction order, no atomics.
  *  - Concurrent calls on different streams are safe; the library holds no
- *    mutable global state.
+ *    mutable global state, except the static scratch of logits_sample_noalloc
+ *    (whose overlapping calls on one GPU race, as stated there).
  */
 #ifndef BQD_H
 #define BQD_H
