@@ -206,6 +206,14 @@ def build_cases(torch, bqd, synth, hot, heads=True):
         cases.append(Case(HEAD_STAGE,
                           [lambda w=w: bqd.f8_matvec(w, sh, xh, out=yh) for w in whs],
                           head_bytes, hd.R))
+        # the head with the greedy token (argmax) fused into its pass
+        ya = torch.empty(1, hd.R, device=dev)
+        aws = torch.empty(bqd.f8_matvec_argmax_workspace_bytes(1), dtype=torch.uint8, device=dev)
+        tok = torch.empty(1, dtype=torch.int32, device=dev)
+        extras.append(Case("f8_head_246272x4096_matvec_argmax",
+                           [lambda w=w: bqd.f8_matvec_argmax(w, sh, xh, workspace=aws, out=ya,
+                                                             token=tok)
+                            for w in whs], head_bytes + 4, hd.R))
         # -- beyond the step: the I8 head (E8M0 scales per 16 columns) and the
         # int8 key cache (quantize 4096 vectors of 128, score one query)
         log("generating I8 head 246272x4096 G16 (seed 5)")
@@ -286,6 +294,7 @@ def build_cases(torch, bqd, synth, hot, heads=True):
                        [lambda: bqd.hadamard_mlp(hn, H, hd1, hd2, hd3, hr, hu, out=ho)],
                        4 * (3 * H + 4 * hn.numel()), hn.numel()))
     data = dict(c4=c4, c3=c3, head=hd, head_logits=yh, small=small,
+                head_dev=(whs[0], sh, xh) if heads else None,
                 outputs=dict(p1=p1, y1=y1, p8=p8, y8=y8, p3=p3, y3=y3, g=g, yh=yh))
     return cases, extras, data
 
@@ -435,6 +444,17 @@ def self_check(data, bqd, state):
         return ratio(yh[r:r + 1], ref, mag), None
 
     tol_rec("f8_head_246272x4096_matvec", rows_ratio(head_row, rows), len(rows))
+    # the head with its argmax fused: y bit-equal to the head's, the token the
+    # argmax of that y (an integer decision on the GPU's values), and that
+    # row's logit against the oracle
+    w0, s0, x0 = data["head_dev"]
+    ya, tok = bqd.f8_matvec_argmax(w0, s0, x0)
+    yan, t = ya.cpu().numpy()[0], int(tok.item())
+    finite = ~np.isnan(yan)
+    t_host = int(np.flatnonzero(yan == yan[finite].max())[0]) if finite.any() else 0
+    r_t, ok_t = head_row(t)
+    res["f8_head_argmax"] = dict(token=t, max_ratio=round(float(r_t), 6),
+                                 ok=bool(bits_eq(yan, yh) and t == t_host and r_t <= 1.0))
     for name, (case, p_dev, y_dev) in data["small"].items():
         y = y_dev.cpu().numpy()[0]
         if name.startswith("f8"):
@@ -731,6 +751,10 @@ def main():
             per_case[c.name] = dict(rec, timing="16 back-to-back launches per graph replay")
         elif c.name.startswith("cq4_3x"):
             extras[c.name] = dict(rec, note="not part of the step: several matrices on one activation")
+        elif c.name.endswith("_argmax"):
+            extras[c.name] = dict(rec, note="not part of the step: the head with its greedy token "
+                                            "(argmax) fused into the pass, plus the one-thread "
+                                            "launch that reads it")
         elif c.name.startswith("cq4_"):
             extras[c.name] = dict(rec, note="not part of the step: the same stage as two calls")
         elif c.name.split("_")[0] in ("cq2", "cq3", "cq5") or c.name.startswith("f8_wkv"):

@@ -43,7 +43,8 @@ LIB_PATH = os.path.join(_HERE, "libbqd.so")
 
 # Every symbol include/bqd.h declares.
 EXPORTS = ("cq_prepare", "cq_matvec", "cq_prepare_matvec", "cq_matvec_multi",
-           "cq_prepare_matvec_multi", "cq_gather_rows", "f8_matvec",
+           "cq_prepare_matvec_multi", "cq_gather_rows", "f8_matvec", "f8_matvec_argmax",
+           "f8_matvec_argmax_workspace_bytes",
            "i8_matvec", "kv_quantize_int8", "kv_int8_dot", "hadamard_mlp", "logits_sample",
            "logits_sample_workspace_bytes", "logits_sample_noalloc", "bqd_dbg_cq_unpack", "bqd_dbg_f16_decode",
            "bqd_dbg_f8_decode", "bqd_dbg_e8m0_decode", "bqd_dbg_read_stream",
@@ -86,6 +87,7 @@ def lib():
                 ("cq_prepare_matvec_multi", [S, I64, P, P, P, P, P, P]),
                 ("cq_gather_rows", [S, P, I64, P, P]),
                 ("f8_matvec", [P, I64, I64, P, I64, I64, P, P, I64, P]),
+                ("f8_matvec_argmax", [P, I64, I64, P, I64, I64, P, P, I64, P, I64, P, P]),
                 ("i8_matvec", [P, I64, I64, P, I64, P, P, I64, P]),
                 ("kv_quantize_int8", [P, I64, I64, P, P, P]),
                 ("kv_int8_dot", [P, P, I64, I64, P, P, I64, P]),
@@ -100,6 +102,8 @@ def lib():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = I
+        L.f8_matvec_argmax_workspace_bytes.argtypes = [I64]
+        L.f8_matvec_argmax_workspace_bytes.restype = I64
         L.logits_sample_workspace_bytes.argtypes = [I64, I64]
         L.logits_sample_workspace_bytes.restype = I64
         L.bqd_status_string.argtypes = [I]
@@ -306,6 +310,42 @@ def f8_matvec(w: torch.Tensor, scale: torch.Tensor, x: torch.Tensor, out: torch.
     _call("f8_matvec", _ptr(w), R, C, _ptr(scale), SR, SC, _ptr(x), _ptr(out), batch,
           _stream(x, stream))
     return out
+
+
+def f8_matvec_argmax_workspace_bytes(batch: int) -> int:
+    need = lib().f8_matvec_argmax_workspace_bytes(int(batch))
+    if need < 0:
+        raise BqdError("f8_matvec_argmax_workspace_bytes", int(need))
+    return int(need)
+
+
+def f8_matvec_argmax(w: torch.Tensor, scale: torch.Tensor, x: torch.Tensor,
+                     workspace: torch.Tensor = None, out: torch.Tensor = None,
+                     token: torch.Tensor = None, stream=None):
+    """f8_matvec with the argmax of each vector's outputs fused into the pass:
+    (y float32 [batch][R], token int32 [batch]).  workspace: uint8 device
+    scratch of f8_matvec_argmax_workspace_bytes(batch) bytes (allocated if
+    None; nothing in it needs clearing)."""
+    w = _dev(w, torch.uint8, "w")
+    scale = _dev(scale, torch.uint8, "scale")
+    x = _dev(x, torch.float32, "x")
+    R, C = w.shape
+    SR, SC = scale.shape
+    if x.shape[-1] != C:
+        raise ValueError("x must have C columns")
+    batch = x.numel() // C
+    out = torch.empty(x.shape[:-1] + (R,), dtype=torch.float32, device=x.device) if out is None \
+        else _dev(out, torch.float32, "out")
+    need = f8_matvec_argmax_workspace_bytes(batch)
+    workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if workspace is None else \
+        _dev(workspace, torch.uint8, "workspace")
+    token = torch.empty(batch, dtype=torch.int32, device=x.device) if token is None else \
+        _dev(token, torch.int32, "token")
+    if out.numel() != batch * R or token.numel() != batch:
+        raise ValueError("out or token has the wrong size")
+    _call("f8_matvec_argmax", _ptr(w), R, C, _ptr(scale), SR, SC, _ptr(x), _ptr(out), batch,
+          _ptr(workspace), workspace.numel(), _ptr(token), _stream(x, stream))
+    return out, token
 
 
 def i8_matvec(w: torch.Tensor, scale: torch.Tensor, x: torch.Tensor, G: int = 16,

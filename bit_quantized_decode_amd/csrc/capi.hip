@@ -66,6 +66,21 @@ int f8_matvec(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int6
   return launch_f8_matvec(w, R, C, scale, SR, SC, x, y, batch, as_stream(stream));
 }
 
+int64_t f8_matvec_argmax_workspace_bytes(int64_t batch) {
+  if (batch < 0 || batch >= kMaxRows) return BQD_EINVAL;
+  return f8_argmax_workspace_need(batch);
+}
+
+int f8_matvec_argmax(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
+                     int64_t SC, const float* x, float* y, int64_t batch, void* workspace,
+                     int64_t workspace_bytes, int32_t* token, void* stream) {
+  int rc = check_f8_argmax(w, R, C, scale, SR, SC, x, y, batch, workspace, workspace_bytes,
+                           token);
+  if (rc || batch == 0) return rc;
+  return launch_f8_matvec_argmax(w, R, C, scale, SR, SC, x, y, batch, workspace, token,
+                                 as_stream(stream));
+}
+
 int i8_matvec(const int8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t G,
               const float* x, float* y, int64_t batch, void* stream) {
   int rc = check_i8(w, R, C, scale, G, x, y, batch);

@@ -9,6 +9,8 @@
 
 #include "device.h"
 #include "launch.h"
+#include "logit_key.h"
+#include "validate.h"
 
 namespace bqd {
 
@@ -39,6 +41,21 @@ __global__ __launch_bounds__(kF8Threads) void f8_matvec_generic(
   }
 }
 
+// The largest key (logit_key.h) over a workgroup of THREADS threads: every
+// lane ends with it.
+template <int THREADS = kF8Threads>
+__device__ __forceinline__ uint64_t block_max_key(uint64_t k) {
+  __shared__ uint64_t wave_best[THREADS / kWave];
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) k = max(k, (uint64_t)__shfl_xor((unsigned long long)k, d));
+  if ((threadIdx.x & (kWave - 1)) == 0) wave_best[threadIdx.x / kWave] = k;
+  __syncthreads();
+  uint64_t m = wave_best[0];
+#pragma unroll
+  for (int i = 1; i < THREADS / kWave; ++i) m = max(m, wave_best[i]);
+  return m;
+}
+
 // -------------------------------------------------------------- fast matvec
 // Rows of C = 16 * n_chunk bytes with 16-byte aligned rows and scale blocks
 // that are a whole number of 16-column chunks wide.  LPR lanes share a row;
@@ -66,12 +83,17 @@ __global__ __launch_bounds__(kF8Threads) void f8_matvec_generic(
 // The workgroup stages x in LDS once (float4 loads where x is 16-byte
 // aligned, x_vec) and each wavefront takes its lanes' activations from there:
 // one copy of x per workgroup from L2 instead of one per wavefront (~1%).
-template <int NJ, int LPR, int U, bool EXACT, bool SHARE>
+//
+// ARGMAX fuses the argmax of y: each lane keeps the largest key (logit_key.h)
+// of the rows it stores, and the workgroup stores the largest of them to its
+// own slot, slots[blockIdx] (a plain store: an atomic per workgroup into one
+// word held every workgroup until it completed, ~20 us over the head).
+template <int NJ, int LPR, int U, bool EXACT, bool SHARE, bool ARGMAX>
 __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(NJ <= 4 ? 4 : 1)))
 void f8_matvec_fast(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ scale, const float* __restrict__ x,
     float* __restrict__ y, int R, int64_t C, int64_t SR, int64_t SC, int64_t cols_per_block,
-    uint32_t blk_magic, int blk_shift, int x_vec) {
+    uint32_t blk_magic, int blk_shift, int x_vec, uint64_t* __restrict__ slots) {
   constexpr int SLOTS = kF8Threads / LPR;
   constexpr int CX = 16 * LPR * NJ;  // = C
   __shared__ __align__(16) float xs[CX];
@@ -102,6 +124,7 @@ void f8_matvec_fast(
   }
   // rows < 2^30: 32-bit row arithmetic
   const int n_steps = (R + SLOTS - 1) / SLOTS;
+  uint64_t best = 0;  // ARGMAX: the largest key of this lane's rows (0: none)
   for (int s0 = (int)blockIdx.x * U; s0 < n_steps; s0 += (int)gridDim.x * U) {
     uint4 d[U][NJ];
     uint32_t sb[U][NJ];
@@ -137,8 +160,15 @@ void f8_matvec_fast(
       }
       acc = group_sum<LPR>(acc);
       const int r = (s0 + u) * SLOTS + slot;
-      if (q == LPR - 1 && r < R) y[r] = acc;
+      if (q == LPR - 1 && r < R) {
+        y[r] = acc;
+        if constexpr (ARGMAX) best = max(best, cand_key(acc, (uint32_t)r));
+      }
     }
+  }
+  if constexpr (ARGMAX) {
+    const uint64_t m = block_max_key(best);
+    if (tid == 0) slots[blockIdx.x] = m;
   }
 }
 
@@ -148,13 +178,20 @@ namespace {
 // 98% of a plain read kernel's rate; fewer leave HBM queues short.
 constexpr int kMaxGrid = 8192;
 
-template <int NJ, int LPR>
-int launch_f8_fast(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
-                   int64_t SC, const float* x, float* y, hipStream_t s) {
+// The streaming kernel's grid for R rows at LPR lanes per row.
+int64_t fast_grid(int64_t R, int lpr) {
+  constexpr int U = 2;
+  const int64_t slots = kF8Threads / lpr;
+  const int64_t n_steps = (R + slots - 1) / slots;
+  return std::min<int64_t>((n_steps + U - 1) / U, kMaxGrid);
+}
+
+template <int NJ, int LPR, bool ARGMAX>
+int launch_f8_fast_a(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
+                     int64_t SC, const float* x, float* y, uint64_t* slots, hipStream_t s) {
   constexpr int U = 2;
   constexpr int SLOTS = kF8Threads / LPR;
-  const int64_t n_steps = (R + SLOTS - 1) / SLOTS;
-  const int64_t grid = std::min<int64_t>((n_steps + U - 1) / U, kMaxGrid);
+  const int64_t grid = fast_grid(R, LPR);
   const int x_vec = is_aligned(x, 16) ? 1 : 0;
   if (R % SR == 0) {
     // rows per scale block d: magic = ceil(2^(31 + l) / d), 2^l >= d > 2^(l - 1)
@@ -163,19 +200,27 @@ int launch_f8_fast(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale,
     while ((uint64_t(1) << l) < d) ++l;
     const uint64_t magic = ((uint64_t(1) << (31 + l)) + d - 1) / d;  // < 2^32
     if (d % (U * SLOTS) == 0)
-      hipLaunchKernelGGL((f8_matvec_fast<NJ, LPR, U, true, true>), dim3((unsigned)grid),
+      hipLaunchKernelGGL((f8_matvec_fast<NJ, LPR, U, true, true, ARGMAX>), dim3((unsigned)grid),
                          dim3(kF8Threads), 0, s, w, scale, x, y, (int)R, C, SR, SC, C / SC,
-                         (uint32_t)magic, 31 + l, x_vec);
+                         (uint32_t)magic, 31 + l, x_vec, slots);
     else
-      hipLaunchKernelGGL((f8_matvec_fast<NJ, LPR, U, true, false>), dim3((unsigned)grid),
+      hipLaunchKernelGGL((f8_matvec_fast<NJ, LPR, U, true, false, ARGMAX>), dim3((unsigned)grid),
                          dim3(kF8Threads), 0, s, w, scale, x, y, (int)R, C, SR, SC, C / SC,
-                         (uint32_t)magic, 31 + l, x_vec);
+                         (uint32_t)magic, 31 + l, x_vec, slots);
   } else {
-    hipLaunchKernelGGL((f8_matvec_fast<NJ, LPR, U, false, false>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((f8_matvec_fast<NJ, LPR, U, false, false, ARGMAX>), dim3((unsigned)grid),
                        dim3(kF8Threads), 0, s, w, scale, x, y, (int)R, C, SR, SC, C / SC, 0u, 0,
-                       x_vec);
+                       x_vec, slots);
   }
   return launch_status();
+}
+
+template <int NJ, int LPR>
+int launch_f8_fast(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
+                   int64_t SC, const float* x, float* y, uint64_t* slots, hipStream_t s) {
+  if (slots != nullptr)
+    return launch_f8_fast_a<NJ, LPR, true>(w, R, C, scale, SR, SC, x, y, slots, s);
+  return launch_f8_fast_a<NJ, LPR, false>(w, R, C, scale, SR, SC, x, y, nullptr, s);
 }
 
 int launch_f8_generic(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
@@ -185,6 +230,44 @@ int launch_f8_generic(const uint8_t* w, int64_t R, int64_t C, const uint8_t* sca
   hipLaunchKernelGGL(f8_matvec_generic, dim3((unsigned)grid), dim3(kF8Threads), 0, s, w, scale, x,
                      y, R, C, SR, SC, batch);
   return launch_status();
+}
+
+// The slots of y's argmax where the generic kernel computed y: workgroup g
+// takes rows [g chunk, (g + 1) chunk) of every vector.
+__global__ __launch_bounds__(kF8Threads) void argmax_slots_from_y(
+    const float* __restrict__ y, int64_t R, int64_t batch, int64_t chunk,
+    uint64_t* __restrict__ slots) {
+  const int64_t r0 = (int64_t)blockIdx.x * chunk, r1 = min(r0 + chunk, R);
+  for (int64_t b = 0; b < batch; ++b) {  // workgroup-uniform
+    uint64_t k = 0;
+    for (int64_t r = r0 + threadIdx.x; r < r1; r += kF8Threads)
+      k = max(k, cand_key(y[b * R + r], (uint32_t)r));
+    const uint64_t m = block_max_key(k);
+    if (threadIdx.x == 0) slots[b * kMaxGrid + blockIdx.x] = m;
+    __syncthreads();  // block_max_key's LDS is reused by the next vector
+  }
+}
+
+// The fused argmax's last step: workgroup b takes the largest of vector b's
+// n_slots (<= kMaxGrid) slot keys, each thread's eight loads issued at once;
+// token[b] is the row in its low word.
+constexpr int kFinishThreads = 1024;
+static_assert(kMaxGrid <= 8 * kFinishThreads, "eight slots per thread");
+__global__ __launch_bounds__(kFinishThreads) void argmax_finish(
+    const uint64_t* __restrict__ slots, int64_t n_slots, int32_t* __restrict__ token) {
+  const uint64_t* sb = slots + (int64_t)blockIdx.x * kMaxGrid;
+  uint64_t v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {  // unconditional loads (a clamped index), then the select
+    const int64_t i = j * kFinishThreads + (int64_t)threadIdx.x;
+    v[j] = sb[min(i, n_slots - 1)];
+    v[j] = i < n_slots ? v[j] : 0;
+  }
+  uint64_t k = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) k = max(k, v[j]);
+  const uint64_t m = block_max_key<kFinishThreads>(k);
+  if (threadIdx.x == 0) token[blockIdx.x] = (int32_t)(0xffffffffu - (uint32_t)m);
 }
 
 // Lane layout for rows of n_chunk 16-byte chunks, or {0, 0}.
@@ -200,31 +283,66 @@ F8Shape f8_shape(int64_t n_chunk) {
   return {0, 0};
 }
 
-}  // namespace
-
-int launch_f8_matvec(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
-                     int64_t SC, const float* x, float* y, int64_t batch, hipStream_t s) {
+F8Shape f8_fast_shape(const uint8_t* w, int64_t C, int64_t SC, const float* x) {
   const bool fast = C % 16 == 0 && is_aligned(w, 16) && is_aligned(x, 4) && C % SC == 0 &&
                     (C / SC) % 16 == 0;
-  const F8Shape f = fast ? f8_shape(C / 16) : F8Shape{0, 0};
+  return fast ? f8_shape(C / 16) : F8Shape{0, 0};
+}
+
+// y; with slots (kMaxGrid per vector), the streaming kernel also leaves each
+// workgroup's largest key in them.
+int run_f8(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR, int64_t SC,
+           const float* x, float* y, int64_t batch, F8Shape f, uint64_t* slots, hipStream_t s) {
   if (f.lpr == 0) return launch_f8_generic(w, R, C, scale, SR, SC, x, y, batch, s);
   // One weight pass per activation vector (the workloads here are batch 1).
   for (int64_t b = 0; b < batch; ++b) {
     const float* xb = x + b * C;
     float* yb = y + b * R;
+    uint64_t* sb = slots ? slots + b * kMaxGrid : nullptr;
     int rc = BQD_EINVAL;
     switch (f.lpr * 16 + f.nj) {
-      case 8 * 16 + 1: rc = launch_f8_fast<1, 8>(w, R, C, scale, SR, SC, xb, yb, s); break;
-      case 16 * 16 + 1: rc = launch_f8_fast<1, 16>(w, R, C, scale, SR, SC, xb, yb, s); break;
-      case 32 * 16 + 1: rc = launch_f8_fast<1, 32>(w, R, C, scale, SR, SC, xb, yb, s); break;
-      case 64 * 16 + 1: rc = launch_f8_fast<1, 64>(w, R, C, scale, SR, SC, xb, yb, s); break;
-      case 64 * 16 + 2: rc = launch_f8_fast<2, 64>(w, R, C, scale, SR, SC, xb, yb, s); break;
-      case 64 * 16 + 4: rc = launch_f8_fast<4, 64>(w, R, C, scale, SR, SC, xb, yb, s); break;
-      case 64 * 16 + 8: rc = launch_f8_fast<8, 64>(w, R, C, scale, SR, SC, xb, yb, s); break;
+      case 8 * 16 + 1: rc = launch_f8_fast<1, 8>(w, R, C, scale, SR, SC, xb, yb, sb, s); break;
+      case 16 * 16 + 1: rc = launch_f8_fast<1, 16>(w, R, C, scale, SR, SC, xb, yb, sb, s); break;
+      case 32 * 16 + 1: rc = launch_f8_fast<1, 32>(w, R, C, scale, SR, SC, xb, yb, sb, s); break;
+      case 64 * 16 + 1: rc = launch_f8_fast<1, 64>(w, R, C, scale, SR, SC, xb, yb, sb, s); break;
+      case 64 * 16 + 2: rc = launch_f8_fast<2, 64>(w, R, C, scale, SR, SC, xb, yb, sb, s); break;
+      case 64 * 16 + 4: rc = launch_f8_fast<4, 64>(w, R, C, scale, SR, SC, xb, yb, sb, s); break;
+      case 64 * 16 + 8: rc = launch_f8_fast<8, 64>(w, R, C, scale, SR, SC, xb, yb, sb, s); break;
     }
     if (rc) return rc;
   }
   return BQD_OK;
+}
+
+}  // namespace
+
+static_assert(kMaxGrid == kF8ArgmaxSlots, "one workspace slot per workgroup");
+
+int launch_f8_matvec(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
+                     int64_t SC, const float* x, float* y, int64_t batch, hipStream_t s) {
+  return run_f8(w, R, C, scale, SR, SC, x, y, batch, f8_fast_shape(w, C, SC, x), nullptr, s);
+}
+
+int launch_f8_matvec_argmax(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale,
+                            int64_t SR, int64_t SC, const float* x, float* y, int64_t batch,
+                            void* workspace, int32_t* token, hipStream_t s) {
+  uint64_t* slots = static_cast<uint64_t*>(workspace);
+  const F8Shape f = f8_fast_shape(w, C, SC, x);
+  int rc = run_f8(w, R, C, scale, SR, SC, x, y, batch, f, f.lpr ? slots : nullptr, s);
+  if (rc) return rc;
+  int64_t n_slots;
+  if (f.lpr) {
+    n_slots = fast_grid(R, f.lpr);
+  } else {
+    n_slots = std::min<int64_t>(kMaxGrid, (R + kF8Threads - 1) / kF8Threads);
+    const int64_t chunk = (R + n_slots - 1) / n_slots;
+    hipLaunchKernelGGL(argmax_slots_from_y, dim3((unsigned)n_slots), dim3(kF8Threads), 0, s, y,
+                       R, batch, chunk, slots);
+    if ((rc = launch_status())) return rc;
+  }
+  hipLaunchKernelGGL(argmax_finish, dim3((unsigned)batch), dim3(kFinishThreads), 0, s, slots,
+                     n_slots, token);
+  return launch_status();
 }
 
 // ------------------------------------------------------------ decode probes

@@ -22,6 +22,9 @@ int launch_cq_unpack(const bqd_cq_matrix* m, int64_t row, uint8_t* idx, hipStrea
 
 int launch_f8_matvec(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
                      int64_t SC, const float* x, float* y, int64_t batch, hipStream_t s);
+int launch_f8_matvec_argmax(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale,
+                            int64_t SR, int64_t SC, const float* x, float* y, int64_t batch,
+                            void* workspace, int32_t* token, hipStream_t s);
 int launch_i8_matvec(const int8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t G,
                      const float* x, float* y, int64_t batch, hipStream_t s);
 int launch_kv_quantize_int8(const float* v, int64_t n_vec, int64_t d, int8_t* q, float* scales,

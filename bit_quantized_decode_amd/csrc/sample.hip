@@ -44,6 +44,7 @@
 
 #include "cq_device.h"
 #include "launch.h"
+#include "logit_key.h"
 #include "validate.h"
 
 namespace bqd {
@@ -54,18 +55,6 @@ constexpr int kPeek = 8;              // keys read per list by the pruned select
 constexpr int kMaxK = 64;
 constexpr int kRankMax = 256;         // survivors ranked by counting (more: sorted)
 constexpr int kTopSlot = kSampleThreads;  // LDS slot of the counted top k
-
-// Unsigned key of a logit: the order of values, NaN below everything, -0 = +0.
-__device__ __forceinline__ uint32_t value_key(float v) {
-  if (v != v) return 0u;
-  uint32_t b = __float_as_uint(v);
-  if ((b << 1) == 0u) b = 0u;  // -0 -> +0
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-__device__ __forceinline__ uint64_t cand_key(float v, uint32_t index) {
-  return ((uint64_t)value_key(v) << 32) | (uint64_t)(0xffffffffu - index);
-}
 
 // A 64-bit key of lane (lane ^ D): both halves through the transform's lane
 // exchange (DPP within 16-lane rows, ds_bpermute beyond), which moves bits

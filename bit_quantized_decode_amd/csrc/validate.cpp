@@ -203,6 +203,23 @@ int check_f8(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64
   return BQD_OK;
 }
 
+int check_f8_argmax(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
+                    int64_t SC, const float* x, const float* y, int64_t batch,
+                    const void* workspace, int64_t workspace_bytes, const int32_t* token) {
+  if (R < 1) return BQD_EINVAL;  // every vector has a largest logit
+  const int rc = check_f8(w, R, C, scale, SR, SC, x, y, batch);
+  if (rc || batch == 0) return rc;
+  if (!mul_ok(batch, kF8ArgmaxSlots, 8)) return BQD_EOVERFLOW;
+  const int64_t need = f8_argmax_workspace_need(batch);
+  if (workspace_bytes < need) return BQD_EINVAL;
+  if (!workspace || !token) return BQD_ENULL;
+  if (!aligned(workspace, 8) || !aligned(token, 4)) return BQD_EALIGN;
+  const Span in[3] = {{w, R * C}, {scale, SR * SC}, {x, batch * C * 4}};
+  const Span out[3] = {{y, batch * R * 4}, {workspace, need}, {token, batch * 4}};
+  if (outputs_overlap(out, 3, in, 3)) return BQD_EINVAL;
+  return BQD_OK;
+}
+
 int check_i8(const int8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t G,
              const float* x, const float* y, int64_t batch) {
   if (R < 0 || R >= kMaxRows || C < 1 || C >= kMaxColumns || G < 1 || G > C || batch < 0)

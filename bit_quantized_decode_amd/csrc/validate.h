@@ -25,6 +25,15 @@ int check_matvec_multi(const bqd_cq_matrix* ms, int64_t n, const int64_t* row_be
 int check_gather(const bqd_cq_matrix* m, const int32_t* rows, int64_t n, const float* out);
 int check_f8(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
              int64_t SC, const float* x, const float* y, int64_t batch);
+// f8_matvec_argmax's workspace: one 8-byte slot per workgroup of the
+// widest launch (8192) per vector.
+constexpr int64_t kF8ArgmaxSlots = 8192;
+inline int64_t f8_argmax_workspace_need(int64_t batch) { return batch * kF8ArgmaxSlots * 8; }
+// f8_matvec_argmax: check_f8's rules, R >= 1, and the workspace (8-byte
+// aligned, large enough) and tokens (4-byte aligned) as two more outputs.
+int check_f8_argmax(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
+                    int64_t SC, const float* x, const float* y, int64_t batch,
+                    const void* workspace, int64_t workspace_bytes, const int32_t* token);
 int check_i8(const int8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t G,
              const float* x, const float* y, int64_t batch);
 int check_kv_quantize(const float* v, int64_t n_vec, int64_t d, const int8_t* q,

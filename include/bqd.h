@@ -174,6 +174,29 @@ int f8_matvec(const uint8_t *w, int64_t R, int64_t C, const uint8_t *scale,
               int64_t SR, int64_t SC, const float *x, float *y, int64_t batch,
               void *stream);
 
+/* f8_matvec with the argmax of each vector's outputs fused into the same
+ * pass ([P4] work item 3 and "Step 3 done": the logits of the head go
+ * straight to token selection; this is its greedy form, the token that
+ * logits_sample returns at temperature 0 or k = 1): token[b] = the row of
+ * the largest y[b][r], equal values taken at the lowest row, NaN below every
+ * number, -0 equal to +0.  Each workgroup of the matvec stores the largest
+ * (value, row) key of the rows it computed to a slot of the workspace; one
+ * small launch then reduces the slots to the token (no atomics; the result
+ * does not depend on scheduling).  Shapes the streaming kernel does not take
+ * fill the slots from y in a pass of their own.
+ *   workspace: device scratch of f8_matvec_argmax_workspace_bytes(batch)
+ *              bytes, 8-byte aligned, caller-owned; nothing in it needs
+ *              clearing; calls that share it must be ordered on one stream
+ *   token:     int32 [batch]
+ * Other arguments as f8_matvec; requires R >= 1.
+ * Errors: as f8_matvec (BQD_EINVAL also for a workspace smaller than the
+ * need; BQD_EALIGN for one not 8-byte aligned; outputs y, the workspace and
+ * token must not overlap one another or the inputs). */
+int64_t f8_matvec_argmax_workspace_bytes(int64_t batch);
+int f8_matvec_argmax(const uint8_t *w, int64_t R, int64_t C, const uint8_t *scale,
+                     int64_t SR, int64_t SC, const float *x, float *y, int64_t batch,
+                     void *workspace, int64_t workspace_bytes, int32_t *token, void *stream);
+
 /* [P4] "Step 4 done" (the I8 matvec: int8 weights widened, one E8M0 scale
  * per group of consecutive columns; the page's groups are 16 wide):
  *   y[b][r] = sum over c < C of w[r][c] * e8m0(scale[r][c / G]) * x[b][c],

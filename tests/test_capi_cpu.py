@@ -324,6 +324,31 @@ def test_binding_refuses_host_tensors():
 A, B, C_, D, E, F, G_ = ((k + 1) << 32 for k in range(7))
 
 
+def test_f8_argmax_argument_rules():
+    """f8_matvec_argmax: f8_matvec's rules, at least one row, a workspace of
+    the stated size and tokens present, aligned and apart from every other
+    buffer."""
+    L = bqd.lib()
+    need = L.f8_matvec_argmax_workspace_bytes(1)
+    assert need == 8192 * 8 and L.f8_matvec_argmax_workspace_bytes(3) == 3 * need
+    assert L.f8_matvec_argmax_workspace_bytes(-1) == EINVAL
+    W, S, X, Y, K, T = FAKE, FAKE + (1 << 24), FAKE + (2 << 24), FAKE + (3 << 24), \
+        FAKE + (4 << 24), FAKE + (5 << 24)
+    call = lambda R=512, ws=K, wsb=need, tok=T, y=Y, batch=1: L.f8_matvec_argmax(
+        W, R, 4096, S, 4, 32, X, y, batch, ws, wsb, tok, None)
+    assert call(R=0) == EINVAL          # no row to take
+    assert call(wsb=need - 1) == EINVAL  # workspace too small
+    assert call(ws=None) == ENULL
+    assert call(tok=None) == ENULL
+    assert call(ws=K + 4) == EALIGN     # slots are 8 bytes
+    assert call(tok=T + 2) == EALIGN
+    assert call(ws=Y + 8) == EINVAL     # workspace over y
+    assert call(tok=K + 8) == EINVAL    # token over the workspace
+    assert call(tok=X) == EINVAL        # token over x
+    assert call(batch=0) == OK          # nothing to do
+    assert call(batch=-1) == EINVAL
+
+
 def test_f8_i8_kv_outputs_overlapping_inputs_are_refused():
     L = bqd.lib()
     f8 = lambda w=A, s=B, x=C_, y=D: L.f8_matvec(w, 512, 4096, s, 4, 32, x, y, 1, None)

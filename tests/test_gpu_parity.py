@@ -534,6 +534,81 @@ def check_f8(case, row_blocks=None):
     return got
 
 
+# ----------------------------------------------- F8 matvec with fused argmax
+def host_argmax(y):
+    """Per vector: the row of the largest value, equal values at the lowest row,
+    NaN below every number (row 0 if all are NaN), -0 equal to +0."""
+    out = []
+    for v in np.atleast_2d(y).astype(np.float64):
+        ok = ~np.isnan(v)
+        out.append(int(np.flatnonzero(v == v[ok].max())[0]) if ok.any() else 0)
+    return np.array(out)
+
+
+def check_f8_argmax(case, workspace=None):
+    """y bit-identical to f8_matvec's; the token the argmax of that y (an
+    integer decision on the GPU's own values); against the oracle, the chosen
+    row is a largest logit within the tolerance of the two rows involved."""
+    w, s, x = dev_f8(case)
+    y, tok = bqd.f8_matvec_argmax(w, s, x, workspace=workspace)
+    y0 = bqd.f8_matvec(w, s, x)
+    yn, tokn = y.cpu().numpy().reshape(-1, case.R), tok.cpu().numpy()
+    assert bits_eq(yn, y0.cpu().numpy().reshape(-1, case.R))
+    assert np.array_equal(tokn, host_argmax(yn)), (tokn, host_argmax(yn))
+    ref, mag = oracle.f8_matvec(case.w, case.R, case.C, case.scale, case.SR, case.SC, case.x)
+    ref, mag = np.atleast_2d(ref), np.atleast_2d(mag)
+    for b, t in enumerate(tokn):
+        if np.isnan(ref[b]).all():
+            continue
+        best = int(np.nanargmax(ref[b]))
+        if ref[b][t] == ref[b][best]:  # also where both are +inf
+            continue
+        tol = 1e-4 * mag[b] + 1e-6
+        assert ref[b][t] >= ref[b][best] - tol[t] - tol[best], (b, t, best)
+    return tokn
+
+
+def test_f8_argmax_head(cache):
+    case = workload(cache, "f8_head_246272x4096")
+    print("[case] f8 head with fused argmax", flush=True)
+    ws = torch.full((bqd.f8_matvec_argmax_workspace_bytes(1),), 0xA5, dtype=torch.uint8, device=DEV)
+    t1 = check_f8_argmax(case, ws)  # a workspace holding garbage
+    assert np.array_equal(check_f8_argmax(case, ws), t1)  # and again, after the first call
+
+
+@pytest.mark.parametrize("k", range(16))
+def test_f8_argmax_random_shapes(k):
+    rng = np.random.default_rng(9000 + k)
+    R = int(rng.integers(1, 5000))
+    C = int(16 * rng.integers(1, 513)) if rng.random() < 0.6 else int(rng.integers(1, 3000))
+    SR = int(rng.integers(1, min(R, 64) + 1))
+    SC = int(rng.choice([d for d in range(1, min(C, 64) + 1) if C % d == 0]))
+    batch = int(rng.choice([1, 1, 2, 3]))
+    print(f"[case] f8 argmax {R}x{C} scales {SR}x{SC} batch {batch}", flush=True)
+    check_f8_argmax(synth.make_f8(R, C, SR, SC, seed=9100 + k, batch=batch))
+
+
+@pytest.mark.parametrize("C", [4096, 100])
+def test_f8_argmax_ties_nan_and_inf(C):
+    """Equal largest logits take the lowest row; a NaN activation makes every
+    logit NaN (row 0); +inf in one column makes the lowest +inf row win.
+    C = 4096 runs the streaming kernel, C = 100 the generic one."""
+    case = synth.make_f8(300, C, 1, 4, seed=91)  # one scale row: equal rows, equal logits
+    case.w[:] = 0x00
+    for r in (200, 50, 123):
+        case.w[r] = 0x38  # 1.0 everywhere: three equal rows
+    case.x[:] = np.abs(case.x)
+    assert check_f8_argmax(case)[0] == 50
+    nan_case = synth.make_f8(300, C, 3, 4, seed=92)
+    nan_case.x[0, 7] = np.nan
+    assert check_f8_argmax(nan_case)[0] == 0
+    inf_case = synth.make_f8(300, C, 3, 4, seed=93)
+    inf_case.w[:, 3] = 0x00
+    inf_case.w[[40, 17, 250], 3] = 0x38
+    inf_case.x[0, 3] = np.inf
+    assert check_f8_argmax(inf_case)[0] == 17
+
+
 def test_f8_wkv(cache):
     check_f8(workload(cache, "f8_wkv_512x4096"))
 
