@@ -85,9 +85,14 @@ __device__ __forceinline__ uint64_t block_max_key(uint64_t k) {
 // one copy of x per workgroup from L2 instead of one per wavefront (~1%).
 //
 // ARGMAX fuses the argmax of y: each lane keeps the largest key (logit_key.h)
-// of the rows it stores, and the workgroup stores the largest of them to its
-// own slot, slots[blockIdx] (a plain store: an atomic per workgroup into one
-// word held every workgroup until it completed, ~20 us over the head).
+// of the rows it stores; each wavefront puts the largest of its lanes' in
+// LDS and takes a ticket from an LDS counter, and the wavefront with the
+// last ticket stores the workgroup's largest to its slot, slots[blockIdx]
+// (plain stores).  No wavefront waits for another: a workgroup barrier there
+// held three wavefronts at every workgroup's end, and an atomic per
+// workgroup into one device word held every workgroup until it completed
+// (~20 us over the head); a slot per wavefront made the last step read 4x
+// the slots.
 template <int NJ, int LPR, int U, bool EXACT, bool SHARE, bool ARGMAX>
 __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(NJ <= 4 ? 4 : 1)))
 void f8_matvec_fast(
@@ -100,6 +105,10 @@ void f8_matvec_fast(
   const int tid = threadIdx.x;
   const int slot = tid / LPR;
   const int q = tid % LPR;
+  __shared__ uint64_t wave_best[kF8Threads / kWave];
+  __shared__ uint32_t tickets;
+  if constexpr (ARGMAX)
+    if (tid == 0) tickets = 0;  // ordered before any ticket by the staging barrier below
   if (x_vec) {
     for (int i = tid; i < CX / 4; i += kF8Threads)
       reinterpret_cast<float4*>(xs)[i] = reinterpret_cast<const float4*>(x)[i];
@@ -167,8 +176,20 @@ void f8_matvec_fast(
     }
   }
   if constexpr (ARGMAX) {
-    const uint64_t m = block_max_key(best);
-    if (tid == 0) slots[blockIdx.x] = m;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1)
+      best = max(best, (uint64_t)__shfl_xor((unsigned long long)best, d));
+    if ((tid & (kWave - 1)) == 0) {
+      wave_best[tid / kWave] = best;
+      __threadfence_block();  // the value before the ticket
+      if (atomicAdd(&tickets, 1u) == kF8Threads / kWave - 1) {
+        __threadfence_block();  // every other wavefront's value after its ticket
+        uint64_t m = wave_best[0];
+#pragma unroll
+        for (int i = 1; i < kF8Threads / kWave; ++i) m = max(m, wave_best[i]);
+        slots[blockIdx.x] = m;
+      }
+    }
   }
 }
 
@@ -177,6 +198,8 @@ namespace {
 // Measured on the 246272 x 4096 head: 8192 workgroups of 256 threads stream at
 // 98% of a plain read kernel's rate; fewer leave HBM queues short.
 constexpr int kMaxGrid = 8192;
+// the fused argmax's slots per vector: one per workgroup of the widest launch
+constexpr int64_t kSlotsPerVector = kMaxGrid;
 
 // The streaming kernel's grid for R rows at LPR lanes per row.
 int64_t fast_grid(int64_t R, int lpr) {
@@ -243,29 +266,30 @@ __global__ __launch_bounds__(kF8Threads) void argmax_slots_from_y(
     for (int64_t r = r0 + threadIdx.x; r < r1; r += kF8Threads)
       k = max(k, cand_key(y[b * R + r], (uint32_t)r));
     const uint64_t m = block_max_key(k);
-    if (threadIdx.x == 0) slots[b * kMaxGrid + blockIdx.x] = m;
+    if (threadIdx.x == 0) slots[b * kSlotsPerVector + blockIdx.x] = m;
     __syncthreads();  // block_max_key's LDS is reused by the next vector
   }
 }
 
 // The fused argmax's last step: workgroup b takes the largest of vector b's
-// n_slots (<= kMaxGrid) slot keys, each thread's eight loads issued at once;
-// token[b] is the row in its low word.
+// n_slots (<= kSlotsPerVector) slot keys, each thread's loads all issued at
+// once; token[b] is the row in its low word.
 constexpr int kFinishThreads = 1024;
-static_assert(kMaxGrid <= 8 * kFinishThreads, "eight slots per thread");
+constexpr int kFinishLoads = (int)(kSlotsPerVector / kFinishThreads);
+static_assert(kSlotsPerVector == (int64_t)kFinishLoads * kFinishThreads, "whole loads per thread");
 __global__ __launch_bounds__(kFinishThreads) void argmax_finish(
     const uint64_t* __restrict__ slots, int64_t n_slots, int32_t* __restrict__ token) {
-  const uint64_t* sb = slots + (int64_t)blockIdx.x * kMaxGrid;
-  uint64_t v[8];
+  const uint64_t* sb = slots + (int64_t)blockIdx.x * kSlotsPerVector;
+  uint64_t v[kFinishLoads];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {  // unconditional loads (a clamped index), then the select
+  for (int j = 0; j < kFinishLoads; ++j) {  // unconditional loads (a clamped index), then the select
     const int64_t i = j * kFinishThreads + (int64_t)threadIdx.x;
     v[j] = sb[min(i, n_slots - 1)];
     v[j] = i < n_slots ? v[j] : 0;
   }
   uint64_t k = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) k = max(k, v[j]);
+  for (int j = 0; j < kFinishLoads; ++j) k = max(k, v[j]);
   const uint64_t m = block_max_key<kFinishThreads>(k);
   if (threadIdx.x == 0) token[blockIdx.x] = (int32_t)(0xffffffffu - (uint32_t)m);
 }
@@ -298,7 +322,7 @@ int run_f8(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t
   for (int64_t b = 0; b < batch; ++b) {
     const float* xb = x + b * C;
     float* yb = y + b * R;
-    uint64_t* sb = slots ? slots + b * kMaxGrid : nullptr;
+    uint64_t* sb = slots ? slots + b * kSlotsPerVector : nullptr;
     int rc = BQD_EINVAL;
     switch (f.lpr * 16 + f.nj) {
       case 8 * 16 + 1: rc = launch_f8_fast<1, 8>(w, R, C, scale, SR, SC, xb, yb, sb, s); break;
@@ -316,7 +340,7 @@ int run_f8(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t
 
 }  // namespace
 
-static_assert(kMaxGrid == kF8ArgmaxSlots, "one workspace slot per workgroup");
+static_assert(kSlotsPerVector == kF8ArgmaxSlots, "one workspace slot per workgroup");
 
 int launch_f8_matvec(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
                      int64_t SC, const float* x, float* y, int64_t batch, hipStream_t s) {
