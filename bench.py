@@ -753,8 +753,8 @@ def main():
             extras[c.name] = dict(rec, note="not part of the step: several matrices on one activation")
         elif c.name.endswith("_argmax"):
             extras[c.name] = dict(rec, note="not part of the step: the head with its greedy token "
-                                            "(argmax) fused into the pass, plus the one-thread "
-                                            "launch that reads it")
+                                            "(argmax) fused into the pass, plus the one-workgroup "
+                                            "launch that reduces its slots")
         elif c.name.startswith("cq4_"):
             extras[c.name] = dict(rec, note="not part of the step: the same stage as two calls")
         elif c.name.split("_")[0] in ("cq2", "cq3", "cq5") or c.name.startswith("f8_wkv"):
