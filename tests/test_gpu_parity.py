@@ -1183,10 +1183,12 @@ def test_empty_problems_are_no_ops():
 def test_graph_replay_matches_eager_beyond_the_path(cache):
     """The entry points beyond the five workloads captured in one HIP graph:
     the fused prepare + matvec, several matrices in one launch, the I8 matvec,
-    storeInt8 and the key dot, the Hadamard MLP and the sampler.  Every
-    replay, with eager fills and synchronizations between replays, equals the
-    eager result bitwise; the sampler's state is reset before each replay and
-    then holds the eager state after one draw."""
+    storeInt8 and the key dot, the Hadamard MLP, the sampler and the F8 matvec
+    with its fused argmax.  Every replay, with eager fills and
+    synchronizations between replays, equals the eager result bitwise; the
+    sampler's state is reset before each replay and then holds the eager
+    state after one draw; the argmax's workspace is filled with garbage
+    before each replay (nothing in it needs clearing)."""
     c4 = workload(cache, "cq4_16384x4096_b8")
     m4 = dev_matrix(c4)
     x1 = to_dev(c4.x[:1])
@@ -1201,6 +1203,11 @@ def test_graph_replay_matches_eager_beyond_the_path(cache):
     hm = synth.make_hmlp(512, 2048, seed=883)
     hn, d1, d2, d3, hr, hu = (to_dev(a) for a in (hm.n, hm.d1, hm.d2, hm.d3, hm.resid, hm.u))
     logits = to_dev(_logits("normal", 50000, 884))
+    fa = synth.make_f8(512, 4096, 4, 32, seed=885)
+    wa, sa, xa = dev_f8(fa)
+    aws = torch.empty(bqd.f8_matvec_argmax_workspace_bytes(1), dtype=torch.uint8, device=DEV)
+    ya = torch.empty(1, fa.R, device=DEV)
+    ta = torch.empty(1, dtype=torch.int32, device=DEV)
     seed = 0x1234567
     state = _state_tensor(seed)
     ws = torch.empty(bqd.logits_sample_workspace_bytes(50000, 16), dtype=torch.uint8, device=DEV)
@@ -1223,8 +1230,9 @@ def test_graph_replay_matches_eager_beyond_the_path(cache):
         bqd.kv_int8_dot(q, qs, xq, out=yk)
         bqd.hadamard_mlp(hn, 2048, d1, d2, d3, hr, hu, out=ho)
         sampled.append(bqd.logits_sample(logits, 16, 0.9, state, ws))
+        bqd.f8_matvec_argmax(wa, sa, xa, workspace=aws, out=ya, token=ta)
 
-    outs = lambda: [p1, y1, pm, *ym, yi, q, qs, yk, ho]
+    outs = lambda: [p1, y1, pm, *ym, yi, q, qs, yk, ho, ya, ta]
     work()
     torch.cuda.synchronize()
     ref = [t.clone() for t in outs()]
@@ -1243,6 +1251,7 @@ def test_graph_replay_matches_eager_beyond_the_path(cache):
     for _ in range(4):
         for t in outs() + list(draw):
             t.fill_(-1)
+        aws.fill_(0xA5)
         state.copy_(_state_tensor(seed))
         graph.replay()
         torch.cuda.synchronize()
