@@ -1,9 +1,9 @@
 /*
  * A plain C caller of the library (test infrastructure): it includes only
  * bqd.h and the HIP runtime API, reads raw inputs from a directory, runs
- * cq_prepare_matvec, cq_gather_rows, f8_matvec and logits_sample on a stream
- * of its own, and writes the outputs back to the directory for the test to
- * compare with the oracle.
+ * cq_prepare_matvec, cq_gather_rows, f8_matvec, logits_sample and
+ * f8_matvec_argmax on a stream of its own, and writes the outputs back to the
+ * directory for the test to compare with the oracle.
  *
  * usage: caller DIR
  * DIR/shape.txt: "R C Cp G BITS ROW_BYTES N_IDS FR FC SR SC NL K" (CQ matrix,
@@ -13,7 +13,7 @@
  * FR x FC), f8_s.bin (uint8 SR x SC), f8_x.bin (float FC), logits.bin (float NL),
  * state.bin (uint32).
  * Outputs: prepared.bin, y.bin, gathered.bin, f8_y.bin, token.bin, topk_ids.bin,
- * topk_logits.bin, state_out.bin.
+ * topk_logits.bin, state_out.bin, argmax_y.bin, argmax_token.bin.
  */
 #include <stdio.h>
 #include <stdlib.h>
@@ -126,6 +126,12 @@ int main(int argc, char **argv)
     const int64_t ws_bytes = logits_sample_workspace_bytes(NL, K);
     if (ws_bytes < 0) fail("logits_sample_workspace_bytes", bqd_status_string((int)ws_bytes));
     void *ws = device_zeros((size_t)ws_bytes);
+    float *ay = device_zeros((size_t)FR * 4);
+    int32_t *atok = device_zeros(4);
+    const int64_t aws_bytes = f8_matvec_argmax_workspace_bytes(1);
+    if (aws_bytes < 0)
+        fail("f8_matvec_argmax_workspace_bytes", bqd_status_string((int)aws_bytes));
+    void *aws = device_zeros((size_t)aws_bytes);
 
     hipStream_t s;
     HIP_OK(hipStreamCreate(&s));
@@ -135,6 +141,7 @@ int main(int argc, char **argv)
     /* top K of the logits and one draw at temperature 0.8 */
     BQD_OK_(logits_sample(logits, NL, K, 0.8f, state, ws, ws_bytes, token, topk_ids, topk_logits,
                           s));
+    BQD_OK_(f8_matvec_argmax(fw, FR, FC, fs, SR, SC, fx, ay, 1, aws, aws_bytes, atok, s));
     HIP_OK(hipStreamSynchronize(s));
 
     save_from_device("prepared.bin", prepared, (size_t)Cp * 4);
@@ -145,6 +152,8 @@ int main(int argc, char **argv)
     save_from_device("topk_ids.bin", topk_ids, (size_t)K * 4);
     save_from_device("topk_logits.bin", topk_logits, (size_t)K * 4);
     save_from_device("state_out.bin", state, 4);
+    save_from_device("argmax_y.bin", ay, (size_t)FR * 4);
+    save_from_device("argmax_token.bin", atok, 4);
     HIP_OK(hipStreamDestroy(s));
     printf("caller: ok\n");
     return 0;

@@ -5,8 +5,9 @@ program (tests/c_abi/caller.c, which includes only bqd.h and the HIP runtime
 API) builds and links against libbqd.so.
 GPU: that program, run as a child process on seeded inputs, returns what the
 oracle computes: the prepared vector, the gathered rows and the top-k bit for
-bit, the CQ and F8 matvecs within 1e-4 * sum|w*x| + 1e-6, and the sampled
-token and advanced state of the oracle's draw.
+bit, the CQ and F8 matvecs within 1e-4 * sum|w*x| + 1e-6, the sampled
+token and advanced state of the oracle's draw, and from f8_matvec_argmax the
+F8 matvec's y bit for bit with the first of its largest rows as the token.
 """
 import os
 import subprocess
@@ -68,7 +69,8 @@ def test_c_caller_matches_oracle(tmp_path):
              "f8_x.bin": f8.x[0], "logits.bin": logits, "state.bin": np.array([state0], np.uint32)}
     for name, a in files.items():
         np.ascontiguousarray(a).tofile(tmp_path / name)
-    print("[case] C caller: cq_prepare_matvec, cq_gather_rows, f8_matvec, logits_sample", flush=True)
+    print("[case] C caller: cq_prepare_matvec, cq_gather_rows, f8_matvec, logits_sample, "
+          "f8_matvec_argmax", flush=True)
     r = subprocess.run([str(exe), str(tmp_path)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     got = lambda name, dt: np.fromfile(tmp_path / name, dtype=dt)
@@ -88,3 +90,7 @@ def test_c_caller_matches_oracle(tmp_path):
     tok, s1 = oracle.sample(oval, oid, 0.8, state0)
     assert int(got("state_out.bin", np.uint32)[0]) == s1
     assert int(got("token.bin", np.int32)[0]) == tok
+    fy = got("f8_y.bin", np.float32)
+    assert not np.isnan(fy).any()
+    assert np.array_equal(got("argmax_y.bin", np.uint32), fy.view(np.uint32))
+    assert int(got("argmax_token.bin", np.int32)[0]) == int(np.argmax(fy))
