@@ -544,6 +544,44 @@ def pin_sample_degenerate_cases():
         assert s2 == oracle.xorshift32(s)
         assert tok == oracle.sample_u(vals, ids, 1.0, s2 / 2**32)
 
+def _xorshift_preimage(t):
+    """The state whose (13, 17, 5) xorshift step gives t: each step
+    s ^= s << a (or >> b) is undone by xoring in the shifted partial results
+    until the shift runs past 32 bits."""
+    mask = 0xFFFFFFFF
+
+    def undo_left(y, a):
+        x = y
+        for _ in range(32 // a + 1):
+            x = y ^ ((x << a) & mask)
+        return x
+
+    def undo_right(y, b):
+        x = y
+        for _ in range(32 // b + 1):
+            x = y ^ (x >> b)
+        return x
+
+    return undo_left(undo_right(undo_left(t, 5), 17), 13)
+
+
+def pin_sample_draw_scale():
+    """The draw is u = state / 2^32 exactly (R21), checked where it decides
+    the token: the state that steps to 2^31 gives u = 1/2; two candidates
+    1 and 1 - 2^-24 at T = 1000 weigh 1 and exp(-2^-24 / 1000), so the first
+    is drawn iff u < 1 / (1 + exp(-2^-24 / 1000)) = 1/2 + 1.49e-11.  Any
+    other scale of the state by ~2^-32 (say 1 / (2^32 - 1), which gives
+    1/2 + 1.16e-10) draws the second."""
+    pre = _xorshift_preimage(1 << 31)
+    vals = np.array([1.0, np.nextafter(np.float32(1), np.float32(0))], np.float32)
+    ids = np.array([5, 9], np.int32)
+    tok, state = oracle.sample(vals, ids, 1000.0, pre)
+    assert state == 1 << 31
+    assert tok == 5
+    # the boundary itself: just above 1/2 + 1.49e-11 the second candidate wins
+    assert oracle.sample_u(vals, ids, 1000.0, 0.5 + 3e-11) == 9
+
+
 def pin_sample_special_candidates():
     """O13 on special candidates: NaNs (which O12 sorts last) carry no weight,
     so over the u grid they are never drawn and the others keep their softmax
@@ -661,6 +699,26 @@ def pin_store_int8_floor_and_specials():
     assert math.isnan(sc) and not q.any()
     q, sc = oracle.store_int8(np.array([1.0, np.inf, -3.0], np.float32))
     assert math.isinf(sc) and not q.any()
+
+
+def pin_store_int8_divides_by_fp64_scale():
+    """Codes divide by the scale as a JavaScript number (fp64), not by the
+    fp32 value the scale array stores (R26).  With largest magnitude 1 the
+    fp64 scale is fl(1/127) and the stored one 3.7e-9 relatively smaller;
+    these two inputs put v / scale within 1e-9 of 79.5 and 95.5, on the lower
+    side for the fp64 scale and the upper side for the fp32 one, so the codes
+    (from exact rational quotients, far from fp64 rounding) are 79 and 95,
+    not 80 and 96."""
+    from fractions import Fraction
+    v = np.array([1.0, 0.625984251499176, 0.751968502998352, -0.625984251499176], np.float32)
+    s64 = Fraction(1.0 / 127.0)
+    s32 = Fraction(float(np.float32(1.0 / 127.0)))
+    for x, code in ((v[1], 79), (v[2], 95)):
+        assert math.floor(Fraction(float(x)) / s64 + Fraction(1, 2)) == code
+        assert math.floor(Fraction(float(x)) / s32 + Fraction(1, 2)) == code + 1
+    q, sc = oracle.store_int8(v)
+    assert q.tolist() == [127, 79, 95, -79]
+    assert sc == np.float32(1.0 / 127.0)
 
 
 # ------------------------------------------- scaled int8 dot (O16) --------

@@ -803,8 +803,12 @@ def test_kv_quantize_special_vectors():
     rows = [np.zeros(16), np.r_[127, 0.5, 1.5, 2.5, -2.5, -63.5, 63.5, -0.5, np.zeros(8)],
             np.r_[1.0, np.nan, -3.0, np.zeros(13)], np.r_[1.0, np.inf, -3.0, np.zeros(13)],
             np.r_[-np.inf, 2.0, np.zeros(14)], np.full(16, 3e-13), np.full(16, -1e30),
-            np.r_[-400.0, np.linspace(-1, 1, 15)]]
-    check_kv_quantize(np.stack(rows).astype(np.float32))
+            np.r_[-400.0, np.linspace(-1, 1, 15)],
+            # v / scale within 1e-9 of 79.5 and 95.5: the fp64 scale gives 79 and
+            # 95, the fp32 value the scale array stores would give 80 and 96
+            np.r_[1.0, 0.625984251499176, 0.751968502998352, -0.625984251499176, np.zeros(12)]]
+    q, _ = check_kv_quantize(np.stack(rows).astype(np.float32))
+    assert q[-1, :4].tolist() == [127, 79, 95, -79]
 
 
 @pytest.mark.parametrize("R,d,batch", [(4096, 128, 1), (300, 64, 2), (77, 100, 1), (40, 4096, 3), (5, 1, 1)])
@@ -1397,6 +1401,21 @@ def test_sample_zeros_and_nans_in_top_k(n, k):
         x[rng.choice(np.setdiff1d(np.arange(n), pos), 4, replace=False)] = nan_bits.view(np.float32)
     check_sample(x, k, 0.9, seed=4242 + n)
     check_sample(x, k, 0.0, seed=99 + n)
+
+
+def test_sample_draw_scale_decides():
+    """The draw is u = state / 2^32 exactly: state 0x88004000 steps to 2^31
+    (u = 1/2), and two logits 1 and 1 - 2^-24 at T = 1000 put the CDF
+    boundary at u = 1/2 + 1.49e-11, so the larger logit is drawn; a state
+    scaled by 1 / (2^32 - 1) would give 1/2 + 1.16e-10 and the other one."""
+    one, below = np.float32(1.0), np.nextafter(np.float32(1.0), np.float32(0.0))
+    for logits, want in (([one, below], 0), ([below, one], 1)):
+        state = _state_tensor(0x88004000)
+        tok, _, _ = bqd.logits_sample(to_dev(np.array(logits, np.float32)), 2, 1000.0, state)
+        assert int(state.cpu().numpy().view(np.uint32)[0]) == 1 << 31
+        assert int(tok.item()) == want
+        ref_ids, ref_vals = oracle.topk(np.array(logits, np.float32), 2)
+        assert oracle.sample(ref_vals, ref_ids, 1000.0, 0x88004000) == (want, 1 << 31)
 
 
 @pytest.mark.parametrize("k", range(30))

@@ -83,6 +83,7 @@ MUTANTS = {
         "    for (int64_t i = 0; i < k; i++) {\n"
         "        run += isnan(vals[i]) ? 0.0 : exp((double)vals[i] / temperature);"),
     "sample_cdf_off_by_one": ("if (target < run) return ids[i];", "if (target <= run) return ids[i > 0 ? i - 1 : 0];"),
+    "sample_u_over_2_32_minus_1": ("(double)*state / 4294967296.0", "(double)*state / 4294967295.0"),
     "i8_group_fixed_16": ("(double)oracle_e8m0(s[r * ns + c / G])", "(double)oracle_e8m0(s[r * ns + c / 16])"),
     "i8_scale_dropped": ("double term = (double)w[r * C + c] * (double)oracle_e8m0(s[r * ns + c / G]) *",
                          "double term = (double)w[r * C + c] * 1.0 *"),
@@ -90,6 +91,8 @@ MUTANTS = {
                        "q[i] = js_to_int8(round((double)v[i] / scale));"),
     "int8_signed_max": ("maximum = js_max(maximum, fabs((double)v[i]));", "maximum = js_max(maximum, (double)v[i]);"),
     "int8_scale_128": ("double scale = maximum / 127.0;", "double scale = maximum / 128.0;"),
+    "int8_divides_by_fp32_scale": ("double scale = maximum / 127.0;",
+                                   "double scale = (double)(float)(maximum / 127.0);"),
     "int8_no_floor": ("double maximum = 1e-12;", "double maximum = 0.0;"),
     "int8_dot_scale_dropped": ("if (y) y[i] = (double)scales[r] * acc;", "if (y) y[i] = acc;"),
     "hmlp_silu_sign": ("z[i] = (float)(t / (1.0 + exp(-t)));", "z[i] = (float)(t / (1.0 + exp(t)));"),
