@@ -364,6 +364,45 @@ def pin_dequantize_inverse_identity():
         assert np.allclose(back, D[r] * math.sqrt(16), rtol=0, atol=1e-5 * np.abs(D[r]).max())
 
 
+def pin_dense_matvec_accumulates_in_fp64():
+    """O7 sums dequantizeRow(r)[c] * x[c] as JavaScript numbers (fp64): against
+    numpy's fp64 dot of the same rows, the difference stays at fp64 rounding
+    (1e-12 of sum |row * x|), where an fp32 sum would be ~1e-7 off."""
+    for case in small_cases():
+        m = oracle.CqMatrix.from_case(case)
+        x = case.x[0]
+        rows = np.stack([oracle.cq_dequantize_row(m, r) for r in range(case.shape.output)])
+        ref = rows.astype(np.float64) @ x.astype(np.float64)
+        bound = np.abs(rows.astype(np.float64)) @ np.abs(x.astype(np.float64))
+        y7 = oracle.cq_dense_matvec(m, x)
+        assert np.all(np.abs(y7 - ref) <= 1e-12 * bound), case.shape
+
+
+def pin_dequantize_scale_rounds_from_fp64():
+    """The row gather scales by 1/sqrt(g) as the prepare does (R9): an fp64
+    product stored to fp32.  Worked in rationals for g = 128: a row whose only
+    nonzero weight is v at column 0 (norm 1) transforms to v in every column,
+    so every gathered value is v's scaled value; the v are ones where an fp32
+    product rounds otherwise."""
+    g = 128
+    s64 = 1.0 / math.sqrt(float(g))
+    packed = np.zeros((1, g // 2), np.uint8)
+    packed[0, 0] = 0x01  # column 0: index 1; every other column: index 0
+    norms = np.array([[0x3C00]], np.uint16)  # fp16 1.0
+    differs = 0
+    for bits in (0x3F800001, 0x3F800006, 0x3F800008, 0x40490FDB, 0x3DCCCCCD, 0x4479C000):
+        v = np.array([bits], np.uint32).view(np.float32)[0]
+        cb = np.zeros(16, np.float32)
+        cb[1] = v
+        m = oracle.CqMatrix(1, g, g, g, 4, g // 2, packed, norms, cb)
+        want = np.float32(float(_round_significand(_round_significand(
+            Fraction(float(v)) * Fraction(s64), 53), 24)))
+        row, _ = oracle.cq_gather(m, np.array([0], np.int32))
+        assert np.array_equal(row[0].view(np.uint32), np.full(g, want).view(np.uint32)), hex(bits)
+        differs += np.float32(v) * np.float32(s64) != want
+    assert differs >= 3
+
+
 def pin_gather():
     case = synth.make_cq(synth.CqShape(11, 100, 128, 32, 5), seed=13, n_ids=9)
     ids = np.concatenate([case.ids, case.ids[:2]])  # duplicates give equal rows
@@ -826,6 +865,65 @@ def pin_hadamard_mlp_matrix_form():
         s_ = t / (1 + np.exp(-t))
         ref = resid + (d3 * (Hn @ s_))[:hidden] - u
         assert np.all(np.abs(out - ref) <= 1e-5 * mag + 1e-6), (hidden, H, np.abs(out - ref).max())
+
+
+def _near_fp32_midpoint(fr: Fraction, rel=Fraction(1, 10 ** 14)) -> bool:
+    """True if a positive rational lies within rel of a point halfway between
+    two fp32 values, where an fp64 intermediate could round either way."""
+    r = _round_significand(fr, 25)  # the nearest 25-bit value: fp32 points and midpoints
+    return abs(fr - r) <= rel * fr and r != _round_significand(fr, 24)
+
+
+def pin_hadamard_mlp_silu_fp64():
+    """silu(t) = t / (1 + exp(-t)) is formed as a JavaScript number (fp64) and
+    stored to fp32 (R29).  With H = hidden = 1 and d1 = d3 = 1, resid = 0 the
+    MLP's output is that stored value for t = d2 * n (exact in fp64), so it
+    must equal the exact silu, taken to 40 digits with the decimal module,
+    rounded to fp32 (inputs whose exact value lies within 1e-14 of an fp32
+    rounding midpoint are skipped: there fp64 may round either way).  An fp32
+    silu differs on many of them."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 40
+    rng = np.random.default_rng(38)
+    ones, zero = np.ones(1, np.float32), np.zeros(1, np.float32)
+    checked = differs = 0
+    for n, d2 in zip(rng.uniform(-6, 6, 300).astype(np.float32), rng.uniform(0.25, 2, 300).astype(np.float32)):
+        t = Fraction(float(n)) * Fraction(float(d2))
+        dt = Decimal(t.numerator) / Decimal(t.denominator)
+        exact = Fraction(dt / (1 + (-dt).exp()))
+        if exact == 0 or _near_fp32_midpoint(abs(exact)):
+            continue
+        mag = _round_significand(abs(exact), 24)
+        want = np.float32(float(mag if exact > 0 else -mag))
+        out, _ = oracle.hadamard_mlp(np.array([n], np.float32), 1, ones, np.array([d2], np.float32),
+                                     ones, zero)
+        assert out[0] == want and out.view(np.uint32)[0] == np.array([want]).view(np.uint32)[0], (n, d2)
+        t32 = np.float32(n) * np.float32(d2)
+        differs += (t32 / (np.float32(1) + np.exp(-t32))) != want
+        checked += 1
+    assert checked >= 290 and differs >= 10, (checked, differs)
+
+
+def pin_hadamard_mlp_scale_rounds_from_fp64():
+    """normalizedFwht multiplies by 1/sqrt(H) in fp64 and stores to fp32
+    (R29), in both transforms.  H = 2, hidden = 1, d1 = 1, d2 = 2^40 (silu(t)
+    = t exactly once t > 40), d3 = 2^-40, resid = 0: the first transform of
+    [x, 0] is [x, x], scaled to v = fl32(fl64(x s)); the second of [2^40 v,
+    2^40 v] is [2^41 v, 0], scaled and brought back by 2^-40, so the output is
+    fl32(fl64(2 v s)), worked in rationals.  An fp32 product rounds otherwise
+    on some of these x."""
+    s64 = 1.0 / math.sqrt(2.0)
+    d1, d2, d3 = (np.full(2, v, np.float32) for v in (1.0, 2.0 ** 40, 2.0 ** -40))
+    rng = np.random.default_rng(39)
+    differs = 0
+    for x in rng.uniform(0.01, 100.0, 200).astype(np.float32):
+        v = _round_significand(_round_significand(Fraction(float(x)) * Fraction(s64), 53), 24)
+        want = np.float32(float(_round_significand(_round_significand(2 * v * Fraction(s64), 53), 24)))
+        out, _ = oracle.hadamard_mlp(np.array([x], np.float32), 2, d1, d2, d3, np.zeros(1, np.float32))
+        assert out.view(np.uint32)[0] == np.array([want]).view(np.uint32)[0], x
+        v32 = np.float32(x) * np.float32(s64)
+        differs += np.float32(2 * v32) * np.float32(s64) != want
+    assert differs >= 5, differs
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -95,6 +95,14 @@ MUTANTS = {
                                    "double scale = (double)(float)(maximum / 127.0);"),
     "int8_no_floor": ("double maximum = 1e-12;", "double maximum = 0.0;"),
     "int8_dot_scale_dropped": ("if (y) y[i] = (double)scales[r] * acc;", "if (y) y[i] = acc;"),
+    "dense_sum_in_fp32": ("        double acc = 0.0;\n        for (int64_t c = 0; c < m->input; c++) acc +=",
+                          "        float acc = 0.0f;\n        for (int64_t c = 0; c < m->input; c++) acc +="),
+    "gather_scale_in_fp32": (
+        "for (int64_t k = 0; k < m->group; k++) tg[k] = scale_store(tg[k], m->group);\n    }\n    memcpy",
+        "for (int64_t k = 0; k < m->group; k++) tg[k] = tg[k] * (float)(1.0 / sqrt((double)m->group));\n    }\n    memcpy"),
+    "hmlp_silu_in_fp32": ("z[i] = (float)(t / (1.0 + exp(-t)));", "z[i] = (float)t / (1.0f + expf(-(float)t));"),
+    "hmlp_scale_in_fp32": ("for (int64_t i = 0; i < H; i++) z[i] = (float)((double)z[i] * scale);",
+                           "for (int64_t i = 0; i < H; i++) z[i] = z[i] * (float)scale;"),
     "hmlp_silu_sign": ("z[i] = (float)(t / (1.0 + exp(-t)));", "z[i] = (float)(t / (1.0 + exp(t)));"),
     "hmlp_pad_ones": ("z[i] = i < hidden ? n[i] : 0.0f;", "z[i] = i < hidden ? n[i] : 1.0f;"),
     "hmlp_no_d3": ("z[i] = (float)((double)z[i] * (double)d3[i]);", ""),
