@@ -867,6 +867,21 @@ def pin_hadamard_mlp_matrix_form():
         assert np.all(np.abs(out - ref) <= 1e-5 * mag + 1e-6), (hidden, H, np.abs(out - ref).max())
 
 
+def pin_hadamard_mlp_update_rounds_block_first():
+    """The block output is stored (fp32) before the update subtracts u (R29:
+    every array store rounds).  H = hidden = 1, n = 1.5, d2 = 64 (t = 96, and
+    silu(96) = 96 in fp64), d3 = 2^-31 make z = 3 * 2^-26 exactly; resid = 1
+    stores the block as 1 (3/8 of an ulp is dropped), and u = -59 * 2^-26
+    gives 1 + 59 * 2^-26 = 1 + 7.375 ulp -> 1 + 7 * 2^-23.  One rounding of
+    resid + z - u (1 + 7.75 ulp) would give 1 + 2^-20."""
+    one = np.ones(1, np.float32)
+    f = lambda v: np.array([v], np.float32)
+    out, _ = oracle.hadamard_mlp(f(1.5), 1, one, f(64.0), f(2.0 ** -31), f(1.0), f(-59 * 2.0 ** -26))
+    assert out[0] == np.float32(1 + 7 * 2.0 ** -23), float(out[0])
+    block, _ = oracle.hadamard_mlp(f(1.5), 1, one, f(64.0), f(2.0 ** -31), f(1.0))
+    assert block[0] == np.float32(1.0)
+
+
 def _near_fp32_midpoint(fr: Fraction, rel=Fraction(1, 10 ** 14)) -> bool:
     """True if a positive rational lies within rel of a point halfway between
     two fp32 values, where an fp64 intermediate could round either way."""

@@ -896,6 +896,30 @@ def test_hadamard_mlp_exact_closed_form():
     assert bits_eq(got, ref)
 
 
+def test_hadamard_mlp_update_rounds_block_first():
+    """The pin's construction on the GPU: the block output 1 + 3 * 2^-26 is
+    stored as 1 before u = -59 * 2^-26 is subtracted, so the update is
+    1 + 7 * 2^-23 (one rounding of the whole sum would give 1 + 2^-20)."""
+    f = lambda v: to_dev(np.array([v], np.float32))
+    one = f(1.0)
+    got = bqd.hadamard_mlp(to_dev(np.array([[1.5]], np.float32)), 1, one, f(64.0), f(2.0 ** -31),
+                           to_dev(np.array([[1.0]], np.float32)), to_dev(np.array([[-59 * 2.0 ** -26]], np.float32)))
+    assert got.cpu().numpy()[0, 0] == np.float32(1 + 7 * 2.0 ** -23)
+
+
+def test_hadamard_mlp_scale_rounds_from_fp64():
+    """The pin's H = 2 construction on the GPU, 200 inputs at once: the output
+    is fl32(fl64(2 v / sqrt 2)) with v = fl32(fl64(x / sqrt 2)), so both
+    transforms' scales are fp64 products stored to fp32; bit-identical to the
+    oracle (pinned to rationals on the same construction)."""
+    x = np.random.default_rng(39).uniform(0.01, 100.0, (200, 1)).astype(np.float32)
+    d1, d2, d3 = (np.full(2, v, np.float32) for v in (1.0, 2.0 ** 40, 2.0 ** -40))
+    resid = np.zeros((200, 1), np.float32)
+    got = bqd.hadamard_mlp(to_dev(x), 2, to_dev(d1), to_dev(d2), to_dev(d3), to_dev(resid)).cpu().numpy()
+    ref = np.stack([oracle.hadamard_mlp(x[b], 2, d1, d2, d3, resid[b])[0] for b in range(200)])
+    assert bits_eq(got, ref)
+
+
 # Buffers past 2 GiB: every byte offset the kernels form is 64-bit.  Weights
 # of more than 2^31 bytes (F8, I8, and CQ4 at batch 1 and 8 plus its row
 # gather), a row range that starts past the mark, and a gather whose output

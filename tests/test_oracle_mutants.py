@@ -103,6 +103,8 @@ MUTANTS = {
     "hmlp_silu_in_fp32": ("z[i] = (float)(t / (1.0 + exp(-t)));", "z[i] = (float)t / (1.0f + expf(-(float)t));"),
     "hmlp_scale_in_fp32": ("for (int64_t i = 0; i < H; i++) z[i] = (float)((double)z[i] * scale);",
                            "for (int64_t i = 0; i < H; i++) z[i] = z[i] * (float)scale;"),
+    "hmlp_update_one_rounding": ("out[i] = u ? (float)((double)block - (double)u[i]) : block;",
+                                 "out[i] = u ? (float)((double)resid[i] + (double)z[i] - (double)u[i]) : block;"),
     "hmlp_silu_sign": ("z[i] = (float)(t / (1.0 + exp(-t)));", "z[i] = (float)(t / (1.0 + exp(t)));"),
     "hmlp_pad_ones": ("z[i] = i < hidden ? n[i] : 0.0f;", "z[i] = i < hidden ? n[i] : 1.0f;"),
     "hmlp_no_d3": ("z[i] = (float)((double)z[i] * (double)d3[i]);", ""),
