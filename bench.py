@@ -214,6 +214,19 @@ def build_cases(torch, bqd, synth, hot, heads=True):
                            [lambda w=w: bqd.f8_matvec_argmax(w, sh, xh, workspace=aws, out=ya,
                                                              token=tok)
                             for w in whs], head_bytes + 4, hd.R))
+        # the head with top-k (k = 64) / temperature sampling fused onto its
+        # pass, and the same work unfused (the head, then logits_sample)
+        sst = torch.tensor([12345], dtype=torch.int32, device=dev)
+        sws = torch.empty(bqd.logits_sample_workspace_bytes(hd.R, 64), dtype=torch.uint8,
+                          device=dev)
+        extras.append(Case("f8_head_246272x4096_matvec_sample_k64",
+                           [lambda w=w: bqd.f8_matvec_sample(w, sh, xh, 64, 0.8, sst,
+                                                             workspace=aws, out=ya)
+                            for w in whs], head_bytes + 4 + 8 * 64, hd.R))
+        extras.append(Case("f8_head_246272x4096_matvec_then_logits_sample_k64",
+                           [lambda w=w: (bqd.f8_matvec(w, sh, xh, out=ya),
+                                         bqd.logits_sample(ya.reshape(-1), 64, 0.8, sst, sws))
+                            for w in whs], head_bytes + 4 + 8 * 64, hd.R))
         # -- beyond the step: the I8 head (E8M0 scales per 16 columns) and the
         # int8 key cache (quantize 4096 vectors of 128, score one query)
         log("generating I8 head 246272x4096 G16 (seed 5)")
@@ -455,6 +468,24 @@ def self_check(data, bqd, state):
     r_t, ok_t = head_row(t)
     res["f8_head_argmax"] = dict(token=t, max_ratio=round(float(r_t), 6),
                                  ok=bool(bits_eq(yan, yh) and t == t_host and r_t <= 1.0))
+    # the head with top-k sampling fused: y bit-equal to the head's; the ids
+    # those of that y's 64 best, and ids, values, token and state equal to
+    # logits_sample's on that y; each selected logit against the oracle
+    st1 = torch.tensor([777], dtype=torch.int32, device=state.device)
+    st2 = st1.clone()
+    ys, tks, sids, svals = bqd.f8_matvec_sample(w0, s0, x0, 64, 0.8, st1)
+    tk2, ids2, vals2 = bqd.logits_sample(ys.reshape(-1), 64, 0.8, st2)
+    ysn, sidn = ys.cpu().numpy()[0], sids.cpu().numpy()[0]
+    nan = np.isnan(ysn.astype(np.float64))
+    want = np.lexsort((np.arange(ysn.size), -np.where(nan, 0.0, ysn.astype(np.float64)), nan))[:64]
+    r_s = max(head_row(int(r))[0] for r in sidn)
+    res["f8_head_sample_k64"] = dict(
+        token=int(tks.item()), max_ratio=round(float(r_s), 6),
+        ok=bool(bits_eq(ysn, yh) and np.array_equal(sidn, want) and
+                np.array_equal(sidn, ids2.cpu().numpy()) and
+                bits_eq(svals.cpu().numpy()[0], vals2.cpu().numpy()) and
+                int(tks.item()) == int(tk2.item()) and int(st1.item()) == int(st2.item()) and
+                r_s <= 1.0))
     for name, (case, p_dev, y_dev) in data["small"].items():
         y = y_dev.cpu().numpy()[0]
         if name.startswith("f8"):
@@ -751,6 +782,12 @@ def main():
             per_case[c.name] = dict(rec, timing="16 back-to-back launches per graph replay")
         elif c.name.startswith("cq4_3x"):
             extras[c.name] = dict(rec, note="not part of the step: several matrices on one activation")
+        elif c.name.endswith("_sample_k64"):
+            extras[c.name] = dict(rec, note="not part of the step: the head with top-k (k = 64, "
+                                            "T = 0.8) sampling of its logits" + (
+                                                " fused onto the pass (f8_matvec_sample)"
+                                                if "then" not in c.name else
+                                                ", unfused: f8_matvec, then logits_sample"))
         elif c.name.endswith("_argmax"):
             extras[c.name] = dict(rec, note="not part of the step: the head with its greedy token "
                                             "(argmax) fused into the pass, plus the one-workgroup "

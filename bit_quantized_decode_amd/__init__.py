@@ -44,7 +44,7 @@ LIB_PATH = os.path.join(_HERE, "libbqd.so")
 # Every symbol include/bqd.h declares.
 EXPORTS = ("cq_prepare", "cq_matvec", "cq_prepare_matvec", "cq_matvec_multi",
            "cq_prepare_matvec_multi", "cq_gather_rows", "f8_matvec", "f8_matvec_argmax",
-           "f8_matvec_argmax_workspace_bytes",
+           "f8_matvec_argmax_workspace_bytes", "f8_matvec_sample",
            "i8_matvec", "kv_quantize_int8", "kv_int8_dot", "hadamard_mlp", "logits_sample",
            "logits_sample_workspace_bytes", "logits_sample_noalloc", "bqd_dbg_cq_unpack", "bqd_dbg_f16_decode",
            "bqd_dbg_f8_decode", "bqd_dbg_e8m0_decode", "bqd_dbg_read_stream",
@@ -88,6 +88,8 @@ def lib():
                 ("cq_gather_rows", [S, P, I64, P, P]),
                 ("f8_matvec", [P, I64, I64, P, I64, I64, P, P, I64, P]),
                 ("f8_matvec_argmax", [P, I64, I64, P, I64, I64, P, P, I64, P, I64, P, P]),
+                ("f8_matvec_sample", [P, I64, I64, P, I64, I64, P, P, I64, I64, ctypes.c_float,
+                                      P, P, I64, P, P, P, P]),
                 ("i8_matvec", [P, I64, I64, P, I64, P, P, I64, P]),
                 ("kv_quantize_int8", [P, I64, I64, P, P, P]),
                 ("kv_int8_dot", [P, P, I64, I64, P, P, I64, P]),
@@ -346,6 +348,41 @@ def f8_matvec_argmax(w: torch.Tensor, scale: torch.Tensor, x: torch.Tensor,
     _call("f8_matvec_argmax", _ptr(w), R, C, _ptr(scale), SR, SC, _ptr(x), _ptr(out), batch,
           _ptr(workspace), workspace.numel(), _ptr(token), _stream(x, stream))
     return out, token
+
+
+def f8_matvec_sample(w: torch.Tensor, scale: torch.Tensor, x: torch.Tensor, k: int,
+                     temperature: float, state: torch.Tensor, workspace: torch.Tensor = None,
+                     out: torch.Tensor = None, stream=None):
+    """f8_matvec with top-k / temperature sampling of each vector's outputs
+    fused onto the pass.  state: int32 or uint32 [batch] on the GPU (the
+    xorshift32 states), advanced in place.  Returns (y float32 [batch][R],
+    token int32 [batch], topk_ids int32 [batch][k], topk_logits float32
+    [batch][k]); workspace as f8_matvec_argmax's (allocated if None)."""
+    w = _dev(w, torch.uint8, "w")
+    scale = _dev(scale, torch.uint8, "scale")
+    x = _dev(x, torch.float32, "x")
+    state = _dev(state, (torch.int32, torch.uint32), "state")
+    R, C = w.shape
+    SR, SC = scale.shape
+    if x.shape[-1] != C:
+        raise ValueError("x must have C columns")
+    batch = x.numel() // C
+    if state.numel() != batch:
+        raise ValueError("state needs one element per vector")
+    out = torch.empty(x.shape[:-1] + (R,), dtype=torch.float32, device=x.device) if out is None \
+        else _dev(out, torch.float32, "out")
+    if out.numel() != batch * R:
+        raise ValueError("out has the wrong size")
+    need = f8_matvec_argmax_workspace_bytes(batch)
+    workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if workspace is None else \
+        _dev(workspace, torch.uint8, "workspace")
+    token = torch.empty(batch, dtype=torch.int32, device=x.device)
+    ids = torch.empty((batch, k), dtype=torch.int32, device=x.device)
+    vals = torch.empty((batch, k), dtype=torch.float32, device=x.device)
+    _call("f8_matvec_sample", _ptr(w), R, C, _ptr(scale), SR, SC, _ptr(x), _ptr(out), batch,
+          int(k), float(temperature), _ptr(state), _ptr(workspace), workspace.numel(),
+          _ptr(token), _ptr(ids), _ptr(vals), _stream(x, stream))
+    return out, token, ids, vals
 
 
 def i8_matvec(w: torch.Tensor, scale: torch.Tensor, x: torch.Tensor, G: int = 16,

@@ -81,6 +81,18 @@ int f8_matvec_argmax(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scal
                                  as_stream(stream));
 }
 
+int f8_matvec_sample(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
+                     int64_t SC, const float* x, float* y, int64_t batch, int64_t k,
+                     float temperature, uint32_t* state, void* workspace,
+                     int64_t workspace_bytes, int32_t* token, int32_t* topk_ids,
+                     float* topk_logits, void* stream) {
+  int rc = check_f8_sample(w, R, C, scale, SR, SC, x, y, batch, k, temperature, state, workspace,
+                           workspace_bytes, token, topk_ids, topk_logits);
+  if (rc || batch == 0) return rc;
+  return launch_f8_matvec_sample(w, R, C, scale, SR, SC, x, y, batch, k, temperature, state,
+                                 workspace, token, topk_ids, topk_logits, as_stream(stream));
+}
+
 int i8_matvec(const int8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t G,
               const float* x, float* y, int64_t batch, void* stream) {
   int rc = check_i8(w, R, C, scale, G, x, y, batch);

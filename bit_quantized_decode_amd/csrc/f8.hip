@@ -85,8 +85,8 @@ __device__ __forceinline__ uint64_t block_max_key(uint64_t k) {
 // one copy of x per workgroup from L2 instead of one per wavefront (~1%).
 //
 // ARGMAX fuses the argmax of y: each lane keeps the largest key (logit_key.h)
-// of the rows it stores; each wavefront puts the largest of its lanes' in
-// LDS and takes a ticket from an LDS counter, and the wavefront with the
+// of the rows it stores; each wavefront reads the largest of its storing
+// lanes' into LDS and takes a ticket from an LDS counter, and the wavefront with the
 // last ticket stores the workgroup's largest to its slot, slots[blockIdx]
 // (plain stores).  No wavefront waits for another: a workgroup barrier there
 // held three wavefronts at every workgroup's end, and an atomic per
@@ -176,11 +176,16 @@ void f8_matvec_fast(
     }
   }
   if constexpr (ARGMAX) {
+    // only lanes q == LPR - 1 store rows: the wavefront's largest key is read
+    // from those lanes directly (no exchange network at every workgroup's end)
+    const uint32_t lo = (uint32_t)best, hi = (uint32_t)(best >> 32);
+    uint64_t wbest = 0;
 #pragma unroll
-    for (int d = 1; d < kWave; d <<= 1)
-      best = max(best, (uint64_t)__shfl_xor((unsigned long long)best, d));
+    for (int ln = LPR - 1; ln < kWave; ln += LPR)
+      wbest = max(wbest, ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, ln) << 32) |
+                             (uint32_t)__builtin_amdgcn_readlane(lo, ln));
     if ((tid & (kWave - 1)) == 0) {
-      wave_best[tid / kWave] = best;
+      wave_best[tid / kWave] = wbest;
       __threadfence_block();  // the value before the ticket
       if (atomicAdd(&tickets, 1u) == kF8Threads / kWave - 1) {
         __threadfence_block();  // every other wavefront's value after its ticket
@@ -367,6 +372,54 @@ int launch_f8_matvec_argmax(const uint8_t* w, int64_t R, int64_t C, const uint8_
   hipLaunchKernelGGL(argmax_finish, dim3((unsigned)batch), dim3(kFinishThreads), 0, s, slots,
                      n_slots, token);
   return launch_status();
+}
+
+// The head's pass with its slots, then top-k / temperature sampling from
+// them (one workgroup per vector reads only the rows of the k groups that can
+// hold a top-k logit).  The group of each slot is described to the sampler:
+// the streaming kernel's workgroup w stores rows w L + t (grid L) + i for
+// i < L = U (threads / LPR); the generic path's slot g covers rows
+// [g chunk, (g + 1) chunk).
+int launch_f8_matvec_sample(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale,
+                            int64_t SR, int64_t SC, const float* x, float* y, int64_t batch,
+                            int64_t k, float temperature, uint32_t* state, void* workspace,
+                            int32_t* token, int32_t* topk_ids, float* topk_logits,
+                            hipStream_t s) {
+  uint64_t* slots = static_cast<uint64_t*>(workspace);
+  const F8Shape f = f8_fast_shape(w, C, SC, x);
+  int rc = run_f8(w, R, C, scale, SR, SC, x, y, batch, f, f.lpr ? slots : nullptr, s);
+  if (rc) return rc;
+  SlotRowsHost h{};
+  h.R = R;
+  if (f.lpr) {
+    constexpr int64_t U = 2;
+    const int64_t per_step = kF8Threads / f.lpr;
+    const int64_t n_steps = (R + per_step - 1) / per_step;
+    const int64_t grid = fast_grid(R, f.lpr);
+    const int64_t L = U * per_step;  // a power of two
+    const int64_t runs = (n_steps + grid * U - 1) / (grid * U);
+    h.n_slots = h.G = grid;
+    h.gstride = L;
+    h.log2_L = ilog2(L);
+    h.l_valid = L;
+    h.S = grid * L;
+    h.rows_pg = L * runs;
+    h.log2_pg = ceil_log2(h.rows_pg);
+  } else {
+    const int64_t n_slots = std::min<int64_t>(kMaxGrid, (R + kF8Threads - 1) / kF8Threads);
+    const int64_t chunk = (R + n_slots - 1) / n_slots;
+    hipLaunchKernelGGL(argmax_slots_from_y, dim3((unsigned)n_slots), dim3(kF8Threads), 0, s, y,
+                       R, batch, chunk, slots);
+    if ((rc = launch_status())) return rc;
+    h.n_slots = h.G = n_slots;
+    h.gstride = chunk;
+    h.log2_pg = h.log2_L = ceil_log2(chunk);
+    h.l_valid = chunk;
+    h.S = 0;
+    h.rows_pg = chunk;
+  }
+  return launch_slots_sample(y, slots, h, batch, k, temperature, state, token, topk_ids,
+                             topk_logits, s);
 }
 
 // ------------------------------------------------------------ decode probes

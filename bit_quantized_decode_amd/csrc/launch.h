@@ -42,6 +42,28 @@ int launch_logits_sample(const float* logits, int64_t n, int64_t k, float temper
                          uint32_t* state, void* workspace, int32_t* token, int32_t* topk_ids,
                          float* topk_logits, hipStream_t s);
 
+// The rows of each per-workgroup slot a matvec leaves for the fused sampling
+// (sample.hip): group g owns rows g gstride + t S + i (t >= 0, i < l_valid,
+// i < 2^log2_L, t 2^log2_L + i < rows_pg <= 2^log2_pg), below R; row r is in
+// group (r / gstride) % G.
+struct SlotRowsHost {
+  int64_t R, n_slots, G, gstride;
+  int log2_L;
+  int64_t l_valid, S;
+  int log2_pg;
+  int64_t rows_pg;
+};
+// Top-k / temperature sampling of each vector's logits [batch][R] from the
+// slots (8192 per vector) of the matvec that wrote them.
+int launch_slots_sample(const float* logits, const uint64_t* slots, const SlotRowsHost& h,
+                        int64_t batch, int64_t k, float temperature, uint32_t* state,
+                        int32_t* token, int32_t* topk_ids, float* topk_logits, hipStream_t s);
+int launch_f8_matvec_sample(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale,
+                            int64_t SR, int64_t SC, const float* x, float* y, int64_t batch,
+                            int64_t k, float temperature, uint32_t* state, void* workspace,
+                            int32_t* token, int32_t* topk_ids, float* topk_logits,
+                            hipStream_t s);
+
 // The allocation-free sampler's device scratch: its size, and its address on
 // the device of stream s (looked up once per device).
 int64_t sample_scratch_bytes();
@@ -61,6 +83,13 @@ inline bool is_aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a -
 inline int ilog2(int64_t v) {
   int r = 0;
   while ((int64_t(1) << (r + 1)) <= v) ++r;
+  return r;
+}
+
+// The smallest r with 2^r >= v (v >= 1).
+inline int ceil_log2(int64_t v) {
+  int r = 0;
+  while ((int64_t(1) << r) < v) ++r;
   return r;
 }
 

@@ -211,6 +211,83 @@ __device__ __forceinline__ int block_rank(const uint64_t* keys, int m, int (*par
   return t < m ? part[0][t] + part[1][t] + part[2][t] + part[3][t] : 0;
 }
 
+// The draw, by one wavefront alone: lane t holds `key`, candidate t of the
+// first k keys (descending; any value on lanes t >= k); the draw stays in
+// registers.  Writes the k ids and values, the token and the advanced
+// generator state.
+__device__ void draw_from_key(uint64_t key, int k, float temperature, uint32_t state_in,
+                              const float* __restrict__ logits, uint32_t* __restrict__ state,
+                              int32_t* __restrict__ token, int32_t* __restrict__ topk_ids,
+                              float* __restrict__ topk_vals) {
+  const int t = threadIdx.x & 63;
+  key = t < k ? key : 0;
+  const int32_t id = (int32_t)(0xffffffffu - (uint32_t)key);
+  const float v = t < k ? key_logit(key, logits) : 0.0f;
+  if (t < k) {
+    topk_ids[t] = id;
+    topk_vals[t] = v;
+  }
+  const float top0 = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(v)));
+  const bool draw = temperature > 0.0f && k > 1 && isfinite(top0);
+  // one xorshift step (13, 17, 5), u = state / 2^32
+  uint32_t s = __builtin_amdgcn_readfirstlane(state_in);
+  s ^= s << 13;
+  s ^= s >> 17;
+  s ^= s << 5;
+  int32_t tok = __builtin_amdgcn_readfirstlane(id);
+  if (draw) {
+    // the softmax weights in fp64, one per lane (NaN values and lanes past k
+    // weigh 0); every sum below is formed as one fp64 add on the previous one
+    const double w = (t < k && v == v) ? exp(((double)v - (double)top0) / (double)temperature)
+                                       : 0.0;
+    // S: the weights added in list order, every lane the same chain, reading
+    // them back from LDS as broadcasts (the same wavefront's writes, in
+    // order), eight requested ahead
+    __shared__ double wsh[64];
+    wsh[t] = w;
+    __builtin_amdgcn_wave_barrier();
+    double S = 0.0;
+    int j = 0;
+    for (; j + 8 <= k; j += 8) {
+      double wj[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) wj[q] = wsh[j + q];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) S += wj[q];
+    }
+    for (; j < k; ++j) S += wsh[j];  // lanes past k weigh 0: the sum is unchanged
+    // the token: the first candidate whose running sum (the same additions
+    // again) exceeds u * S, else the last one
+    const double target = ((double)s / 4294967296.0) * S;
+    double run = 0.0;
+    int pick = k - 1;
+    for (j = 0; j < k; ++j) {
+      run += wsh[j];
+      if (__builtin_amdgcn_readfirstlane(run > target ? 1 : 0)) {
+        pick = j;
+        break;
+      }
+    }
+    tok = __builtin_amdgcn_readlane(id, pick);
+  }
+  if (t == 0) {
+    *state = s;
+    *token = tok;
+  }
+}
+
+// draw_from_key with the keys in LDS: top[0 .. k), descending.
+__device__ __forceinline__ void draw_from_top(const uint64_t* top, int k, float temperature,
+                                              uint32_t state_in, const float* __restrict__ logits,
+                                              uint32_t* __restrict__ state,
+                                              int32_t* __restrict__ token,
+                                              int32_t* __restrict__ topk_ids,
+                                              float* __restrict__ topk_vals) {
+  const int t = threadIdx.x & 63;
+  draw_from_key(t < k ? top[t] : 0, k, temperature, state_in, logits, state, token, topk_ids,
+                topk_vals);
+}
+
 // Stage 2 (one block): the blocks' lists (k keys each, padded to 64) merged,
 // the first k kept, then the draw.  `lists` is the workgroup's LDS buffer of
 // kMaxCandidates keys.
@@ -311,49 +388,8 @@ __device__ void select_and_draw(const float* __restrict__ logits, const uint64_t
     block_merge_lists(lists, n_lists);
   }
   if (wave != 0) return;
-  // Wavefront 0: lane t holds candidate t (t < k); the draw stays in registers.
-  const uint64_t key = t < k ? lists[top_at + t] : 0;
-  const int32_t id = (int32_t)(0xffffffffu - (uint32_t)key);
-  const float v = t < k ? key_logit(key, logits) : 0.0f;
-  if (t < k) {
-    topk_ids[t] = id;
-    topk_vals[t] = v;
-  }
-  const float top = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(v)));
-  const bool draw = temperature > 0.0f && k > 1 && isfinite(top);
-  // one xorshift step (13, 17, 5), u = state / 2^32
-  uint32_t s = __builtin_amdgcn_readfirstlane(state_in);
-  s ^= s << 13;
-  s ^= s >> 17;
-  s ^= s << 5;
-  int32_t tok = __builtin_amdgcn_readfirstlane(id);
-  if (draw) {
-    // the softmax weights in fp64, one per lane (NaN values and lanes past k
-    // weigh 0), then the running sums in list order: lane j receives
-    // w_0 + ... + w_j, each sum formed as one fp64 add on the previous one
-    const double w = (t < k && v == v) ? exp(((double)v - (double)top) / (double)temperature)
-                                       : 0.0;
-    const uint64_t wb = __builtin_bit_cast(uint64_t, w);
-    const uint32_t wlo = (uint32_t)wb, whi = (uint32_t)(wb >> 32);
-    double run = 0.0, mine = 0.0;
-#pragma unroll
-    for (int j = 0; j < 64; ++j) {
-      const uint64_t bj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(whi, j) << 32) |
-                          (uint32_t)__builtin_amdgcn_readlane(wlo, j);
-      run += __builtin_bit_cast(double, bj);
-      if (t == j) mine = run;
-    }
-    // S = run (the zeros past k leave it unchanged); the token is the first
-    // candidate whose running sum exceeds u * S, else the last one
-    const double target = ((double)s / 4294967296.0) * run;
-    const uint64_t over = __ballot(t < k && target < mine);
-    const int pick = over ? __ffsll((unsigned long long)over) - 1 : k - 1;
-    tok = __builtin_amdgcn_readlane(id, pick);
-  }
-  if (t == 0) {
-    *state = s;
-    *token = tok;
-  }
+  draw_from_top(lists + top_at, k, temperature, state_in, logits, state, token, topk_ids,
+                topk_vals);
 }
 
 // Stage 1: block b keeps the first k keys of its logits in workspace slots
@@ -373,6 +409,283 @@ __global__ __launch_bounds__(kSampleThreads) void topk_select_kernel(
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_vals) {
   __shared__ uint64_t lists[kMaxCandidates];
   select_and_draw(logits, ws, n_lists, k, temperature, state, token, topk_ids, topk_vals, lists);
+}
+
+// ---------------------------------------------------------------------------
+// Sampling fused onto a matvec that leaves, per vector, one slot per
+// workgroup holding the largest key of the rows that workgroup stored (the
+// F8 head's pass; f8.hip).  Workgroup (group) g owns the rows
+//   g gstride + t S + i   for t >= 0 and i < L with i < l_valid, below R,
+// rows_pg of them at most, and a row r belongs to group (r / gstride) % G.
+//
+// Why the slots suffice: a logit >= X lies in a group whose slot key is >= X.
+// Let H be the k-th largest of 256 maxima of 32 slots each: those k maxima
+// are k distinct logits >= H, so the k-th largest logit is >= H, and each of
+// the k best logits lies in a group whose slot key is >= H.  One workgroup
+// reads only those groups' rows (about k groups of rows_pg rows on the
+// head's logits; 32 k groups at most) instead of the whole vector.  Where
+// their rows would not fit its LDS, it narrows them first to the k groups of
+// the k largest slot keys, T the k-th of them.
+struct SlotRows {
+  int64_t R;        // rows of a vector
+  int n_slots;      // groups (slots) per vector, <= kSlotCapacity
+  int G;            // the group of row r is (r / gstride) % G
+  int gstride;      // first row of group g: g gstride
+  int log2_L;       // rows of a run: L = 2^log2_L, the first l_valid of them real
+  int l_valid;
+  int64_t S;        // run t starts at g gstride + t S
+  int log2_pg;      // 2^log2_pg >= the positions of a group's rows (runs of L)
+  int rows_pg;      // positions of a group that are rows: [0, rows_pg)
+};
+constexpr int kSlotCapacity = 8192;
+constexpr int kSlotLoads = kSlotCapacity / kSampleThreads;
+// Slots that pass the first bound: 32 k at most (H real: the keys >= H lie in
+// the k sets of 32 whose maxima are >= H), or every real slot where fewer
+// than k of the 256 sets hold one (then fewer than 256 slots are real).
+constexpr int kMaxPass = 32 * kMaxK;
+
+// The first min(k, m) of m distinct keys keys[0 .. m) (m <= kMaxCandidates),
+// descending, in LDS; returns where they start.  Up to 256 keys are ranked by
+// counting, more are sorted in lists of 64 and merged.  Every thread calls it
+// after the keys are written (it begins with a barrier).
+__device__ int block_first_k(uint64_t* keys, int m, int k, int (*part)[256]) {
+  const int t = threadIdx.x, wave = t >> 6, l = t & 63;
+  if (m <= kRankMax) {
+    if (t == m && (m & 1)) keys[m] = 0;  // the counting reads keys in pairs
+    __syncthreads();
+    const int rank = block_rank(keys, m, part);
+    if (t < m && rank < k) keys[kTopSlot + rank] = keys[t];
+    __syncthreads();
+    return kTopSlot;
+  }
+  const int n_lists = (m + 63) / 64;
+  for (int i = m + t; i < 64 * n_lists; i += kSampleThreads) keys[i] = (uint64_t)i;  // below all
+  __syncthreads();
+  for (int li = wave; li < n_lists; li += kSampleThreads / 64) {
+    uint64_t v[1] = {keys[64 * li + l]};
+    wave_sort_desc<1>(v);
+    keys[64 * li + l] = v[0];
+  }
+  block_merge_lists(keys, n_lists);
+  return 0;
+}
+
+// Appends the keys whose pass flag is set to out[] (and idx[] to out_idx[]
+// at the same places, if given), at offsets taken from an LDS counter once
+// per wavefront (the wavefront's count from ballots, each
+// lane's place from the lanes below it): the order of the packed keys
+// depends on scheduling, the set does not.
+template <int N>
+__device__ __forceinline__ void wave_pack(const bool (&pass)[N], const uint64_t (&key)[N],
+                                          int* counter, uint64_t* out,
+                                          const int* idx = nullptr, int* out_idx = nullptr) {
+  uint64_t mask[N];
+  int n = 0;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    mask[j] = __ballot(pass[j]);
+    n += __popcll(mask[j]);
+  }
+  if (n == 0) return;  // uniform
+  int base = 0;
+  if ((threadIdx.x & 63) == 0) base = atomicAdd(counter, n);
+  base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const uint32_t lo = (uint32_t)mask[j], hi = (uint32_t)(mask[j] >> 32);
+    const int below = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0));
+    if (pass[j]) {
+      out[base + below] = key[j];
+      if (idx) out_idx[base + below] = idx[j];
+    }
+    base += __popcll(mask[j]);
+  }
+}
+
+// The first k of up to 128 distinct keys keys[0 .. m), ranked by one
+// wavefront: a key's rank is the number of larger keys (each lane counts for
+// keys l and l + 64, reading every key as a broadcast); the first k go to
+// out[rank] and lane l returns out[l] (0 past min(k, m)).  out must not
+// overlap keys[0 .. m).
+__device__ __forceinline__ uint64_t wave_rank_small(const uint64_t* keys, int m, int k,
+                                                    uint64_t* out) {
+  const int l = threadIdx.x & 63;
+  const uint64_t a = l < m ? keys[l] : 0, b = l + 64 < m ? keys[l + 64] : 0;
+  int ra = 0, rb = 0;
+  const ulonglong2* p = reinterpret_cast<const ulonglong2*>(keys);
+  int u = 0;
+  for (; 2 * u + 8 <= m; u += 4) {
+    ulonglong2 r[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = p[u + q];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ra += (r[q].x > a) + (r[q].y > a);
+      rb += (r[q].x > b) + (r[q].y > b);
+    }
+  }
+  for (int j = 2 * u; j < m; ++j) {
+    const uint64_t kj = keys[j];
+    ra += kj > a;
+    rb += kj > b;
+  }
+  if (l < m && ra < k) out[ra] = a;
+  if (l + 64 < m && rb < k) out[rb] = b;
+  __builtin_amdgcn_wave_barrier();
+  return l < min(k, m) ? out[l] : 0;
+}
+
+// One workgroup per vector b: the k best logits of logits[b][0 .. R) and the
+// draw, from the vector's slots (slot keys are >= 2^31; a smaller one marks
+// a group with no rows).  Phases: the slots and H (counting over the 256
+// maxima); the slots >= H packed by an LDS counter (their order there is
+// immaterial: what follows depends only on the keys); the candidates (the
+// rows of those groups with keys >= H, or >= T), packed the same way; their
+// first k (one wavefront where at most 128 passed, else the workgroup); the
+// draw.
+__global__ __launch_bounds__(kSampleThreads) void slots_sample_kernel(
+    const float* __restrict__ logits, const uint64_t* __restrict__ slots, SlotRows g, int k,
+    float temperature, uint32_t* __restrict__ state, int32_t* __restrict__ token,
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_vals) {
+  __shared__ __align__(16) uint64_t lists[kMaxCandidates];
+  __shared__ int part[4][256];
+  __shared__ int grp[kMaxPass];
+  __shared__ uint64_t bound, thr;
+  __shared__ int n_pass, n_cand;
+  const int t = threadIdx.x, wave = t >> 6;
+  const int64_t b = blockIdx.x;
+  logits += b * g.R;
+  slots += b * kSlotCapacity;
+  state += b;
+  token += b;
+  topk_ids += b * k;
+  topk_vals += b * k;
+  const uint32_t state_in = wave == 0 ? *state : 0u;  // requested first
+  constexpr uint64_t kReal = uint64_t(1) << 31;
+  if (t == 0) n_pass = n_cand = 0;  // ordered before their atomics by the barriers below
+
+  // the slots, all of a thread's loads issued at once (clamped index, then
+  // the select), and each thread's largest real one (t where it has none:
+  // distinct, below every real key)
+  uint64_t sk[kSlotLoads];
+#pragma unroll
+  for (int j = 0; j < kSlotLoads; ++j) {
+    const int i = j * kSampleThreads + t;
+    sk[j] = slots[min(i, g.n_slots - 1)];
+    sk[j] = (i < g.n_slots && sk[j] >= kReal) ? sk[j] : 0;
+  }
+  uint64_t mx = 0;
+#pragma unroll
+  for (int j = 0; j < kSlotLoads; ++j) mx = max(mx, sk[j]);
+  mx = mx ? mx : (uint64_t)t;
+  // maxima of 4 threads (32 slots each): 256 distinct keys; H = the k-th
+  // largest, found by counting (a key's rank is the number of larger ones)
+  mx = max(mx, key_xor<1>(mx));
+  mx = max(mx, key_xor<2>(mx));
+  if ((t & 3) == 0) lists[t >> 2] = mx;
+  __syncthreads();
+  if (block_rank(lists, 256, part) == k - 1 && t < 256) bound = lists[t];
+  __syncthreads();
+  const uint64_t H = bound;
+  // the real slots with keys >= H: keys packed into lists[0 .. m), their
+  // slot (group) numbers at the same places in grp
+  {
+    bool pass[kSlotLoads];
+    int idx[kSlotLoads];
+#pragma unroll
+    for (int j = 0; j < kSlotLoads; ++j) {
+      pass[j] = sk[j] >= kReal && sk[j] >= H;
+      idx[j] = j * kSampleThreads + t;
+    }
+    wave_pack<kSlotLoads>(pass, sk, &n_pass, lists, idx, grp);
+  }
+  __syncthreads();
+  const int m = n_pass;
+  // The groups to read and the threshold.  Where their rows fit, every group
+  // that passed, with H: each of the k best logits is >= T >= H and lies in
+  // a group whose slot key is >= T.  Otherwise T and the k groups of the k
+  // largest slot keys (every group that passed where fewer than k: then
+  // they are all the groups with rows, and T = 0 admits every row).
+  int n_grp = m;
+  if ((m << g.log2_pg) <= kMaxCandidates) {
+    if (t == 0) thr = H;
+  } else {
+    n_grp = min(m, k);
+    const int top_at = block_first_k(lists, m, k, part);
+    if (t < n_grp) {
+      const uint64_t key = lists[top_at + t];
+      grp[t] = (int)(0xffffffffu - (uint32_t)key) / g.gstride % g.G;
+      if (t == k - 1) thr = key;
+    }
+    if (t == 0 && m < k) thr = 0;
+  }
+  __syncthreads();
+  const uint64_t T = thr;
+  // candidates: the rows of those groups with keys >= T, every load issued
+  // before the first compare; positions past the groups' rows are skipped
+  // (at most kMaxCandidates positions, 16 per thread)
+  const int total = n_grp << g.log2_pg;
+  constexpr int kPosLoads = kMaxCandidates / kSampleThreads;
+  float v[kPosLoads];
+  int rw[kPosLoads];  // the row, or -1 (rows < 2^20)
+#pragma unroll
+  for (int j = 0; j < kPosLoads; ++j) {
+    rw[j] = -1;
+    v[j] = 0.0f;
+    if (j * kSampleThreads < total) {  // uniform
+      const int p = j * kSampleThreads + t;
+      const int gi = p >> g.log2_pg, within = p & ((1 << g.log2_pg) - 1);
+      const int run = within >> g.log2_L, i = within & ((1 << g.log2_L) - 1);
+      const int64_t row = (int64_t)grp[min(gi, kMaxPass - 1)] * g.gstride + run * g.S + i;
+      const bool ok = p < total && within < g.rows_pg && i < g.l_valid && row < g.R;
+      rw[j] = ok ? (int)row : -1;
+      v[j] = logits[ok ? row : 0];
+    }
+  }
+  {
+    uint64_t ck[kPosLoads];
+    bool pass[kPosLoads];
+#pragma unroll
+    for (int j = 0; j < kPosLoads; ++j) {
+      ck[j] = rw[j] >= 0 ? cand_key(v[j], (uint32_t)rw[j]) : 0;
+      pass[j] = rw[j] >= 0 && ck[j] >= T;
+    }
+    wave_pack<kPosLoads>(pass, ck, &n_cand, lists);
+  }
+  __syncthreads();
+  const int nc = n_cand;
+  if (nc <= 128) {
+    if (wave != 0) return;
+    const uint64_t key = wave_rank_small(lists, nc, k, lists + kTopSlot);
+    draw_from_key(key, k, temperature, state_in, logits, state, token, topk_ids, topk_vals);
+    return;
+  }
+  const int at = block_first_k(lists, nc, k, part);
+  if (wave != 0) return;
+  draw_from_top(lists + at, k, temperature, state_in, logits, state, token, topk_ids, topk_vals);
+}
+
+int launch_slots_sample(const float* logits, const uint64_t* slots, const SlotRowsHost& h,
+                        int64_t batch, int64_t k, float temperature, uint32_t* state,
+                        int32_t* token, int32_t* topk_ids, float* topk_logits, hipStream_t s) {
+  if (h.n_slots < 1 || h.n_slots > kSlotCapacity || h.rows_pg < 1 ||
+      (int64_t(1) << h.log2_pg) * kMaxK > kMaxCandidates || h.rows_pg > (1 << h.log2_pg) ||
+      h.log2_L > h.log2_pg || h.l_valid > (1 << h.log2_L) || h.G < 1 || h.gstride < 1 ||
+      k < 1 || k > kMaxK || batch < 1)
+    return BQD_EINVAL;  // a layout the kernel cannot take (never for validated calls)
+  SlotRows g;
+  g.R = h.R;
+  g.n_slots = (int)h.n_slots;
+  g.G = (int)h.G;
+  g.gstride = (int)h.gstride;
+  g.log2_L = h.log2_L;
+  g.l_valid = (int)h.l_valid;
+  g.S = h.S;
+  g.log2_pg = h.log2_pg;
+  g.rows_pg = (int)h.rows_pg;
+  hipLaunchKernelGGL(slots_sample_kernel, dim3((unsigned)batch), dim3(kSampleThreads), 0, s,
+                     logits, slots, g, (int)k, temperature, state, token, topk_ids, topk_logits);
+  return launch_status();
 }
 
 int launch_logits_sample(const float* logits, int64_t n, int64_t k, float temperature,

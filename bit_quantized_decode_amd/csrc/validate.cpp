@@ -220,6 +220,31 @@ int check_f8_argmax(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale
   return BQD_OK;
 }
 
+int check_f8_sample(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
+                    int64_t SC, const float* x, const float* y, int64_t batch, int64_t k,
+                    float temperature, const uint32_t* state, const void* workspace,
+                    int64_t workspace_bytes, const int32_t* token, const int32_t* topk_ids,
+                    const float* topk_logits) {
+  if (R < 1 || R > kMaxSampleLogits || k < 1 || k > kMaxSampleK || k > R) return BQD_EINVAL;
+  if (!(temperature >= 0.0f) || temperature > 3.4e38f) return BQD_EINVAL;  // NaN, < 0, inf
+  const int rc = check_f8(w, R, C, scale, SR, SC, x, y, batch);
+  if (rc || batch == 0) return rc;
+  if (!mul_ok(batch, kF8ArgmaxSlots, 8) || !mul_ok(batch, k, 4)) return BQD_EOVERFLOW;
+  const int64_t need = f8_argmax_workspace_need(batch);
+  if (workspace_bytes < need) return BQD_EINVAL;
+  if (!workspace || !state || !token || !topk_ids || !topk_logits) return BQD_ENULL;
+  if (!aligned(workspace, 8) || !aligned(state, 4) || !aligned(token, 4) ||
+      !aligned(topk_ids, 4) || !aligned(topk_logits, 4))
+    return BQD_EALIGN;
+  // the generator states are read and written: they count as outputs
+  const Span in[3] = {{w, R * C}, {scale, SR * SC}, {x, batch * C * 4}};
+  const Span out[6] = {{y, batch * R * 4},        {workspace, need},
+                       {state, batch * 4},        {token, batch * 4},
+                       {topk_ids, batch * k * 4}, {topk_logits, batch * k * 4}};
+  if (outputs_overlap(out, 6, in, 3)) return BQD_EINVAL;
+  return BQD_OK;
+}
+
 int check_i8(const int8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t G,
              const float* x, const float* y, int64_t batch) {
   if (R < 0 || R >= kMaxRows || C < 1 || C >= kMaxColumns || G < 1 || G > C || batch < 0)

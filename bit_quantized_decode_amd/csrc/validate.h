@@ -34,6 +34,15 @@ inline int64_t f8_argmax_workspace_need(int64_t batch) { return batch * kF8Argma
 int check_f8_argmax(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
                     int64_t SC, const float* x, const float* y, int64_t batch,
                     const void* workspace, int64_t workspace_bytes, const int32_t* token);
+// f8_matvec_sample: check_f8's rules, 1 <= R <= kMaxSampleLogits,
+// 1 <= k <= min(kMaxSampleK, R), a finite temperature >= 0, the workspace as
+// f8_matvec_argmax's, and state / token [batch], topk_ids / topk_logits
+// [batch][k] (4-byte aligned) as more outputs.
+int check_f8_sample(const uint8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t SR,
+                    int64_t SC, const float* x, const float* y, int64_t batch, int64_t k,
+                    float temperature, const uint32_t* state, const void* workspace,
+                    int64_t workspace_bytes, const int32_t* token, const int32_t* topk_ids,
+                    const float* topk_logits);
 int check_i8(const int8_t* w, int64_t R, int64_t C, const uint8_t* scale, int64_t G,
              const float* x, const float* y, int64_t batch);
 int check_kv_quantize(const float* v, int64_t n_vec, int64_t d, const int8_t* q,

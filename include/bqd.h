@@ -197,6 +197,37 @@ int f8_matvec_argmax(const uint8_t *w, int64_t R, int64_t C, const uint8_t *scal
                      int64_t SR, int64_t SC, const float *x, float *y, int64_t batch,
                      void *workspace, int64_t workspace_bytes, int32_t *token, void *stream);
 
+/* f8_matvec with top-k / temperature sampling of each vector's outputs
+ * fused onto the pass ([P4] work item 3 and "Step 3 done": the head's logits
+ * go straight to the sampler).  Per vector b, the results are those of
+ * logits_sample on y[b] with k, temperature and state[b], bit for bit:
+ * topk_ids[b][0..k) / topk_logits[b][0..k) the k best logits (larger value
+ * first, equal values at the lower row, NaN after every number, -0 equal to
+ * +0), state[b] advanced one xorshift32 step, token[b] drawn as logits_sample
+ * draws it.  How: each workgroup of the matvec stores the largest (value,
+ * row) key of its rows to its slot of the workspace (as f8_matvec_argmax);
+ * then one workgroup per vector bounds the k-th largest logit from the
+ * slots and reads only the rows of the workgroups whose slots pass the bound
+ * (about k workgroups of 32 rows on the 246272-row head) instead of all R.
+ * No device atomics: the result does not depend on scheduling.
+ *   state:       uint32 [batch], read and written
+ *   workspace:   f8_matvec_argmax_workspace_bytes(batch) bytes, 8-byte
+ *                aligned, caller-owned, no initial contents needed; calls that
+ *                share it must be ordered on one stream
+ *   token:       int32 [batch]     topk_ids: int32 [batch][k]
+ *   topk_logits: fp32 [batch][k]
+ * Other arguments as f8_matvec.  Requires 1 <= R <= 2^20,
+ * 1 <= k <= min(64, R), 0 <= temperature < inf.
+ * Errors: as f8_matvec (BQD_EINVAL also for R, k, temperature or a workspace
+ * smaller than the need; BQD_EALIGN for a workspace not 8-byte aligned; the
+ * outputs y, workspace, state, token, topk_ids and topk_logits must not
+ * overlap one another or the inputs). */
+int f8_matvec_sample(const uint8_t *w, int64_t R, int64_t C, const uint8_t *scale,
+                     int64_t SR, int64_t SC, const float *x, float *y, int64_t batch,
+                     int64_t k, float temperature, uint32_t *state, void *workspace,
+                     int64_t workspace_bytes, int32_t *token, int32_t *topk_ids,
+                     float *topk_logits, void *stream);
+
 /* [P4] "Step 4 done" (the I8 matvec: int8 weights widened, one E8M0 scale
  * per group of consecutive columns; the page's groups are 16 wide):
  *   y[b][r] = sum over c < C of w[r][c] * e8m0(scale[r][c / G]) * x[b][c],

@@ -349,6 +349,44 @@ def test_f8_argmax_argument_rules():
     assert call(batch=-1) == EINVAL
 
 
+def test_f8_sample_argument_rules():
+    """f8_matvec_sample: f8_matvec's rules, 1 <= R <= 2^20, 1 <= k <= min(64,
+    R), a finite temperature >= 0, the argmax workspace, and every output
+    (y, workspace, states, tokens, ids, values) present, aligned and apart."""
+    L = bqd.lib()
+    need = L.f8_matvec_argmax_workspace_bytes(1)
+    W, S, X, Y, K, ST, T, I, V = (FAKE + (j << 24) for j in range(9))
+    def call(R=512, k=64, temp=0.8, ws=K, wsb=need, st=ST, tok=T, ids=I, vals=V, y=Y, batch=1,
+             C=4096):
+        return L.f8_matvec_sample(W, R, C, S, 4, 32, X, y, batch, k, temp, st, ws, wsb, tok, ids,
+                                  vals, None)
+    assert call(R=0, k=1) == EINVAL            # no row to take
+    assert call(R=(1 << 20) + 1) == EINVAL     # past the sampler's range
+    assert call(k=0) == EINVAL
+    assert call(k=65) == EINVAL
+    assert call(R=10, k=11) == EINVAL          # k > R
+    assert call(temp=-1.0) == EINVAL
+    assert call(temp=float("nan")) == EINVAL
+    assert call(temp=float("inf")) == EINVAL
+    assert call(wsb=need - 1) == EINVAL        # workspace too small
+    for kw in ("ws", "st", "tok", "ids", "vals"):
+        assert call(**{kw: None}) == ENULL, kw
+    assert call(ws=K + 4) == EALIGN            # slots are 8 bytes
+    for kw, base in (("st", ST), ("tok", T), ("ids", I), ("vals", V)):
+        assert call(**{kw: base + 2}) == EALIGN, kw
+    assert call(ws=Y + 8) == EINVAL            # workspace over y
+    assert call(st=K + 8) == EINVAL            # state over the workspace
+    assert call(tok=ST) == EINVAL              # token on the state
+    assert call(ids=T) == EINVAL               # ids over the token
+    assert call(vals=I + 64 * 4 - 4) == EINVAL  # values over the last id
+    assert call(ids=X + 16) == EINVAL          # ids over x
+    assert call(st=W + 100) == EINVAL          # state over the weights
+    assert call(batch=2, tok=ST + 4) == EINVAL  # two tokens over two states
+    assert call(batch=2) == EINVAL             # a workspace for one vector only
+    assert call(batch=0) == OK                 # nothing to do
+    assert call(batch=-1) == EINVAL
+
+
 def test_f8_i8_kv_outputs_overlapping_inputs_are_refused():
     L = bqd.lib()
     f8 = lambda w=A, s=B, x=C_, y=D: L.f8_matvec(w, 512, 4096, s, 4, 32, x, y, 1, None)

@@ -609,6 +609,197 @@ def test_f8_argmax_ties_nan_and_inf(C):
     assert check_f8_argmax(inf_case)[0] == 17
 
 
+# ---------------------------------------- F8 matvec with fused top-k sampling
+def host_topk_ids(y, k):
+    """Rows of the k best of y: a larger value first, equal values (+0 = -0)
+    at the lower row, NaN after every number."""
+    v = np.asarray(y, np.float64)
+    nan = np.isnan(v)
+    order = np.lexsort((np.arange(v.size), -np.where(nan, 0.0, v), nan))
+    return order[:k].astype(np.int32)
+
+
+def _states(seeds):
+    return torch.tensor(np.array(seeds, np.uint32).view(np.int32), dtype=torch.int32, device=DEV)
+
+
+def check_f8_sample(case, k, T, seeds, workspace=None):
+    """y bit-identical to f8_matvec's; per vector, the k ids those of y's k
+    best (an integer decision on the GPU's own values), the values y's at
+    them bit for bit, the state one xorshift32 step on, and ids, values,
+    token and state equal to logits_sample's on that y.  Returns
+    (y, tokens, ids, vals) as numpy arrays."""
+    w, s, x = dev_f8(case)
+    st = _states(seeds)
+    y, tok, ids, vals = bqd.f8_matvec_sample(w, s, x, k, T, st, workspace=workspace)
+    y0 = bqd.f8_matvec(w, s, x)
+    yn = y.cpu().numpy().reshape(-1, case.R)
+    assert bits_eq(yn, y0.cpu().numpy().reshape(-1, case.R))
+    tokn, idsn, valsn = tok.cpu().numpy(), ids.cpu().numpy(), vals.cpu().numpy()
+    stn = st.cpu().numpy().view(np.uint32)
+    for b in range(yn.shape[0]):
+        want = host_topk_ids(yn[b], k)
+        assert np.array_equal(idsn[b], want), (b, idsn[b][:8], want[:8])
+        assert bits_eq(valsn[b], yn[b][want])
+        assert int(stn[b]) == oracle.xorshift32(int(seeds[b]))
+        st2 = _states([seeds[b]])
+        t2, i2, v2 = bqd.logits_sample(y[b].reshape(-1) if y.dim() > 1 else y, k, T, st2)
+        assert np.array_equal(i2.cpu().numpy(), idsn[b])
+        assert bits_eq(v2.cpu().numpy(), valsn[b])
+        assert int(t2.item()) == int(tokn[b]) and int(st2.cpu().numpy().view(np.uint32)[0]) == stn[b]
+        if k == 1 or T == 0.0:
+            assert int(tokn[b]) == int(want[0])
+        else:
+            assert int(tokn[b]) in set(want.tolist())
+    return yn, tokn, idsn, valsn
+
+
+def test_f8_sample_head(cache):
+    """The 246272 x 4096 head with top-k sampling fused: the checks of
+    check_f8_sample, then against the oracle's logits (every row): the k
+    selected values are, in order, the k largest oracle logits within the
+    tolerance (the i-th largest moves by at most the largest row error), and
+    each selected logit is within tolerance of its own row's oracle value."""
+    case = workload(cache, "f8_head_246272x4096")
+    print("[case] f8 head with fused top-k sampling", flush=True)
+    ws = torch.full((bqd.f8_matvec_argmax_workspace_bytes(1),), 0xA5, dtype=torch.uint8, device=DEV)
+    ref, mag = oracle_all_rows(lambda a, c: oracle.f8_matvec(
+        case.w, case.R, case.C, case.scale, case.SR, case.SC, case.x[0], a, c), case.R)
+    tol = 1e-4 * mag + 1e-6
+    for k, T in ((64, 0.8), (1, 1.0), (8, 0.0), (17, 2.5)):
+        _, tok, ids, vals = check_f8_sample(case, k, T, [0x9E3779B9 + k], workspace=ws)
+        ids, vals = ids[0], vals[0].astype(np.float64)
+        assert np.all(np.abs(vals - ref[ids]) <= tol[ids])
+        ref_top = np.sort(ref)[::-1][:k]
+        assert np.all(np.abs(vals - ref_top) <= tol.max()), k
+        print(f"[case] head k={k} T={T}: token {int(tok[0])}, top id {int(ids[0])}", flush=True)
+
+
+def _exact_f8(R, C, seed, batch=1):
+    """F8 weights of exact small values (0, +-0.5, +-1, +-2; scale 2^0) and
+    integer activations in [-8, 8]: every product and partial sum is a
+    multiple of 0.5 below 2^23 in magnitude, so any summation order gives the
+    exact logit and the GPU's y equals the oracle's bit for bit (many equal
+    logits, so the order of ties is exercised too)."""
+    rng = np.random.default_rng(seed)
+    codes = np.array([0x00, 0x30, 0x38, 0x40, 0xB0, 0xB8, 0xC0], np.uint8)
+    case = synth.make_f8(R, C, 1, 1, seed=seed, batch=batch)
+    case.w[:] = codes[rng.integers(0, codes.size, (R, C), dtype=np.uint8)]
+    case.scale[:] = 127
+    case.x[:] = rng.integers(-8, 9, case.x.shape).astype(np.float32)
+    return case
+
+
+@pytest.mark.parametrize("R,C,k,T", [(246272, 4096, 64, 0.8), (50000, 4096, 33, 1.5),
+                                     (100000, 128, 64, 0.5), (3000, 100, 10, 0.9)])
+def test_f8_sample_exact_logits_equal_oracle(R, C, k, T):
+    """Where the logits are exact, the fused result equals the oracle's top-k
+    and draw on the oracle's own logits, over three chained draws."""
+    case = _exact_f8(R, C, seed=R + C)
+    print(f"[case] f8 sample exact {R}x{C} k={k} T={T}", flush=True)
+    ref, _ = oracle_all_rows(lambda a, c: oracle.f8_matvec(
+        case.w, case.R, case.C, case.scale, case.SR, case.SC, case.x[0], a, c), case.R)
+    ref = ref.astype(np.float32)
+    w, s, x = dev_f8(case)
+    seed = 0x12345 + R
+    st = _states([seed])
+    rid, rval = oracle.topk(ref, k)
+    for _ in range(3):
+        y, tok, ids, vals = bqd.f8_matvec_sample(w, s, x, k, T, st)
+        assert np.array_equal(y.cpu().numpy().reshape(-1), ref)
+        assert np.array_equal(ids.cpu().numpy()[0], rid)
+        assert np.array_equal(vals.cpu().numpy()[0], rval)
+        rtok, seed = oracle.sample(rval, rid, T, seed)
+        assert int(st.cpu().numpy().view(np.uint32)[0]) == seed
+        if int(tok[0].item()) != rtok:
+            assert _near_cdf_boundary(rval, T, seed / 2**32), (int(tok[0].item()), rtok)
+
+
+@pytest.mark.parametrize("j", range(12))
+def test_f8_sample_random_shapes(j):
+    """Random shapes through the streaming kernel (C a multiple of 16) and the
+    generic one, batches of 1-3 with a state each, k from 1 to min(64, R)."""
+    rng = np.random.default_rng(9500 + j)
+    R = int(rng.integers(1, 70000)) if j % 3 else int(rng.integers(1, 300))
+    C = int(16 * rng.integers(1, 300)) if rng.random() < 0.6 else int(rng.integers(1, 2000))
+    SR = int(rng.integers(1, min(R, 64) + 1))
+    SC = int(rng.choice([d for d in range(1, min(C, 64) + 1) if C % d == 0]))
+    batch = int(rng.choice([1, 1, 2, 3]))
+    k = int(rng.integers(1, min(64, R) + 1))
+    T = float(rng.choice([0.0, 0.6, 1.0, 3.0]))
+    print(f"[case] f8 sample {R}x{C} scales {SR}x{SC} batch {batch} k {k} T {T}", flush=True)
+    case = synth.make_f8(R, C, SR, SC, seed=9600 + j, batch=batch)
+    check_f8_sample(case, k, T, [int(v) for v in rng.integers(1, 2**32, batch)])
+
+
+def _grouped_f8(R, C, rows, seed, tied):
+    """Weights zero except on `rows` (codes 1.0-1.875 on the first 16 columns,
+    the same codes on every such row if tied), activations positive: the
+    large logits sit in chosen rows, all other logits are 0."""
+    rng = np.random.default_rng(seed)
+    case = synth.make_f8(R, C, 1, 1, seed=seed)
+    case.w[:] = 0
+    case.scale[:] = 127
+    if tied:
+        case.w[np.ix_(rows, np.arange(16))] = rng.integers(0x38, 0x40, 16).astype(np.uint8)
+    else:
+        case.w[np.ix_(rows, np.arange(16))] = rng.integers(0x38, 0x40, (rows.size, 16)).astype(np.uint8)
+    case.x[:] = np.abs(case.x) + 0.25
+    return case
+
+
+@pytest.mark.parametrize("tied", [False, True])
+@pytest.mark.parametrize("k", [64, 5])
+def test_f8_sample_top_rows_crowded_in_few_workgroups(tied, k):
+    """524288 rows of 128 columns: workgroup w of the streaming kernel stores
+    rows [64 w, 64 w + 64); the large logits fill the workgroups whose index
+    is below 4k modulo 1024, so the slots that pass the first bound crowd in
+    k sets of 32 (thousands of survivors: the sorted path); tied, the top
+    workgroups hold thousands of equal candidates (the sorted path again)."""
+    R, C = 524288, 128
+    wg = np.arange(R // 64)
+    sel = wg[(wg % 1024) < 4 * k]
+    rows = (64 * sel[:, None] + np.arange(64)[None, :]).reshape(-1)
+    case = _grouped_f8(R, C, rows, seed=31 + k, tied=tied)
+    print(f"[case] f8 sample crowded k={k} tied={tied}", flush=True)
+    check_f8_sample(case, k, 0.7, [4242 + k])
+
+
+@pytest.mark.parametrize("C", [4096, 100])
+def test_f8_sample_ties_nan_and_inf(C):
+    """Every logit 0 (the first k rows, in order), every logit NaN (NaN
+    values, the first k rows), +inf in three rows (those first, by row, and
+    the token the first since the top value is not finite)."""
+    case = synth.make_f8(300, C, 1, 4, seed=94)
+    case.w[:] = 0x00
+    _, _, ids, vals = check_f8_sample(case, 20, 1.0, [5])
+    assert np.array_equal(ids[0], np.arange(20))
+    nan_case = synth.make_f8(300, C, 3, 4, seed=95)
+    nan_case.x[0, 7] = np.nan
+    _, tok, ids, vals = check_f8_sample(nan_case, 7, 1.0, [6])
+    assert np.array_equal(ids[0], np.arange(7)) and np.isnan(vals[0]).all()
+    inf_case = synth.make_f8(300, C, 3, 4, seed=96)
+    inf_case.w[:, 3] = 0x00
+    inf_case.w[[40, 17, 250], 3] = 0x38
+    inf_case.x[0, 3] = np.inf
+    _, tok, ids, _ = check_f8_sample(inf_case, 5, 1.0, [7])
+    assert list(ids[0][:3]) == [17, 40, 250] and int(tok[0]) == 17
+
+
+def test_f8_sample_workspace_reuse_and_batch(cache):
+    """One workspace holding garbage, reused: a batch of 3 vectors (a state
+    each), then a smaller call, then the first again with the same results."""
+    case = synth.make_f8(20000, 4096, 157, 32, seed=97, batch=3)
+    small = synth.make_f8(700, 512, 7, 8, seed=98)
+    ws = torch.full((bqd.f8_matvec_argmax_workspace_bytes(3),), 0x5A, dtype=torch.uint8, device=DEV)
+    a = check_f8_sample(case, 64, 0.9, [11, 22, 33], workspace=ws)
+    check_f8_sample(small, 9, 0.9, [44], workspace=ws)
+    b = check_f8_sample(case, 64, 0.9, [11, 22, 33], workspace=ws)
+    for u, v in zip(a, b):
+        assert np.array_equal(np.asarray(u).view(np.uint32) if u.dtype == np.float32 else u,
+                              np.asarray(v).view(np.uint32) if v.dtype == np.float32 else v)
+
+
 def test_f8_wkv(cache):
     check_f8(workload(cache, "f8_wkv_512x4096"))
 
@@ -1211,12 +1402,12 @@ def test_empty_problems_are_no_ops():
 def test_graph_replay_matches_eager_beyond_the_path(cache):
     """The entry points beyond the five workloads captured in one HIP graph:
     the fused prepare + matvec, several matrices in one launch, the I8 matvec,
-    storeInt8 and the key dot, the Hadamard MLP, the sampler and the F8 matvec
-    with its fused argmax.  Every replay, with eager fills and
+    storeInt8 and the key dot, the Hadamard MLP, the sampler, the F8 matvec
+    with its fused argmax and with its fused top-k sampling.  Every replay, with eager fills and
     synchronizations between replays, equals the eager result bitwise; the
-    sampler's state is reset before each replay and then holds the eager
-    state after one draw; the argmax's workspace is filled with garbage
-    before each replay (nothing in it needs clearing)."""
+    samplers' states are reset before each replay and then hold the eager
+    states after one draw; the fused kernels' workspaces are filled with
+    garbage before each replay (nothing in them needs clearing)."""
     c4 = workload(cache, "cq4_16384x4096_b8")
     m4 = dev_matrix(c4)
     x1 = to_dev(c4.x[:1])
@@ -1249,6 +1440,13 @@ def test_graph_replay_matches_eager_beyond_the_path(cache):
     yk = torch.empty(1, 1000, device=DEV)
     ho = torch.empty_like(hn)
     sampled = []
+    ff = synth.make_f8(70000, 4096, 70, 32, seed=886)
+    wf, sf, xf = dev_f8(ff)
+    fws = torch.empty(bqd.f8_matvec_argmax_workspace_bytes(1), dtype=torch.uint8, device=DEV)
+    yf = torch.empty(1, ff.R, device=DEV)
+    fseed = 0x7654321
+    fstate = _state_tensor(fseed)
+    fused = []
 
     def work():
         bqd.cq_prepare_matvec(m4, x1, prepared=p1, out=y1)
@@ -1259,13 +1457,16 @@ def test_graph_replay_matches_eager_beyond_the_path(cache):
         bqd.hadamard_mlp(hn, 2048, d1, d2, d3, hr, hu, out=ho)
         sampled.append(bqd.logits_sample(logits, 16, 0.9, state, ws))
         bqd.f8_matvec_argmax(wa, sa, xa, workspace=aws, out=ya, token=ta)
+        fused.append(bqd.f8_matvec_sample(wf, sf, xf, 24, 0.7, fstate, workspace=fws, out=yf)[1:])
 
-    outs = lambda: [p1, y1, pm, *ym, yi, q, qs, yk, ho, ya, ta]
+    outs = lambda: [p1, y1, pm, *ym, yi, q, qs, yk, ho, ya, ta, yf]
     work()
     torch.cuda.synchronize()
     ref = [t.clone() for t in outs()]
     ref_draw = [t.clone() for t in sampled[-1]]
+    ref_fused = [t.clone() for t in fused[-1]]
     ref_state = state.clone()
+    ref_fstate = fstate.clone()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -1276,18 +1477,24 @@ def test_graph_replay_matches_eager_beyond_the_path(cache):
     with torch.cuda.graph(graph):
         work()
     draw = sampled[-1]
+    fdraw = fused[-1]
     for _ in range(4):
-        for t in outs() + list(draw):
+        for t in outs() + list(draw) + list(fdraw):
             t.fill_(-1)
         aws.fill_(0xA5)
+        fws.fill_(0x5A)
         state.copy_(_state_tensor(seed))
+        fstate.copy_(_state_tensor(fseed))
         graph.replay()
         torch.cuda.synchronize()
         for t, r in zip(outs(), ref):
             assert torch.equal(t, r)
         for t, r in zip(draw, ref_draw):
             assert torch.equal(t, r)
+        for t, r in zip(fdraw, ref_fused):
+            assert torch.equal(t, r)
         assert torch.equal(state, ref_state)
+        assert torch.equal(fstate, ref_fstate)
 
 
 def test_graph_replay_matches_eager(cache):
