@@ -1,8 +1,8 @@
 /*
  * A plain C caller of the library (test infrastructure): it includes only
  * bqd.h and the HIP runtime API, reads raw inputs from a directory, runs
- * cq_prepare_matvec, cq_gather_rows, f8_matvec, logits_sample and
- * f8_matvec_argmax on a stream of its own, and writes the outputs back to the
+ * cq_prepare_matvec, cq_gather_rows, f8_matvec, logits_sample,
+ * f8_matvec_argmax and f8_matvec_sample on a stream of its own, and writes the outputs back to the
  * directory for the test to compare with the oracle.
  *
  * usage: caller DIR
@@ -13,7 +13,10 @@
  * FR x FC), f8_s.bin (uint8 SR x SC), f8_x.bin (float FC), logits.bin (float NL),
  * state.bin (uint32).
  * Outputs: prepared.bin, y.bin, gathered.bin, f8_y.bin, token.bin, topk_ids.bin,
- * topk_logits.bin, state_out.bin, argmax_y.bin, argmax_token.bin.
+ * topk_logits.bin, state_out.bin, argmax_y.bin, argmax_token.bin, sample_y.bin,
+ * sample_token.bin, sample_ids.bin, sample_logits.bin, sample_state_out.bin
+ * (f8_matvec_sample: top K of the F8 matvec's outputs, drawn at temperature
+ * 0.8 from its own copy of the initial state).
  */
 #include <stdio.h>
 #include <stdlib.h>
@@ -115,6 +118,7 @@ int main(int argc, char **argv)
     const float *fx = load_to_device("f8_x.bin", (size_t)FC * 4);
     const float *logits = load_to_device("logits.bin", (size_t)NL * 4);
     uint32_t *state = load_to_device("state.bin", 4);
+    uint32_t *sstate = load_to_device("state.bin", 4);
 
     float *prepared = device_zeros((size_t)Cp * 4);
     float *y = device_zeros((size_t)R * 4);
@@ -132,6 +136,11 @@ int main(int argc, char **argv)
     if (aws_bytes < 0)
         fail("f8_matvec_argmax_workspace_bytes", bqd_status_string((int)aws_bytes));
     void *aws = device_zeros((size_t)aws_bytes);
+    float *sy = device_zeros((size_t)FR * 4);
+    int32_t *stok = device_zeros(4);
+    int32_t *sids = device_zeros((size_t)K * 4);
+    float *svals = device_zeros((size_t)K * 4);
+    void *sws = device_zeros((size_t)aws_bytes);
 
     hipStream_t s;
     HIP_OK(hipStreamCreate(&s));
@@ -142,6 +151,8 @@ int main(int argc, char **argv)
     BQD_OK_(logits_sample(logits, NL, K, 0.8f, state, ws, ws_bytes, token, topk_ids, topk_logits,
                           s));
     BQD_OK_(f8_matvec_argmax(fw, FR, FC, fs, SR, SC, fx, ay, 1, aws, aws_bytes, atok, s));
+    BQD_OK_(f8_matvec_sample(fw, FR, FC, fs, SR, SC, fx, sy, 1, K, 0.8f, sstate, sws, aws_bytes,
+                             stok, sids, svals, s));
     HIP_OK(hipStreamSynchronize(s));
 
     save_from_device("prepared.bin", prepared, (size_t)Cp * 4);
@@ -154,6 +165,11 @@ int main(int argc, char **argv)
     save_from_device("state_out.bin", state, 4);
     save_from_device("argmax_y.bin", ay, (size_t)FR * 4);
     save_from_device("argmax_token.bin", atok, 4);
+    save_from_device("sample_y.bin", sy, (size_t)FR * 4);
+    save_from_device("sample_token.bin", stok, 4);
+    save_from_device("sample_ids.bin", sids, (size_t)K * 4);
+    save_from_device("sample_logits.bin", svals, (size_t)K * 4);
+    save_from_device("sample_state_out.bin", sstate, 4);
     HIP_OK(hipStreamDestroy(s));
     printf("caller: ok\n");
     return 0;

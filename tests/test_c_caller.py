@@ -6,8 +6,11 @@ API) builds and links against libbqd.so.
 GPU: that program, run as a child process on seeded inputs, returns what the
 oracle computes: the prepared vector, the gathered rows and the top-k bit for
 bit, the CQ and F8 matvecs within 1e-4 * sum|w*x| + 1e-6, the sampled
-token and advanced state of the oracle's draw, and from f8_matvec_argmax the
-F8 matvec's y bit for bit with the first of its largest rows as the token.
+token and advanced state of the oracle's draw, from f8_matvec_argmax the
+F8 matvec's y bit for bit with the first of its largest rows as the token,
+and from f8_matvec_sample that y again with its k best rows (value, then
+row) and their values bit for bit, the state one xorshift step on and a
+token among those rows.
 """
 import os
 import subprocess
@@ -70,7 +73,7 @@ def test_c_caller_matches_oracle(tmp_path):
     for name, a in files.items():
         np.ascontiguousarray(a).tofile(tmp_path / name)
     print("[case] C caller: cq_prepare_matvec, cq_gather_rows, f8_matvec, logits_sample, "
-          "f8_matvec_argmax", flush=True)
+          "f8_matvec_argmax, f8_matvec_sample", flush=True)
     r = subprocess.run([str(exe), str(tmp_path)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     got = lambda name, dt: np.fromfile(tmp_path / name, dtype=dt)
@@ -94,3 +97,10 @@ def test_c_caller_matches_oracle(tmp_path):
     assert not np.isnan(fy).any()
     assert np.array_equal(got("argmax_y.bin", np.uint32), fy.view(np.uint32))
     assert int(got("argmax_token.bin", np.int32)[0]) == int(np.argmax(fy))
+    assert np.array_equal(got("sample_y.bin", np.uint32), fy.view(np.uint32))
+    want = np.lexsort((np.arange(fy.size), -fy.astype(np.float64)))[:k]
+    sids = got("sample_ids.bin", np.int32)
+    assert np.array_equal(sids, want)
+    assert np.array_equal(got("sample_logits.bin", np.uint32), fy[want].view(np.uint32))
+    assert int(got("sample_state_out.bin", np.uint32)[0]) == s1
+    assert int(got("sample_token.bin", np.int32)[0]) in set(want.tolist())
