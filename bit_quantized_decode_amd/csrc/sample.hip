@@ -34,10 +34,15 @@
 // wavefronts, with no sorting network.  More survivors are sorted and merged;
 // where a list may hold more than 8 such keys, or more than 1024 survive, or
 // there are fewer than k lists, every list is merged in full instead.  The
-// token is drawn in fp64 in one wavefront's registers.  The k values are
-// rebuilt from the keys (the order map is invertible except for the sign of
-// zero and NaN payloads; those few are re-read from the logits), so they are
-// copied bit for bit.
+// token is drawn in fp64 by one wavefront (one weight per lane, the sums over
+// LDS broadcasts).  The k values are rebuilt from the keys (the order map is
+// invertible except for the sign of zero and NaN payloads; those few are
+// re-read from the logits), so they are copied bit for bit.
+//
+// The same selection and draw also run fused onto a matvec that leaves one
+// slot per workgroup (the largest key of the rows it stored): one launch then
+// reads only the rows of the workgroups whose slots can hold a top-k logit
+// (slots_sample_kernel below), with the same results.
 #include <math.h>
 
 #include <mutex>
