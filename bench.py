@@ -820,6 +820,32 @@ def main():
         us_mean=round(float(ms.mean() * 1e3), 3), us_median=round(float(np.median(ms) * 1e3), 3),
         logits=logits.numel(), k=64, temperature=0.8, launches=2,
         note="not part of the step: the sampler over the head's logits")
+    # The plain read probe at the batch-1 CQ4 stage's size (34,078,720 bytes,
+    # 16 rotating copies, graphs of 16 launches as the stages): what one cold
+    # launch of that size reads in without any decode.
+    nb = 34078720
+    bufs = [torch.full((nb // 4,), 0x3C5A96E1 + j, dtype=torch.int32, device="cuda")
+            for j in range(16)]
+    xo = torch.empty(bqd.READ_STREAM_WORDS, dtype=torch.int32, device="cuda")
+    g = capture(torch, lambda: [bqd.dbg_read_stream(bufs[j % 16], xo)
+                                for j in range(STAGE_LAUNCHES)])
+    g.replay()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) / STAGE_LAUNCHES
+    extras["read_stream_34078720_bytes"] = dict(
+        us_mean=round(float(ms.mean() * 1e3), 3), us_median=round(float(np.median(ms) * 1e3), 3),
+        bytes=nb, gbs=round(nb / (ms.mean() * 1e-3) / 1e9, 1),
+        frac_hbm=round(nb / (ms.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        note="not part of the step: the plain read probe (no decode) over the bytes of the "
+             "batch-1 CQ4 16384x4096 stage, cold, the reference for one launch of that size")
+    del bufs, xo, g
+    torch.cuda.synchronize()
     # The achievable-HBM reference: the library's plain read probe over 2 GiB
     # (past the Infinity Cache), median of 8 timed calls.
     buf = torch.full((1 << 29,), 0x5A3C96E1, dtype=torch.int32, device="cuda")
