@@ -313,13 +313,24 @@ def build_cases(torch, bqd, synth, hot, heads=True):
 
 
 def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo, with its family, model
+    and stepping numbers (a virtualized host may report a bare name)."""
+    fields = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                key, val = (t.strip() for t in line.split(":", 1))
+                if key in ("model name", "cpu family", "model", "stepping") and key not in fields:
+                    fields[key] = val
+            elif fields:
+                break  # the first processor's block is enough
     except OSError:
-        pass
-    return None
+        return None
+    name = fields.get("model name")
+    if name is None:
+        return None
+    ids = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields]
+    return f"{name} ({', '.join(ids)})" if ids else name
 
 
 def cpu_baseline(data, threads):
